@@ -1,0 +1,136 @@
+/*
+ * specverify.h -- C ABI of libspecverify, the verify step of speculative
+ * sampling (modified rejection sampling) on AMD MI355X (gfx950).
+ *
+ * What one call computes, per request b of a batch of B (the pages:
+ *   [P1] "Speculative Decoding（投機的デコーディング）— 小さなモデルでLLM推論を高速化する",
+ *   [P2] "論文解説: Fast Inference from Transformers via Speculative Decoding",
+ *   [P3] "投機的デコーディングとは：同時リクエストが多いと遅くなる理由",
+ *   [P4] "LLM推測デコーディング最適化実踐"):
+ *
+ *   1. p_i = softmax(z_p[b,i,:] / T) for the gamma_b+1 target rows and
+ *      q_i = softmax(z_q[b,i,:] / T) for the gamma_b draft rows, one T for both
+ *      (P2 code sketch; P4 section 検証アルゴリズムの実装).
+ *   2. draft token x_i is accepted iff u_accept[b,i] < min(1, p_i(x_i)/q_i(x_i))
+ *      (P1 section ステップ3: 受理・棄却判定; P2 section 投機的サンプリング
+ *      アルゴリズム, accept equation).
+ *   3. k = index of the first rejection (gamma_b if none); drafts 0..k-1 are
+ *      emitted, later drafts are discarded (P1 section ステップ3).
+ *   4. if k < gamma_b the token at position k is drawn from
+ *      max(0, p_k - q_k) / sum max(0, p_k - q_k) (P1 section 修正分布の定義;
+ *      P2 modified-distribution equation); if that mass is exactly zero the draw
+ *      falls back to p_k (P1 simulation code).  If k == gamma_b a bonus token
+ *      is drawn from p_{gamma_b} (P1 section ステップ3; P4 bonus draw).
+ *      The draw is the inverse CDF in vocabulary order with the one supplied
+ *      uniform u_sample[b]: the smallest v with u*Z < w[0] + ... + w[v].
+ *   5. T == 0 selects greedy verification: x_i is accepted iff it equals the
+ *      lowest-index arg-max of target row i, and the token at position k is the
+ *      arg-max of target row k (P2 section 実装のポイント; P3 worked example in
+ *      section 先読みは、一回の順伝播で進むトークンを増やす).  Greedy requests
+ *      read neither draft logits nor uniforms.
+ *
+ * Outputs: accepted_count[b] = k (number of accepted drafts, 0..gamma_b);
+ * out_tokens[b][0..k] = the k accepted drafts followed by the sampled token;
+ * out_tokens[b][k+1..gamma] = -1.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_logits, draft_tokens, u_*, accepted_count, out_tokens,
+ *     workspace and the spec_verify_ex temperature / draft_lens arrays are
+ *     DEVICE pointers (hipMalloc'd or torch tensors on the GPU).  The caller
+ *     owns all of them; the library allocates nothing and keeps no state.
+ *   - Layouts are dense row-major: target_logits [B][gamma+1][V],
+ *     draft_logits [B][gamma][V], draft_tokens / u_accept [B][gamma],
+ *     u_sample / accepted_count [B], out_tokens [B][gamma+1].  Logits may be
+ *     any element-aligned address; 16-byte aligned rows take the fast path.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronising.  Outputs are valid once the
+ *     stream reaches that point.
+ *   - Arguments are checked on the host before anything is enqueued; a failed
+ *     check returns SV_EINVAL / SV_EWORKSPACE and touches nothing.  A failed
+ *     launch returns SV_EHIP.  Values that live in device memory (token ids in
+ *     [0, V), uniforms in [0, 1), per-request T >= 0 and finite, draft lengths
+ *     in [0, gamma]) are the caller's contract and are not checked.  Logits must
+ *     be finite on every row that the method reads (padding rows of ragged
+ *     requests are never read and may hold anything).
+ *   - Two calls may run concurrently only with distinct workspaces.
+ *   - Results are deterministic: identical inputs give bit-identical outputs.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of the logits */
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* return codes */
+enum {
+    SV_OK = 0,
+    SV_EINVAL = -1,     /* bad pointer, size, dtype or temperature           */
+    SV_EWORKSPACE = -2, /* workspace NULL, misaligned (256 B) or too small    */
+    SV_EHIP = -3        /* a HIP launch or runtime call failed                */
+};
+
+/* largest supported draft length gamma */
+#define SV_GAMMA_MAX 32
+
+/* Bytes of device workspace one call with these sizes needs (0 if the sizes are
+ * invalid).  The workspace must be 256-byte aligned; its contents on entry do
+ * not matter. */
+size_t spec_verify_workspace_bytes(int B, int gamma, int V, int dtype);
+
+/* Uniform batch: every request has gamma drafts and the same temperature.
+ * temperature: host scalar, >= 0 and finite; 0 = greedy for every request
+ *   (then draft_logits and u_accept may be NULL).
+ * B >= 1, 0 <= gamma <= SV_GAMMA_MAX, V >= 1, dtype one of sv_dtype. */
+int spec_verify(const void *target_logits, const void *draft_logits,
+                const int32_t *draft_tokens, const float *u_accept,
+                const float *u_sample, float temperature, int B, int gamma,
+                int V, int dtype, int32_t *accepted_count,
+                int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* Optional per-call diagnostics for tests and profiling (device pointers, any
+ * may be NULL; pass a NULL sv_debug in timed runs).  Entries that a request
+ * does not produce (e.g. draft probabilities of greedy requests, positions
+ * after the first rejection) are left untouched. */
+typedef struct {
+    double *p_draft;       /* [B][gamma] p_i(x_i)                                   */
+    double *q_draft;       /* [B][gamma] q_i(x_i)                                   */
+    double *accept_prob;   /* [B][gamma] min(1, p_i(x_i)/q_i(x_i))                   */
+    float *row_max;        /* [B][2*gamma+1] max logit; target rows 0..gamma first   */
+    double *row_sum;       /* [B][2*gamma+1] sum_v exp((z_v - max)/T)                */
+    int32_t *row_argmax;   /* [B][gamma+1] lowest-index arg-max of greedy target rows */
+    double *residual_mass; /* [B] Z, the mass of the distribution sampled at k       */
+    void *k1_events[2];    /* hipEvent_t pair recorded around the row-statistics
+                              kernel on `stream` (both or neither)                  */
+} sv_debug;
+
+/* Ragged / mixed batch.
+ * temperature: DEVICE array [B]; 0 = greedy request, else > 0 and finite.
+ * draft_lens:  DEVICE array [B] of gamma_b in [0, gamma], or NULL (= gamma);
+ *              gamma is then the padding stride of the draft dimension.
+ * dbg: NULL or diagnostics as above.
+ * draft_logits and u_accept must be non-NULL when gamma > 0 (greedy requests
+ * do not read them). */
+int spec_verify_ex(const void *target_logits, const void *draft_logits,
+                   const int32_t *draft_tokens, const float *u_accept,
+                   const float *u_sample, const float *temperature,
+                   const int32_t *draft_lens, int B, int gamma, int V,
+                   int dtype, int32_t *accepted_count, int32_t *out_tokens,
+                   void *workspace, size_t workspace_bytes, void *stream,
+                   const sv_debug *dbg);
+
+/* Static description of a return code. */
+const char *spec_verify_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,313 @@
+/*
+ * spec_verify_oracle.c -- plain CPU oracle for the verify step of speculative
+ * sampling (modified rejection sampling).
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this code.  The GPU library never calls it and shares
+ * no source with it.
+ *
+ * Style: one thread, IEEE fp64 for every value, every sum taken sequentially in
+ * vocabulary order, one step of the method after the other in the order the
+ * pages give.  Nothing is blocked, fused or reordered.  bf16 inputs are widened
+ * exactly (bf16 -> fp32 -> fp64); fp32 uniforms are widened exactly.
+ *
+ * What is computed, with the passage each step follows:
+ *
+ *   [P1] "Speculative Decoding（投機的デコーディング）— 小さなモデルでLLM推論を高速化する"
+ *        (disassemble-channel.com/speculative-decoding-theory/)
+ *   [P2] "論文解説: Fast Inference from Transformers via Speculative Decoding"
+ *        (0h-n0.github.io/posts/paper-2211-17192)
+ *   [P3] "投機的デコーディングとは：同時リクエストが多いと遅くなる理由"
+ *        (zvxbase.com/blog/speculative-decoding-draft-length-by-load/)
+ *   [P4] "LLM推測デコーディング最適化実踐" (toolsku.com), section 検証アルゴリズムの実装
+ *
+ *   - p_i = softmax(z_p[i] / T), q_i = softmax(z_q[i] / T), one T for target and
+ *     draft: P2 code sketch (softmax of logits / temperature on both models);
+ *     P4 section 検証アルゴリズムの実装 (same).  Target has gamma+1 rows (P4, the
+ *     slice of the last gamma+1 positions), draft has gamma rows.
+ *   - accept draft i with probability min(1, p_i(x_i) / q_i(x_i)); with a
+ *     supplied uniform u this is "accept iff u < min(1, p/q)": P1 section
+ *     ステップ3: 受理・棄却判定 (alpha_i equation) and the simulation's
+ *     comparison of a uniform draw against the acceptance probability; P2
+ *     section 投機的サンプリングアルゴリズム (accept equation).
+ *   - stop at the first rejection, keep the accepted prefix, discard the rest:
+ *     P1 section ステップ3 (bullet list after the alpha_i equation).
+ *   - on a rejection at position k, sample from
+ *     p'(x) = max(0, p_k(x) - q_k(x)) / sum_x' max(0, p_k(x') - q_k(x')):
+ *     P1 section 修正分布の定義 (the p' equation); P2 section 投機的サンプリング
+ *     アルゴリズム (modified-distribution equation).  If that sum is zero the
+ *     P1 simulation falls back to p (section Pythonによるシミュレーション実装);
+ *     this oracle does the same and raises a flag.
+ *   - if every draft is accepted, sample a bonus token from target row gamma:
+ *     P1 section ステップ3 (bonus sentence, garbled in the extraction) and the
+ *     simulation's final draw from p; P4 (bonus drawn from the last target row).
+ *   - T == 0 is greedy: draft i is accepted iff it equals argmax p_i, and the
+ *     emitted replacement / bonus is argmax of the target row: P2 section
+ *     実装のポイント (greedy decoding reduces acceptance to an argmax match); P3
+ *     worked example in section 先読みは、一回の順伝播で進むトークンを増やす.
+ *
+ * Readings where the pages are silent (each one is listed in the design notes):
+ *   R1 strict comparison u < a;  R2 no epsilon guards (q(x) = 0 gives ratio
+ *   +inf if p(x) > 0, else 0);  R4 zero residual mass falls back to p_k;
+ *   R5 sampling is the inverse CDF in vocabulary order with one supplied uniform:
+ *   the smallest v with u*Z < P(v), P(v) = w[0] + ... + w[v]; if rounding leaves
+ *   no such v the last v with w[v] > 0 is taken;  R6 one u_sample per request;
+ *   R7 accepted_count = number of accepted drafts (0..gamma_b); out[0..k] holds
+ *   the emitted tokens, later entries are -1;  R8 argmax ties go to the lowest
+ *   index;  R9 T is per request, T == 0 selects greedy;  R10 greedy requests do
+ *   not read draft logits or uniforms;  R11 the bonus uses target row gamma_b;
+ *   R12 ragged requests use rows 0..gamma_b only.
+ *
+ * Near-boundary flags (for parity comparison, not part of the method):
+ *   bit 0  some decided position i has |u_i - a_i| < 1e-6
+ *   bit 1  the sampled token's normalised CDF interval [C(v-1), C(v)) has u
+ *          within 1e-6 of one of its ends
+ *   bit 2  the zero-residual-mass fallback was used
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "spec_verify_oracle.h"
+
+#define BAND 1e-6
+
+/* ------------------------------------------------------------------ input access */
+static double widen(const void *base, int dtype, size_t idx)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[idx];
+    /* bf16: the 16 stored bits are the top half of an fp32 value */
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    const void *base;
+    int dtype;
+    size_t off; /* element offset of the row */
+    int V;
+} row_t;
+
+static double z_at(const row_t *r, int v) { return widen(r->base, r->dtype, r->off + (size_t)v); }
+
+static row_t target_row(const void *t, int dtype, int gamma, int V, int b, int i)
+{
+    row_t r = {t, dtype, ((size_t)b * (size_t)(gamma + 1) + (size_t)i) * (size_t)V, V};
+    return r;
+}
+
+static row_t draft_row(const void *d, int dtype, int gamma, int V, int b, int i)
+{
+    row_t r = {d, dtype, ((size_t)b * (size_t)gamma + (size_t)i) * (size_t)V, V};
+    return r;
+}
+
+/* ------------------------------------------------------------------ softmax(z / T) */
+/* m = max_v z[v];  s = sum_v exp((z[v] - m) / T);  p(v) = exp((z[v] - m) / T) / s.
+ * Subtracting the maximum changes nothing mathematically and keeps exp finite. */
+typedef struct {
+    double m, s, T;
+} softmax_t;
+
+static softmax_t softmax_stats(const row_t *r, double T)
+{
+    softmax_t st;
+    st.T = T;
+    st.m = z_at(r, 0);
+    for (int v = 1; v < r->V; ++v) {
+        double z = z_at(r, v);
+        if (z > st.m) st.m = z;
+    }
+    st.s = 0.0;
+    for (int v = 0; v < r->V; ++v)
+        st.s += exp((z_at(r, v) - st.m) / T);
+    return st;
+}
+
+static double prob(const row_t *r, const softmax_t *st, int v)
+{
+    return exp((z_at(r, v) - st->m) / st->T) / st->s;
+}
+
+/* ------------------------------------------------------------------ argmax */
+static int argmax_lowest(const row_t *r)
+{
+    int best = 0;
+    double bz = z_at(r, 0);
+    for (int v = 1; v < r->V; ++v) {
+        double z = z_at(r, v);
+        if (z > bz) { /* strict: equal values keep the earlier index */
+            bz = z;
+            best = v;
+        }
+    }
+    return best;
+}
+
+/* ------------------------------------------------------------------ acceptance */
+/* a = min(1, p(x) / q(x)), no epsilon guard. */
+static double accept_probability(double px, double qx)
+{
+    if (qx == 0.0) return px > 0.0 ? 1.0 : 0.0;
+    double ratio = px / qx;
+    return ratio < 1.0 ? ratio : 1.0;
+}
+
+/* ------------------------------------------------------------------ inverse CDF */
+/* Smallest v with u*Z < w[0] + ... + w[v]; Z = w[0] + ... + w[V-1].
+ * Returns the token; writes Z and the distance of u from the ends of the chosen
+ * token's normalised CDF interval. */
+static int inverse_cdf(const double *w, int V, double u, double *Z_out, double *margin)
+{
+    double Z = 0.0;
+    for (int v = 0; v < V; ++v) Z += w[v];
+    *Z_out = Z;
+    double target = u * Z;
+    double acc = 0.0;
+    int tok = -1;
+    double lo = 0.0, hi = 0.0;
+    for (int v = 0; v < V; ++v) {
+        double before = acc;
+        acc += w[v];
+        if (target < acc) {
+            tok = v;
+            lo = before;
+            hi = acc;
+            break;
+        }
+    }
+    if (tok < 0) { /* rounding left u*Z at or above the running total */
+        for (int v = V - 1; v >= 0; --v)
+            if (w[v] > 0.0) { tok = v; break; }
+        if (tok < 0) tok = V - 1;
+        *margin = 0.0;
+        return tok;
+    }
+    double c_lo = lo / Z, c_hi = hi / Z;
+    double m1 = u - c_lo, m2 = c_hi - u;
+    *margin = m1 < m2 ? m1 : m2;
+    return tok;
+}
+
+/* ------------------------------------------------------------------ one request */
+static void verify_request(const oracle_args *a, int b, double *w)
+{
+    const int gamma = a->gamma, V = a->V, dt = a->dtype;
+    const int g = a->lens ? a->lens[b] : gamma;
+    const double T = (double)a->temperature[b];
+    const int nrows = 2 * gamma + 1;
+    oracle_trace *tr = a->trace;
+    int32_t *out = a->out_tokens + (size_t)b * (size_t)(gamma + 1);
+    for (int i = 0; i <= gamma; ++i) out[i] = -1;
+    int flags = 0;
+    double acc_margin = INFINITY, cdf_margin = INFINITY, Zrep = NAN;
+
+    if (T == 0.0) {
+        /* greedy: accept while the draft equals the target arg-max */
+        int tmax[ORACLE_GAMMA_MAX + 1];
+        for (int i = 0; i <= g; ++i) {
+            row_t r = target_row(a->target, dt, gamma, V, b, i);
+            tmax[i] = argmax_lowest(&r);
+            if (tr && tr->row_argmax) tr->row_argmax[(size_t)b * (gamma + 1) + i] = tmax[i];
+        }
+        int k = g;
+        for (int i = 0; i < g; ++i) {
+            if (a->draft_tokens[(size_t)b * gamma + i] != tmax[i]) { k = i; break; }
+        }
+        for (int i = 0; i < k; ++i) out[i] = a->draft_tokens[(size_t)b * gamma + i];
+        out[k] = tmax[k];
+        a->accepted_count[b] = k;
+    } else {
+        /* softmax statistics of every row the method uses */
+        softmax_t sp[ORACLE_GAMMA_MAX + 1], sq[ORACLE_GAMMA_MAX];
+        for (int i = 0; i <= g; ++i) {
+            row_t r = target_row(a->target, dt, gamma, V, b, i);
+            sp[i] = softmax_stats(&r, T);
+            if (tr && tr->row_max) tr->row_max[(size_t)b * nrows + i] = sp[i].m;
+            if (tr && tr->row_sum) tr->row_sum[(size_t)b * nrows + i] = sp[i].s;
+        }
+        for (int i = 0; i < g; ++i) {
+            row_t r = draft_row(a->draft, dt, gamma, V, b, i);
+            sq[i] = softmax_stats(&r, T);
+            if (tr && tr->row_max) tr->row_max[(size_t)b * nrows + gamma + 1 + i] = sq[i].m;
+            if (tr && tr->row_sum) tr->row_sum[(size_t)b * nrows + gamma + 1 + i] = sq[i].s;
+        }
+        /* accept / reject in order; stop at the first rejection */
+        int k = g;
+        for (int i = 0; i < g; ++i) {
+            int x = a->draft_tokens[(size_t)b * gamma + i];
+            row_t rp = target_row(a->target, dt, gamma, V, b, i);
+            row_t rq = draft_row(a->draft, dt, gamma, V, b, i);
+            double px = prob(&rp, &sp[i], x);
+            double qx = prob(&rq, &sq[i], x);
+            double ai = accept_probability(px, qx);
+            double u = (double)a->u_accept[(size_t)b * gamma + i];
+            if (tr && tr->p_draft) tr->p_draft[(size_t)b * gamma + i] = px;
+            if (tr && tr->q_draft) tr->q_draft[(size_t)b * gamma + i] = qx;
+            if (tr && tr->accept_prob) tr->accept_prob[(size_t)b * gamma + i] = ai;
+            double d = fabs(u - ai);
+            if (d < acc_margin) acc_margin = d;
+            if (!(u < ai)) { k = i; break; }
+        }
+        for (int i = 0; i < k; ++i) out[i] = a->draft_tokens[(size_t)b * gamma + i];
+        a->accepted_count[b] = k;
+
+        /* the distribution of the emitted token at position k */
+        row_t rp = target_row(a->target, dt, gamma, V, b, k);
+        if (k < g) {
+            row_t rq = draft_row(a->draft, dt, gamma, V, b, k);
+            for (int v = 0; v < V; ++v) {
+                double diff = prob(&rp, &sp[k], v) - prob(&rq, &sq[k], v);
+                w[v] = diff > 0.0 ? diff : 0.0;
+            }
+        } else {
+            for (int v = 0; v < V; ++v) w[v] = prob(&rp, &sp[k], v);
+        }
+        double Z = 0.0;
+        for (int v = 0; v < V; ++v) Z += w[v];
+        if (Z == 0.0) { /* fallback to p_k */
+            flags |= 4;
+            for (int v = 0; v < V; ++v) w[v] = prob(&rp, &sp[k], v);
+        }
+        double m;
+        out[k] = inverse_cdf(w, V, (double)a->u_sample[b], &Zrep, &m);
+        cdf_margin = m;
+        if (m < BAND) flags |= 2;
+        if (acc_margin < BAND) flags |= 1;
+    }
+    if (tr && tr->residual_mass) tr->residual_mass[b] = Zrep;
+    if (tr && tr->flags) tr->flags[b] = flags;
+    if (tr && tr->accept_margin) tr->accept_margin[b] = acc_margin;
+    if (tr && tr->cdf_margin) tr->cdf_margin[b] = cdf_margin;
+}
+
+/* ------------------------------------------------------------------ entry point */
+int oracle_spec_verify(const oracle_args *a)
+{
+    if (!a || !a->target || !a->out_tokens || !a->accepted_count || !a->u_sample || !a->temperature)
+        return -1;
+    if (a->B < 1 || a->gamma < 0 || a->gamma > ORACLE_GAMMA_MAX || a->V < 1) return -1;
+    if (a->dtype != ORACLE_F32 && a->dtype != ORACLE_BF16) return -1;
+    if (a->gamma > 0 && !a->draft_tokens) return -1;
+    for (int b = 0; b < a->B; ++b) {
+        float T = a->temperature[b];
+        int g = a->lens ? a->lens[b] : a->gamma;
+        if (!(T >= 0.0f) || isinf(T)) return -1;
+        if (g < 0 || g > a->gamma) return -1;
+        if (T > 0.0f && g > 0 && (!a->draft || !a->u_accept)) return -1;
+        for (int i = 0; i < g; ++i) {
+            int x = a->draft_tokens[(size_t)b * a->gamma + i];
+            if (x < 0 || x >= a->V) return -1;
+        }
+    }
+    double *w = (double *)malloc(sizeof(double) * (size_t)a->V);
+    if (!w) return -2;
+    for (int b = 0; b < a->B; ++b) verify_request(a, b, w);
+    free(w);
+    return 0;
+}

@@ -1,0 +1,18 @@
+"""libspecverify: the verify step of speculative sampling on AMD MI355X (gfx950).
+
+The work happens in hand-written HIP kernels behind a C ABI
+(``include/specverify.h``).  ``binding`` marshals torch tensors to that ABI;
+``workloads`` builds the seeded synthetic inputs used by tests and the
+benchmark.
+"""
+from .binding import (  # noqa: F401
+    SV_BF16,
+    SV_F32,
+    LibraryMissing,
+    SpecVerifyError,
+    load_library,
+    spec_verify,
+    spec_verify_ex,
+    spec_verify_strerror,
+    spec_verify_workspace_bytes,
+)

@@ -1,0 +1,196 @@
+"""Thin ctypes binding of libspecverify (include/specverify.h).
+
+Argument marshalling only: shapes and dtypes are read off torch tensors, their
+device pointers and torch's current HIP stream are handed to the C ABI, and
+every step of the verify path runs in the library's HIP kernels.  There is no
+fallback: if the compiled library is missing the calls raise ``LibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SV_F32 = 0
+SV_BF16 = 1
+SV_GAMMA_MAX = 32
+
+SV_OK = 0
+SV_EINVAL = -1
+SV_EWORKSPACE = -2
+SV_EHIP = -3
+
+EXPORTED_SYMBOLS = (
+    "spec_verify_workspace_bytes",
+    "spec_verify",
+    "spec_verify_ex",
+    "spec_verify_strerror",
+)
+
+
+class LibraryMissing(RuntimeError):
+    """The compiled HIP library is not there (run ``__graft_entry__.build()``)."""
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where} failed: {spec_verify_strerror(code)} (code {code})")
+
+
+class SvDebug(ctypes.Structure):
+    _fields_ = [
+        ("p_draft", ctypes.c_void_p),
+        ("q_draft", ctypes.c_void_p),
+        ("accept_prob", ctypes.c_void_p),
+        ("row_max", ctypes.c_void_p),
+        ("row_sum", ctypes.c_void_p),
+        ("row_argmax", ctypes.c_void_p),
+        ("residual_mass", ctypes.c_void_p),
+        ("k1_events", ctypes.c_void_p * 2),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libspecverify.so; raises ``LibraryMissing`` if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise LibraryMissing(f"{path} not found: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spec_verify_workspace_bytes.restype = sz
+    lib.spec_verify.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32,
+                                vp, vp, vp, sz, vp]
+    lib.spec_verify.restype = i32
+    lib.spec_verify_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                   vp, vp, vp, sz, vp, ctypes.POINTER(SvDebug)]
+    lib.spec_verify_ex.restype = i32
+    lib.spec_verify_strerror.argtypes = [i32]
+    lib.spec_verify_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def spec_verify_strerror(code: int) -> str:
+    return load_library().spec_verify_strerror(int(code)).decode()
+
+
+def spec_verify_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_verify_workspace_bytes(B, gamma, V, dtype))
+
+
+# --------------------------------------------------------------------------- torch marshalling
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libspecverify must be contiguous")
+    return t.data_ptr()
+
+
+def _check_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libspecverify takes device tensors")
+
+
+def _shapes(target_logits):
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, gamma+1, V]")
+    B, g1, V = target_logits.shape
+    return int(B), int(g1) - 1, int(V)
+
+
+def _outputs(B, gamma, device, accepted_count, out_tokens):
+    import torch
+    if accepted_count is None:
+        accepted_count = torch.empty(B, dtype=torch.int32, device=device)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=device)
+    return accepted_count, out_tokens
+
+
+def _workspace(B, gamma, V, dt, device, workspace):
+    import torch
+    need = spec_verify_workspace_bytes(B, gamma, V, dt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def spec_verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature: float,
+                accepted_count=None, out_tokens=None, workspace=None, stream=None):
+    """Uniform batch (one temperature, gamma drafts per request).  Returns (accepted_count, out_tokens)."""
+    lib = load_library()
+    B, gamma, V = _shapes(target_logits)
+    dt = _dtype_code(target_logits)
+    _check_device(target_logits, draft_logits, draft_tokens, u_accept, u_sample)
+    accepted_count, out_tokens = _outputs(B, gamma, target_logits.device, accepted_count, out_tokens)
+    workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace)
+    rc = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
+                         _ptr(u_sample), float(temperature), B, gamma, V, dt,
+                         _ptr(accepted_count), _ptr(out_tokens), _ptr(workspace),
+                         workspace.numel(), _stream(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify")
+    return accepted_count, out_tokens
+
+
+def spec_verify_ex(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature,
+                   draft_lens=None, accepted_count=None, out_tokens=None, workspace=None,
+                   stream=None, debug: Optional[dict] = None, k1_events=None):
+    """Ragged / mixed batch: ``temperature`` and ``draft_lens`` are device tensors [B].
+
+    ``debug``: optional dict of preallocated device tensors keyed like ``sv_debug``.
+    ``k1_events``: optional pair of recorded ``torch.cuda.Event(enable_timing=True)``
+    that the library records around its row-statistics kernel.
+    """
+    lib = load_library()
+    B, gamma, V = _shapes(target_logits)
+    dt = _dtype_code(target_logits)
+    _check_device(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, draft_lens)
+    accepted_count, out_tokens = _outputs(B, gamma, target_logits.device, accepted_count, out_tokens)
+    workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace)
+    dbg = None
+    if debug or k1_events:
+        d = SvDebug()
+        for name in ("p_draft", "q_draft", "accept_prob", "row_max", "row_sum", "row_argmax",
+                     "residual_mass"):
+            t = (debug or {}).get(name)
+            setattr(d, name, _ptr(t))
+        if k1_events:
+            d.k1_events[0] = k1_events[0].cuda_event
+            d.k1_events[1] = k1_events[1].cuda_event
+        dbg = ctypes.pointer(d)
+    rc = lib.spec_verify_ex(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
+                            _ptr(u_sample), _ptr(temperature), _ptr(draft_lens), B, gamma, V, dt,
+                            _ptr(accepted_count), _ptr(out_tokens), _ptr(workspace), workspace.numel(),
+                            _stream(stream), dbg)
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_ex")
+    return accepted_count, out_tokens

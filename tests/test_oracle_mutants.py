@@ -1,0 +1,90 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins catch each one.
+
+Every mutant is the oracle source with one small edit (a dropped term, a wrong
+sign or index, a flipped comparison), compiled into a temporary library.  The
+pin tests of ``test_oracle_pins`` are then run against it; at least one of
+them must fail.  This runs on the CPU only.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = oracle.oracle.SRC
+
+MUTANTS = {
+    "residual_abs_instead_of_max": ("w[v] = diff > 0.0 ? diff : 0.0;", "w[v] = diff > 0.0 ? diff : -diff;"),
+    "residual_sign_flipped": ("double diff = prob(&rp, &sp[k], v) - prob(&rq, &sq[k], v);",
+                              "double diff = prob(&rq, &sq[k], v) - prob(&rp, &sp[k], v);"),
+    "accept_non_strict": ("if (!(u < ai)) { k = i; break; }", "if (!(u <= ai)) { k = i; break; }"),
+    "no_break_at_first_reject": ("if (!(u < ai)) { k = i; break; }", "if (!(u < ai)) { k = i; }"),
+    "ratio_inverted": ("double ratio = px / qx;", "double ratio = qx / px;"),
+    "no_fallback": ("if (Z == 0.0) { /* fallback to p_k */", "if (0) { /* fallback to p_k */"),
+    "argmax_last_tie": ("if (z > bz) { /* strict", "if (z >= bz) { /* strict"),
+    "temperature_ignored": ("st.s += exp((z_at(r, v) - st.m) / T);", "st.s += exp((z_at(r, v) - st.m));"),
+    "inverse_cdf_non_strict": ("if (target < acc) {", "if (target <= acc) {"),
+    "inverse_cdf_unnormalised": ("double target = u * Z;", "double target = u;"),
+    "bonus_from_previous_row": ("row_t rp = target_row(a->target, dt, gamma, V, b, k);\n        if (k < g) {",
+                                "row_t rp = target_row(a->target, dt, gamma, V, b, k < g ? k : (k > 0 ? k - 1 : 0));\n        if (k < g) {"),
+    "greedy_uses_draft_row": ("row_t r = target_row(a->target, dt, gamma, V, b, i);\n            tmax[i]",
+                              "row_t r = (i < g) ? draft_row(a->draft, dt, gamma, V, b, i) : target_row(a->target, dt, gamma, V, b, i);\n            tmax[i]"),
+    "draft_row_shifted": ("row_t rq = draft_row(a->draft, dt, gamma, V, b, i);\n            double px",
+                          "row_t rq = draft_row(a->draft, dt, gamma, V, b, i + 1 < g ? i + 1 : i);\n            double px"),
+}
+
+PIN_TESTS = [
+    (pins.test_t1_exact_enumeration_position0, {}),
+    (pins.test_t1_exact_enumeration_later_position, {}),
+    (pins.test_t1_bonus_marginal, {}),
+    (pins.test_t1_exact_integration_random_distributions, {"seed": 0, "T": 0.6}),
+    (pins.test_t2_accepted_run_law_and_expected_tokens, {"gamma": 3}),
+    (pins.test_t3_greedy_worked_example, {}),
+    (pins.test_t4_library_cross_checks, {"dtype": "f32"}),
+    (pins.test_t4_argmax_matches_numpy_with_ties, {}),
+    (pins.test_t5_u_zero_accepts_and_strict_comparison, {}),
+    (pins.test_t5_zero_residual_mass_falls_back_to_p, {}),
+    (pins.test_t5_inverse_cdf_is_strict_at_exact_breakpoints, {}),
+    (pins.test_t5_identical_rows_accept_everything, {}),
+]
+
+
+class _MutantOracle:
+    """Same call surface as the ``oracle`` package, bound to a mutant build."""
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def spec_verify(self, *a, **k):
+        return oracle.spec_verify(*a, lib=self._lib, **k)
+
+    def run_workload(self, w, trace=True):
+        return oracle.run_workload(w, trace=trace, lib=self._lib)
+
+
+def test_mutation_sources_apply():
+    src = open(SRC).read()
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) == 1, name
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1
+    msrc = tmp_path / "mutant.c"
+    msrc.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / f"libmutant_{name}.so")
+    oracle.build(src=str(msrc), out=lib_path)
+    mo = _MutantOracle(oracle.load(lib_path))
+    caught = []
+    for fn, kw in PIN_TESTS:
+        try:
+            fn(mo, **kw)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(fn.__name__)
+    assert caught, f"mutant {name} survived every pin"
