@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the verify step (spec_verify) on one MI355X.
+
+Workload: B=64 requests, gamma=5 drafts each, vocabulary V=128256, bf16 logits,
+temperature 1.0 (target logits 4 N(0,1) plus a Zipf-like bias, draft logits =
+target + 0.5 N(0,1), drafts sampled from the draft distribution, seeded
+uniforms).  One step = one spec_verify call over the whole batch: row
+statistics of the 11 logit rows of every request, acceptance and first
+rejection, residual / bonus sampling.
+
+Inputs are resident in HBM before timing starts.  The step is replayed from HIP
+graphs (one per input copy) over C copies of the logits totalling more than
+1 GB, so that every call streams its logits from HBM and not from the 256 MB
+last-level cache.
+
+Printed: one JSON line with the metric, the per-step time, the roofline figure
+of the dominant kernel (row statistics, timed with HIP events that the library
+records around it on the launch stream) and the single-threaded CPU oracle's
+rate on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/s + achieved HBM GB/s vs peak (B×(2γ+1)×V logits)"
+HBM_PEAK_GBS = 8000.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "k1_row_stats_B64_g5_V128256_bf16.pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verification_spec_amd", "csrc", "specverify.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0: enough for 1.2 GB)")
+    ap.add_argument("--mode", choices=["stochastic", "greedy"], default="stochastic")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
+    ap.add_argument("--eager", action="store_true", help="launch every step eagerly instead of graph replay")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(requests are independent, so a multi-GPU run would shard the batch with no exchange).",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import rejection_sampling_verification_spec_amd as sv
+    from rejection_sampling_verification_spec_amd import workloads as W
+
+    lib = sv.load_library()
+    dev = torch.device("cuda:0")
+    greedy = args.mode == "greedy"
+    t0 = time.perf_counter()
+    w = W.make_config(3, greedy=greedy)
+    log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")
+    B, gamma, V = w.B, w.gamma, w.V
+    T = float(w.scalar_temperature)
+    positions = w.positions()
+    bytes_alg = w.bytes_alg()                       # rows the method must read x V x 2 B
+    formula_bytes = B * (2 * gamma + 1) * V * 2     # the metric's B x (2 gamma + 1) x V logits
+    t = w.to_torch(dev)
+    copy_bytes = (t["target"].numel() + t["draft"].numel()) * 2
+    copies = args.copies or max(2, math.ceil(1.2e9 / copy_bytes))
+    targets = [t["target"]] + [t["target"].clone() for _ in range(copies - 1)]
+    drafts = [t["draft"]] + [t["draft"].clone() for _ in range(copies - 1)]
+    count = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    need = sv.spec_verify_workspace_bytes(B, gamma, V, sv.SV_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    log(f"[bench] {copies} input copies ({copies * copy_bytes / 1e9:.2f} GB), workspace {need} B")
+
+    def step(c, s):
+        return sv.spec_verify(targets[c], None if greedy else drafts[c], t["draft_tokens"],
+                              None if greedy else t["u_accept"], t["u_sample"], T,
+                              accepted_count=count, out_tokens=out, workspace=ws, stream=s)
+
+    # eager reference result
+    with torch.cuda.stream(stream):
+        step(0, stream)
+    torch.cuda.synchronize()
+    ref_count, ref_out = count.cpu().clone(), out.cpu().clone()
+
+    graphs = []
+    if not args.eager:
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(c, stream)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(count.cpu(), ref_count) and torch.equal(out.cpu(), ref_out), "graph replay differs"
+
+    def run_steps(n, start=0):
+        with torch.cuda.stream(stream):
+            for k in range(n):
+                c = (start + k) % copies
+                if graphs:
+                    graphs[c].replay()
+                else:
+                    step(c, stream)
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0 = time.perf_counter()
+    e0.record(stream)
+    run_steps(args.steps, start=args.warmup)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    h1 = time.perf_counter()
+    dev_ms = e0.elapsed_time(e1)
+    host_ms = (h1 - h0) * 1e3
+    ms_per_step = host_ms / args.steps
+    value = positions * args.steps / (host_ms / 1e3)
+    # every copy holds the same logits, so the last replay must reproduce the eager result
+    assert torch.equal(count.cpu(), ref_count) and torch.equal(out.cpu(), ref_out), "timed replay differs"
+    log(f"[bench] timed {args.steps} steps: host {host_ms:.3f} ms, device {dev_ms:.3f} ms")
+
+    # dominant kernel: row statistics, timed by events the library records around it
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for k, (a, b) in enumerate(evs):
+            c = (args.warmup + k) % copies
+            sv.spec_verify_ex(targets[c], drafts[c], t["draft_tokens"], t["u_accept"], t["u_sample"],
+                              t["temperature"], None, accepted_count=count, out_tokens=out, workspace=ws,
+                              stream=stream, k1_events=(a, b))
+    torch.cuda.synchronize()
+    k1_ms = [a.elapsed_time(b) for a, b in evs]
+    k1_avg_s = float(np.mean(k1_ms)) / 1e3
+    achieved = bytes_alg / k1_avg_s / 1e9
+    traffic = None
+    if os.path.exists(PROFILE_PMC):
+        pmc = json.load(open(PROFILE_PMC))
+        if pmc.get("kernel_source_sha256_16") == source_hash() and pmc.get("mode") == args.mode:
+            traffic = pmc.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "k1_row_stats", "kernel_avg_us": round(k1_avg_s * 1e6, 3),
+                "bytes_per_launch": bytes_alg}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n, spent = 0, 0.0
+        while spent < args.cpu_seconds or n == 0:
+            c0 = time.perf_counter()
+            oracle.run_workload(w, trace=False)
+            spent += time.perf_counter() - c0
+            n += 1
+        cpu = {"value": round(positions * n / spent, 2), "unit": "positions/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} full calls of the same B=64 workload (single-threaded fp64 C, gcc -O2), "
+                         f"{spent:.1f} s", "host_cpus": os.cpu_count(), "host": platform.processor() or
+                         platform.machine()}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "gamma": gamma, "V": V, "input_dtype": "bf16",
+                   "temperature": T, "mode": args.mode, "copies_rotated": copies,
+                   "launch": "eager" if args.eager else "hip graph replay", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": {"step_GBps_alg": round(bytes_alg / (ms_per_step / 1e3) / 1e9, 1),
+                  "step_GBps_formula": round(formula_bytes / (ms_per_step / 1e3) / 1e9, 1),
+                  "bytes_alg": bytes_alg, "bytes_formula": formula_bytes,
+                  "device_ms_per_step": round(dev_ms / args.steps, 5),
+                  "k1_us_min": round(min(k1_ms) * 1e3, 3), "k1_us_max": round(max(k1_ms) * 1e3, 3),
+                  "alpha_hat": round(float(ref_count.float().mean()) / gamma, 4),
+                  "kernel_source_sha256_16": source_hash()},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -47,11 +47,13 @@
  *     stream reaches that point.
  *   - Arguments are checked on the host before anything is enqueued; a failed
  *     check returns SV_EINVAL / SV_EWORKSPACE and touches nothing.  A failed
- *     launch returns SV_EHIP.  Values that live in device memory (token ids in
- *     [0, V), uniforms in [0, 1), per-request T >= 0 and finite, draft lengths
- *     in [0, gamma]) are the caller's contract and are not checked.  Logits must
- *     be finite on every row that the method reads (padding rows of ragged
- *     requests are never read and may hold anything).
+ *     launch returns SV_EHIP.  Values that live in device memory (uniforms in
+ *     [0, 1), per-request T >= 0 and finite) are the caller's contract and are
+ *     not checked; memory safety does not depend on them: a draft length
+ *     outside [0, gamma] is clamped to that range, and a draft token id outside
+ *     [0, V) is treated as rejected at its position.  Logits must be finite on
+ *     every row that the method reads (padding rows of ragged requests are
+ *     never read and may hold anything).
  *   - Two calls may run concurrently only with distinct workspaces.
  *   - Results are deterministic: identical inputs give bit-identical outputs.
  */

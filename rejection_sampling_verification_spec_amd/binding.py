@@ -119,6 +119,33 @@ def _shapes(target_logits):
     return int(B), int(g1) - 1, int(V)
 
 
+def _expect(t, shape, dtype, name, optional=False):
+    """Host-side shape / dtype check before anything reaches the kernels."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_all(target_logits, draft_logits, draft_tokens, u_accept, u_sample, accepted_count,
+               out_tokens, greedy_only: bool):
+    import torch
+    B, gamma, V = _shapes(target_logits)
+    need_draft = gamma > 0 and not greedy_only
+    _expect(draft_logits, (B, gamma, V), target_logits.dtype, "draft_logits", optional=not need_draft)
+    _expect(draft_tokens, (B, gamma), torch.int32, "draft_tokens", optional=gamma == 0)
+    _expect(u_accept, (B, gamma), torch.float32, "u_accept", optional=not need_draft)
+    _expect(u_sample, (B,), torch.float32, "u_sample")
+    _expect(accepted_count, (B,), torch.int32, "accepted_count")
+    _expect(out_tokens, (B, gamma + 1), torch.int32, "out_tokens")
+
+
 def _outputs(B, gamma, device, accepted_count, out_tokens):
     import torch
     if accepted_count is None:
@@ -151,6 +178,8 @@ def spec_verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample, t
     dt = _dtype_code(target_logits)
     _check_device(target_logits, draft_logits, draft_tokens, u_accept, u_sample)
     accepted_count, out_tokens = _outputs(B, gamma, target_logits.device, accepted_count, out_tokens)
+    _check_all(target_logits, draft_logits, draft_tokens, u_accept, u_sample, accepted_count, out_tokens,
+               greedy_only=float(temperature) == 0.0)
     workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace)
     rc = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
                          _ptr(u_sample), float(temperature), B, gamma, V, dt,
@@ -175,13 +204,25 @@ def spec_verify_ex(target_logits, draft_logits, draft_tokens, u_accept, u_sample
     dt = _dtype_code(target_logits)
     _check_device(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, draft_lens)
     accepted_count, out_tokens = _outputs(B, gamma, target_logits.device, accepted_count, out_tokens)
+    _check_all(target_logits, draft_logits, draft_tokens, u_accept, u_sample, accepted_count, out_tokens,
+               greedy_only=False)
+    import torch
+    _expect(temperature, (B,), torch.float32, "temperature")
+    _expect(draft_lens, (B,), torch.int32, "draft_lens", optional=True)
     workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     dbg = None
     if debug or k1_events:
         d = SvDebug()
-        for name in ("p_draft", "q_draft", "accept_prob", "row_max", "row_sum", "row_argmax",
-                     "residual_mass"):
+        rows = 2 * gamma + 1
+        dshapes = {"p_draft": ((B, gamma), torch.float64), "q_draft": ((B, gamma), torch.float64),
+                   "accept_prob": ((B, gamma), torch.float64), "row_max": ((B, rows), torch.float32),
+                   "row_sum": ((B, rows), torch.float64), "row_argmax": ((B, gamma + 1), torch.int32),
+                   "residual_mass": ((B,), torch.float64)}
+        for name, (shape, dtype) in dshapes.items():
             t = (debug or {}).get(name)
+            _expect(t, shape, dtype, f"debug[{name}]", optional=True)
             setattr(d, name, _ptr(t))
         if k1_events:
             d.k1_events[0] = k1_events[0].cuda_event

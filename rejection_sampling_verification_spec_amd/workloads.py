@@ -108,14 +108,17 @@ class Workload:
                 return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
             return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
+        def plain(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
         d = dict(
             target=logits(self.target),
             draft=logits(self.draft),
-            draft_tokens=torch.from_numpy(self.draft_tokens).to(device),
-            u_accept=torch.from_numpy(self.u_accept).to(device),
-            u_sample=torch.from_numpy(self.u_sample).to(device),
-            temperature=torch.from_numpy(self.temperature).to(device),
-            lens=None if self.lens is None else torch.from_numpy(self.lens).to(device),
+            draft_tokens=plain(self.draft_tokens),
+            u_accept=plain(self.u_accept),
+            u_sample=plain(self.u_sample),
+            temperature=plain(self.temperature),
+            lens=None if self.lens is None else plain(self.lens),
         )
         return d
 
@@ -281,9 +284,9 @@ def from_logits(target_f32: np.ndarray, draft_f32: np.ndarray, draft_tokens, u_a
         temps = np.full(B, temps, dtype=np.float32)
     return Workload(name=name, B=B, gamma=gamma, V=V, dtype=dtype,
                     target=_cast(target_f32, dtype), draft=_cast(draft_f32, dtype),
-                    draft_tokens=np.asarray(draft_tokens, dtype=np.int32).reshape(B, gamma),
-                    u_accept=np.asarray(u_accept, dtype=np.float32).reshape(B, gamma),
-                    u_sample=np.asarray(u_sample, dtype=np.float32).reshape(B),
-                    temperature=np.asarray(temps, dtype=np.float32).reshape(B),
-                    lens=None if lens is None else np.asarray(lens, dtype=np.int32),
+                    draft_tokens=np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(B, gamma),
+                    u_accept=np.ascontiguousarray(u_accept, dtype=np.float32).reshape(B, gamma),
+                    u_sample=np.ascontiguousarray(u_sample, dtype=np.float32).reshape(B),
+                    temperature=np.ascontiguousarray(temps, dtype=np.float32).reshape(B),
+                    lens=None if lens is None else np.ascontiguousarray(lens, dtype=np.int32),
                     scalar_temperature=scalar_T)

@@ -1,0 +1,112 @@
+"""GPU-vs-oracle comparison helpers (used by the GPU tests only)."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+import oracle
+
+# probability tolerances: fp32 logits 1e-5 absolute, bf16 logits 2e-3 absolute
+PROB_TOL = {"f32": 1e-5, "bf16": 2e-3}
+ROW_SUM_RTOL = 1e-6
+
+
+@dataclass
+class GpuResult:
+    count: np.ndarray
+    out: np.ndarray
+    dbg: Optional[dict] = None
+
+
+def say(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+
+
+def gpu_run(w, debug: bool = False, force_ex: bool = False, stream=None, workspace=None) -> GpuResult:
+    import torch
+
+    import rejection_sampling_verification_spec_amd as sv
+
+    dev = torch.device("cuda:0")
+    t = w.to_torch(dev)
+    B, gamma = w.B, w.gamma
+    g0 = gamma > 0
+    use_plain = w.scalar_temperature is not None and w.lens is None and not debug and not force_ex
+    dbg = None
+    if use_plain:
+        greedy = w.scalar_temperature == 0.0
+        count, out = sv.spec_verify(t["target"], t["draft"] if (g0 and not greedy) else None,
+                                    t["draft_tokens"] if g0 else None,
+                                    t["u_accept"] if (g0 and not greedy) else None, t["u_sample"],
+                                    w.scalar_temperature, stream=stream, workspace=workspace)
+    else:
+        if debug:
+            f64 = dict(dtype=torch.float64, device=dev)
+            rows = 2 * gamma + 1
+            dbg = dict(p_draft=torch.full((B, gamma), float("nan"), **f64),
+                       q_draft=torch.full((B, gamma), float("nan"), **f64),
+                       accept_prob=torch.full((B, gamma), float("nan"), **f64),
+                       row_max=torch.full((B, rows), float("nan"), dtype=torch.float32, device=dev),
+                       row_sum=torch.full((B, rows), float("nan"), **f64),
+                       row_argmax=torch.full((B, gamma + 1), -1, dtype=torch.int32, device=dev),
+                       residual_mass=torch.full((B,), float("nan"), **f64))
+        count, out = sv.spec_verify_ex(t["target"], t["draft"] if g0 else None,
+                                       t["draft_tokens"] if g0 else None, t["u_accept"] if g0 else None,
+                                       t["u_sample"], t["temperature"], t["lens"], debug=dbg,
+                                       stream=stream, workspace=workspace)
+    torch.cuda.synchronize()
+    return GpuResult(count.cpu().numpy(), out.cpu().numpy(),
+                     {k: v.cpu().numpy() for k, v in dbg.items()} if dbg else None)
+
+
+def check_parity(w, g: GpuResult, o, require_no_flags: bool = True) -> dict:
+    """Bit-exact counts/tokens outside the near-boundary band; greedy fully exact; probability tolerances."""
+    greedy = w.temperature == 0
+    np.testing.assert_array_equal(g.count[greedy], o.accepted_count[greedy], err_msg=f"{w.name} greedy counts")
+    np.testing.assert_array_equal(g.out[greedy], o.out_tokens[greedy], err_msg=f"{w.name} greedy tokens")
+    flagged = o.flags != 0
+    same = (g.count == o.accepted_count) & np.all(g.out == o.out_tokens, axis=1)
+    bad = ~same & ~flagged
+    if bad.any():
+        b = int(np.nonzero(bad)[0][0])
+        raise AssertionError(f"{w.name}: {int(bad.sum())} unflagged mismatches; first b={b} "
+                             f"gpu count={g.count[b]} out={g.out[b]} oracle count={o.accepted_count[b]} "
+                             f"out={o.out_tokens[b]} margins acc={o.accept_margin[b]} cdf={o.cdf_margin[b]}")
+    report = dict(name=w.name, flagged=int(flagged.sum()), flagged_mismatch=int((~same & flagged).sum()))
+    if require_no_flags:
+        assert report["flagged"] == 0, f"{w.name}: {report['flagged']} near-boundary requests"
+    if g.dbg is not None:
+        tol = PROB_TOL[w.dtype]
+        errs = {}
+        for name in ("p_draft", "q_draft", "accept_prob"):
+            ref = getattr(o, name)
+            m = np.isfinite(ref)
+            if m.any():
+                d = np.abs(g.dbg[name][m] - ref[m])
+                errs[name] = float(d.max())
+                assert errs[name] <= tol, f"{w.name} {name} max err {errs[name]}"
+        m = np.isfinite(o.residual_mass) & ~flagged
+        if m.any():
+            errs["residual_mass"] = float(np.abs(g.dbg["residual_mass"][m] - o.residual_mass[m]).max())
+            assert errs["residual_mass"] <= tol, f"{w.name} residual mass err {errs['residual_mass']}"
+        m = np.isfinite(o.row_sum)
+        if m.any():
+            rel = np.abs(g.dbg["row_sum"][m] / o.row_sum[m] - 1.0)
+            errs["row_sum_rel"] = float(rel.max())
+            assert errs["row_sum_rel"] <= ROW_SUM_RTOL, f"{w.name} row_sum rel err {errs['row_sum_rel']}"
+            np.testing.assert_array_equal(g.dbg["row_max"][m].astype(np.float64), o.row_max[m])
+        m = o.row_argmax >= 0
+        np.testing.assert_array_equal(g.dbg["row_argmax"][m], o.row_argmax[m])
+        report["errors"] = errs
+    return report
+
+
+def run_and_check(w, debug: bool = True, require_no_flags: bool = True, **kw) -> dict:
+    say(f"{w.name} B={w.B} gamma={w.gamma} V={w.V} {w.dtype} debug={debug}")
+    g = gpu_run(w, debug=debug, **kw)
+    o = oracle.run_workload(w)
+    rep = check_parity(w, g, o, require_no_flags=require_no_flags)
+    say(f"ok {rep}")
+    return rep

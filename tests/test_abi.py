@@ -1,0 +1,101 @@
+"""The C-ABI library loads and exports every entry point include/specverify.h declares.
+
+No compute call is made here: argument checks run on the host before anything
+is enqueued, so invalid calls are safe without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rejection_sampling_verification_spec_amd as sv
+from rejection_sampling_verification_spec_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify\w*)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from rejection_sampling_verification_spec_amd import build_lib
+        build_lib.build()
+    return binding.load_library()
+
+
+def test_header_declares_the_binding_surface():
+    assert declared_functions() == sorted(binding.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_constants_match_header():
+    text = open(HEADER).read()
+    assert re.search(r"SV_F32\s*=\s*0", text) and re.search(r"SV_BF16\s*=\s*1", text)
+    assert int(re.search(r"#define SV_GAMMA_MAX (\d+)", text).group(1)) == binding.SV_GAMMA_MAX
+    for name in ("SV_OK", "SV_EINVAL", "SV_EWORKSPACE", "SV_EHIP"):
+        assert int(re.search(name + r"\s*=\s*(-?\d+)", text).group(1)) == getattr(binding, name)
+
+
+def test_workspace_bytes(lib):
+    assert sv.spec_verify_workspace_bytes(64, 5, 128256, sv.SV_BF16) > 0
+    assert sv.spec_verify_workspace_bytes(64, 5, 128256, sv.SV_BF16) % 256 == 0
+    assert sv.spec_verify_workspace_bytes(0, 5, 100, sv.SV_F32) == 0
+    assert sv.spec_verify_workspace_bytes(1, -1, 100, sv.SV_F32) == 0
+    assert sv.spec_verify_workspace_bytes(1, 33, 100, sv.SV_F32) == 0
+    assert sv.spec_verify_workspace_bytes(1, 32, 100, sv.SV_F32) > 0
+    assert sv.spec_verify_workspace_bytes(1, 3, 0, sv.SV_F32) == 0
+    assert sv.spec_verify_workspace_bytes(1, 3, 10, 7) == 0
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, 99):
+        assert isinstance(sv.spec_verify_strerror(code), str) and sv.spec_verify_strerror(code)
+
+
+def _call(lib, **kw):
+    a = dict(t=1, d=1, tok=1, ua=1, us=1, T=1.0, B=2, g=3, V=10, dt=sv.SV_F32, cnt=1, out=1,
+             ws=256, wsb=1 << 20)
+    a.update(kw)
+    return lib.spec_verify(a["t"], a["d"], a["tok"], a["ua"], a["us"], a["T"], a["B"], a["g"], a["V"],
+                           a["dt"], a["cnt"], a["out"], a["ws"], a["wsb"], None)
+
+
+def test_host_argument_checks(lib):
+    # every case fails on the host before anything is enqueued
+    assert _call(lib, B=0) == sv.binding.SV_EINVAL
+    assert _call(lib, g=-1) == sv.binding.SV_EINVAL
+    assert _call(lib, g=33) == sv.binding.SV_EINVAL
+    assert _call(lib, V=0) == sv.binding.SV_EINVAL
+    assert _call(lib, dt=5) == sv.binding.SV_EINVAL
+    assert _call(lib, T=-1.0) == sv.binding.SV_EINVAL
+    assert _call(lib, T=float("nan")) == sv.binding.SV_EINVAL
+    assert _call(lib, T=float("inf")) == sv.binding.SV_EINVAL
+    assert _call(lib, t=None) == sv.binding.SV_EINVAL
+    assert _call(lib, us=None) == sv.binding.SV_EINVAL
+    assert _call(lib, cnt=None) == sv.binding.SV_EINVAL
+    assert _call(lib, tok=None) == sv.binding.SV_EINVAL
+    assert _call(lib, d=None) == sv.binding.SV_EINVAL          # stochastic needs draft logits
+    assert _call(lib, ua=None) == sv.binding.SV_EINVAL
+    assert _call(lib, ws=None) == sv.binding.SV_EWORKSPACE
+    assert _call(lib, ws=128) == sv.binding.SV_EWORKSPACE      # not 256-byte aligned
+    assert _call(lib, wsb=16) == sv.binding.SV_EWORKSPACE      # too small
+    ex = lib.spec_verify_ex(1, 1, 1, 1, 1, None, None, 2, 3, 10, sv.SV_F32, 1, 1, 256, 1 << 20, None, None)
+    assert ex == sv.binding.SV_EINVAL                           # device temperature array is required
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(binding.LibraryMissing):
+        binding.load_library(str(tmp_path / "nope.so"))
