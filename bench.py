@@ -8,10 +8,10 @@ uniforms).  One step = one spec_verify call over the whole batch: row
 statistics of the 11 logit rows of every request, acceptance and first
 rejection, residual / bonus sampling.
 
-Inputs are resident in HBM before timing starts.  The step is replayed from HIP
-graphs (one per input copy) over C copies of the logits totalling more than
-1 GB, so that every call streams its logits from HBM and not from the 256 MB
-last-level cache.
+Inputs are resident in HBM before timing starts.  Steps rotate over C copies of
+the logits totalling more than 1 GB, so that every call streams its logits
+from HBM and not from the 256 MB last-level cache; C consecutive steps are
+captured in one HIP graph and replayed.
 
 Printed: one JSON line with the metric, the per-step time, the roofline figure
 of the dominant kernel (row statistics, timed with HIP events that the library
@@ -128,33 +128,46 @@ def main():
     torch.cuda.synchronize()
     ref_count, ref_out = count.cpu().clone(), out.cpu().clone()
 
-    graphs = []
-    if not args.eager:
-        for c in range(copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
+    # HIP graphs: one graph holds `copies` consecutive steps (copy 0, 1, ..., C-1);
+    # a shorter graph covers a remainder so that exactly K steps are timed
+    graphs = {}
+
+    def chain_graph(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in range(n):
                 step(c, stream)
-            graphs.append(g)
+        return g
+
+    if not args.eager:
+        graphs[copies] = chain_graph(copies)
         torch.cuda.synchronize()
-        graphs[0].replay()
+        graphs[copies].replay()
         torch.cuda.synchronize()
         assert torch.equal(count.cpu(), ref_count) and torch.equal(out.cpu(), ref_out), "graph replay differs"
 
-    def run_steps(n, start=0):
+    def run_steps(n):
         with torch.cuda.stream(stream):
-            for k in range(n):
-                c = (start + k) % copies
-                if graphs:
-                    graphs[c].replay()
-                else:
-                    step(c, stream)
+            if args.eager:
+                for k in range(n):
+                    step(k % copies, stream)
+                return
+            full, rem = divmod(n, copies)
+            for _ in range(full):
+                graphs[copies].replay()
+            if rem:
+                if rem not in graphs:
+                    graphs[rem] = chain_graph(rem)
+                graphs[rem].replay()
 
     run_steps(args.warmup)
+    if args.steps % copies and not args.eager and (args.steps % copies) not in graphs:
+        graphs[args.steps % copies] = chain_graph(args.steps % copies)   # built before timing
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     h0 = time.perf_counter()
     e0.record(stream)
-    run_steps(args.steps, start=args.warmup)
+    run_steps(args.steps)
     e1.record(stream)
     torch.cuda.synchronize()
     h1 = time.perf_counter()
@@ -223,7 +236,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "gamma": gamma, "V": V, "input_dtype": "bf16",
                    "temperature": T, "mode": args.mode, "copies_rotated": copies,
-                   "launch": "eager" if args.eager else "hip graph replay", "parallelism": "single GPU"},
+                   "launch": "eager" if args.eager else f"hip graph replay, {copies} steps per graph",
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": {"step_GBps_alg": round(bytes_alg / (ms_per_step / 1e3) / 1e9, 1),

@@ -57,11 +57,16 @@ class SvDebug(ctypes.Structure):
 _lib: Optional[ctypes.CDLL] = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libspecverify.so; raises ``LibraryMissing`` if it has not been built."""
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libspecverify.so; raises ``LibraryMissing`` if it has not been built.
+
+    ``path`` (or the SPECVERIFY_LIB environment variable) selects another build
+    of the same library."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = os.environ.get("SPECVERIFY_LIB", LIB_PATH)
     if not os.path.exists(path):
         raise LibraryMissing(f"{path} not found: build it with __graft_entry__.build()")
     lib = ctypes.CDLL(path)

@@ -13,25 +13,26 @@
 //   [P4] "LLM推測デコーディング最適化実踐", section 検証アルゴリズムの実装
 //        (gamma+1 target rows, bonus draw from the last one)
 //
-// Three launches on the caller's stream, no host synchronisation:
+// Four launches on the caller's stream, no host synchronisation, no
+// device-wide fences (each kernel boundary is the only cross-workgroup sync):
 //
-//   K1 row_stats   one workgroup per (request, logit row, vocabulary tile).
-//                  Streams the tile once with 16-byte loads and produces, for a
-//                  stochastic row, (M, s) with M an integer upper bound of
-//                  max(z)*log2(e)/T and s = sum 2^(z*c - M); for a greedy row,
-//                  the maximum and its lowest index.  The integer M makes every
-//                  rescale between partial sums an exact power of two (ldexp).
-//   K2 decide      one workgroup per request.  Merges the tile partials of each
+//   K1  row_stats  one workgroup per (request, logit row, vocabulary chunk).
+//                  Streams the chunk once (16-byte non-temporal loads, next tile
+//                  prefetched) and produces, for a stochastic row, (M, s) with M
+//                  an integer upper bound of max(z)*log2(e)/T and
+//                  s = sum 2^(z*c - M); for a greedy row, the maximum and its
+//                  lowest index.  Integer M makes every rescale between partial
+//                  sums an exact power of two (ldexp).
+//   K2  decide     one workgroup per request.  Merges the chunk partials of each
 //                  row in a fixed order, evaluates a_i = min(1, p_i(x_i)/q_i(x_i))
 //                  in fp64 from the two gathered logits, finds the first
 //                  rejection with a wave ballot, writes accepted_count and the
 //                  accepted prefix, and prepares the one row pair to sample.
-//   K3 sample      B x NW workgroups.  Re-reads the selected target row (and
-//                  draft row after a rejection), forms w = max(0, p - q) (or p
-//                  for the bonus), writes one fp64 mass per 512-token sub-chunk,
-//                  and the last workgroup of each request to finish finds u*Z by
-//                  a scan over the sub-chunk masses and then inside the one
-//                  sub-chunk that holds it.
+//   K3a mass       re-reads the selected target row (and draft row after a
+//                  rejection) and writes the mass of w = max(0, p - q) (or p for
+//                  the bonus) per 2048-token sub-chunk, one wave each.
+//   K3b select     one wave per request: the sub-chunk whose prefix crosses u*Z,
+//                  then the token inside it.
 //
 // Numerics: bf16 -> fp32 widening is exact; exponentials are v_exp_f32 of
 // fma(z, c, -M); per-thread partial sums are fp32 over at most 64 terms and
@@ -49,7 +50,7 @@ namespace {
 constexpr int kBlock = 256;          // threads per workgroup (4 waves of 64)
 constexpr int kWave = 64;
 constexpr int kWaves = kBlock / kWave;
-constexpr int kSub = 512;            // tokens per K3 sub-chunk (64 lanes x 8)
+constexpr int kSub = 2048;           // tokens per K3 sub-chunk (64 lanes x 32)
 constexpr int kEmptyM = -(1 << 28);  // exponent of an empty partial
 constexpr double kLog2e = 1.4426950408889634073599246810019;
 constexpr size_t kAlign = 256;
@@ -174,19 +175,106 @@ struct alignas(16) SubSums {
 // are draft rows r - gamma - 1.  A row is needed if it is a target row i <= g_b,
 // or a draft row i < g_b of a stochastic request (greedy requests never read
 // draft logits).
+//
+// Workgroup w handles chunk j = w % NCH of row slot w / NCH.  A chunk is a run
+// of 16-byte vectors [v0, v1) streamed in tiles of U vectors per thread; the
+// next tile's loads are issued before the current tile is reduced, and loads
+// are non-temporal (each logit is read once here).  Elements that do not fill
+// a whole aligned vector (the row tail, or every element of a row that is not
+// 16-byte aligned) are read one by one by the row's last chunk / by all chunks.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 load_nt(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+
+template <int DT>
+__device__ __forceinline__ void widen_vec(u32x4 v, float *x) {
+  if constexpr (DT == SV_F32) {
+    x[0] = __uint_as_float(v.x);
+    x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z);
+    x[3] = __uint_as_float(v.w);
+  } else {
+    x[0] = bf16_lo(v.x);
+    x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y);
+    x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z);
+    x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w);
+    x[7] = bf16_hi(v.w);
+  }
+}
+
+// -inf in every element of a vector (neutral for max and for sums of exponentials)
+template <int DT>
+__device__ __forceinline__ u32x4 neg_inf_vec() {
+  if constexpr (DT == SV_F32) return u32x4{0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u};
+  return u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+}
+
+// Tile statistics folded into a thread's running (M, s, max): M_t = ceil(max*c)
+// makes every term 2^(z*c - M_t) <= 1 (up to one rounding), and the fold
+// rescales by an exact power of two.
+template <int N>
+__device__ __forceinline__ void fold_values(const float *x, float c, int &M, double &s, float &mx) {
+  float tmx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < N; ++e) tmx = fmaxf(tmx, x[e]);
+  if (tmx > -INFINITY) {
+    const float Mf = ceilf(tmx * c);
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < N; ++e) acc += __builtin_amdgcn_exp2f(fmaf(x[e], c, -Mf));
+    merge_sm(M, s, mx, static_cast<int>(Mf), static_cast<double>(acc), tmx);
+  }
+}
+
+// The same for a tile held as U raw 16-byte vectors; the vectors are widened
+// twice (once for the maximum, once for the sum) instead of being kept widened,
+// which halves the registers the tile occupies.
+template <int DT, int U>
+__device__ __forceinline__ void fold_tile(const u32x4 *v, float c, int &M, double &s, float &mx) {
+  constexpr int kV = Elem<DT>::kVec;
+  float tmx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float x[kV];
+    widen_vec<DT>(v[u], x);
+#pragma unroll
+    for (int e = 0; e < kV; ++e) tmx = fmaxf(tmx, x[e]);
+  }
+  if (tmx > -INFINITY) {
+    const float Mf = ceilf(tmx * c);
+    const float nM = -Mf;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[kV];
+      widen_vec<DT>(v[u], x);
+#pragma unroll
+      for (int e = 0; e < kV; ++e) acc[(u * kV + e) & 7] += __builtin_amdgcn_exp2f(fmaf(x[e], c, nM));
+    }
+    const float ts = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    merge_sm(M, s, mx, static_cast<int>(Mf), static_cast<double>(ts), tmx);
+  }
+}
+
 template <int DT, int U>
 __global__ __launch_bounds__(kBlock) void k1_row_stats(
     const void *__restrict__ target, const void *__restrict__ draft,
-    const float *__restrict__ temps, float scalar_T, const int32_t *__restrict__ lens, int gamma,
-    int V, int NS, Partial *__restrict__ part) {
+    const int32_t *__restrict__ tokens, const float *__restrict__ temps, float scalar_T,
+    const int32_t *__restrict__ lens, int gamma, int V, int NCH, int chunk_vecs,
+    Partial *__restrict__ part, float *__restrict__ zx) {
   constexpr int kV = Elem<DT>::kVec;
-  constexpr long kTile = static_cast<long>(kBlock) * U * kV;
+  constexpr int kTileVecs = U * kBlock;
   const int rows = 2 * gamma + 1;
-  const long tile = blockIdx.x;
-  const int j = static_cast<int>(tile % NS);
-  const long slot = tile / NS;
-  const int r = static_cast<int>(slot % rows);
-  const int b = static_cast<int>(slot / rows);
+  const int wgid = blockIdx.x;
+  const int slot = wgid / NCH;
+  const int j = wgid - slot * NCH;
+  const int b = slot / rows;
+  const int r = slot - b * rows;
   const int g = request_len(lens, gamma, b);
   const float T = request_T(temps, scalar_T, b);
   const bool is_target = r <= gamma;
@@ -194,58 +282,64 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   const bool greedy = !(T > 0.0f);
   if (is_target ? (i > g) : (greedy || i >= g)) return;
 
-  const void *row =
-      is_target
-          ? static_cast<const void *>(static_cast<const char *>(target) +
-                                      (static_cast<long>(b) * (gamma + 1) + i) * V * Elem<DT>::kBytes)
-          : static_cast<const void *>(static_cast<const char *>(draft) +
-                                      (static_cast<long>(b) * gamma + i) * V * Elem<DT>::kBytes);
+  const char *row =
+      is_target ? static_cast<const char *>(target) +
+                      (static_cast<long>(b) * (gamma + 1) + i) * V * Elem<DT>::kBytes
+                : static_cast<const char *>(draft) +
+                      (static_cast<long>(b) * gamma + i) * V * Elem<DT>::kBytes;
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-  const long t0 = j * kTile;
-  const long t1 = (t0 + kTile < V) ? t0 + kTile : V;
+  const int nvec = aligned ? V / kV : 0;  // whole aligned vectors of the row
+  const int v0 = min(j * chunk_vecs, nvec);
+  const int v1 = min(v0 + chunk_vecs, nvec);
+  // elements read one by one: the tail after the last whole vector (last
+  // chunk), or this chunk's share of a row that is not 16-byte aligned
+  const long se0 = aligned ? (j == NCH - 1 ? static_cast<long>(nvec) * kV : V)
+                           : min(static_cast<long>(j) * chunk_vecs * kV, static_cast<long>(V));
+  const long se1 = aligned ? V : min(static_cast<long>(j + 1) * chunk_vecs * kV, static_cast<long>(V));
+  const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
   const int tid = threadIdx.x;
-
-  float x[U][kV];
-  if (aligned && t1 - t0 == kTile) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_vec<DT>(row, t0 + static_cast<long>(tid + u * kBlock) * kV, x[u]);
-  } else {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      load_vec_guarded<DT>(row, aligned, t0 + static_cast<long>(tid + u * kBlock) * kV, t1, x[u]);
+  // the logit at this position's draft token, picked up by the chunk that owns it
+  // (stochastic rows i < g only; ids outside [0, V) are never dereferenced)
+  if (tid == 0 && !greedy && i < g) {
+    const int x = tokens[static_cast<long>(b) * gamma + i];
+    if (x >= 0 && x < V) {
+      const int xv = x / kV;
+      const bool owns = aligned ? (xv < nvec ? (xv >= v0 && xv < v1) : (j == NCH - 1))
+                                : (x >= se0 && x < se1);
+      if (owns) zx[slot] = load_one<DT>(row, x);
+    }
   }
-
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   __shared__ double sh_s[kWaves];
   __shared__ float sh_mx[kWaves];
   __shared__ int sh_mi[kWaves];
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+
+  u32x4 cur[U], nxt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int vi = v0 + u * kBlock + tid;
+    cur[u] = (vi < v1) ? load_nt(rv + vi) : neg_inf_vec<DT>();
+  }
 
   if (!greedy) {
     const float c = temp_scale(T);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int e = 0; e < kV; ++e) mx = fmaxf(mx, x[u][e]);
     int M = kEmptyM;
     double s = 0.0;
-    if (mx > -INFINITY) {
-      const float Mf = ceilf(mx * c);
-      M = static_cast<int>(Mf);
-      const float nM = -Mf;
-      float acc[kV];
+    float mx = -INFINITY;
+    for (int t0 = v0; t0 < v1; t0 += kTileVecs) {
 #pragma unroll
-      for (int e = 0; e < kV; ++e) acc[e] = 0.0f;
+      for (int u = 0; u < U; ++u) {
+        const int vi = t0 + kTileVecs + u * kBlock + tid;
+        nxt[u] = (vi < v1) ? load_nt(rv + vi) : neg_inf_vec<DT>();
+      }
+      fold_tile<DT, U>(cur, c, M, s, mx);
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int e = 0; e < kV; ++e) acc[e] += __builtin_amdgcn_exp2f(fmaf(x[u][e], c, nM));
-#pragma unroll
-      for (int w = kV / 2; w >= 1; w /= 2)
-#pragma unroll
-        for (int e = 0; e < w; ++e) acc[e] += acc[e + w];
-      s = static_cast<double>(acc[0]);
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+    for (long e = se0 + tid; e < se1; e += kBlock) {
+      const float z = load_one<DT>(row, e);
+      fold_values<1>(&z, c, M, s, mx);
     }
 #pragma unroll
     for (int off = kWave / 2; off >= 1; off /= 2) {
@@ -269,21 +363,42 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
       pr.s = st;
       pr.mx = mt;
       pr.mi = Mt;
-      part[tile] = pr;
+      part[wgid] = pr;
     }
   } else {
-    // lowest index of the maximum (fp32 compare; bf16 widening is exact)
+    // lowest index of the maximum; a thread's elements are visited in
+    // increasing index order, so a strict > keeps the first occurrence
     float bv = -INFINITY;
     int bi = 0x7fffffff;
+    for (int t0 = v0; t0 < v1; t0 += kTileVecs) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long e0 = t0 + static_cast<long>(tid + u * kBlock) * kV;
+      for (int u = 0; u < U; ++u) {
+        const int vi = t0 + kTileVecs + u * kBlock + tid;
+        nxt[u] = (vi < v1) ? load_nt(rv + vi) : neg_inf_vec<DT>();
+      }
 #pragma unroll
-      for (int e = 0; e < kV; ++e) {
-        if (e0 + e < t1 && (x[u][e] > bv || bi == 0x7fffffff)) {
-          bv = x[u][e];
-          bi = static_cast<int>(e0 + e);
+      for (int u = 0; u < U; ++u) {
+        const int vi = t0 + u * kBlock + tid;
+        if (vi < v1) {
+          float x[kV];
+          widen_vec<DT>(cur[u], x);
+#pragma unroll
+          for (int e = 0; e < kV; ++e) {
+            if (x[e] > bv || bi == 0x7fffffff) {
+              bv = x[e];
+              bi = vi * kV + e;
+            }
+          }
         }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+    for (long e = se0 + tid; e < se1; e += kBlock) {
+      const float z = load_one<DT>(row, e);
+      if (z > bv || bi == 0x7fffffff) {
+        bv = z;
+        bi = static_cast<int>(e);
       }
     }
 #pragma unroll
@@ -305,35 +420,62 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
       pr.s = 0.0;
       pr.mx = v;
       pr.mi = ix;
-      part[tile] = pr;
+      part[wgid] = pr;
     }
   }
 }
 
 // ================================================================== K2
-constexpr int kK2Block = 128;  // covers the 2*SV_GAMMA_MAX+1 rows of a request
+constexpr int kK2Batch = 8;  // chunk partials fetched together per row
 
+struct DecideShared {
+  double L[2 * SV_GAMMA_MAX + 1];  // log2 of each row's partition sum
+  double s[2 * SV_GAMMA_MAX + 1];
+  int M[2 * SV_GAMMA_MAX + 1];
+  int arg[2 * SV_GAMMA_MAX + 1];
+  int k;
+  SelParams sp;
+};
+
+// The decision for request b, computed by one 256-thread workgroup: merge the
+// chunk partials of each row in chunk order, evaluate the acceptance of each
+// draft, find the first rejection.  Every workgroup of a request computes the
+// same result (the arithmetic is deterministic); only the `writer` workgroup
+// stores the outputs and the sampling parameters.  Returns them in sh.sp.
 template <int DT>
-__global__ __launch_bounds__(kK2Block) void k2_decide(
+__device__ __forceinline__ void decide_request(
     const void *__restrict__ target, const void *__restrict__ draft,
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
     const float *__restrict__ temps, float scalar_T, const int32_t *__restrict__ lens, int gamma,
-    int V, int NS, const Partial *__restrict__ part, int32_t *__restrict__ accepted_count,
-    int32_t *__restrict__ out_tokens, SelParams *__restrict__ sel, unsigned *__restrict__ counters,
-    sv_debug dbg) {
-  const int b = blockIdx.x;
+    int V, int NS, const Partial *__restrict__ part, const float *__restrict__ zx,
+    int32_t *__restrict__ accepted_count, int32_t *__restrict__ out_tokens,
+    SelParams *__restrict__ sel, const sv_debug &dbg_in, int b, bool writer, DecideShared &sh) {
   const int tid = threadIdx.x;
   const int rows = 2 * gamma + 1;
   const int g = request_len(lens, gamma, b);
   const float T = request_T(temps, scalar_T, b);
   const bool greedy = !(T > 0.0f);
   const float c = greedy ? 0.0f : temp_scale(T);
+  sv_debug dbg = dbg_in;
+  if (!writer) memset(&dbg, 0, sizeof dbg);
+  double *sh_L = sh.L;
+  double *sh_s = sh.s;
+  int *sh_M = sh.M;
+  int *sh_arg = sh.arg;
+  int &sh_k = sh.k;
 
-  __shared__ double sh_L[2 * SV_GAMMA_MAX + 1];   // log2 of the row's partition sum
-  __shared__ double sh_s[2 * SV_GAMMA_MAX + 1];
-  __shared__ int sh_M[2 * SV_GAMMA_MAX + 1];
-  __shared__ int sh_arg[2 * SV_GAMMA_MAX + 1];
-  __shared__ int sh_k;
+  // thread i < g also evaluates draft i: its id, its uniform, and the two logits
+  // at it (picked up by K1), fetched together with the row partials below
+  int x = -1;
+  float zpx = 0.0f, zqx = 0.0f, ua = 0.0f;
+  if (tid < g) {
+    x = tokens[static_cast<long>(b) * gamma + tid];
+    if (!greedy) {
+      zpx = zx[static_cast<long>(b) * rows + tid];
+      zqx = zx[static_cast<long>(b) * rows + gamma + 1 + tid];
+      ua = u_accept[static_cast<long>(b) * gamma + tid];
+    }
+  }
 
   // merge the tile partials of each needed row, tiles in increasing order
   if (tid < rows) {
@@ -343,11 +485,25 @@ __global__ __launch_bounds__(kK2Block) void k2_decide(
     const bool needed = is_target ? (i <= g) : (!greedy && i < g);
     if (needed) {
       const Partial *pp = part + (static_cast<long>(b) * rows + r) * NS;
+      int M = kEmptyM;
+      double s = 0.0;
+      float mx = -INFINITY;
+      float v = -INFINITY;
+      int ix = 0x7fffffff;
+      for (int j0 = 0; j0 < NS; j0 += kK2Batch) {
+        Partial buf[kK2Batch];
+#pragma unroll
+        for (int u = 0; u < kK2Batch; ++u)
+          if (j0 + u < NS) buf[u] = pp[j0 + u];
+#pragma unroll
+        for (int u = 0; u < kK2Batch; ++u) {
+          if (j0 + u < NS) {
+            if (!greedy) merge_sm(M, s, mx, buf[u].mi, buf[u].s, buf[u].mx);
+            else merge_arg(v, ix, buf[u].mx, buf[u].mi);
+          }
+        }
+      }
       if (!greedy) {
-        int M = pp[0].mi;
-        double s = pp[0].s;
-        float mx = pp[0].mx;
-        for (int jj = 1; jj < NS; ++jj) merge_sm(M, s, mx, pp[jj].mi, pp[jj].s, pp[jj].mx);
         sh_M[r] = M;
         sh_s[r] = s;
         sh_L[r] = static_cast<double>(M) + log2(s);
@@ -356,9 +512,6 @@ __global__ __launch_bounds__(kK2Block) void k2_decide(
           dbg.row_sum[static_cast<long>(b) * rows + r] =
               s * exp2(static_cast<double>(M) - static_cast<double>(mx) * static_cast<double>(c));
       } else {
-        float v = pp[0].mx;
-        int ix = pp[0].mi;
-        for (int jj = 1; jj < NS; ++jj) merge_arg(v, ix, pp[jj].mx, pp[jj].mi);
         sh_arg[r] = ix;
         if (dbg.row_argmax && is_target) dbg.row_argmax[static_cast<long>(b) * (gamma + 1) + r] = ix;
       }
@@ -370,23 +523,18 @@ __global__ __launch_bounds__(kK2Block) void k2_decide(
   if (tid < kWave) {
     bool reject = false;
     if (tid < g) {
-      const int x = tokens[static_cast<long>(b) * gamma + tid];
       if (x < 0 || x >= V) {
         reject = true;  // a draft id outside the vocabulary is rejected, never dereferenced
       } else if (greedy) {
         reject = (x != sh_arg[tid]);
       } else {
-        const char *trow = static_cast<const char *>(target) +
-                           (static_cast<long>(b) * (gamma + 1) + tid) * V * Elem<DT>::kBytes;
-        const char *drow = static_cast<const char *>(draft) +
-                           (static_cast<long>(b) * gamma + tid) * V * Elem<DT>::kBytes;
         const double cd = static_cast<double>(c);
         // log2 p_i(x) and log2 q_i(x) in fp64: z*c - log2(sum 2^(z c))
-        const double lp = static_cast<double>(load_one<DT>(trow, x)) * cd - sh_L[tid];
-        const double lq = static_cast<double>(load_one<DT>(drow, x)) * cd - sh_L[gamma + 1 + tid];
+        const double lp = static_cast<double>(zpx) * cd - sh_L[tid];
+        const double lq = static_cast<double>(zqx) * cd - sh_L[gamma + 1 + tid];
         const double ratio = exp2(lp - lq);
         const double a = ratio < 1.0 ? ratio : 1.0;
-        reject = !(static_cast<double>(u_accept[static_cast<long>(b) * gamma + tid]) < a);
+        reject = !(static_cast<double>(ua) < a);
         const long o = static_cast<long>(b) * gamma + tid;
         if (dbg.p_draft) dbg.p_draft[o] = exp2(lp);
         if (dbg.q_draft) dbg.q_draft[o] = exp2(lq);
@@ -400,14 +548,16 @@ __global__ __launch_bounds__(kK2Block) void k2_decide(
   const int k = sh_k;
 
   // accepted prefix, the greedy replacement / bonus, -1 padding
-  for (int t = tid; t <= gamma; t += kK2Block) {
-    int32_t v = -1;
-    if (t < k) v = tokens[static_cast<long>(b) * gamma + t];
-    else if (t == k && greedy) v = sh_arg[k];
-    out_tokens[static_cast<long>(b) * (gamma + 1) + t] = v;
+  if (writer) {
+    for (int t = tid; t <= gamma; t += kBlock) {
+      int32_t v = -1;
+      if (t < k) v = tokens[static_cast<long>(b) * gamma + t];
+      else if (t == k && greedy) v = sh_arg[k];
+      out_tokens[static_cast<long>(b) * (gamma + 1) + t] = v;
+    }
   }
   if (tid == 0) {
-    accepted_count[b] = k;
+    if (writer) accepted_count[b] = k;
     SelParams sp;
     sp.k = k;
     sp.c = c;
@@ -428,46 +578,57 @@ __global__ __launch_bounds__(kK2Block) void k2_decide(
         sp.r = 0.0f;
       }
     }
-    sel[b] = sp;
-    counters[b] = 0u;
+    if (writer) sel[b] = sp;
+    sh.sp = sp;
   }
+  __syncthreads();
 }
 
 // ================================================================== K3
-// w(v) in units of the target row's scale s'_p:  p(v) - q(v) = (e_p - e_q r) / s'_p
-// with e_p = 2^(z_p c - M_p), e_q = 2^(z_q c - M_q), r = s'_p / s'_q.  A common
-// scale does not move the normalised CDF, so sampling never divides by s'_p.
-template <int DT>
-__device__ __forceinline__ void residual_lane(const SelParams &sp, const void *trow,
-                                              const void *drow, bool aligned, long e0, long V,
-                                              float *w, float *p) {
-  float zp[8], zq[8];
-  if constexpr (DT == SV_BF16) {
-    load_vec_guarded<DT>(trow, aligned, e0, V, zp);
-    if (sp.mode == 1) load_vec_guarded<DT>(drow, aligned, e0, V, zq);
+// Sampling at position k of a stochastic request.  With e_p = 2^(z_p c - M_p),
+// e_q = 2^(z_q c - M_q) and r = s'_p / s'_q,
+//   p(v) - q(v) = (e_p(v) - r e_q(v)) / s'_p,
+// so the residual is handled in units of the target row's scale s'_p: a common
+// scale does not move the normalised CDF, and sampling never divides by s'_p.
+// The bonus (k == gamma_b) samples w = e_p.  The sum of e_p is kept alongside
+// for the zero-residual-mass fallback to p_k.
+//
+// The row is cut into sub-chunks of kSub = 2048 tokens, one wave each, 32
+// tokens per lane.  K3a writes the mass of every sub-chunk; K3b (one wave per
+// request) finds the sub-chunk whose prefix crosses u*Z and then the token in it.
+constexpr int kLaneElems = kSub / kWave;  // 32
+
+__device__ __forceinline__ void residual_value(const SelParams &sp, float zp, float zq, float &w,
+                                               float &p) {
+  const float ep = __builtin_amdgcn_exp2f(fmaf(zp, sp.c, sp.negMp));  // -inf -> 0
+  p = ep;
+  if (sp.mode == 1) {
+    const float eq = __builtin_amdgcn_exp2f(fmaf(zq, sp.c, sp.negMq));
+    w = fmaxf(0.0f, fmaf(-eq, sp.r, ep));
   } else {
-    load_vec_guarded<DT>(trow, aligned, e0, V, zp);
-    load_vec_guarded<DT>(trow, aligned, e0 + 4, V, zp + 4);
-    if (sp.mode == 1) {
-      load_vec_guarded<DT>(drow, aligned, e0, V, zq);
-      load_vec_guarded<DT>(drow, aligned, e0 + 4, V, zq + 4);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float ep = __builtin_amdgcn_exp2f(fmaf(zp[e], sp.c, sp.negMp));  // -inf -> 0
-    p[e] = ep;
-    if (sp.mode == 1) {
-      const float eq = __builtin_amdgcn_exp2f(fmaf(zq[e], sp.c, sp.negMq));
-      w[e] = fmaxf(0.0f, fmaf(-eq, sp.r, ep));
-    } else {
-      w[e] = ep;
-    }
+    w = ep;
   }
 }
 
-__device__ __forceinline__ float sum8(const float *a) {
-  return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+// The 32 logits of one lane in a sub-chunk starting at token `base`.
+// INTERLEAVED: vector u of the lane is vector u*64 + lane of the sub-chunk
+//   (each load instruction of the wave reads one contiguous 1 KiB run);
+// otherwise the lane's 32 tokens are contiguous (base + lane*32 + k), which the
+//   in-sub-chunk scan needs.  Tokens at or beyond V read as -inf.
+template <int DT, bool INTERLEAVED>
+__device__ __forceinline__ void load_lane32(const void *row, bool aligned, long base, int lane, long V,
+                                            float *z, int *idx) {
+  constexpr int kV = Elem<DT>::kVec;
+#pragma unroll
+  for (int u = 0; u < kLaneElems / kV; ++u) {
+    const long e0 = INTERLEAVED ? base + static_cast<long>(u * kWave + lane) * kV
+                                : base + static_cast<long>(lane) * kLaneElems + u * kV;
+    load_vec_guarded<DT>(row, aligned, e0, V, z + u * kV);
+    if (idx) {
+#pragma unroll
+      for (int e = 0; e < kV; ++e) idx[u * kV + e] = static_cast<int>(e0 + e);
+    }
+  }
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
@@ -486,164 +647,272 @@ __device__ __forceinline__ double wave_scan(double v, int lane) {
   return v;
 }
 
-// inclusive prefix over the 256 threads of a workgroup (fp64); returns the total in *total
-__device__ __forceinline__ double block_scan(double v, double *sh, double *total) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  v = wave_scan(v, lane);
-  if (lane == kWave - 1) sh[wave] = v;
-  __syncthreads();
-  double before = 0.0;
-  for (int w = 0; w < wave; ++w) before += sh[w];
-  double tot = 0.0;
-  for (int w = 0; w < kWaves; ++w) tot += sh[w];
-  __syncthreads();
-  *total = tot;
-  return v + before;
+struct RowPair {
+  const void *trow, *drow;
+  bool aligned;
+};
+
+template <int DT>
+__device__ __forceinline__ RowPair selected_rows(const void *target, const void *draft, int gamma, int V,
+                                                 int b, const SelParams &sp) {
+  RowPair rp;
+  rp.trow = static_cast<const char *>(target) +
+            (static_cast<long>(b) * (gamma + 1) + sp.k) * V * Elem<DT>::kBytes;
+  rp.drow = (sp.mode == 1) ? static_cast<const void *>(static_cast<const char *>(draft) +
+                                                       (static_cast<long>(b) * gamma + sp.k) * V *
+                                                           Elem<DT>::kBytes)
+                           : nullptr;
+  rp.aligned = ((reinterpret_cast<uintptr_t>(rp.trow) | reinterpret_cast<uintptr_t>(rp.drow)) & 15u) == 0;
+  return rp;
+}
+
+// Raw 16-byte vectors holding one lane's 32 tokens of a sub-chunk, interleaved
+// layout (vector u of the lane is vector u*64 + lane of the sub-chunk, so each
+// load instruction of the wave reads one contiguous 1 KiB run).  Tokens at or
+// beyond V, and every token of a row that is not 16-byte aligned, are read one
+// by one; out-of-range tokens hold -inf.
+template <int DT>
+__device__ __forceinline__ u32x4 pack_guarded(const char *row, long e0, long V) {
+  uint32_t w[4];
+  if constexpr (DT == SV_F32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (e0 + e < V) ? reinterpret_cast<const uint32_t *>(row)[e0 + e] : 0xff800000u;
+  } else {
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(row);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = (e0 + 2 * e < V) ? h[e0 + 2 * e] : 0xff80u;
+      const uint32_t hi = (e0 + 2 * e + 1 < V) ? h[e0 + 2 * e + 1] : 0xff80u;
+      w[e] = lo | (hi << 16);
+    }
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
 }
 
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k3_sample(
-    const void *__restrict__ target, const void *__restrict__ draft,
-    const float *__restrict__ u_sample, int gamma, int V, int NSUB, int SPW, int NW,
-    const SelParams *__restrict__ sel, SubSums *__restrict__ sums, unsigned *__restrict__ counters,
-    int32_t *__restrict__ out_tokens, double *__restrict__ dbg_mass) {
-  const int b = blockIdx.x / NW;
-  const int wg = blockIdx.x % NW;
-  const SelParams sp = sel[b];
-  if (sp.mode == 0) return;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const void *trow = static_cast<const char *>(target) +
-                     (static_cast<long>(b) * (gamma + 1) + sp.k) * V * Elem<DT>::kBytes;
-  const void *drow = (sp.mode == 1)
-                         ? static_cast<const void *>(static_cast<const char *>(draft) +
-                                                     (static_cast<long>(b) * gamma + sp.k) * V *
-                                                         Elem<DT>::kBytes)
-                         : nullptr;
-  const bool aligned = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;
-  SubSums *bs = sums + static_cast<long>(b) * NSUB;
+__device__ __forceinline__ void load_lane_raw(const void *row, bool aligned, long base, int lane, long V,
+                                              u32x4 *raw) {
+  constexpr int kV = Elem<DT>::kVec;
+  const char *r = static_cast<const char *>(row);
+#pragma unroll
+  for (int u = 0; u < kLaneElems / kV; ++u) {
+    const long e0 = base + static_cast<long>(u * kWave + lane) * kV;
+    raw[u] = (aligned && e0 + kV <= V)
+                 ? *reinterpret_cast<const u32x4 *>(r + e0 * Elem<DT>::kBytes)
+                 : pack_guarded<DT>(r, e0, V);
+  }
+}
 
-  // pass 1: the mass of each 512-token sub-chunk this workgroup owns
+// K2 (decide) fused with K3a (mass): NW workgroups per request.  Each one
+// recomputes the request's decision (cheap and deterministic) and workgroup 0
+// stores it; then every wave writes the masses of SPW consecutive 2048-token
+// sub-chunks of the row pair to sample, loading sub-chunk t+1 while it reduces
+// sub-chunk t.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k2_decide_mass(
+    const void *__restrict__ target, const void *__restrict__ draft,
+    const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
+    const float *__restrict__ temps, float scalar_T, const int32_t *__restrict__ lens, int gamma,
+    int V, int NS, int NSUB, int NW, int SPW, const Partial *__restrict__ part,
+    const float *__restrict__ zx, int32_t *__restrict__ accepted_count,
+    int32_t *__restrict__ out_tokens, SelParams *__restrict__ sel, SubSums *__restrict__ sums,
+    sv_debug dbg) {
+  constexpr int kN = kLaneElems / Elem<DT>::kVec;
+  const int b = blockIdx.x / NW;
+  const int wg = blockIdx.x - b * NW;
+  // greedy requests need the decision only (workgroup 0)
+  if (wg > 0 && !(request_T(temps, scalar_T, b) > 0.0f)) return;
+  __shared__ DecideShared sh;
+  decide_request<DT>(target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V, NS, part, zx,
+                     accepted_count, out_tokens, sel, dbg, b, wg == 0, sh);
+  const SelParams sp = sh.sp;
+  const int first = (wg * kWaves + static_cast<int>(threadIdx.x) / kWave) * SPW;
+  if (sp.mode == 0 || first >= NSUB) return;  // uniform per wave; no barrier below
+  const int lane = threadIdx.x & (kWave - 1);
+  const RowPair rp = selected_rows<DT>(target, draft, gamma, V, b, sp);
+  u32x4 tc[kN], dc[kN], tn[kN], dn[kN];
+  load_lane_raw<DT>(rp.trow, rp.aligned, static_cast<long>(first) * kSub, lane, V, tc);
+  if (sp.mode == 1) load_lane_raw<DT>(rp.drow, rp.aligned, static_cast<long>(first) * kSub, lane, V, dc);
   for (int t = 0; t < SPW; ++t) {
-    const int s = (wg * kWaves + wave) * SPW + t;
-    if (s >= NSUB) break;
-    float w[8], p[8];
-    residual_lane<DT>(sp, trow, drow, aligned, static_cast<long>(s) * kSub + lane * 8, V, w, p);
-    const double sw = wave_sum(static_cast<double>(sum8(w)));
-    const double spp = wave_sum(static_cast<double>(sum8(p)));
+    const int sub = first + t;
+    if (sub >= NSUB) break;
+    if (t + 1 < SPW && sub + 1 < NSUB) {
+      load_lane_raw<DT>(rp.trow, rp.aligned, static_cast<long>(sub + 1) * kSub, lane, V, tn);
+      if (sp.mode == 1) load_lane_raw<DT>(rp.drow, rp.aligned, static_cast<long>(sub + 1) * kSub, lane, V, dn);
+    }
+    float aw[8], ap[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) aw[e] = ap[e] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+      float zp[Elem<DT>::kVec], zq[Elem<DT>::kVec];
+      widen_vec<DT>(tc[u], zp);
+      if (sp.mode == 1) widen_vec<DT>(dc[u], zq);
+#pragma unroll
+      for (int e = 0; e < Elem<DT>::kVec; ++e) {
+        float w, p;
+        residual_value(sp, zp[e], sp.mode == 1 ? zq[e] : 0.0f, w, p);
+        aw[e & 7] += w;
+        ap[e & 7] += p;
+      }
+    }
+    const float lw = ((aw[0] + aw[1]) + (aw[2] + aw[3])) + ((aw[4] + aw[5]) + (aw[6] + aw[7]));
+    const float lp = ((ap[0] + ap[1]) + (ap[2] + ap[3])) + ((ap[4] + ap[5]) + (ap[6] + ap[7]));
+    const double sw = wave_sum(static_cast<double>(lw));
+    const double spp = wave_sum(static_cast<double>(lp));
     if (lane == 0) {
       SubSums ss;
       ss.w = sw;
       ss.p = spp;
-      bs[s] = ss;
-      __threadfence();  // release the sums before the arrival count
+      sums[static_cast<long>(b) * NSUB + sub] = ss;
+    }
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+      tc[u] = tn[u];
+      dc[u] = dn[u];
     }
   }
-  __shared__ int sh_last;
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(&counters[b], 1u);
-    sh_last = (prev == static_cast<unsigned>(NW - 1));
-  }
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();  // acquire: every workgroup's sums are visible
+}
 
-  // pass 2 (last workgroup): total mass, then the sub-chunk holding u*Z
-  __shared__ double sh_scan[kWaves];
-  __shared__ int sh_sub;
-  __shared__ double sh_base;
-  double Zw = 0.0, Zp = 0.0;
-  for (int base = 0; base < NSUB; base += kBlock) {
-    const int s = base + tid;
-    double tw, tp;
-    block_scan((s < NSUB) ? bs[s].w : 0.0, sh_scan, &tw);
-    block_scan((s < NSUB) ? bs[s].p : 0.0, sh_scan, &tp);
-    Zw += tw;
-    Zp += tp;
+// K3b: one workgroup per request.  Every wave redundantly finds the total mass
+// Z (zero residual mass falls back to p_k) and the lowest sub-chunk with mass
+// whose inclusive prefix exceeds u*Z; then wave w scans tokens
+// [512 w, 512 w + 512) of that sub-chunk, 8 contiguous tokens per lane, and the
+// lowest token with mass whose running prefix exceeds u*Z is emitted.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k3_select(
+    const void *__restrict__ target, const void *__restrict__ draft,
+    const float *__restrict__ u_sample, int gamma, int V, int NSUB,
+    const SelParams *__restrict__ sel, const SubSums *__restrict__ sums,
+    int32_t *__restrict__ out_tokens, double *__restrict__ dbg_mass) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const SubSums *bs = sums + static_cast<long>(b) * NSUB;
+  // the first 64 sub-chunk masses are fetched together with the parameters
+  const double w0 = (lane < NSUB) ? bs[lane].w : 0.0;
+  const double p0 = (lane < NSUB) ? bs[lane].p : 0.0;
+  const SelParams sp = sel[b];
+  if (sp.mode == 0) return;  // uniform per workgroup
+  const float u = u_sample[b];
+
+  double Zw = wave_sum(w0), Zp = wave_sum(p0);
+  for (int base = kWave; base < NSUB; base += kWave) {
+    const int s = base + lane;
+    Zw += wave_sum(s < NSUB ? bs[s].w : 0.0);
+    Zp += wave_sum(s < NSUB ? bs[s].p : 0.0);
   }
   const bool use_p = !(Zw > 0.0);  // zero residual mass: fall back to p_k
   const double Z = use_p ? Zp : Zw;
-  const double target_mass = static_cast<double>(u_sample[b]) * Z;
-  if (tid == 0) sh_sub = 0x7fffffff;
-  __syncthreads();
-  double run = 0.0;
-  for (int base = 0; base < NSUB; base += kBlock) {
-    const int s = base + tid;
-    const double v = (s < NSUB) ? (use_p ? bs[s].p : bs[s].w) : 0.0;
-    double tot;
-    const double incl = block_scan(v, sh_scan, &tot);
-    // lowest sub-chunk with mass whose inclusive prefix exceeds u*Z
-    if (s < NSUB && v > 0.0 && run + incl > target_mass) atomicMin(&sh_sub, s);
-    __syncthreads();
-    if (s == sh_sub) sh_base = run + (incl - v);
-    __syncthreads();
-    if (sh_sub != 0x7fffffff) break;
-    run += tot;
-  }
-  if (sh_sub == 0x7fffffff) {  // rounding left u*Z at the very end: last sub-chunk with mass
-    __syncthreads();
-    if (tid == 0) {
-      int last = NSUB - 1;
-      for (int s = NSUB - 1; s >= 0; --s) {
-        if ((use_p ? bs[s].p : bs[s].w) > 0.0) {
-          last = s;
-          break;
-        }
-      }
-      double acc = 0.0;
-      for (int s = 0; s < last; ++s) acc += use_p ? bs[s].p : bs[s].w;
-      sh_sub = last;
-      sh_base = acc;
-    }
-    __syncthreads();
-  }
-  const int sub = sh_sub;
-  const double base_mass = sh_base;
+  const double target_mass = static_cast<double>(u) * Z;
 
-  // pass 3 (wave 0 of the last workgroup): the token inside the sub-chunk.  Each
-  // lane proposes its first token with mass whose running prefix exceeds u*Z;
-  // the lowest proposing lane wins.  Tokens with zero mass are never chosen.
-  if (wave == 0) {
-    float w[8], p[8];
-    const long e0 = static_cast<long>(sub) * kSub + lane * 8;
-    residual_lane<DT>(sp, trow, drow, aligned, e0, V, w, p);
-    const float *vals = use_p ? p : w;
-    const double lsum = static_cast<double>(sum8(vals));
-    const double incl = wave_scan(lsum, lane);
-    double acc = base_mass + (incl - lsum);
-    int cand = -1, last_pos = -1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (vals[e] > 0.0f) {
-        last_pos = e;
-        acc += static_cast<double>(vals[e]);
-        if (cand < 0 && target_mass < acc) cand = e;
+  int sub = -1;
+  double base_mass = 0.0, run = 0.0;
+  for (int base = 0; base < NSUB; base += kWave) {
+    const int s = base + lane;
+    const double v = (base == 0) ? (use_p ? p0 : w0) : (s < NSUB ? (use_p ? bs[s].p : bs[s].w) : 0.0);
+    const double incl = wave_scan(v, lane);
+    const unsigned long long hit = __ballot(s < NSUB && v > 0.0 && run + incl > target_mass);
+    if (hit) {
+      const int L = __ffsll(static_cast<long long>(hit)) - 1;
+      sub = base + L;
+      base_mass = run + __shfl(incl - v, L);
+      break;
+    }
+    run += __shfl(incl, kWave - 1);
+  }
+  if (sub < 0) {  // rounding left u*Z at the very end: the last sub-chunk with mass
+    run = 0.0;
+    for (int base = 0; base < NSUB; base += kWave) {
+      const int s = base + lane;
+      const double v = s < NSUB ? (use_p ? bs[s].p : bs[s].w) : 0.0;
+      const double incl = wave_scan(v, lane);
+      const unsigned long long has = __ballot(s < NSUB && v > 0.0);
+      if (has) {
+        const int L = 63 - __clzll(static_cast<long long>(has));
+        sub = base + L;
+        base_mass = run + __shfl(incl - v, L);
       }
+      run += __shfl(incl, kWave - 1);
     }
-    const unsigned long long props = __ballot(cand >= 0);
-    const long dst = static_cast<long>(b) * (gamma + 1) + sp.k;
-    if (props) {
-      const int L = __ffsll(static_cast<long long>(props)) - 1;
-      if (lane == L) out_tokens[dst] = static_cast<int>(e0 + cand);
-    } else {
-      // rounding left u*Z past the sub-chunk: its last token with mass
-      const unsigned long long has = __ballot(last_pos >= 0);
-      const int L = has ? 63 - __clzll(static_cast<long long>(has)) : 0;
-      if (lane == L) out_tokens[dst] = static_cast<int>(e0 + (last_pos >= 0 ? last_pos : 0));
+    if (sub < 0) {
+      sub = 0;
+      base_mass = 0.0;
     }
-    if (lane == 0 && dbg_mass) dbg_mass[b] = Z * sp.ip;
+  }
+
+  // tokens [first, first + 8) of this lane, in order through waves and lanes
+  const RowPair rp = selected_rows<DT>(target, draft, gamma, V, b, sp);
+  const long first = static_cast<long>(sub) * kSub + wave * (kSub / kWaves) + lane * 8;
+  float zp[8], zq[8];
+  load_vec_guarded<DT>(rp.trow, rp.aligned, first, V, zp);
+  if constexpr (DT == SV_F32) load_vec_guarded<DT>(rp.trow, rp.aligned, first + 4, V, zp + 4);
+  if (sp.mode == 1) {
+    load_vec_guarded<DT>(rp.drow, rp.aligned, first, V, zq);
+    if constexpr (DT == SV_F32) load_vec_guarded<DT>(rp.drow, rp.aligned, first + 4, V, zq + 4);
+  }
+  float vals[8];
+  double lsum = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float w, p;
+    residual_value(sp, zp[e], sp.mode == 1 ? zq[e] : 0.0f, w, p);
+    vals[e] = use_p ? p : w;
+    lsum += static_cast<double>(vals[e]);
+  }
+  const double incl = wave_scan(lsum, lane);
+  __shared__ double sh_tot[kWaves];
+  __shared__ int sh_pick[kWaves];
+  __shared__ int sh_last[kWaves];
+  if (lane == kWave - 1) sh_tot[wave] = incl;
+  __syncthreads();
+  double before = base_mass;
+  for (int w = 0; w < wave; ++w) before += sh_tot[w];
+  double acc = before + (incl - lsum);
+  int cand = -1, last_pos = -1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (vals[e] > 0.0f) {
+      last_pos = e;
+      acc += static_cast<double>(vals[e]);
+      if (cand < 0 && target_mass < acc) cand = e;
+    }
+  }
+  const unsigned long long props = __ballot(cand >= 0);
+  const unsigned long long has = __ballot(last_pos >= 0);
+  const int Lp = props ? __ffsll(static_cast<long long>(props)) - 1 : -1;
+  const int Lh = has ? 63 - __clzll(static_cast<long long>(has)) : -1;
+  // the winning token of this wave (first proposal), and its last token with mass
+  const int pick = Lp >= 0 ? static_cast<int>(__shfl(first + cand, Lp)) : -1;
+  const int lastm = Lh >= 0 ? static_cast<int>(__shfl(first + last_pos, Lh)) : -1;
+  if (lane == 0) {
+    sh_pick[wave] = pick;
+    sh_last[wave] = lastm;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int tok = -1;
+    for (int w = 0; w < kWaves && tok < 0; ++w) tok = sh_pick[w];
+    // rounding left u*Z past the sub-chunk: its last token with mass
+    for (int w = kWaves - 1; w >= 0 && tok < 0; --w) tok = sh_last[w];
+    if (tok < 0) tok = static_cast<int>(static_cast<long>(sub) * kSub);
+    out_tokens[static_cast<long>(b) * (gamma + 1) + sp.k] = tok;
+    if (dbg_mass) dbg_mass[b] = Z * sp.ip;
   }
 }
 
 // ================================================================== host side
 struct Plan {
-  int rows, U, NS, NSUB, SPW, NW;
-  long k1_tiles, k3_groups;
-  size_t part_off, sel_off, sums_off, cnt_off, total;
+  int rows, NS, chunk_vecs, NSUB, SPW, NW;
+  long k1_groups, k3_groups;
+  size_t part_off, zx_off, sel_off, sums_off, total;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+constexpr int kK1U = 8;                 // 16-byte vectors per thread per K1 tile
+constexpr long kK1TargetGroups = 2816;  // about 11 workgroups per CU on 256 CUs
+constexpr long kK3TargetWaves = 2048;   // waves of the mass pass (8 per CU)
 
 bool make_plan(int B, int gamma, int V, int dtype, Plan *P) {
   if (B < 1 || gamma < 0 || gamma > SV_GAMMA_MAX || V < 1) return false;
@@ -651,47 +920,47 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P) {
   const int vec = dtype == SV_BF16 ? 8 : 4;
   P->rows = 2 * gamma + 1;
   const long slots = static_cast<long>(B) * P->rows;
-  // largest tile (up to 64 elements per thread) that still gives >= 1024 workgroups
-  int U = 8;
-  while (U > 1 && slots * ((V + static_cast<long>(kBlock) * U * vec - 1) / (static_cast<long>(kBlock) * U * vec)) < 1024)
-    U /= 2;
-  P->U = U;
-  const long tile = static_cast<long>(kBlock) * U * vec;
-  P->NS = static_cast<int>((V + tile - 1) / tile);
-  P->k1_tiles = slots * P->NS;
+  // split each row into NS chunks of whole K1 tiles: enough workgroups to fill
+  // the chip, no chunk shorter than one tile
+  const long vecs = (V + vec - 1) / vec;
+  const long tile = static_cast<long>(kK1U) * kBlock;
+  const long tiles_per_row = (vecs + tile - 1) / tile;
+  long NS = (kK1TargetGroups + slots / 2) / slots;
+  if (NS < 1) NS = 1;
+  if (NS > tiles_per_row) NS = tiles_per_row;
+  P->NS = static_cast<int>(NS);
+  P->chunk_vecs = static_cast<int>((vecs + NS - 1) / NS);
+  P->k1_groups = slots * NS;
   P->NSUB = (V + kSub - 1) / kSub;
-  int SPW = 4;
-  while (SPW > 1 && static_cast<long>(B) * ((P->NSUB + kWaves * SPW - 1) / (kWaves * SPW)) < 1024) SPW /= 2;
-  P->SPW = SPW;
-  P->NW = (P->NSUB + kWaves * SPW - 1) / (kWaves * SPW);
+  // sub-chunks per wave in the mass pass: pipeline two per wave when the batch
+  // still gives about 2048 waves, else one
+  const long subs = static_cast<long>(B) * P->NSUB;
+  P->SPW = subs >= 2 * kK3TargetWaves ? 2 : 1;
+  P->NW = (P->NSUB + kWaves * P->SPW - 1) / (kWaves * P->SPW);
   P->k3_groups = static_cast<long>(B) * P->NW;
   // 1-D grids: work-items per launch must stay below 2^32
   const long max_groups = (1L << 32) / kBlock - 1;
-  if (P->k1_tiles > max_groups || P->k3_groups > max_groups) return false;
+  if (P->k1_groups > max_groups || P->k3_groups > max_groups) return false;
   size_t off = 0;
   P->part_off = off;
-  off = align_up(off + sizeof(Partial) * static_cast<size_t>(P->k1_tiles));
+  off = align_up(off + sizeof(Partial) * static_cast<size_t>(P->k1_groups));
+  P->zx_off = off;
+  off = align_up(off + sizeof(float) * static_cast<size_t>(slots));
   P->sel_off = off;
   off = align_up(off + sizeof(SelParams) * static_cast<size_t>(B));
   P->sums_off = off;
   off = align_up(off + sizeof(SubSums) * static_cast<size_t>(B) * P->NSUB);
-  P->cnt_off = off;
-  off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B));
   P->total = off;
   return true;
 }
 
 template <int DT>
-hipError_t launch_k1(int U, const void *target, const void *draft, const float *temps, float scalar_T,
-                     const int32_t *lens, int gamma, int V, const Plan &P, Partial *part,
-                     hipStream_t st) {
-  dim3 grid(static_cast<unsigned>(P.k1_tiles)), block(kBlock);
-  switch (U) {
-    case 8: hipLaunchKernelGGL((k1_row_stats<DT, 8>), grid, block, 0, st, target, draft, temps, scalar_T, lens, gamma, V, P.NS, part); break;
-    case 4: hipLaunchKernelGGL((k1_row_stats<DT, 4>), grid, block, 0, st, target, draft, temps, scalar_T, lens, gamma, V, P.NS, part); break;
-    case 2: hipLaunchKernelGGL((k1_row_stats<DT, 2>), grid, block, 0, st, target, draft, temps, scalar_T, lens, gamma, V, P.NS, part); break;
-    default: hipLaunchKernelGGL((k1_row_stats<DT, 1>), grid, block, 0, st, target, draft, temps, scalar_T, lens, gamma, V, P.NS, part); break;
-  }
+hipError_t launch_k1(const void *target, const void *draft, const int32_t *tokens, const float *temps,
+                     float scalar_T, const int32_t *lens, int gamma, int V, const Plan &P, Partial *part,
+                     float *zx, hipStream_t st) {
+  hipLaunchKernelGGL((k1_row_stats<DT, kK1U>), dim3(static_cast<unsigned>(P.k1_groups)), dim3(kBlock), 0,
+                     st, target, draft, tokens, temps, scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, part,
+                     zx);
   return hipGetLastError();
 }
 
@@ -702,24 +971,26 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
         const Plan &P, hipStream_t st, const sv_debug *dbgp) {
   char *base = static_cast<char *>(ws);
   Partial *part = reinterpret_cast<Partial *>(base + P.part_off);
+  float *zx = reinterpret_cast<float *>(base + P.zx_off);
   SelParams *sel = reinterpret_cast<SelParams *>(base + P.sel_off);
   SubSums *sums = reinterpret_cast<SubSums *>(base + P.sums_off);
-  unsigned *cnt = reinterpret_cast<unsigned *>(base + P.cnt_off);
   sv_debug dbg;
   memset(&dbg, 0, sizeof dbg);
   if (dbgp) dbg = *dbgp;
   const bool timed = dbg.k1_events[0] && dbg.k1_events[1];
   if (timed && hipEventRecord(static_cast<hipEvent_t>(dbg.k1_events[0]), st) != hipSuccess) return SV_EHIP;
-  hipError_t e = launch_k1<DT>(P.U, target, draft, temps, scalar_T, lens, gamma, V, P, part, st);
+  hipError_t e = launch_k1<DT>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx, st);
   if (e != hipSuccess) return SV_EHIP;
   if (timed && hipEventRecord(static_cast<hipEvent_t>(dbg.k1_events[1]), st) != hipSuccess) return SV_EHIP;
-  hipLaunchKernelGGL((k2_decide<DT>), dim3(B), dim3(kK2Block), 0, st, target, draft, tokens, u_accept,
-                     temps, scalar_T, lens, gamma, V, P.NS, part, count, out, sel, cnt, dbg);
+  // greedy-only batches need the decision alone: one workgroup per request
+  const int nw = all_greedy ? 1 : P.NW;
+  hipLaunchKernelGGL((k2_decide_mass<DT>), dim3(static_cast<unsigned>(static_cast<long>(B) * nw)),
+                     dim3(kBlock), 0, st, target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V,
+                     P.NS, P.NSUB, nw, P.SPW, part, zx, count, out, sel, sums, dbg);
   if (hipGetLastError() != hipSuccess) return SV_EHIP;
   if (!all_greedy) {
-    hipLaunchKernelGGL((k3_sample<DT>), dim3(static_cast<unsigned>(P.k3_groups)), dim3(kBlock), 0, st,
-                       target, draft, u_sample, gamma, V, P.NSUB, P.SPW, P.NW, sel, sums, cnt, out,
-                       dbg.residual_mass);
+    hipLaunchKernelGGL((k3_select<DT>), dim3(B), dim3(kBlock), 0, st, target, draft, u_sample, gamma, V,
+                       P.NSUB, sel, sums, out, dbg.residual_mass);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
   }
   return SV_OK;
