@@ -58,7 +58,105 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly instead of graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="summarise rocprofv3 CSV output under DIR (kt/, pmc_FETCH_SIZE/, pmc_WRITE_SIZE/, "
+                         "copy_FETCH_SIZE/, copy_WRITE_SIZE/) into profiles/")
     return ap.parse_args()
+
+
+# --------------------------------------------------------------------------- profile summaries
+PROFILE_COMMANDS = {
+    "kt": "rocprofv3 --kernel-trace --stats -d DIR/kt -o kt --output-format csv -- python3 bench.py",
+    "pmc_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -d DIR/pmc_FETCH_SIZE -o pmc --output-format csv -- "
+                      "python3 bench.py --steps 14 --warmup 7 --no-cpu-baseline --eager",
+    "pmc_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -d DIR/pmc_WRITE_SIZE -o pmc --output-format csv -- "
+                      "python3 bench.py --steps 14 --warmup 7 --no-cpu-baseline --eager",
+    "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -d DIR/copy_FETCH_SIZE -o pmc --output-format csv -- "
+                       "python3 bench.py --copy-calibration",
+    "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -d DIR/copy_WRITE_SIZE -o pmc --output-format csv -- "
+                       "python3 bench.py --copy-calibration",
+}
+
+
+def _kernel_short(name: str) -> str:
+    import re
+    m = re.search(r"::(k\w+)<", name)
+    if m:
+        return m.group(1)
+    return name.split("(")[0][:60]
+
+
+def _find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def summarize_profile(root: str):
+    import csv
+    import statistics
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    # kernel trace statistics
+    stats = list(csv.DictReader(open(_find_csv(os.path.join(root, "kt"), "kernel_stats.csv"))))
+    lines = ["# Kernel durations: B=64, gamma=5, V=128256 bf16, T=1 (stochastic)", "",
+             "Command (from the repository root, output under DIR):", "",
+             "    " + PROFILE_COMMANDS["kt"], "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    k1_avg_ns = None
+    for r in stats:
+        n = _kernel_short(r["Name"])
+        lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+        if n == "k1_row_stats":
+            k1_avg_ns = float(r["AverageNs"])
+    lines += ["", "The copy kernels are the benchmark's set-up (input copies), outside the timed region.", ""]
+    open(os.path.join(out_dir, "kernels_B64_g5_V128256_bf16.md"), "w").write("\n".join(lines))
+
+    def pmc_medians(d):
+        rows = list(csv.DictReader(open(_find_csv(os.path.join(root, d), "counter_collection.csv"))))
+        by = {}
+        for r in rows:
+            by.setdefault(_kernel_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in by.items()}, {k: len(v) for k, v in by.items()}
+
+    fetch, nf = pmc_medians("pmc_FETCH_SIZE")
+    write, nw = pmc_medians("pmc_WRITE_SIZE")
+    cfetch, _ = pmc_medians("copy_FETCH_SIZE")
+    cwrite, _ = pmc_medians("copy_WRITE_SIZE")
+    copy_name = max(cfetch, key=lambda k: cfetch[k])   # the 1 GiB copy kernel (the fill reads nothing)
+    copy_kib = (1 << 30) / 1024
+    f_fetch = copy_kib / cfetch[copy_name]
+    f_write = copy_kib / cwrite[copy_name]
+    k1_bytes = (fetch["k1_row_stats"] * f_fetch + write["k1_row_stats"] * f_write) * 1024
+    bytes_alg = 64 * 11 * 128256 * 2
+    rec = {"kernel": "k1_row_stats", "mode": "stochastic", "kernel_source_sha256_16": source_hash(),
+           "fetch_kib_per_dispatch": fetch["k1_row_stats"], "write_kib_per_dispatch": write["k1_row_stats"],
+           "copy_kernel": copy_name, "copy_fetch_kib": cfetch[copy_name], "copy_write_kib": cwrite[copy_name],
+           "fetch_scale": f_fetch, "write_scale": f_write, "hbm_bytes_per_launch": round(k1_bytes),
+           "bytes_alg_per_launch": bytes_alg, "traffic_over_alg": k1_bytes / bytes_alg,
+           "k1_avg_us_kernel_trace": None if k1_avg_ns is None else k1_avg_ns / 1e3,
+           "commands": {k: PROFILE_COMMANDS[k] for k in ("pmc_FETCH_SIZE", "pmc_WRITE_SIZE", "copy_FETCH_SIZE",
+                                                          "copy_WRITE_SIZE")}}
+    json.dump(rec, open(PROFILE_PMC, "w"), indent=2)
+    lines = ["# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE, KiB)", "",
+             "Workload: B=64, gamma=5, V=128256 bf16, T=1 (stochastic), eager launches.", "",
+             "Commands (from the repository root, output under DIR):", ""]
+    lines += ["    " + PROFILE_COMMANDS[k] for k in ("pmc_FETCH_SIZE", "pmc_WRITE_SIZE", "copy_FETCH_SIZE",
+                                                       "copy_WRITE_SIZE")]
+    lines += ["", "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) |", "|---|---|---|---|"]
+    for k in fetch:
+        lines.append(f"| {k} | {nf[k]} | {fetch[k]:.1f} | {write.get(k, float('nan')):.1f} |")
+    lines += ["", f"Calibration: the plain 1 GiB device copy ({copy_name}) reads {cfetch[copy_name]:.1f} KiB "
+              f"and writes {cwrite[copy_name]:.1f} KiB by these counters, so FETCH_SIZE is scaled by "
+              f"{f_fetch:.4f} and WRITE_SIZE by {f_write:.4f} to give bytes.",
+              "", f"k1_row_stats: {k1_bytes / 1e6:.2f} MB per launch against {bytes_alg / 1e6:.2f} MB algorithmic "
+              f"(ratio {k1_bytes / bytes_alg:.4f}).", ""]
+    open(os.path.join(out_dir, "hbm_traffic_B64_g5_V128256_bf16.md"), "w").write("\n".join(lines))
+    print(json.dumps(rec, indent=2))
 
 
 def copy_calibration():
@@ -76,6 +174,9 @@ def copy_calibration():
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(requests are independent, so a multi-GPU run would shard the batch with no exchange).",

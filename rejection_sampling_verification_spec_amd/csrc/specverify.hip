@@ -37,6 +37,7 @@
 // Numerics: bf16 -> fp32 widening is exact; exponentials are v_exp_f32 of
 // fma(z, c, -M); per-thread partial sums are fp32 over at most 64 terms and
 // everything above a thread (wave, workgroup, tile, CDF prefix) is fp64.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -429,7 +430,6 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
 constexpr int kK2Batch = 8;  // chunk partials fetched together per row
 
 struct DecideShared {
-  double L[2 * SV_GAMMA_MAX + 1];  // log2 of each row's partition sum
   double s[2 * SV_GAMMA_MAX + 1];
   int M[2 * SV_GAMMA_MAX + 1];
   int arg[2 * SV_GAMMA_MAX + 1];
@@ -458,7 +458,6 @@ __device__ __forceinline__ void decide_request(
   const float c = greedy ? 0.0f : temp_scale(T);
   sv_debug dbg = dbg_in;
   if (!writer) memset(&dbg, 0, sizeof dbg);
-  double *sh_L = sh.L;
   double *sh_s = sh.s;
   int *sh_M = sh.M;
   int *sh_arg = sh.arg;
@@ -506,7 +505,6 @@ __device__ __forceinline__ void decide_request(
       if (!greedy) {
         sh_M[r] = M;
         sh_s[r] = s;
-        sh_L[r] = static_cast<double>(M) + log2(s);
         if (dbg.row_max) dbg.row_max[static_cast<long>(b) * rows + r] = mx;
         if (dbg.row_sum)  // sum_v exp((z_v - max)/T) = s * 2^(M - max c)
           dbg.row_sum[static_cast<long>(b) * rows + r] =
@@ -529,15 +527,18 @@ __device__ __forceinline__ void decide_request(
         reject = (x != sh_arg[tid]);
       } else {
         const double cd = static_cast<double>(c);
-        // log2 p_i(x) and log2 q_i(x) in fp64: z*c - log2(sum 2^(z c))
-        const double lp = static_cast<double>(zpx) * cd - sh_L[tid];
-        const double lq = static_cast<double>(zqx) * cd - sh_L[gamma + 1 + tid];
-        const double ratio = exp2(lp - lq);
+        // p_i(x) / q_i(x) = 2^((zp - zq) c - (Mp - Mq)) * s'_q / s'_p, in fp64; the
+        // logit difference is exact and the exponent stays O(1)
+        const int Mp = sh_M[tid], Mq = sh_M[gamma + 1 + tid];
+        const double sp_ = sh_s[tid], sq_ = sh_s[gamma + 1 + tid];
+        const double d = (static_cast<double>(zpx) - static_cast<double>(zqx)) * cd -
+                         static_cast<double>(Mp - Mq);
+        const double ratio = exp2(d) * (sq_ / sp_);
         const double a = ratio < 1.0 ? ratio : 1.0;
         reject = !(static_cast<double>(ua) < a);
         const long o = static_cast<long>(b) * gamma + tid;
-        if (dbg.p_draft) dbg.p_draft[o] = exp2(lp);
-        if (dbg.q_draft) dbg.q_draft[o] = exp2(lq);
+        if (dbg.p_draft) dbg.p_draft[o] = exp2(static_cast<double>(zpx) * cd - Mp) / sp_;
+        if (dbg.q_draft) dbg.q_draft[o] = exp2(static_cast<double>(zqx) * cd - Mq) / sq_;
         if (dbg.accept_prob) dbg.accept_prob[o] = a;
       }
     }
@@ -954,13 +955,20 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P) {
   return true;
 }
 
+// K1 launch; with an event pair the dispatch itself is timestamped (the
+// events bracket the kernel's execution, as a kernel trace does).
 template <int DT>
 hipError_t launch_k1(const void *target, const void *draft, const int32_t *tokens, const float *temps,
                      float scalar_T, const int32_t *lens, int gamma, int V, const Plan &P, Partial *part,
-                     float *zx, hipStream_t st) {
-  hipLaunchKernelGGL((k1_row_stats<DT, kK1U>), dim3(static_cast<unsigned>(P.k1_groups)), dim3(kBlock), 0,
-                     st, target, draft, tokens, temps, scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, part,
-                     zx);
+                     float *zx, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const dim3 grid(static_cast<unsigned>(P.k1_groups)), block(kBlock);
+  if (ev0 && ev1) {
+    hipExtLaunchKernelGGL((k1_row_stats<DT, kK1U>), grid, block, 0, st, ev0, ev1, 0, target, draft, tokens,
+                          temps, scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, part, zx);
+  } else {
+    hipLaunchKernelGGL((k1_row_stats<DT, kK1U>), grid, block, 0, st, target, draft, tokens, temps, scalar_T,
+                       lens, gamma, V, P.NS, P.chunk_vecs, part, zx);
+  }
   return hipGetLastError();
 }
 
@@ -977,11 +985,10 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
   sv_debug dbg;
   memset(&dbg, 0, sizeof dbg);
   if (dbgp) dbg = *dbgp;
-  const bool timed = dbg.k1_events[0] && dbg.k1_events[1];
-  if (timed && hipEventRecord(static_cast<hipEvent_t>(dbg.k1_events[0]), st) != hipSuccess) return SV_EHIP;
-  hipError_t e = launch_k1<DT>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx, st);
+  hipError_t e = launch_k1<DT>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx, st,
+                               static_cast<hipEvent_t>(dbg.k1_events[0]),
+                               static_cast<hipEvent_t>(dbg.k1_events[1]));
   if (e != hipSuccess) return SV_EHIP;
-  if (timed && hipEventRecord(static_cast<hipEvent_t>(dbg.k1_events[1]), st) != hipSuccess) return SV_EHIP;
   // greedy-only batches need the decision alone: one workgroup per request
   const int nw = all_greedy ? 1 : P.NW;
   hipLaunchKernelGGL((k2_decide_mass<DT>), dim3(static_cast<unsigned>(static_cast<long>(B) * nw)),
