@@ -262,14 +262,52 @@ __device__ __forceinline__ void fold_tile(const u32x4 *v, float c, int &M, doubl
   }
 }
 
+// U vectors per thread of the tile starting at vector t0 of the chunk [.., v1).
+// Every lane loads (indices are clamped into the chunk, so the code is straight
+// line and the compiler can wait for exactly the older tile); lanes past v1
+// then hold -inf.
 template <int DT, int U>
+__device__ __forceinline__ void load_tile(const u32x4 *rv, int t0, int v1, int tid, u32x4 *dst) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int vi = t0 + u * kBlock + tid;
+    const u32x4 x = load_nt(rv + min(vi, v1 - 1));
+    dst[u] = (vi < v1) ? x : neg_inf_vec<DT>();
+  }
+}
+
+// Streams the vectors [v0, v1) of a row in tiles of U vectors per thread with
+// two register buffers: the next tile is in flight while the current one is
+// folded.  fold(tile, t0) sees each tile once, in order.
+template <int DT, int U, typename Fold>
+__device__ __forceinline__ void stream_chunk(const u32x4 *rv, int v0, int v1, int tid, Fold &&fold) {
+  constexpr int kTileVecs = U * kBlock;
+  if (v0 >= v1) return;
+  u32x4 a[U], b[U];
+  load_tile<DT, U>(rv, v0, v1, tid, a);
+  for (int t0 = v0;;) {
+    load_tile<DT, U>(rv, t0 + kTileVecs, v1, tid, b);
+    fold(a, t0);
+    t0 += kTileVecs;
+    if (t0 >= v1) break;
+    load_tile<DT, U>(rv, t0 + kTileVecs, v1, tid, a);
+    fold(b, t0);
+    t0 += kTileVecs;
+    if (t0 >= v1) break;
+  }
+}
+
+// Which request kinds a K1 instantiation handles: the uniform entry point knows
+// on the host whether every row is stochastic or every row greedy.
+enum { kMixed = 0, kStochasticOnly = 1, kGreedyOnly = 2 };
+
+template <int DT, int U, int KIND>
 __global__ __launch_bounds__(kBlock) void k1_row_stats(
     const void *__restrict__ target, const void *__restrict__ draft,
     const int32_t *__restrict__ tokens, const float *__restrict__ temps, float scalar_T,
     const int32_t *__restrict__ lens, int gamma, int V, int NCH, int chunk_vecs,
     Partial *__restrict__ part, float *__restrict__ zx) {
   constexpr int kV = Elem<DT>::kVec;
-  constexpr int kTileVecs = U * kBlock;
   const int rows = 2 * gamma + 1;
   const int wgid = blockIdx.x;
   const int slot = wgid / NCH;
@@ -280,7 +318,7 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   const float T = request_T(temps, scalar_T, b);
   const bool is_target = r <= gamma;
   const int i = is_target ? r : r - gamma - 1;
-  const bool greedy = !(T > 0.0f);
+  const bool greedy = KIND == kGreedyOnly ? true : (KIND == kStochasticOnly ? false : !(T > 0.0f));
   if (is_target ? (i > g) : (greedy || i >= g)) return;
 
   const char *row =
@@ -316,28 +354,12 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   __shared__ float sh_mx[kWaves];
   __shared__ int sh_mi[kWaves];
 
-  u32x4 cur[U], nxt[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int vi = v0 + u * kBlock + tid;
-    cur[u] = (vi < v1) ? load_nt(rv + vi) : neg_inf_vec<DT>();
-  }
-
   if (!greedy) {
     const float c = temp_scale(T);
     int M = kEmptyM;
     double s = 0.0;
     float mx = -INFINITY;
-    for (int t0 = v0; t0 < v1; t0 += kTileVecs) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int vi = t0 + kTileVecs + u * kBlock + tid;
-        nxt[u] = (vi < v1) ? load_nt(rv + vi) : neg_inf_vec<DT>();
-      }
-      fold_tile<DT, U>(cur, c, M, s, mx);
-#pragma unroll
-      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-    }
+    stream_chunk<DT, U>(rv, v0, v1, tid, [&](const u32x4 *tile, int) { fold_tile<DT, U>(tile, c, M, s, mx); });
     for (long e = se0 + tid; e < se1; e += kBlock) {
       const float z = load_one<DT>(row, e);
       fold_values<1>(&z, c, M, s, mx);
@@ -371,18 +393,13 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
     // increasing index order, so a strict > keeps the first occurrence
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int t0 = v0; t0 < v1; t0 += kTileVecs) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int vi = t0 + kTileVecs + u * kBlock + tid;
-        nxt[u] = (vi < v1) ? load_nt(rv + vi) : neg_inf_vec<DT>();
-      }
+    stream_chunk<DT, U>(rv, v0, v1, tid, [&](const u32x4 *tile, int t0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int vi = t0 + u * kBlock + tid;
         if (vi < v1) {
           float x[kV];
-          widen_vec<DT>(cur[u], x);
+          widen_vec<DT>(tile[u], x);
 #pragma unroll
           for (int e = 0; e < kV; ++e) {
             if (x[e] > bv || bi == 0x7fffffff) {
@@ -392,9 +409,7 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
           }
         }
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-    }
+    });
     for (long e = se0 + tid; e < se1; e += kBlock) {
       const float z = load_one<DT>(row, e);
       if (z > bv || bi == 0x7fffffff) {
@@ -632,21 +647,37 @@ __device__ __forceinline__ void load_lane32(const void *row, bool aligned, long 
   }
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off /= 2) v += __shfl_xor(v, off);
+// fp64 wave scan / sum with DPP row shifts and row broadcasts (no LDS round
+// trip).  Lanes without a source read 0, the identity of the sum.  Called with
+// the whole wave active.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const long long bits = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), CTRL, ROW_MASK, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), CTRL, ROW_MASK, 0xf, true);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
+// inclusive prefix over the 64 lanes of a wave
+__device__ __forceinline__ double wave_scan(double v, int /*lane*/) {
+  v += dpp_f64<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_f64<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_f64<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_f64<0x118, 0xf>(v);  // row_shr:8   (each row of 16 now holds its own prefix)
+  v += dpp_f64<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f64<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
-// inclusive prefix over the 64 lanes of a wave (fp64)
-__device__ __forceinline__ double wave_scan(double v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off *= 2) {
-    const double o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
-  return v;
+__device__ __forceinline__ double lane_value(double v, int lane) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(bits), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(bits >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
 }
+
+// sum over the wave, the same value in every lane
+__device__ __forceinline__ double wave_sum(double v) { return lane_value(wave_scan(v, 0), kWave - 1); }
 
 struct RowPair {
   const void *trow, *drow;
@@ -817,10 +848,10 @@ __global__ __launch_bounds__(kBlock) void k3_select(
     if (hit) {
       const int L = __ffsll(static_cast<long long>(hit)) - 1;
       sub = base + L;
-      base_mass = run + __shfl(incl - v, L);
+      base_mass = run + lane_value(incl - v, L);
       break;
     }
-    run += __shfl(incl, kWave - 1);
+    run += lane_value(incl, kWave - 1);
   }
   if (sub < 0) {  // rounding left u*Z at the very end: the last sub-chunk with mass
     run = 0.0;
@@ -832,9 +863,9 @@ __global__ __launch_bounds__(kBlock) void k3_select(
       if (has) {
         const int L = 63 - __clzll(static_cast<long long>(has));
         sub = base + L;
-        base_mass = run + __shfl(incl - v, L);
+        base_mass = run + lane_value(incl - v, L);
       }
-      run += __shfl(incl, kWave - 1);
+      run += lane_value(incl, kWave - 1);
     }
     if (sub < 0) {
       sub = 0;
@@ -957,19 +988,33 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P) {
 
 // K1 launch; with an event pair the dispatch itself is timestamped (the
 // events bracket the kernel's execution, as a kernel trace does).
+template <int DT, int KIND>
+hipError_t launch_k1_kind(const void *target, const void *draft, const int32_t *tokens, const float *temps,
+                          float scalar_T, const int32_t *lens, int gamma, int V, const Plan &P,
+                          Partial *part, float *zx, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const dim3 grid(static_cast<unsigned>(P.k1_groups)), block(kBlock);
+  if (ev0 && ev1) {
+    hipExtLaunchKernelGGL((k1_row_stats<DT, kK1U, KIND>), grid, block, 0, st, ev0, ev1, 0, target, draft,
+                          tokens, temps, scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, part, zx);
+  } else {
+    hipLaunchKernelGGL((k1_row_stats<DT, kK1U, KIND>), grid, block, 0, st, target, draft, tokens, temps,
+                       scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, part, zx);
+  }
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_k1(const void *target, const void *draft, const int32_t *tokens, const float *temps,
                      float scalar_T, const int32_t *lens, int gamma, int V, const Plan &P, Partial *part,
                      float *zx, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  const dim3 grid(static_cast<unsigned>(P.k1_groups)), block(kBlock);
-  if (ev0 && ev1) {
-    hipExtLaunchKernelGGL((k1_row_stats<DT, kK1U>), grid, block, 0, st, ev0, ev1, 0, target, draft, tokens,
-                          temps, scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, part, zx);
-  } else {
-    hipLaunchKernelGGL((k1_row_stats<DT, kK1U>), grid, block, 0, st, target, draft, tokens, temps, scalar_T,
-                       lens, gamma, V, P.NS, P.chunk_vecs, part, zx);
-  }
-  return hipGetLastError();
+  if (temps)
+    return launch_k1_kind<DT, kMixed>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx,
+                                      st, ev0, ev1);
+  if (scalar_T > 0.0f)
+    return launch_k1_kind<DT, kStochasticOnly>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P,
+                                               part, zx, st, ev0, ev1);
+  return launch_k1_kind<DT, kGreedyOnly>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx,
+                                         st, ev0, ev1);
 }
 
 template <int DT>
