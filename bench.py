@@ -308,6 +308,40 @@ def main():
                 "kernel": "k1_row_stats", "kernel_avg_us": round(k1_avg_s * 1e6, 3),
                 "bytes_per_launch": bytes_alg}
 
+    # draft-side sampling (one token per row of softmax(z/T)) on the same draft logits:
+    # 64 rows (one drafting step of the batch) and 320 rows (all five positions)
+    sample = {}
+    if not greedy:
+        for R in (B, B * gamma):
+            rows = [d.view(B * gamma, V)[:R] for d in drafts]
+            us = t["u_accept"].reshape(-1)[:R].contiguous()
+            toks = torch.empty(R, dtype=torch.int32, device=dev)
+            sws = torch.empty(sv.spec_sample_workspace_bytes(R, V, sv.SV_BF16), dtype=torch.uint8, device=dev)
+
+            def sstep(c, R=R, rows=rows, us=us, toks=toks, sws=sws):
+                sv.spec_sample(rows[c], us, T, tokens=toks, workspace=sws, stream=stream)
+
+            with torch.cuda.stream(stream):
+                sstep(0)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for c in range(copies):
+                    sstep(c)
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, args.steps // copies)
+            s0 = time.perf_counter()
+            with torch.cuda.stream(stream):
+                for _ in range(reps):
+                    g.replay()
+            torch.cuda.synchronize()
+            per = (time.perf_counter() - s0) / (reps * copies)
+            sample[f"rows_{R}"] = {"us_per_call": round(per * 1e6, 3), "rows_per_s": round(R / per, 1),
+                                   "GBps": round(R * V * 2 / per / 1e9, 1)}
+        log(f"[bench] spec_sample {sample}")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -347,6 +381,7 @@ def main():
                   "device_ms_per_step": round(dev_ms / args.steps, 5),
                   "k1_us_min": round(min(k1_ms) * 1e3, 3), "k1_us_max": round(max(k1_ms) * 1e3, 3),
                   "alpha_hat": round(float(ref_count.float().mean()) / gamma, 4),
+                  "spec_sample": sample,
                   "kernel_source_sha256_16": source_hash()},
     }
     print(json.dumps(rec), flush=True)

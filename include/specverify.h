@@ -128,6 +128,25 @@ int spec_verify_ex(const void *target_logits, const void *draft_logits,
                    void *workspace, size_t workspace_bytes, void *stream,
                    const sv_debug *dbg);
 
+/* Draft-side sampling: one token per row of softmax(logits[r] / T_r), drawn by
+ * the inverse CDF in vocabulary order with the supplied uniform u[r]: the
+ * smallest v with u*Z < w[0] + ... + w[v] (the categorical draw that drafting
+ * performs before verification: P2 code sketch, multinomial over
+ * softmax(logits / temperature); P4 section 検証アルゴリズムの実装).  T_r == 0
+ * gives the lowest-index arg-max.  This runs the verify kernels with no drafts.
+ * logits:       DEVICE [R][V] dt, row-major
+ * u:            DEVICE [R] in [0, 1)
+ * temperature:  host scalar used when `temperatures` is NULL (>= 0, finite)
+ * temperatures: DEVICE [R] per-row temperatures, or NULL
+ * tokens:       DEVICE out [R]
+ * workspace:    spec_sample_workspace_bytes(R, V, dtype) bytes, 256-byte aligned
+ * Errors as for spec_verify. */
+size_t spec_sample_workspace_bytes(int R, int V, int dtype);
+int spec_sample(const void *logits, const float *u, float temperature,
+                const float *temperatures, int R, int V, int dtype,
+                int32_t *tokens, void *workspace, size_t workspace_bytes,
+                void *stream);
+
 /* Static description of a return code. */
 const char *spec_verify_strerror(int code);
 

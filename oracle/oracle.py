@@ -141,3 +141,14 @@ def run_workload(w, trace: bool = True, lib: Optional[ctypes.CDLL] = None) -> Or
     """Convenience: run the oracle on a ``workloads.Workload``."""
     return spec_verify(w.target, w.draft, w.draft_tokens, w.u_accept, w.u_sample, w.temperature,
                        lens=w.lens, dtype=w.dtype, trace=trace, lib=lib)
+
+
+def sample(logits, u, temperature, dtype: Optional[str] = None, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """One token per row of softmax(logits / T) by inverse CDF with the uniforms u.
+
+    This is the oracle's verify step with no drafts (every row is a bonus row)."""
+    logits = np.asarray(logits)
+    R, V = logits.shape
+    res = spec_verify(logits.reshape(R, 1, V), np.zeros((R, 0, V), dtype=logits.dtype), np.zeros((R, 0)),
+                      np.zeros((R, 0)), u, temperature, dtype=dtype, trace=True, lib=lib)
+    return res.out_tokens[:, 0].copy(), res

@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     LibraryMissing,
     SpecVerifyError,
     load_library,
+    spec_sample,
+    spec_sample_workspace_bytes,
     spec_verify,
     spec_verify_ex,
     spec_verify_strerror,

@@ -27,6 +27,8 @@ EXPORTED_SYMBOLS = (
     "spec_verify_workspace_bytes",
     "spec_verify",
     "spec_verify_ex",
+    "spec_sample_workspace_bytes",
+    "spec_sample",
     "spec_verify_strerror",
 )
 
@@ -79,6 +81,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                    vp, vp, vp, sz, vp, ctypes.POINTER(SvDebug)]
     lib.spec_verify_ex.restype = i32
+    lib.spec_sample_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spec_sample_workspace_bytes.restype = sz
+    lib.spec_sample.argtypes = [vp, vp, ctypes.c_float, vp, i32, i32, i32, vp, vp, sz, vp]
+    lib.spec_sample.restype = i32
     lib.spec_verify_strerror.argtypes = [i32]
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -240,3 +246,39 @@ def spec_verify_ex(target_logits, draft_logits, draft_tokens, u_accept, u_sample
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_ex")
     return accepted_count, out_tokens
+
+
+def spec_sample_workspace_bytes(R: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_sample_workspace_bytes(R, V, dtype))
+
+
+def spec_sample(logits, u, temperature, tokens=None, workspace=None, stream=None):
+    """One token per row of softmax(logits / T) by inverse CDF with the uniforms ``u``.
+
+    logits: device [R, V] bf16/fp32; u: device [R] fp32; temperature: float, or a
+    device fp32 tensor [R] of per-row temperatures (0 = arg-max).  Returns tokens [R] int32.
+    """
+    import torch
+    lib = load_library()
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R, V]")
+    R, V = int(logits.shape[0]), int(logits.shape[1])
+    dt = _dtype_code(logits)
+    per_row = isinstance(temperature, torch.Tensor)
+    _check_device(logits, u, temperature if per_row else None)
+    _expect(logits, (R, V), None, "logits")
+    _expect(u, (R,), torch.float32, "u")
+    if per_row:
+        _expect(temperature, (R,), torch.float32, "temperature")
+    if tokens is None:
+        tokens = torch.empty(R, dtype=torch.int32, device=logits.device)
+    _expect(tokens, (R,), torch.int32, "tokens")
+    need = spec_sample_workspace_bytes(R, V, dt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    rc = lib.spec_sample(_ptr(logits), _ptr(u), 0.0 if per_row else float(temperature),
+                         _ptr(temperature) if per_row else None, R, V, dt, _ptr(tokens), _ptr(workspace),
+                         workspace.numel(), _stream(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_sample")
+    return tokens

@@ -933,6 +933,206 @@ __global__ __launch_bounds__(kBlock) void k3_select(
   }
 }
 
+// ================================================================== single-pass sampler
+// Draft-side sampling, one token per row of softmax(z/T), in one kernel: a
+// 1024-thread workgroup per row.  Wave w streams sub-chunks w, w+16, ... of
+// 2048 tokens and leaves each one's (M_j, s_j = sum 2^(z c - M_j)) in LDS, with
+// M_j = ceil(max_j * c) the sub-chunk's own integer reference.  The row's
+// masses are then m_j = s_j * 2^(M_j - M) (exact), the sub-chunk holding u*Z is
+// found by a scan, and only that sub-chunk is read again.  Greedy rows keep the
+// (max, lowest index) of each sub-chunk instead.
+constexpr int kSBlock = 1024;
+constexpr int kSWaves = kSBlock / kWave;
+constexpr int kSMaxSub = 2048;  // sub-chunk records held in LDS: V <= 2048 * 2048
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x111, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x112, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x114, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x118, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x142, 0xa, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+template <int DT>
+__global__ __launch_bounds__(kSBlock) void k_sample_rows(const void *__restrict__ logits,
+                                                         const float *__restrict__ u,
+                                                         const float *__restrict__ temps, float scalar_T,
+                                                         int V, int NSUB, int32_t *__restrict__ tokens) {
+  constexpr int kN = kLaneElems / Elem<DT>::kVec;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const float T = temps ? temps[r] : scalar_T;
+  const bool greedy = !(T > 0.0f);
+  const float c = greedy ? 0.0f : temp_scale(T);
+  const char *row = static_cast<const char *>(logits) + static_cast<long>(r) * V * Elem<DT>::kBytes;
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  __shared__ double sh_s[kSMaxSub];
+  __shared__ float sh_f[kSMaxSub];
+  __shared__ int sh_i[kSMaxSub];
+
+  for (int sub = wave; sub < NSUB; sub += kSWaves) {
+    u32x4 raw[kN];
+    load_lane_raw<DT>(row, aligned, static_cast<long>(sub) * kSub, lane, V, raw);
+    if (!greedy) {
+      float lmx = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kN; ++q) {
+        float x[Elem<DT>::kVec];
+        widen_vec<DT>(raw[q], x);
+#pragma unroll
+        for (int e = 0; e < Elem<DT>::kVec; ++e) lmx = fmaxf(lmx, x[e]);
+      }
+      const float wmx = wave_max_f32(lmx);
+      int M = kEmptyM;
+      double sw = 0.0;
+      if (wmx > -INFINITY) {
+        const float Mf = ceilf(wmx * c);
+        M = static_cast<int>(Mf);
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kN; ++q) {
+          float x[Elem<DT>::kVec];
+          widen_vec<DT>(raw[q], x);
+#pragma unroll
+          for (int e = 0; e < Elem<DT>::kVec; ++e)
+            acc[(q * Elem<DT>::kVec + e) & 7] += __builtin_amdgcn_exp2f(fmaf(x[e], c, -Mf));
+        }
+        const float ls = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+        sw = wave_sum(static_cast<double>(ls));
+      }
+      if (lane == 0) {
+        sh_s[sub] = sw;
+        sh_i[sub] = M;
+      }
+    } else {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int q = 0; q < kN; ++q) {  // the lane's tokens in increasing index order
+        float x[Elem<DT>::kVec];
+        widen_vec<DT>(raw[q], x);
+        const long e0 = static_cast<long>(sub) * kSub + static_cast<long>(q * kWave + lane) * Elem<DT>::kVec;
+#pragma unroll
+        for (int e = 0; e < Elem<DT>::kVec; ++e) {
+          if (e0 + e < V && (x[e] > bv || bi == 0x7fffffff)) {
+            bv = x[e];
+            bi = static_cast<int>(e0 + e);
+          }
+        }
+      }
+#pragma unroll
+      for (int off = kWave / 2; off >= 1; off /= 2) {
+        const float vo = __shfl_xor(bv, off);
+        const int io = __shfl_xor(bi, off);
+        merge_arg(bv, bi, vo, io);
+      }
+      if (lane == 0) {
+        sh_f[sub] = bv;
+        sh_i[sub] = bi;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;  // the rest is wave 0's, with no barrier
+
+  if (greedy) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int j = lane; j < NSUB; j += kWave) merge_arg(bv, bi, sh_f[j], sh_i[j]);
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off /= 2) {
+      const float vo = __shfl_xor(bv, off);
+      const int io = __shfl_xor(bi, off);
+      merge_arg(bv, bi, vo, io);
+    }
+    if (lane == 0) tokens[r] = bi;
+    return;
+  }
+  // the row's reference exponent and the sub-chunk masses m_j = s_j 2^(M_j - M)
+  int M = kEmptyM;
+  for (int j = lane; j < NSUB; j += kWave) M = max(M, sh_i[j]);
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off /= 2) M = max(M, __shfl_xor(M, off));
+  double Z = 0.0;
+  for (int base = 0; base < NSUB; base += kWave) {
+    const int j = base + lane;
+    Z += wave_sum(j < NSUB ? ldexp(sh_s[j], sh_i[j] - M) : 0.0);
+  }
+  const double target_mass = static_cast<double>(u[r]) * Z;
+  int sub = -1;
+  double base_mass = 0.0, run = 0.0;
+  for (int base = 0; base < NSUB; base += kWave) {
+    const int j = base + lane;
+    const double v = j < NSUB ? ldexp(sh_s[j], sh_i[j] - M) : 0.0;
+    const double incl = wave_scan(v, lane);
+    const unsigned long long hit = __ballot(j < NSUB && v > 0.0 && run + incl > target_mass);
+    if (hit) {
+      const int L = __ffsll(static_cast<long long>(hit)) - 1;
+      sub = base + L;
+      base_mass = run + lane_value(incl - v, L);
+      break;
+    }
+    run += lane_value(incl, kWave - 1);
+  }
+  if (sub < 0) {  // rounding left u*Z at the very end: the last sub-chunk with mass
+    run = 0.0;
+    for (int base = 0; base < NSUB; base += kWave) {
+      const int j = base + lane;
+      const double v = j < NSUB ? ldexp(sh_s[j], sh_i[j] - M) : 0.0;
+      const double incl = wave_scan(v, lane);
+      const unsigned long long has = __ballot(j < NSUB && v > 0.0);
+      if (has) {
+        const int L = 63 - __clzll(static_cast<long long>(has));
+        sub = base + L;
+        base_mass = run + lane_value(incl - v, L);
+      }
+      run += lane_value(incl, kWave - 1);
+    }
+    if (sub < 0) {
+      sub = 0;
+      base_mass = 0.0;
+    }
+  }
+  // the token inside the sub-chunk: the same per-token values as the first
+  // pass (reference M_sub), rescaled exactly to the row reference
+  const int Ms = sh_i[sub];
+  const long first = static_cast<long>(sub) * kSub + static_cast<long>(lane) * kLaneElems;
+  float z[kLaneElems];
+#pragma unroll
+  for (int q = 0; q < kLaneElems / Elem<DT>::kVec; ++q)
+    load_vec_guarded<DT>(row, aligned, first + q * Elem<DT>::kVec, V, z + q * Elem<DT>::kVec);
+  double vals[kLaneElems];
+  double lsum = 0.0;
+#pragma unroll
+  for (int e = 0; e < kLaneElems; ++e) {
+    vals[e] = ldexp(static_cast<double>(__builtin_amdgcn_exp2f(fmaf(z[e], c, -static_cast<float>(Ms)))), Ms - M);
+    lsum += vals[e];
+  }
+  const double incl = wave_scan(lsum, lane);
+  double acc = base_mass + (incl - lsum);
+  int cand = -1, last_pos = -1;
+#pragma unroll
+  for (int e = 0; e < kLaneElems; ++e) {
+    if (vals[e] > 0.0) {
+      last_pos = e;
+      acc += vals[e];
+      if (cand < 0 && target_mass < acc) cand = e;
+    }
+  }
+  const unsigned long long props = __ballot(cand >= 0);
+  if (props) {
+    if (lane == __ffsll(static_cast<long long>(props)) - 1) tokens[r] = static_cast<int>(first + cand);
+  } else {
+    const unsigned long long has = __ballot(last_pos >= 0);
+    const int L = has ? 63 - __clzll(static_cast<long long>(has)) : 0;
+    if (lane == L) tokens[r] = static_cast<int>(first + (last_pos >= 0 ? last_pos : 0));
+  }
+}
+
 // ================================================================== host side
 struct Plan {
   int rows, NS, chunk_vecs, NSUB, SPW, NW;
@@ -1097,6 +1297,42 @@ int spec_verify_ex(const void *target_logits, const void *draft_logits, const in
   return dispatch(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, 0.0f,
                   false, draft_lens, B, gamma, V, dtype, accepted_count, out_tokens, workspace,
                   workspace_bytes, stream, dbg);
+}
+
+size_t spec_sample_workspace_bytes(int R, int V, int dtype) {
+  Plan P;
+  if (!make_plan(R, 0, V, dtype, &P)) return 0;
+  return P.total + align_up(sizeof(int32_t) * static_cast<size_t>(R));
+}
+
+// Sampling one token per row is the verify step with no drafts: every row is a
+// bonus row, drawn by the same kernels.  The per-row counts (always 0) go to
+// the tail of the workspace.
+int spec_sample(const void *logits, const float *u, float temperature, const float *temperatures, int R,
+                int V, int dtype, int32_t *tokens, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!temperatures && (!(temperature >= 0.0f) || isinf(temperature))) return SV_EINVAL;
+  Plan P;
+  if (!make_plan(R, 0, V, dtype, &P)) return SV_EINVAL;
+  if (!logits || !u || !tokens) return SV_EINVAL;
+  const size_t need = P.total + align_up(sizeof(int32_t) * static_cast<size_t>(R));
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < need)
+    return SV_EWORKSPACE;
+  const int nsub = (V + kSub - 1) / kSub;
+  if (nsub <= kSMaxSub) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == SV_BF16)
+      hipLaunchKernelGGL((k_sample_rows<SV_BF16>), dim3(R), dim3(kSBlock), 0, st, logits, u, temperatures,
+                         temperature, V, nsub, tokens);
+    else
+      hipLaunchKernelGGL((k_sample_rows<SV_F32>), dim3(R), dim3(kSBlock), 0, st, logits, u, temperatures,
+                         temperature, V, nsub, tokens);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+  }
+  // rows longer than the LDS records: the verify kernels with no drafts
+  int32_t *counts = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + P.total);
+  return dispatch(logits, nullptr, nullptr, nullptr, u, temperatures, temperature,
+                  temperatures == nullptr && temperature == 0.0f, nullptr, R, 0, V, dtype, counts, tokens,
+                  workspace, P.total, stream, nullptr);
 }
 
 const char *spec_verify_strerror(int code) {

@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "specverify.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -99,3 +99,23 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(binding.LibraryMissing):
         binding.load_library(str(tmp_path / "nope.so"))
+
+
+def test_sample_host_argument_checks(lib):
+    f = lib.spec_sample
+    ok = dict(l=1, u=1, T=1.0, Ts=None, R=4, V=10, dt=sv.SV_F32, tok=1, ws=256, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["l"], a["u"], a["T"], a["Ts"], a["R"], a["V"], a["dt"], a["tok"], a["ws"], a["wsb"], None)
+
+    assert call(R=0) == sv.binding.SV_EINVAL
+    assert call(V=0) == sv.binding.SV_EINVAL
+    assert call(T=-0.5) == sv.binding.SV_EINVAL
+    assert call(T=float("nan")) == sv.binding.SV_EINVAL
+    assert call(l=None) == sv.binding.SV_EINVAL
+    assert call(tok=None) == sv.binding.SV_EINVAL
+    assert call(ws=None) == sv.binding.SV_EWORKSPACE
+    assert call(wsb=8) == sv.binding.SV_EWORKSPACE
+    assert sv.spec_sample_workspace_bytes(4, 10, sv.SV_F32) > sv.spec_verify_workspace_bytes(4, 0, 10, sv.SV_F32)

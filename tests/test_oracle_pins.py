@@ -450,3 +450,20 @@ def test_t5_inverse_cdf_is_strict_at_exact_breakpoints(oracle_mod):
             np.zeros((B, 0), int), np.zeros((B, 0)), us, 1.0)
     np.testing.assert_array_equal(r.out_tokens[:, 0], [0, 1, 2, 3, 0])
     assert np.all(r.flags[1:4] & 2)   # exact breakpoints are inside the comparison band
+
+
+def test_oracle_sample_is_inverse_cdf_of_softmax(oracle_mod):
+    rng = np.random.default_rng(17)
+    R, V = 40, 300
+    z = (2.5 * rng.standard_normal((R, V))).astype(np.float32)
+    u = rng.random(R, dtype=np.float32)
+    T = rng.choice(np.array([0.0, 0.5, 1.0, 2.0], np.float32), size=R)
+    tok, tr = oracle_mod.sample(z, u, T)
+    for r in range(R):
+        if T[r] == 0:
+            assert tok[r] == np.argmax(z[r])
+            continue
+        if tr.flags[r]:
+            continue
+        cdf = np.cumsum(softmax(z[r].astype(np.float64) / T[r]))
+        assert tok[r] == np.searchsorted(cdf, u[r] * cdf[-1], side="right")
