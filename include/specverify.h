@@ -147,6 +147,56 @@ int spec_sample(const void *logits, const float *u, float temperature,
                 int32_t *tokens, void *workspace, size_t workspace_bytes,
                 void *stream);
 
+/* ---- Adaptive draft length (host only, no GPU work) ----------------------
+ * Policies that pick the next gamma from the accepted counts of past steps
+ * (P3 section vLLM は利用者が書く表で、SGLang は実行中に観測した受理の長さで
+ * 先読み数を変える; P4 section 動的推測戦略).  The caller owns the state; all
+ * arguments are HOST memory.
+ *   SV_GAMMA_BY_BATCH    gamma from a table of batch-size ranges (defaults
+ *                        1-64 -> 3, 65-128 -> 1, 129-512 -> 0; past the table,
+ *                        its last entry); observe() is a no-op.
+ *   SV_GAMMA_EMA         per batch-size bucket (upper bounds 1, 2, 4, 8, 16,
+ *                        31) an exponential moving average (weight 0.2) of the
+ *                        mean accepted count; next = round(avg) + 1 clamped to
+ *                        [1, 7]; 7 before the bucket has data; batches >= 32
+ *                        use 1.
+ *   SV_GAMMA_RATE_WINDOW mean of the last 100 per-step acceptance rates
+ *                        (mean accepted count / gamma used); above 0.85 gamma
+ *                        grows by one (max 8), below 0.65 it shrinks by one
+ *                        (min 2); starts at 5.
+ * Fields may be edited after init to change the defaults.  Functions return
+ * SV_EINVAL on a NULL policy, B < 1 or an unknown kind; spec_gamma_next returns
+ * the draft length (>= 0) otherwise. */
+enum { SV_GAMMA_BY_BATCH = 0, SV_GAMMA_EMA = 1, SV_GAMMA_RATE_WINDOW = 2 };
+#define SV_GAMMA_POLICY_SLOTS 16
+#define SV_GAMMA_WINDOW_MAX 256
+
+typedef struct {
+    int kind;
+    /* SV_GAMMA_BY_BATCH */
+    int n_ranges;
+    int range_max_batch[SV_GAMMA_POLICY_SLOTS];
+    int range_gamma[SV_GAMMA_POLICY_SLOTS];
+    /* SV_GAMMA_EMA */
+    int n_buckets;
+    int bucket_max_batch[SV_GAMMA_POLICY_SLOTS];
+    double ema[SV_GAMMA_POLICY_SLOTS];
+    int ema_count[SV_GAMMA_POLICY_SLOTS];
+    double ema_weight;
+    int steps_min, steps_max;
+    int fixed_from_batch, fixed_steps;
+    /* SV_GAMMA_RATE_WINDOW */
+    int window, hist_len, hist_pos;
+    double history[SV_GAMMA_WINDOW_MAX];
+    double raise_above, lower_below;
+    int gamma_min, gamma_max, gamma_current;
+} sv_gamma_policy;
+
+int spec_gamma_policy_init(sv_gamma_policy *policy, int kind);
+int spec_gamma_next(const sv_gamma_policy *policy, int batch_size);
+int spec_gamma_observe(sv_gamma_policy *policy, const int32_t *accepted_count,
+                       int B, int gamma_used);
+
 /* Static description of a return code. */
 const char *spec_verify_strerror(int code);
 

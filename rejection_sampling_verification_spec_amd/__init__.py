@@ -8,6 +8,10 @@ benchmark.
 from .binding import (  # noqa: F401
     SV_BF16,
     SV_F32,
+    SV_GAMMA_BY_BATCH,
+    SV_GAMMA_EMA,
+    SV_GAMMA_RATE_WINDOW,
+    GammaPolicy,
     LibraryMissing,
     SpecVerifyError,
     load_library,

@@ -29,8 +29,17 @@ EXPORTED_SYMBOLS = (
     "spec_verify_ex",
     "spec_sample_workspace_bytes",
     "spec_sample",
+    "spec_gamma_policy_init",
+    "spec_gamma_next",
+    "spec_gamma_observe",
     "spec_verify_strerror",
 )
+
+SV_GAMMA_BY_BATCH = 0
+SV_GAMMA_EMA = 1
+SV_GAMMA_RATE_WINDOW = 2
+SV_GAMMA_POLICY_SLOTS = 16
+SV_GAMMA_WINDOW_MAX = 256
 
 
 class LibraryMissing(RuntimeError):
@@ -53,6 +62,26 @@ class SvDebug(ctypes.Structure):
         ("row_argmax", ctypes.c_void_p),
         ("residual_mass", ctypes.c_void_p),
         ("k1_events", ctypes.c_void_p * 2),
+    ]
+
+
+class SvGammaPolicy(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int),
+        ("n_ranges", ctypes.c_int),
+        ("range_max_batch", ctypes.c_int * SV_GAMMA_POLICY_SLOTS),
+        ("range_gamma", ctypes.c_int * SV_GAMMA_POLICY_SLOTS),
+        ("n_buckets", ctypes.c_int),
+        ("bucket_max_batch", ctypes.c_int * SV_GAMMA_POLICY_SLOTS),
+        ("ema", ctypes.c_double * SV_GAMMA_POLICY_SLOTS),
+        ("ema_count", ctypes.c_int * SV_GAMMA_POLICY_SLOTS),
+        ("ema_weight", ctypes.c_double),
+        ("steps_min", ctypes.c_int), ("steps_max", ctypes.c_int),
+        ("fixed_from_batch", ctypes.c_int), ("fixed_steps", ctypes.c_int),
+        ("window", ctypes.c_int), ("hist_len", ctypes.c_int), ("hist_pos", ctypes.c_int),
+        ("history", ctypes.c_double * SV_GAMMA_WINDOW_MAX),
+        ("raise_above", ctypes.c_double), ("lower_below", ctypes.c_double),
+        ("gamma_min", ctypes.c_int), ("gamma_max", ctypes.c_int), ("gamma_current", ctypes.c_int),
     ]
 
 
@@ -85,6 +114,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_sample_workspace_bytes.restype = sz
     lib.spec_sample.argtypes = [vp, vp, ctypes.c_float, vp, i32, i32, i32, vp, vp, sz, vp]
     lib.spec_sample.restype = i32
+    lib.spec_gamma_policy_init.argtypes = [ctypes.POINTER(SvGammaPolicy), i32]
+    lib.spec_gamma_policy_init.restype = i32
+    lib.spec_gamma_next.argtypes = [ctypes.POINTER(SvGammaPolicy), i32]
+    lib.spec_gamma_next.restype = i32
+    lib.spec_gamma_observe.argtypes = [ctypes.POINTER(SvGammaPolicy), vp, i32, i32]
+    lib.spec_gamma_observe.restype = i32
     lib.spec_verify_strerror.argtypes = [i32]
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -282,3 +317,42 @@ def spec_sample(logits, u, temperature, tokens=None, workspace=None, stream=None
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_sample")
     return tokens
+
+
+class GammaPolicy:
+    """Adaptive draft length (host-side state owned here; the arithmetic is in the C library).
+
+    kind: SV_GAMMA_BY_BATCH, SV_GAMMA_EMA or SV_GAMMA_RATE_WINDOW.  ``next(batch)``
+    returns the draft length for the next step; ``observe(accepted_count, gamma)``
+    feeds back a step's accepted counts (host array or CPU/GPU tensor).
+    """
+
+    def __init__(self, kind: int, **fields):
+        self._lib = load_library()
+        self.state = SvGammaPolicy()
+        rc = self._lib.spec_gamma_policy_init(ctypes.byref(self.state), int(kind))
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, "spec_gamma_policy_init")
+        for k, v in fields.items():
+            cur = getattr(self.state, k)
+            if isinstance(cur, ctypes.Array):
+                for i, x in enumerate(v):
+                    cur[i] = x
+            else:
+                setattr(self.state, k, v)
+
+    def next(self, batch_size: int) -> int:
+        g = self._lib.spec_gamma_next(ctypes.byref(self.state), int(batch_size))
+        if g < 0:
+            raise SpecVerifyError(g, "spec_gamma_next")
+        return g
+
+    def observe(self, accepted_count, gamma_used: int) -> None:
+        import numpy as np
+        if hasattr(accepted_count, "detach"):
+            accepted_count = accepted_count.detach().cpu().numpy()
+        a = np.ascontiguousarray(accepted_count, dtype=np.int32).reshape(-1)
+        rc = self._lib.spec_gamma_observe(ctypes.byref(self.state), a.ctypes.data_as(ctypes.c_void_p),
+                                          int(a.size), int(gamma_used))
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, "spec_gamma_observe")

@@ -12,6 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "specverify.hip")
+SOURCES = [SRC, os.path.join(HERE, "csrc", "gamma_policy.cpp")]
 OUT = os.path.join(HERE, "libspecverify.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -30,7 +31,7 @@ FLAGS = [
 
 def build(out: str = OUT, extra=()) -> str:
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, SRC]
+    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *SOURCES]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
