@@ -37,6 +37,7 @@ class _Args(ctypes.Structure):
         ("target", ctypes.c_void_p), ("draft", ctypes.c_void_p), ("dtype", ctypes.c_int),
         ("draft_tokens", ctypes.c_void_p), ("u_accept", ctypes.c_void_p), ("u_sample", ctypes.c_void_p),
         ("temperature", ctypes.c_void_p), ("lens", ctypes.c_void_p),
+        ("top_k", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
         ("B", ctypes.c_int), ("gamma", ctypes.c_int), ("V", ctypes.c_int),
         ("accepted_count", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
         ("trace", ctypes.POINTER(_Trace)),
@@ -89,8 +90,8 @@ def _ptr(a):
 
 
 def spec_verify(target, draft, draft_tokens, u_accept, u_sample, temperature, lens=None,
-                dtype: Optional[str] = None, trace: bool = True, lib: Optional[ctypes.CDLL] = None
-                ) -> OracleResult:
+                dtype: Optional[str] = None, trace: bool = True, lib: Optional[ctypes.CDLL] = None,
+                top_k=None, top_p=None) -> OracleResult:
     """Run the oracle on host arrays.
 
     target: [B, gamma+1, V] float32, or uint16 holding bf16 bits (dtype="bf16").
@@ -110,6 +111,12 @@ def spec_verify(target, draft, draft_tokens, u_accept, u_sample, temperature, le
         temperature = np.full(B, temperature, dtype=np.float32)
     temps = np.ascontiguousarray(temperature, dtype=np.float32).reshape(B)
     lens_a = None if lens is None else np.ascontiguousarray(lens, dtype=np.int32).reshape(B)
+    if top_k is not None and np.isscalar(top_k):
+        top_k = np.full(B, top_k, dtype=np.int32)
+    if top_p is not None and np.isscalar(top_p):
+        top_p = np.full(B, top_p, dtype=np.float32)
+    tk_a = None if top_k is None else np.ascontiguousarray(top_k, dtype=np.int32).reshape(B)
+    tp_a = None if top_p is None else np.ascontiguousarray(top_p, dtype=np.float32).reshape(B)
 
     count = np.zeros(B, dtype=np.int32)
     out = np.full((B, gamma + 1), -7, dtype=np.int32)
@@ -129,7 +136,7 @@ def spec_verify(target, draft, draft_tokens, u_accept, u_sample, temperature, le
         res.cdf_margin = np.full(B, np.inf)
         tr = _Trace(*[_ptr(getattr(res, n)) for n, _ in _Trace._fields_])
     args = _Args(_ptr(target), _ptr(draft), ORACLE_BF16 if dtype == "bf16" else ORACLE_F32,
-                 _ptr(tokens), _ptr(ua), _ptr(us), _ptr(temps), _ptr(lens_a), B, gamma, V,
+                 _ptr(tokens), _ptr(ua), _ptr(us), _ptr(temps), _ptr(lens_a), _ptr(tk_a), _ptr(tp_a), B, gamma, V,
                  _ptr(count), _ptr(out), ctypes.pointer(tr) if tr is not None else None)
     rc = (lib or load()).oracle_spec_verify(ctypes.byref(args))
     if rc != 0:
@@ -140,7 +147,8 @@ def spec_verify(target, draft, draft_tokens, u_accept, u_sample, temperature, le
 def run_workload(w, trace: bool = True, lib: Optional[ctypes.CDLL] = None) -> OracleResult:
     """Convenience: run the oracle on a ``workloads.Workload``."""
     return spec_verify(w.target, w.draft, w.draft_tokens, w.u_accept, w.u_sample, w.temperature,
-                       lens=w.lens, dtype=w.dtype, trace=trace, lib=lib)
+                       lens=w.lens, dtype=w.dtype, trace=trace, lib=lib,
+                       top_k=getattr(w, "top_k", None), top_p=getattr(w, "top_p", None))
 
 
 def sample(logits, u, temperature, dtype: Optional[str] = None, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:

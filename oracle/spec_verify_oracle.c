@@ -46,6 +46,12 @@
  *     実装のポイント (greedy decoding reduces acceptance to an argmax match); P3
  *     worked example in section 先読みは、一回の順伝播で進むトークンを増やす.
  *
+ *   - optional top-k / top-p filtering (only the deployment example of P4,
+ *     section vLLM推測デコーディング設定, names top_p; the semantics are a
+ *     reading): both filters apply to every target and draft row of the
+ *     request, temperature first, then top-k, then top-p on what top-k kept;
+ *     the rule above then runs on the renormalised distributions.
+ *
  * Readings where the pages are silent (each one is listed in the design notes):
  *   R1 strict comparison u < a;  R2 no epsilon guards (q(x) = 0 gives ratio
  *   +inf if p(x) > 0, else 0);  R4 zero residual mass falls back to p_k;
@@ -63,6 +69,7 @@
  *   bit 1  the sampled token's normalised CDF interval [C(v-1), C(v)) has u
  *          within 1e-6 of one of its ends
  *   bit 2  the zero-residual-mass fallback was used
+ *   bit 3  a top-p cut lies within 1e-6 (of the kept mass) of a value group
  */
 #include <math.h>
 #include <stddef.h>
@@ -108,30 +115,76 @@ static row_t draft_row(const void *d, int dtype, int gamma, int V, int b, int i)
 }
 
 /* ------------------------------------------------------------------ softmax(z / T) */
-/* m = max_v z[v];  s = sum_v exp((z[v] - m) / T);  p(v) = exp((z[v] - m) / T) / s.
- * Subtracting the maximum changes nothing mathematically and keeps exp finite. */
+/* m = max_v z[v];  e(v) = exp((z[v] - m) / T);  p(v) = e(v) / s, s = sum_v e(v).
+ * Subtracting the maximum changes nothing mathematically and keeps exp finite.
+ *
+ * Optional filtering (top-k, then top-p), applied alike to every target and
+ * draft row of a request: tau_k is the k-th largest logit; F(t) = sum of e(v)
+ * over z[v] >= t; tau_p is the largest logit value t with
+ * F(t) >= top_p * F(tau_k) (equal logits enter together).  Tokens with
+ * z[v] < tau = max(tau_k, tau_p) get probability 0 and s sums the rest. */
 typedef struct {
-    double m, s, T;
+    double m, s, T, tau;
+    int near_cut; /* the top-p cut lies within 1e-6 (of the kept mass) of a value group */
 } softmax_t;
 
-static softmax_t softmax_stats(const row_t *r, double T)
+static int cmp_desc(const void *a, const void *b)
+{
+    double x = *(const double *)a, y = *(const double *)b;
+    return (x < y) - (x > y);
+}
+
+static softmax_t softmax_stats(const row_t *r, double T, int top_k, double top_p)
 {
     softmax_t st;
     st.T = T;
+    st.tau = -INFINITY;
+    st.near_cut = 0;
     st.m = z_at(r, 0);
     for (int v = 1; v < r->V; ++v) {
         double z = z_at(r, v);
         if (z > st.m) st.m = z;
     }
+    const int use_k = top_k > 0 && top_k < r->V;
+    const int use_p = top_p < 1.0;
+    if (use_k || use_p) {
+        double *zs = (double *)malloc(sizeof(double) * (size_t)r->V);
+        for (int v = 0; v < r->V; ++v) zs[v] = z_at(r, v);
+        qsort(zs, (size_t)r->V, sizeof(double), cmp_desc);
+        double tau_k = use_k ? zs[top_k - 1] : -INFINITY;
+        double tau = tau_k;
+        if (use_p) {
+            double Fk = 0.0;
+            for (int v = 0; v < r->V; ++v)
+                if (zs[v] >= tau_k) Fk += exp((zs[v] - st.m) / T);
+            double target = top_p * Fk, cum = 0.0;
+            int i = 0;
+            while (i < r->V) {
+                double t = zs[i], before = cum;
+                while (i < r->V && zs[i] == t) cum += exp((zs[i++] - st.m) / T);
+                if (cum >= target) {
+                    if ((target - before) < 1e-6 * Fk || (cum - target) < 1e-6 * Fk) st.near_cut = 1;
+                    if (t > tau) tau = t;
+                    break;
+                }
+            }
+        }
+        st.tau = tau;
+        free(zs);
+    }
     st.s = 0.0;
-    for (int v = 0; v < r->V; ++v)
-        st.s += exp((z_at(r, v) - st.m) / T);
+    for (int v = 0; v < r->V; ++v) {
+        double z = z_at(r, v);
+        if (z >= st.tau) st.s += exp((z - st.m) / T);
+    }
     return st;
 }
 
 static double prob(const row_t *r, const softmax_t *st, int v)
 {
-    return exp((z_at(r, v) - st->m) / st->T) / st->s;
+    double z = z_at(r, v);
+    if (z < st->tau) return 0.0;
+    return exp((z - st->m) / st->T) / st->s;
 }
 
 /* ------------------------------------------------------------------ argmax */
@@ -200,6 +253,8 @@ static void verify_request(const oracle_args *a, int b, double *w)
     const int gamma = a->gamma, V = a->V, dt = a->dtype;
     const int g = a->lens ? a->lens[b] : gamma;
     const double T = (double)a->temperature[b];
+    const int tk = a->top_k ? a->top_k[b] : 0;
+    const double tp = a->top_p ? (double)a->top_p[b] : 1.0;
     const int nrows = 2 * gamma + 1;
     oracle_trace *tr = a->trace;
     int32_t *out = a->out_tokens + (size_t)b * (size_t)(gamma + 1);
@@ -227,13 +282,15 @@ static void verify_request(const oracle_args *a, int b, double *w)
         softmax_t sp[ORACLE_GAMMA_MAX + 1], sq[ORACLE_GAMMA_MAX];
         for (int i = 0; i <= g; ++i) {
             row_t r = target_row(a->target, dt, gamma, V, b, i);
-            sp[i] = softmax_stats(&r, T);
+            sp[i] = softmax_stats(&r, T, tk, tp);
+            if (sp[i].near_cut) flags |= 8;
             if (tr && tr->row_max) tr->row_max[(size_t)b * nrows + i] = sp[i].m;
             if (tr && tr->row_sum) tr->row_sum[(size_t)b * nrows + i] = sp[i].s;
         }
         for (int i = 0; i < g; ++i) {
             row_t r = draft_row(a->draft, dt, gamma, V, b, i);
-            sq[i] = softmax_stats(&r, T);
+            sq[i] = softmax_stats(&r, T, tk, tp);
+            if (sq[i].near_cut) flags |= 8;
             if (tr && tr->row_max) tr->row_max[(size_t)b * nrows + gamma + 1 + i] = sq[i].m;
             if (tr && tr->row_sum) tr->row_sum[(size_t)b * nrows + gamma + 1 + i] = sq[i].s;
         }
@@ -300,6 +357,8 @@ int oracle_spec_verify(const oracle_args *a)
         if (!(T >= 0.0f) || isinf(T)) return -1;
         if (g < 0 || g > a->gamma) return -1;
         if (T > 0.0f && g > 0 && (!a->draft || !a->u_accept)) return -1;
+        if (a->top_k && a->top_k[b] < 0) return -1;
+        if (a->top_p && !(a->top_p[b] > 0.0f && a->top_p[b] <= 1.0f)) return -1;
         for (int i = 0; i < g; ++i) {
             int x = a->draft_tokens[(size_t)b * a->gamma + i];
             if (x < 0 || x >= a->V) return -1;

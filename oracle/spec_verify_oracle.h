@@ -20,7 +20,8 @@ typedef struct {
     double *row_sum;       /* [B*(2*gamma+1)] sum_v exp((z - max)/T)                 */
     int32_t *row_argmax;   /* [B*(gamma+1)] greedy target rows                       */
     double *residual_mass; /* [B] mass of the sampled distribution (NaN if greedy)   */
-    int32_t *flags;        /* [B] bit0 accept band, bit1 CDF band, bit2 fallback     */
+    int32_t *flags;        /* [B] bit0 accept band, bit1 CDF band, bit2 fallback,
+                              bit3 a top-p cut within the band                      */
     double *accept_margin; /* [B] min |u_i - a_i| over decided positions             */
     double *cdf_margin;    /* [B] distance of u_sample from its CDF interval's ends  */
 } oracle_trace;
@@ -34,6 +35,8 @@ typedef struct {
     const float *u_sample;       /* [B]                                               */
     const float *temperature;    /* [B], 0 = greedy request                           */
     const int32_t *lens;         /* [B] draft lengths or NULL (= gamma)               */
+    const int32_t *top_k;        /* [B] keep the k largest logits (0 or >= V: off), or NULL */
+    const float *top_p;          /* [B] keep the top mass fraction p (>= 1: off), or NULL  */
     int B, gamma, V;
     int32_t *accepted_count;     /* out [B]                                           */
     int32_t *out_tokens;         /* out [B][gamma+1]                                  */

@@ -12,6 +12,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_filter_pins as fpins
 from tests import test_oracle_pins as pins
 
 SRC = oracle.oracle.SRC
@@ -25,7 +26,7 @@ MUTANTS = {
     "ratio_inverted": ("double ratio = px / qx;", "double ratio = qx / px;"),
     "no_fallback": ("if (Z == 0.0) { /* fallback to p_k */", "if (0) { /* fallback to p_k */"),
     "argmax_last_tie": ("if (z > bz) { /* strict", "if (z >= bz) { /* strict"),
-    "temperature_ignored": ("st.s += exp((z_at(r, v) - st.m) / T);", "st.s += exp((z_at(r, v) - st.m));"),
+    "temperature_ignored": ("if (z >= st.tau) st.s += exp((z - st.m) / T);", "if (z >= st.tau) st.s += exp((z - st.m));"),
     "inverse_cdf_non_strict": ("if (target < acc) {", "if (target <= acc) {"),
     "inverse_cdf_unnormalised": ("double target = u * Z;", "double target = u;"),
     "bonus_from_previous_row": ("row_t rp = target_row(a->target, dt, gamma, V, b, k);\n        if (k < g) {",
@@ -34,6 +35,13 @@ MUTANTS = {
                               "row_t r = (i < g) ? draft_row(a->draft, dt, gamma, V, b, i) : target_row(a->target, dt, gamma, V, b, i);\n            tmax[i]"),
     "draft_row_shifted": ("row_t rq = draft_row(a->draft, dt, gamma, V, b, i);\n            double px",
                           "row_t rq = draft_row(a->draft, dt, gamma, V, b, i + 1 < g ? i + 1 : i);\n            double px"),
+    "topk_off_by_one": ("double tau_k = use_k ? zs[top_k - 1] : -INFINITY;",
+                        "double tau_k = use_k ? zs[top_k] : -INFINITY;"),
+    "topp_over_full_mass": ("if (zs[v] >= tau_k) Fk += exp", "if (1) Fk += exp"),
+    "draft_rows_unfiltered": ("sq[i] = softmax_stats(&r, T, tk, tp);", "sq[i] = softmax_stats(&r, T, 0, 1.0);"),
+    "prob_ignores_cut": ("if (z < st->tau) return 0.0;", "if (0) return 0.0;"),
+    "sum_ignores_cut": ("if (z >= st.tau) st.s += exp((z - st.m) / T);", "st.s += exp((z - st.m) / T);"),
+    "topp_first_group_kept_only": ("if (cum >= target) {", "if (1) {"),
 }
 
 PIN_TESTS = [
@@ -49,6 +57,10 @@ PIN_TESTS = [
     (pins.test_t5_zero_residual_mass_falls_back_to_p, {}),
     (pins.test_t5_inverse_cdf_is_strict_at_exact_breakpoints, {}),
     (pins.test_t5_identical_rows_accept_everything, {}),
+    (fpins.test_f1_filter_matches_brute_force_definition, {"coarse": True}),
+    (fpins.test_f2_exact_integration_gives_filtered_target, {"seed": 0, "top_k": 6, "top_p": 0.9}),
+    (fpins.test_f4_three_token_top_p_cut, {}),
+    (fpins.test_f4_ties_at_the_top_k_cut_are_kept, {}),
 ]
 
 
