@@ -35,7 +35,7 @@
  *
  * Conventions for every entry point:
  *   - Pointers named *_logits, draft_tokens, u_*, accepted_count, out_tokens,
- *     workspace and the spec_verify_ex temperature / draft_lens arrays are
+ *     workspace and the temperature / draft_lens / top_k / top_p arrays are
  *     DEVICE pointers (hipMalloc'd or torch tensors on the GPU).  The caller
  *     owns all of them; the library allocates nothing and keeps no state.
  *   - Layouts are dense row-major: target_logits [B][gamma+1][V],
@@ -127,6 +127,45 @@ int spec_verify_ex(const void *target_logits, const void *draft_logits,
                    int dtype, int32_t *accepted_count, int32_t *out_tokens,
                    void *workspace, size_t workspace_bytes, void *stream,
                    const sv_debug *dbg);
+
+/* Largest vocabulary accepted by spec_verify_filtered: the filter's masses are
+ * 64-bit fixed-point integers with 61 - ceil(log2 V) fractional bits, so a row's
+ * truncation loss stays below 2^-21 of its top token's mass. */
+#define SV_FILTER_MAX_V (1 << 20)
+
+/* Top-k / top-p filtered verification: spec_verify_ex with every target and
+ * draft row of a filtered request truncated before steps 2-4.  The pages name
+ * top_p only as a serving parameter (P4, section vLLM推測デコーディング設定:
+ * temperature 0.7 with top_p 0.9) and give no rule; the rule used here is:
+ *   - temperature first, then top-k, then top-p, the same cut on every row of
+ *     the request (target and draft alike);
+ *   - top-k keeps the tokens whose logit is >= the k-th largest logit of the
+ *     row (equal logits are kept together, so ties can keep more than k);
+ *   - top-p then keeps the tokens whose logit is >= the largest logit value t
+ *     such that the tokens with logit >= t hold at least a fraction top_p of
+ *     the probability that top-k kept (equal logits enter and leave together);
+ *   - p_i, q_i are renormalised over the kept tokens; a cut token has
+ *     probability 0, and a draft token with q_i(x) = 0 is accepted iff
+ *     p_i(x) > 0.  Residual, bonus and fallback use the renormalised rows.
+ * top_k: DEVICE [B] or NULL; k in [1, V-1] filters, any other value (0, >= V,
+ *        negative) leaves top-k off for that request.
+ * top_p: DEVICE [B] or NULL; p in (0, 1) filters, any other value (1, <= 0,
+ *        > 1, NaN) leaves top-p off for that request.
+ * Greedy requests (T == 0) ignore both: the arg-max is never cut.  With both
+ * arrays NULL this is spec_verify_ex.  V <= SV_FILTER_MAX_V when either array is
+ * given (else SV_EINVAL).  Stochastic rows of filtered requests must not hold
+ * NaN.  The workspace is the one spec_verify_workspace_bytes sizes; the other
+ * arguments are those of spec_verify_ex.  diagnostics report the filtered
+ * quantities: row_sum is the kept mass, p_draft / q_draft the renormalised
+ * probabilities. */
+int spec_verify_filtered(const void *target_logits, const void *draft_logits,
+                         const int32_t *draft_tokens, const float *u_accept,
+                         const float *u_sample, const float *temperature,
+                         const int32_t *draft_lens, const int32_t *top_k,
+                         const float *top_p, int B, int gamma, int V, int dtype,
+                         int32_t *accepted_count, int32_t *out_tokens,
+                         void *workspace, size_t workspace_bytes, void *stream,
+                         const sv_debug *dbg);
 
 /* Draft-side sampling: one token per row of softmax(logits[r] / T_r), drawn by
  * the inverse CDF in vocabulary order with the supplied uniform u[r]: the

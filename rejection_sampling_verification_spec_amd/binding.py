@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 SV_F32 = 0
 SV_BF16 = 1
 SV_GAMMA_MAX = 32
+SV_FILTER_MAX_V = 1 << 20
 
 SV_OK = 0
 SV_EINVAL = -1
@@ -27,6 +28,7 @@ EXPORTED_SYMBOLS = (
     "spec_verify_workspace_bytes",
     "spec_verify",
     "spec_verify_ex",
+    "spec_verify_filtered",
     "spec_sample_workspace_bytes",
     "spec_sample",
     "spec_gamma_policy_init",
@@ -110,6 +112,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                    vp, vp, vp, sz, vp, ctypes.POINTER(SvDebug)]
     lib.spec_verify_ex.restype = i32
+    lib.spec_verify_filtered.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                         vp, vp, vp, sz, vp, ctypes.POINTER(SvDebug)]
+    lib.spec_verify_filtered.restype = i32
     lib.spec_sample_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_sample_workspace_bytes.restype = sz
     lib.spec_sample.argtypes = [vp, vp, ctypes.c_float, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -245,16 +250,40 @@ def spec_verify_ex(target_logits, draft_logits, draft_tokens, u_accept, u_sample
     ``k1_events``: optional pair of recorded ``torch.cuda.Event(enable_timing=True)``
     that the library records around its row-statistics kernel.
     """
+    return _verify_device_params("spec_verify_ex", target_logits, draft_logits, draft_tokens, u_accept,
+                                 u_sample, temperature, draft_lens, None, None, accepted_count, out_tokens,
+                                 workspace, stream, debug, k1_events)
+
+
+def spec_verify_filtered(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature,
+                         draft_lens=None, top_k=None, top_p=None, accepted_count=None, out_tokens=None,
+                         workspace=None, stream=None, debug: Optional[dict] = None, k1_events=None):
+    """``spec_verify_ex`` with per-request top-k / top-p filtering.
+
+    ``top_k``: device int32 [B] or None (k in [1, V-1] filters, other values leave it off);
+    ``top_p``: device float32 [B] or None (p in (0, 1) filters, other values leave it off).
+    """
+    return _verify_device_params("spec_verify_filtered", target_logits, draft_logits, draft_tokens, u_accept,
+                                 u_sample, temperature, draft_lens, top_k, top_p, accepted_count, out_tokens,
+                                 workspace, stream, debug, k1_events)
+
+
+def _verify_device_params(entry, target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature,
+                          draft_lens, top_k, top_p, accepted_count, out_tokens, workspace, stream, debug,
+                          k1_events):
     lib = load_library()
     B, gamma, V = _shapes(target_logits)
     dt = _dtype_code(target_logits)
-    _check_device(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, draft_lens)
+    _check_device(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, draft_lens,
+                  top_k, top_p)
     accepted_count, out_tokens = _outputs(B, gamma, target_logits.device, accepted_count, out_tokens)
     _check_all(target_logits, draft_logits, draft_tokens, u_accept, u_sample, accepted_count, out_tokens,
                greedy_only=False)
     import torch
     _expect(temperature, (B,), torch.float32, "temperature")
     _expect(draft_lens, (B,), torch.int32, "draft_lens", optional=True)
+    _expect(top_k, (B,), torch.int32, "top_k", optional=True)
+    _expect(top_p, (B,), torch.float32, "top_p", optional=True)
     workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace)
     if workspace.numel() < need:
         raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
@@ -274,12 +303,16 @@ def spec_verify_ex(target_logits, draft_logits, draft_tokens, u_accept, u_sample
             d.k1_events[0] = k1_events[0].cuda_event
             d.k1_events[1] = k1_events[1].cuda_event
         dbg = ctypes.pointer(d)
-    rc = lib.spec_verify_ex(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
-                            _ptr(u_sample), _ptr(temperature), _ptr(draft_lens), B, gamma, V, dt,
-                            _ptr(accepted_count), _ptr(out_tokens), _ptr(workspace), workspace.numel(),
-                            _stream(stream), dbg)
+    head = (_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_sample),
+            _ptr(temperature), _ptr(draft_lens))
+    tail = (B, gamma, V, dt, _ptr(accepted_count), _ptr(out_tokens), _ptr(workspace), workspace.numel(),
+            _stream(stream), dbg)
+    if entry == "spec_verify_filtered":
+        rc = lib.spec_verify_filtered(*head, _ptr(top_k), _ptr(top_p), *tail)
+    else:
+        rc = lib.spec_verify_ex(*head, *tail)
     if rc != SV_OK:
-        raise SpecVerifyError(rc, "spec_verify_ex")
+        raise SpecVerifyError(rc, entry)
     return accepted_count, out_tokens
 
 

@@ -164,6 +164,8 @@ struct alignas(16) SelParams {
   float negMq;   // -M of draft row k
   float r;       // s'_p / s'_q: residual in units of the target row's scale
   double ip;     // 1 / s'_p (only for the diagnostic residual mass)
+  float tau_p;   // target row k keeps z >= tau_p (-inf: no filter)
+  float tau_q;   // draft row k keeps z >= tau_q
 };
 
 struct alignas(16) SubSums {
@@ -441,11 +443,61 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   }
 }
 
+// ================================================================== top-k / top-p
+// Optional filtering of a stochastic request (the pages name top_p only as a
+// serving parameter, so its rule is a reading): every target and draft row of
+// the request keeps the tokens with z >= tau, where tau_k is the k-th largest
+// logit (equal logits are kept together), tau_p the largest logit value t whose
+// tokens {z >= t} hold at least a fraction top_p of the mass that top-k keeps,
+// and tau = max(tau_k, tau_p).  The rejection rule then runs on the
+// renormalised rows: K2 and K3 treat z < tau as probability zero and use the
+// kept mass in place of the row sum.
+//
+// k_filter_rows: one 512-thread workgroup per row.  A token's mass is
+// e(z) = 2^(z c - M) with the row's integer M from K1, held as the fixed-point
+// integer floor(e * 2^fs), fs = 61 - ceil(log2 V), so that every sum is exact,
+// independent of the order of the additions, and a whole row fits 64 bits.
+//   pass 1   (count, mass) histogram over 2048 bins of y = z c - M, each 1/32
+//            of a binary order of magnitude, down to y = -64, and one bin below.
+//            The bin index is monotone in z, so equal logits share a bin.
+//   resolve  a scan of the bins from the top finds the bin where the count
+//            reaches k (top-k) or the mass reaches top_p * kept mass (top-p).
+//            That bin covers an interval of order-preserving 32-bit keys; its
+//            logits are gathered into LDS in one more pass, sorted, and scanned
+//            group by group.  A bin holding more than kFCap logits is first
+//            split by 2048-way histograms of the key (one pass each, at most
+//            three: a key interval shrinks 2048-fold per pass).
+// The result per row is (tau, kept mass); rows of requests without a filter
+// are not touched.
+constexpr int kFBlock = 512;
+constexpr int kFWaves = kFBlock / kWave;
+constexpr int kFBins = 2048;   // y bins; index kFBins collects y <= -64
+constexpr int kFCap = 2048;    // logits resolved exactly in LDS
+static_assert(SV_FILTER_MAX_V == (1 << 20), "fs >= 41 keeps a row's truncation below 2^-21");
+
+struct alignas(16) FilterStats {
+  double s_kept;  // sum of 2^(z c - M) over the kept tokens
+  float tau;      // tokens with z >= tau are kept
+  int pad;
+};
+
+// Whether request b filters, with its k (0: none) and p (1: none).  Values
+// outside the documented ranges switch the corresponding filter off.
+__device__ __forceinline__ bool request_filter(const int32_t *topk, const float *topp, int b, int V,
+                                               int &k, float &p) {
+  k = topk ? topk[b] : 0;
+  p = topp ? topp[b] : 1.0f;
+  if (!(k > 0 && k < V)) k = 0;
+  if (!(p > 0.0f && p < 1.0f)) p = 1.0f;
+  return k > 0 || p < 1.0f;
+}
+
 // ================================================================== K2
 constexpr int kK2Batch = 8;  // chunk partials fetched together per row
 
 struct DecideShared {
   double s[2 * SV_GAMMA_MAX + 1];
+  float tau[2 * SV_GAMMA_MAX + 1];
   int M[2 * SV_GAMMA_MAX + 1];
   int arg[2 * SV_GAMMA_MAX + 1];
   int k;
@@ -463,6 +515,7 @@ __device__ __forceinline__ void decide_request(
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
     const float *__restrict__ temps, float scalar_T, const int32_t *__restrict__ lens, int gamma,
     int V, int NS, const Partial *__restrict__ part, const float *__restrict__ zx,
+    const int32_t *__restrict__ topk, const float *__restrict__ topp, const FilterStats *__restrict__ fst,
     int32_t *__restrict__ accepted_count, int32_t *__restrict__ out_tokens,
     SelParams *__restrict__ sel, const sv_debug &dbg_in, int b, bool writer, DecideShared &sh) {
   const int tid = threadIdx.x;
@@ -471,6 +524,9 @@ __device__ __forceinline__ void decide_request(
   const float T = request_T(temps, scalar_T, b);
   const bool greedy = !(T > 0.0f);
   const float c = greedy ? 0.0f : temp_scale(T);
+  int fk;
+  float fp;
+  const bool filtered = !greedy && fst && request_filter(topk, topp, b, V, fk, fp);
   sv_debug dbg = dbg_in;
   if (!writer) memset(&dbg, 0, sizeof dbg);
   double *sh_s = sh.s;
@@ -518,8 +574,15 @@ __device__ __forceinline__ void decide_request(
         }
       }
       if (!greedy) {
+        float tau = -INFINITY;
+        if (filtered) {  // the kept mass replaces the row sum
+          const FilterStats f = fst[static_cast<long>(b) * rows + r];
+          s = f.s_kept;
+          tau = f.tau;
+        }
         sh_M[r] = M;
         sh_s[r] = s;
+        sh.tau[r] = tau;
         if (dbg.row_max) dbg.row_max[static_cast<long>(b) * rows + r] = mx;
         if (dbg.row_sum)  // sum_v exp((z_v - max)/T) = s * 2^(M - max c)
           dbg.row_sum[static_cast<long>(b) * rows + r] =
@@ -546,14 +609,24 @@ __device__ __forceinline__ void decide_request(
         // logit difference is exact and the exponent stays O(1)
         const int Mp = sh_M[tid], Mq = sh_M[gamma + 1 + tid];
         const double sp_ = sh_s[tid], sq_ = sh_s[gamma + 1 + tid];
-        const double d = (static_cast<double>(zpx) - static_cast<double>(zqx)) * cd -
-                         static_cast<double>(Mp - Mq);
-        const double ratio = exp2(d) * (sq_ / sp_);
-        const double a = ratio < 1.0 ? ratio : 1.0;
+        // a token cut by the filter has probability zero; q(x) = 0 accepts
+        // when p(x) > 0 and rejects otherwise
+        const bool pin = zpx >= sh.tau[tid], qin = zqx >= sh.tau[gamma + 1 + tid];
+        double a;
+        if (!qin) {
+          a = pin ? 1.0 : 0.0;
+        } else if (!pin) {
+          a = 0.0;
+        } else {
+          const double d = (static_cast<double>(zpx) - static_cast<double>(zqx)) * cd -
+                           static_cast<double>(Mp - Mq);
+          const double ratio = exp2(d) * (sq_ / sp_);
+          a = ratio < 1.0 ? ratio : 1.0;
+        }
         reject = !(static_cast<double>(ua) < a);
         const long o = static_cast<long>(b) * gamma + tid;
-        if (dbg.p_draft) dbg.p_draft[o] = exp2(static_cast<double>(zpx) * cd - Mp) / sp_;
-        if (dbg.q_draft) dbg.q_draft[o] = exp2(static_cast<double>(zqx) * cd - Mq) / sq_;
+        if (dbg.p_draft) dbg.p_draft[o] = pin ? exp2(static_cast<double>(zpx) * cd - Mp) / sp_ : 0.0;
+        if (dbg.q_draft) dbg.q_draft[o] = qin ? exp2(static_cast<double>(zqx) * cd - Mq) / sq_ : 0.0;
         if (dbg.accept_prob) dbg.accept_prob[o] = a;
       }
     }
@@ -577,6 +650,7 @@ __device__ __forceinline__ void decide_request(
     SelParams sp;
     sp.k = k;
     sp.c = c;
+    sp.tau_p = sp.tau_q = -INFINITY;
     if (greedy) {
       sp.mode = 0;
       sp.negMp = sp.negMq = 0.0f;
@@ -586,9 +660,11 @@ __device__ __forceinline__ void decide_request(
       sp.mode = (k < g) ? 1 : 2;
       sp.negMp = -static_cast<float>(sh_M[k]);
       sp.ip = 1.0 / sh_s[k];
+      sp.tau_p = sh.tau[k];
       if (k < g) {
         sp.negMq = -static_cast<float>(sh_M[gamma + 1 + k]);
         sp.r = static_cast<float>(sh_s[k] / sh_s[gamma + 1 + k]);
+        sp.tau_q = sh.tau[gamma + 1 + k];
       } else {
         sp.negMq = 0.0f;
         sp.r = 0.0f;
@@ -616,10 +692,11 @@ constexpr int kLaneElems = kSub / kWave;  // 32
 
 __device__ __forceinline__ void residual_value(const SelParams &sp, float zp, float zq, float &w,
                                                float &p) {
-  const float ep = __builtin_amdgcn_exp2f(fmaf(zp, sp.c, sp.negMp));  // -inf -> 0
+  // -inf -> 0; tokens cut by a top-k / top-p filter carry no mass
+  const float ep = zp >= sp.tau_p ? __builtin_amdgcn_exp2f(fmaf(zp, sp.c, sp.negMp)) : 0.0f;
   p = ep;
   if (sp.mode == 1) {
-    const float eq = __builtin_amdgcn_exp2f(fmaf(zq, sp.c, sp.negMq));
+    const float eq = zq >= sp.tau_q ? __builtin_amdgcn_exp2f(fmaf(zq, sp.c, sp.negMq)) : 0.0f;
     w = fmaxf(0.0f, fmaf(-eq, sp.r, ep));
   } else {
     w = ep;
@@ -747,7 +824,8 @@ __global__ __launch_bounds__(kBlock) void k2_decide_mass(
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
     const float *__restrict__ temps, float scalar_T, const int32_t *__restrict__ lens, int gamma,
     int V, int NS, int NSUB, int NW, int SPW, const Partial *__restrict__ part,
-    const float *__restrict__ zx, int32_t *__restrict__ accepted_count,
+    const float *__restrict__ zx, const int32_t *__restrict__ topk, const float *__restrict__ topp,
+    const FilterStats *__restrict__ fst, int32_t *__restrict__ accepted_count,
     int32_t *__restrict__ out_tokens, SelParams *__restrict__ sel, SubSums *__restrict__ sums,
     sv_debug dbg) {
   constexpr int kN = kLaneElems / Elem<DT>::kVec;
@@ -757,7 +835,7 @@ __global__ __launch_bounds__(kBlock) void k2_decide_mass(
   if (wg > 0 && !(request_T(temps, scalar_T, b) > 0.0f)) return;
   __shared__ DecideShared sh;
   decide_request<DT>(target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V, NS, part, zx,
-                     accepted_count, out_tokens, sel, dbg, b, wg == 0, sh);
+                     topk, topp, fst, accepted_count, out_tokens, sel, dbg, b, wg == 0, sh);
   const SelParams sp = sh.sp;
   const int first = (wg * kWaves + static_cast<int>(threadIdx.x) / kWave) * SPW;
   if (sp.mode == 0 || first >= NSUB) return;  // uniform per wave; no barrier below
@@ -930,6 +1008,389 @@ __global__ __launch_bounds__(kBlock) void k3_select(
     if (tok < 0) tok = static_cast<int>(static_cast<long>(sub) * kSub);
     out_tokens[static_cast<long>(b) * (gamma + 1) + sp.k] = tok;
     if (dbg_mass) dbg_mass[b] = Z * sp.ip;
+  }
+}
+
+// ================================================================== top-k / top-p kernel
+// Order-preserving key of a logit (larger value, larger key); -0 is folded
+// into +0 so that equal values have equal keys.
+__device__ __forceinline__ uint32_t order_key(float z) {
+  const uint32_t u = __float_as_uint(z == 0.0f ? 0.0f : z);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// y bin of a logit: 0 holds the top 1/32 of an order of magnitude below 2^M.
+__device__ __forceinline__ int ybin(float z, float c, float negM) {
+  const float y = fmaf(z, c, negM);
+  if (!(y > -64.0f)) return kFBins;
+  const float t = floorf(-32.0f * y);
+  return t <= 0.0f ? 0 : static_cast<int>(fminf(t, static_cast<float>(kFBins - 1)));
+}
+
+// floor(2^(z c - M) * 2^fs), the exponential being the same v_exp_f32 as K1's.
+__device__ __forceinline__ unsigned long long fixed_mass(float z, float c, float negM, int fs) {
+  const uint32_t bits = __float_as_uint(__builtin_amdgcn_exp2f(fmaf(z, c, negM)));
+  const int ex = static_cast<int>(bits >> 23);  // biased exponent of a value >= 0
+  if (ex == 0) return 0ull;                     // zero or below 2^-126
+  const unsigned long long mant = (bits & 0x7fffffu) | 0x800000u;
+  const int sh = ex - 150 + fs;                 // value = mant * 2^(ex - 150)
+  if (sh >= 0) return mant << sh;
+  return sh > -24 ? (mant >> -sh) : 0ull;
+}
+
+struct FilterShared {
+  unsigned cnt0[kFBins + 1];
+  unsigned long long mass0[kFBins + 1];
+  unsigned cnt1[kFBins];
+  unsigned long long mass1[kFBins];  // sub-bin masses, then the gathered logits' masses
+  unsigned cand[kFCap];              // keys of the gathered logits
+  unsigned long long red[2 * kFWaves];
+  unsigned long long pick_c, pick_m, res_m;
+  unsigned klo, khi, ncand;
+  int pick;
+};
+
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const unsigned long long o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive prefix of (a, b) over the workgroup's threads, with the totals.
+__device__ __forceinline__ void wg_excl_scan2(unsigned long long &a, unsigned long long &b,
+                                              unsigned long long &ta, unsigned long long &tb,
+                                              unsigned long long *red) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const unsigned long long ia = wave_incl_scan_u64(a, lane), ib = wave_incl_scan_u64(b, lane);
+  if (lane == kWave - 1) {
+    red[wave] = ia;
+    red[kFWaves + wave] = ib;
+  }
+  __syncthreads();
+  unsigned long long pa = 0, pb = 0;
+  ta = tb = 0;
+#pragma unroll
+  for (int w = 0; w < kFWaves; ++w) {
+    const unsigned long long ra = red[w], rb = red[kFWaves + w];
+    if (w < wave) {
+      pa += ra;
+      pb += rb;
+    }
+    ta += ra;
+    tb += rb;
+  }
+  __syncthreads();
+  a = pa + ia - a;
+  b = pb + ib - b;
+}
+
+// First bin j of (cnt, mass)[0, n) whose inclusive prefix (of the counts, or of
+// the masses when by_mass) reaches `target`, with the count and mass of the
+// bins before it.  With no such bin (not reached for consistent sums) the last
+// bin is returned.
+__device__ int find_cross(const unsigned *cnt, const unsigned long long *mass, int n, bool by_mass,
+                          unsigned long long target, unsigned long long &before_c,
+                          unsigned long long &before_m, FilterShared &sh) {
+  const int per = (n + kFBlock - 1) / kFBlock;
+  const int j0 = threadIdx.x * per, j1 = min(n, j0 + per);
+  unsigned long long lc = 0, lm = 0;
+  for (int j = j0; j < j1; ++j) {
+    lc += cnt[j];
+    lm += mass[j];
+  }
+  if (threadIdx.x == 0) sh.pick = -1;
+  unsigned long long ec = lc, em = lm, tc, tm;
+  wg_excl_scan2(ec, em, tc, tm, sh.red);
+  const unsigned long long e = by_mass ? em : ec, l = by_mass ? lm : lc;
+  if (j0 < j1 && e < target && target <= e + l) {  // exactly one thread
+    unsigned long long rc = ec, rm = em;
+    for (int j = j0; j < j1; ++j) {
+      const unsigned long long v = by_mass ? mass[j] : cnt[j];
+      if ((by_mass ? rm : rc) + v >= target) {
+        sh.pick = j;
+        sh.pick_c = rc;
+        sh.pick_m = rm;
+        break;
+      }
+      rc += cnt[j];
+      rm += mass[j];
+    }
+  }
+  __syncthreads();
+  int j = sh.pick;
+  if (j < 0) {
+    j = n - 1;
+    before_c = tc - cnt[j];
+    before_m = tm - mass[j];
+  } else {
+    before_c = sh.pick_c;
+    before_m = sh.pick_m;
+  }
+  __syncthreads();
+  return j;
+}
+
+// Calls f(z) for every logit of the row: U 16-byte loads in flight per thread,
+// widened one vector at a time.
+template <int DT, typename F>
+__device__ __forceinline__ void for_each_logit(const void *row, bool aligned, int V, F &&f) {
+  constexpr int kV = Elem<DT>::kVec;
+  constexpr int U = 4;
+  const char *r = static_cast<const char *>(row);
+  const long nvec = (static_cast<long>(V) + kV - 1) / kV;
+  for (long v0 = threadIdx.x; v0 < nvec; v0 += U * kFBlock) {
+    u32x4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long e0 = (v0 + static_cast<long>(u) * kFBlock) * kV;
+      raw[u] = (aligned && e0 + kV <= V) ? *reinterpret_cast<const u32x4 *>(r + e0 * Elem<DT>::kBytes)
+                                         : pack_guarded<DT>(r, e0, V);
+    }
+#pragma unroll 1
+    for (int u = 0; u < U; ++u) {
+      const long e0 = (v0 + static_cast<long>(u) * kFBlock) * kV;
+      if (e0 >= V) break;
+      float x[kV];
+      widen_vec<DT>(raw[u], x);
+#pragma unroll
+      for (int e = 0; e < kV; ++e)
+        if (e0 + e < V) f(x[e]);
+    }
+  }
+}
+
+// The key interval of y bin j: every key in [lo, hi] maps to bin j and no
+// other key does (the bin index is monotone in the key over the non-NaN keys).
+__device__ __forceinline__ void bin_key_range(int j, float c, float negM, unsigned &lo, unsigned &hi) {
+  const unsigned kmin = order_key(-INFINITY), kmax = order_key(INFINITY);
+  unsigned a = kmin, z = kmax;  // smallest key with bin <= j
+  while (a < z) {
+    const unsigned mid = a + (z - a) / 2;
+    if (ybin(key_value(mid), c, negM) <= j) z = mid;
+    else a = mid + 1;
+  }
+  lo = a;
+  a = kmin;
+  z = kmax;  // largest key with bin >= j
+  while (a < z) {
+    const unsigned mid = a + (z - a + 1) / 2;
+    if (ybin(key_value(mid), c, negM) >= j) a = mid;
+    else z = mid - 1;
+  }
+  hi = a;
+}
+
+// The threshold for one criterion: the first group of equal logits, from the
+// top, whose inclusive count (by_mass false) or mass (by_mass true) reaches
+// `target`.  Returns its value; `kept` receives the mass of all logits >= it.
+template <int DT>
+__device__ float resolve_cut(const void *row, bool aligned, int V, float c, float negM, int fs,
+                             bool by_mass, unsigned long long target, unsigned long long &kept,
+                             FilterShared &sh) {
+  const int tid = threadIdx.x;
+  unsigned long long bc, bm;
+  const int j = find_cross(sh.cnt0, sh.mass0, kFBins + 1, by_mass, target, bc, bm, sh);
+  unsigned count = sh.cnt0[j];
+  if (tid == 0) bin_key_range(j, c, negM, sh.klo, sh.khi);
+  __syncthreads();
+  unsigned klo = sh.klo, khi = sh.khi;
+  unsigned long long before_c = bc, before_m = bm;
+
+  // split a crowded bin by the key until it fits the LDS buffer
+  while (count > static_cast<unsigned>(kFCap)) {
+    const unsigned range = khi - klo;
+    const int shb = range >= static_cast<unsigned>(kFBins) ? (32 - __clz(range)) - 11 : 0;
+    for (int i = tid; i < kFBins; i += kFBlock) {
+      sh.cnt1[i] = 0;
+      sh.mass1[i] = 0;
+    }
+    __syncthreads();
+    for_each_logit<DT>(row, aligned, V, [&](float z) {
+      const unsigned key = order_key(z);
+      if (key >= klo && key <= khi) {
+        const unsigned s = (khi - key) >> shb;
+        atomicAdd(&sh.cnt1[s], 1u);
+        const unsigned long long m = fixed_mass(z, c, negM, fs);
+        if (m) atomicAdd(&sh.mass1[s], m);
+      }
+    });
+    __syncthreads();
+    const unsigned long long rel = target - (by_mass ? before_m : before_c);
+    unsigned long long sc, sm;
+    const int s = find_cross(sh.cnt1, sh.mass1, kFBins, by_mass, rel, sc, sm, sh);
+    before_c += sc;
+    before_m += sm;
+    count = sh.cnt1[s];
+    const unsigned long long smass = sh.mass1[s];
+    const long long top = static_cast<long long>(khi) - (static_cast<long long>(s) << shb);
+    const long long bot = static_cast<long long>(khi) - (static_cast<long long>(s + 1) << shb) + 1;
+    khi = static_cast<unsigned>(top);
+    klo = bot > static_cast<long long>(klo) ? static_cast<unsigned>(bot) : klo;
+    if (shb == 0) {  // one key: the whole group is one value
+      kept = before_m + smass;
+      __syncthreads();
+      return key_value(khi);
+    }
+    __syncthreads();
+  }
+
+  // gather the bin's logits, sort them by key (descending)
+  if (tid == 0) sh.ncand = 0;
+  __syncthreads();
+  for_each_logit<DT>(row, aligned, V, [&](float z) {
+    const unsigned key = order_key(z);
+    if (key >= klo && key <= khi) {
+      const unsigned slot = atomicAdd(&sh.ncand, 1u);
+      if (slot < static_cast<unsigned>(kFCap)) sh.cand[slot] = key;
+    }
+  });
+  __syncthreads();
+  const int n = min(static_cast<int>(sh.ncand), kFCap);
+  int N = 2;
+  while (N < n) N <<= 1;
+  for (int i = n + tid; i < N; i += kFBlock) sh.cand[i] = 0u;  // below every non-NaN key
+  __syncthreads();
+  for (int size = 2; size <= N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < N / 2; i += kFBlock) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const unsigned a = sh.cand[lo], b = sh.cand[hi];
+        if (((lo & size) == 0) == (a < b)) {
+          sh.cand[lo] = b;
+          sh.cand[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // inclusive mass prefix in sorted order; the first group end meeting the target
+  constexpr int kPer = kFCap / kFBlock;
+  const int i0 = tid * kPer;
+  unsigned long long m[kPer];
+  unsigned long long lsum = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    m[q] = (i0 + q < n) ? fixed_mass(key_value(sh.cand[i0 + q]), c, negM, fs) : 0ull;
+    lsum += m[q];
+  }
+  unsigned long long ex = lsum, dummy = 0, tot, tdummy;
+  wg_excl_scan2(ex, dummy, tot, tdummy, sh.red);
+  if (tid == 0) sh.pick = 0x7fffffff;
+  __syncthreads();
+  unsigned long long run = before_m + ex;
+  int mine = -1;
+  unsigned long long mine_m = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = i0 + q;
+    if (i < n) {
+      run += m[q];
+      const bool group_end = (i == n - 1) || sh.cand[i + 1] != sh.cand[i];
+      const unsigned long long crit = by_mass ? run : before_c + static_cast<unsigned long long>(i) + 1;
+      if (mine < 0 && group_end && crit >= target) {
+        mine = i;
+        mine_m = run;
+      }
+    }
+  }
+  if (mine >= 0) atomicMin(&sh.pick, mine);
+  __syncthreads();
+  const int pick = sh.pick;
+  if (mine >= 0 && mine == pick) sh.res_m = mine_m;
+  __syncthreads();
+  float tau;
+  if (pick == 0x7fffffff) {  // not reached for consistent sums: keep the whole bin
+    tau = n > 0 ? key_value(sh.cand[n - 1]) : key_value(klo);
+    kept = before_m + tot;
+  } else {
+    tau = key_value(sh.cand[pick]);
+    kept = sh.res_m;
+  }
+  __syncthreads();
+  return tau;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kFBlock) void k_filter_rows(
+    const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
+    const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
+    int gamma, int V, int NS, int fs, const Partial *__restrict__ part, FilterStats *__restrict__ fst) {
+  const int rows = 2 * gamma + 1;
+  const int slot = blockIdx.x;
+  const int b = slot / rows, r = slot - b * rows;
+  const float T = temps[b];
+  int k;
+  float p;
+  if (!(T > 0.0f) || !request_filter(topk, topp, b, V, k, p)) return;  // uniform per workgroup
+  const int g = request_len(lens, gamma, b);
+  const bool is_target = r <= gamma;
+  const int i = is_target ? r : r - gamma - 1;
+  if (is_target ? i > g : i >= g) return;
+  const void *row = is_target
+                        ? static_cast<const void *>(static_cast<const char *>(target) +
+                                                    (static_cast<long>(b) * (gamma + 1) + i) * V *
+                                                        Elem<DT>::kBytes)
+                        : static_cast<const void *>(static_cast<const char *>(draft) +
+                                                    (static_cast<long>(b) * gamma + i) * V * Elem<DT>::kBytes);
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  // the row's M, as K2 merges it
+  int M = kEmptyM;
+  double s = 0.0;
+  float mx = -INFINITY;
+  for (int j = 0; j < NS; ++j) {
+    const Partial q = part[static_cast<long>(slot) * NS + j];
+    merge_sm(M, s, mx, q.mi, q.s, q.mx);
+  }
+  const float c = temp_scale(T), negM = -static_cast<float>(M);
+  __shared__ FilterShared sh;
+  const int tid = threadIdx.x;
+  for (int j = tid; j <= kFBins; j += kFBlock) {
+    sh.cnt0[j] = 0;
+    sh.mass0[j] = 0;
+  }
+  __syncthreads();
+  for_each_logit<DT>(row, aligned, V, [&](float z) {
+    const int j = ybin(z, c, negM);
+    atomicAdd(&sh.cnt0[j], 1u);
+    const unsigned long long m = fixed_mass(z, c, negM, fs);
+    if (m) atomicAdd(&sh.mass0[j], m);
+  });
+  __syncthreads();
+  unsigned long long total = 0;
+  {
+    unsigned long long lm = 0, lc = 0, tc;
+    for (int j = tid; j <= kFBins; j += kFBlock) lm += sh.mass0[j];
+    wg_excl_scan2(lm, lc, total, tc, sh.red);
+  }
+  float tau = -INFINITY;
+  unsigned long long kept = total;
+  if (k > 0) tau = resolve_cut<DT>(row, aligned, V, c, negM, fs, false, static_cast<unsigned long long>(k), kept, sh);
+  if (p < 1.0f) {
+    double t = ceil(static_cast<double>(p) * static_cast<double>(kept));
+    if (t < 1.0) t = 1.0;
+    unsigned long long tgt = static_cast<unsigned long long>(t);
+    if (tgt > kept) tgt = kept;
+    unsigned long long kept_p;
+    const float tau_p = resolve_cut<DT>(row, aligned, V, c, negM, fs, true, tgt, kept_p, sh);
+    if (tau_p > tau) {
+      tau = tau_p;
+      kept = kept_p;
+    }
+  }
+  if (tid == 0) {
+    FilterStats f;
+    f.s_kept = ldexp(static_cast<double>(kept), -fs);
+    f.tau = tau;
+    f.pad = 0;
+    fst[slot] = f;
   }
 }
 
@@ -1137,7 +1598,7 @@ __global__ __launch_bounds__(kSBlock) void k_sample_rows(const void *__restrict_
 struct Plan {
   int rows, NS, chunk_vecs, NSUB, SPW, NW;
   long k1_groups, k3_groups;
-  size_t part_off, zx_off, sel_off, sums_off, total;
+  size_t part_off, zx_off, sel_off, sums_off, fst_off, total;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -1182,6 +1643,8 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P) {
   off = align_up(off + sizeof(SelParams) * static_cast<size_t>(B));
   P->sums_off = off;
   off = align_up(off + sizeof(SubSums) * static_cast<size_t>(B) * P->NSUB);
+  P->fst_off = off;
+  off = align_up(off + sizeof(FilterStats) * static_cast<size_t>(slots));
   P->total = off;
   return true;
 }
@@ -1217,16 +1680,24 @@ hipError_t launch_k1(const void *target, const void *draft, const int32_t *token
                                          st, ev0, ev1);
 }
 
+// fractional bits of the filter's fixed-point masses: V * 2^(fs + 1) <= 2^62
+int filter_frac_bits(int V) {
+  int l = 0;
+  while ((1L << l) < V) ++l;
+  return 61 - l;
+}
+
 template <int DT>
 int run(const void *target, const void *draft, const int32_t *tokens, const float *u_accept,
         const float *u_sample, const float *temps, float scalar_T, bool all_greedy,
-        const int32_t *lens, int B, int gamma, int V, int32_t *count, int32_t *out, void *ws,
-        const Plan &P, hipStream_t st, const sv_debug *dbgp) {
+        const int32_t *lens, const int32_t *topk, const float *topp, int B, int gamma, int V,
+        int32_t *count, int32_t *out, void *ws, const Plan &P, hipStream_t st, const sv_debug *dbgp) {
   char *base = static_cast<char *>(ws);
   Partial *part = reinterpret_cast<Partial *>(base + P.part_off);
   float *zx = reinterpret_cast<float *>(base + P.zx_off);
   SelParams *sel = reinterpret_cast<SelParams *>(base + P.sel_off);
   SubSums *sums = reinterpret_cast<SubSums *>(base + P.sums_off);
+  FilterStats *fst = (topk || topp) ? reinterpret_cast<FilterStats *>(base + P.fst_off) : nullptr;
   sv_debug dbg;
   memset(&dbg, 0, sizeof dbg);
   if (dbgp) dbg = *dbgp;
@@ -1234,11 +1705,17 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
                                static_cast<hipEvent_t>(dbg.k1_events[0]),
                                static_cast<hipEvent_t>(dbg.k1_events[1]));
   if (e != hipSuccess) return SV_EHIP;
+  if (fst) {
+    hipLaunchKernelGGL((k_filter_rows<DT>), dim3(static_cast<unsigned>(static_cast<long>(B) * P.rows)),
+                       dim3(kFBlock), 0, st, target, draft, temps, lens, topk, topp, gamma, V, P.NS,
+                       filter_frac_bits(V), part, fst);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  }
   // greedy-only batches need the decision alone: one workgroup per request
   const int nw = all_greedy ? 1 : P.NW;
   hipLaunchKernelGGL((k2_decide_mass<DT>), dim3(static_cast<unsigned>(static_cast<long>(B) * nw)),
                      dim3(kBlock), 0, st, target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V,
-                     P.NS, P.NSUB, nw, P.SPW, part, zx, count, out, sel, sums, dbg);
+                     P.NS, P.NSUB, nw, P.SPW, part, zx, topk, topp, fst, count, out, sel, sums, dbg);
   if (hipGetLastError() != hipSuccess) return SV_EHIP;
   if (!all_greedy) {
     hipLaunchKernelGGL((k3_select<DT>), dim3(B), dim3(kBlock), 0, st, target, draft, u_sample, gamma, V,
@@ -1250,10 +1727,14 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
 
 int dispatch(const void *target, const void *draft, const int32_t *tokens, const float *u_accept,
              const float *u_sample, const float *temps, float scalar_T, bool all_greedy,
-             const int32_t *lens, int B, int gamma, int V, int dtype, int32_t *count, int32_t *out,
-             void *ws, size_t ws_bytes, void *stream, const sv_debug *dbg) {
+             const int32_t *lens, const int32_t *topk, const float *topp, int B, int gamma, int V,
+             int dtype, int32_t *count, int32_t *out, void *ws, size_t ws_bytes, void *stream,
+             const sv_debug *dbg) {
   Plan P;
   if (!make_plan(B, gamma, V, dtype, &P)) return SV_EINVAL;
+  if ((topk || topp) &&
+      (!temps || V > SV_FILTER_MAX_V || static_cast<long>(B) * P.rows * kFBlock >= (1L << 32)))
+    return SV_EINVAL;
   if (!target || !u_sample || !count || !out) return SV_EINVAL;
   if (gamma > 0 && !tokens) return SV_EINVAL;
   if (gamma > 0 && !all_greedy && (!draft || !u_accept)) return SV_EINVAL;
@@ -1261,10 +1742,10 @@ int dispatch(const void *target, const void *draft, const int32_t *tokens, const
   if (dbg && ((dbg->k1_events[0] == nullptr) != (dbg->k1_events[1] == nullptr))) return SV_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == SV_BF16)
-    return run<SV_BF16>(target, draft, tokens, u_accept, u_sample, temps, scalar_T, all_greedy, lens, B,
-                        gamma, V, count, out, ws, P, st, dbg);
-  return run<SV_F32>(target, draft, tokens, u_accept, u_sample, temps, scalar_T, all_greedy, lens, B,
-                     gamma, V, count, out, ws, P, st, dbg);
+    return run<SV_BF16>(target, draft, tokens, u_accept, u_sample, temps, scalar_T, all_greedy, lens, topk,
+                        topp, B, gamma, V, count, out, ws, P, st, dbg);
+  return run<SV_F32>(target, draft, tokens, u_accept, u_sample, temps, scalar_T, all_greedy, lens, topk, topp,
+                     B, gamma, V, count, out, ws, P, st, dbg);
 }
 
 }  // namespace
@@ -1284,8 +1765,8 @@ int spec_verify(const void *target_logits, const void *draft_logits, const int32
                 size_t workspace_bytes, void *stream) {
   if (!(temperature >= 0.0f) || isinf(temperature)) return SV_EINVAL;
   return dispatch(target_logits, draft_logits, draft_tokens, u_accept, u_sample, nullptr, temperature,
-                  temperature == 0.0f, nullptr, B, gamma, V, dtype, accepted_count, out_tokens,
-                  workspace, workspace_bytes, stream, nullptr);
+                  temperature == 0.0f, nullptr, nullptr, nullptr, B, gamma, V, dtype, accepted_count,
+                  out_tokens, workspace, workspace_bytes, stream, nullptr);
 }
 
 int spec_verify_ex(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
@@ -1295,8 +1776,19 @@ int spec_verify_ex(const void *target_logits, const void *draft_logits, const in
                    size_t workspace_bytes, void *stream, const sv_debug *dbg) {
   if (!temperature) return SV_EINVAL;
   return dispatch(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, 0.0f,
-                  false, draft_lens, B, gamma, V, dtype, accepted_count, out_tokens, workspace,
-                  workspace_bytes, stream, dbg);
+                  false, draft_lens, nullptr, nullptr, B, gamma, V, dtype, accepted_count, out_tokens,
+                  workspace, workspace_bytes, stream, dbg);
+}
+
+int spec_verify_filtered(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
+                         const float *u_accept, const float *u_sample, const float *temperature,
+                         const int32_t *draft_lens, const int32_t *top_k, const float *top_p, int B,
+                         int gamma, int V, int dtype, int32_t *accepted_count, int32_t *out_tokens,
+                         void *workspace, size_t workspace_bytes, void *stream, const sv_debug *dbg) {
+  if (!temperature) return SV_EINVAL;
+  return dispatch(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, 0.0f,
+                  false, draft_lens, top_k, top_p, B, gamma, V, dtype, accepted_count, out_tokens,
+                  workspace, workspace_bytes, stream, dbg);
 }
 
 size_t spec_sample_workspace_bytes(int R, int V, int dtype) {
@@ -1331,8 +1823,8 @@ int spec_sample(const void *logits, const float *u, float temperature, const flo
   // rows longer than the LDS records: the verify kernels with no drafts
   int32_t *counts = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + P.total);
   return dispatch(logits, nullptr, nullptr, nullptr, u, temperatures, temperature,
-                  temperatures == nullptr && temperature == 0.0f, nullptr, R, 0, V, dtype, counts, tokens,
-                  workspace, P.total, stream, nullptr);
+                  temperatures == nullptr && temperature == 0.0f, nullptr, nullptr, nullptr, R, 0, V, dtype,
+                  counts, tokens, workspace, P.total, stream, nullptr);
 }
 
 const char *spec_verify_strerror(int code) {

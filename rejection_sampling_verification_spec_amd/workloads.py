@@ -74,7 +74,13 @@ class Workload:
     temperature: np.ndarray   # [B] float32, 0 = greedy request
     lens: Optional[np.ndarray] = None  # [B] int32 draft lengths, None = all gamma
     scalar_temperature: Optional[float] = None  # set when every request shares T
+    top_k: Optional[np.ndarray] = None  # [B] int32 per-request top-k (0: off), None = no filter
+    top_p: Optional[np.ndarray] = None  # [B] float32 per-request top-p (1: off), None = no filter
     meta: dict = field(default_factory=dict)
+
+    @property
+    def filtered(self) -> bool:
+        return self.top_k is not None or self.top_p is not None
 
     @property
     def draft_lens(self) -> np.ndarray:
@@ -119,6 +125,8 @@ class Workload:
             u_sample=plain(self.u_sample),
             temperature=plain(self.temperature),
             lens=None if self.lens is None else plain(self.lens),
+            top_k=None if self.top_k is None else plain(self.top_k),
+            top_p=None if self.top_p is None else plain(self.top_p),
         )
         return d
 

@@ -44,6 +44,8 @@ def test_constants_match_header():
     text = open(HEADER).read()
     assert re.search(r"SV_F32\s*=\s*0", text) and re.search(r"SV_BF16\s*=\s*1", text)
     assert int(re.search(r"#define SV_GAMMA_MAX (\d+)", text).group(1)) == binding.SV_GAMMA_MAX
+    assert re.search(r"#define SV_FILTER_MAX_V \(1 << (\d+)\)", text).group(1) == "20"
+    assert binding.SV_FILTER_MAX_V == 1 << 20
     for name in ("SV_OK", "SV_EINVAL", "SV_EWORKSPACE", "SV_EHIP"):
         assert int(re.search(name + r"\s*=\s*(-?\d+)", text).group(1)) == getattr(binding, name)
 
@@ -119,3 +121,17 @@ def test_sample_host_argument_checks(lib):
     assert call(ws=None) == sv.binding.SV_EWORKSPACE
     assert call(wsb=8) == sv.binding.SV_EWORKSPACE
     assert sv.spec_sample_workspace_bytes(4, 10, sv.SV_F32) > sv.spec_verify_workspace_bytes(4, 0, 10, sv.SV_F32)
+
+
+def test_filtered_host_argument_checks(lib):
+    f = lib.spec_verify_filtered
+
+    def call(V=10, T=1, k=1, p=None, B=2):
+        return f(1, 1, 1, 1, 1, T, None, k, p, B, 3, V, sv.SV_F32, 1, 1, 256, 1 << 30, None, None)
+
+    assert call(T=None) == sv.binding.SV_EINVAL                 # device temperature array is required
+    assert call(V=(1 << 20) + 1) == sv.binding.SV_EINVAL        # beyond the fixed-point range
+    assert call(V=(1 << 20) + 1, k=None, p=1) == sv.binding.SV_EINVAL
+    assert call(B=0) == sv.binding.SV_EINVAL
+    ws = f(1, 1, 1, 1, 1, 1, None, 1, None, 2, 3, 10, sv.SV_F32, 1, 1, 256, 16, None, None)
+    assert ws == sv.binding.SV_EWORKSPACE
