@@ -342,6 +342,45 @@ def main():
                                    "GBps": round(R * V * 2 / per / 1e9, 1)}
         log(f"[bench] spec_sample {sample}")
 
+    # top-k / top-p filtered verification on the same logits at T = 0.7 (the pages' vLLM
+    # example: temperature 0.7, top_p 0.9), with and without top_k = 50
+    filtered = {}
+    if not greedy:
+        temps07 = torch.full((B,), 0.7, dtype=torch.float32, device=dev)
+        fws = torch.empty(sv.spec_verify_filtered_workspace_bytes(B, gamma, V, sv.SV_BF16), dtype=torch.uint8,
+                          device=dev)
+        for label, k, p in (("top_p0.9", None, 0.9), ("top_k50_top_p0.9", 50, 0.9)):
+            tk = None if k is None else torch.full((B,), k, dtype=torch.int32, device=dev)
+            tp = torch.full((B,), p, dtype=torch.float32, device=dev)
+
+            def fstep(c, tk=tk, tp=tp):
+                sv.spec_verify_filtered(targets[c], drafts[c], t["draft_tokens"], t["u_accept"], t["u_sample"],
+                                        temps07, None, top_k=tk, top_p=tp, accepted_count=count,
+                                        out_tokens=out, workspace=fws, stream=stream)
+
+            with torch.cuda.stream(stream):
+                fstep(0)
+            torch.cuda.synchronize()
+            fc, fo = count.cpu().clone(), out.cpu().clone()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for c in range(copies):
+                    fstep(c)
+            with torch.cuda.stream(stream):
+                g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, args.steps // copies)
+            s0 = time.perf_counter()
+            with torch.cuda.stream(stream):
+                for _ in range(reps):
+                    g.replay()
+            torch.cuda.synchronize()
+            per = (time.perf_counter() - s0) / (reps * copies)
+            assert torch.equal(count.cpu(), fc) and torch.equal(out.cpu(), fo), "filtered replay differs"
+            filtered[label] = {"us_per_call": round(per * 1e6, 3), "positions_per_s": round(positions / per, 1),
+                               "alpha_hat": round(float(fc.float().mean()) / gamma, 4)}
+        log(f"[bench] spec_verify_filtered {filtered}")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -382,6 +421,7 @@ def main():
                   "k1_us_min": round(min(k1_ms) * 1e3, 3), "k1_us_max": round(max(k1_ms) * 1e3, 3),
                   "alpha_hat": round(float(ref_count.float().mean()) / gamma, 4),
                   "spec_sample": sample,
+                  "spec_verify_filtered": filtered,
                   "kernel_source_sha256_16": source_hash()},
     }
     print(json.dumps(rec), flush=True)

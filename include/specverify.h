@@ -154,10 +154,16 @@ int spec_verify_ex(const void *target_logits, const void *draft_logits,
  * Greedy requests (T == 0) ignore both: the arg-max is never cut.  With both
  * arrays NULL this is spec_verify_ex.  V <= SV_FILTER_MAX_V when either array is
  * given (else SV_EINVAL).  Stochastic rows of filtered requests must not hold
- * NaN.  The workspace is the one spec_verify_workspace_bytes sizes; the other
- * arguments are those of spec_verify_ex.  diagnostics report the filtered
- * quantities: row_sum is the kept mass, p_draft / q_draft the renormalised
- * probabilities. */
+ * NaN.  The workspace is sized by spec_verify_filtered_workspace_bytes (larger
+ * than spec_verify_workspace_bytes: it holds the filter's per-row candidate
+ * lists); the other arguments are those of spec_verify_ex.  Diagnostics report
+ * the filtered quantities: row_sum is the kept mass, p_draft / q_draft the
+ * renormalised probabilities. */
+/* Bytes of device workspace one spec_verify_filtered call with these sizes
+ * needs (0 if the sizes are invalid or V > SV_FILTER_MAX_V); 256-byte aligned,
+ * contents on entry do not matter. */
+size_t spec_verify_filtered_workspace_bytes(int B, int gamma, int V, int dtype);
+
 int spec_verify_filtered(const void *target_logits, const void *draft_logits,
                          const int32_t *draft_tokens, const float *u_accept,
                          const float *u_sample, const float *temperature,

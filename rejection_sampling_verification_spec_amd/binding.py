@@ -29,6 +29,7 @@ EXPORTED_SYMBOLS = (
     "spec_verify",
     "spec_verify_ex",
     "spec_verify_filtered",
+    "spec_verify_filtered_workspace_bytes",
     "spec_sample_workspace_bytes",
     "spec_sample",
     "spec_gamma_policy_init",
@@ -115,6 +116,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_filtered.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                          vp, vp, vp, sz, vp, ctypes.POINTER(SvDebug)]
     lib.spec_verify_filtered.restype = i32
+    lib.spec_verify_filtered_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spec_verify_filtered_workspace_bytes.restype = sz
     lib.spec_sample_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_sample_workspace_bytes.restype = sz
     lib.spec_sample.argtypes = [vp, vp, ctypes.c_float, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -137,6 +140,10 @@ def spec_verify_strerror(code: int) -> str:
 
 def spec_verify_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:
     return int(load_library().spec_verify_workspace_bytes(B, gamma, V, dtype))
+
+
+def spec_verify_filtered_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_verify_filtered_workspace_bytes(B, gamma, V, dtype))
 
 
 # --------------------------------------------------------------------------- torch marshalling
@@ -206,9 +213,9 @@ def _outputs(B, gamma, device, accepted_count, out_tokens):
     return accepted_count, out_tokens
 
 
-def _workspace(B, gamma, V, dt, device, workspace):
+def _workspace(B, gamma, V, dt, device, workspace, filtered=False):
     import torch
-    need = spec_verify_workspace_bytes(B, gamma, V, dt)
+    need = (spec_verify_filtered_workspace_bytes if filtered else spec_verify_workspace_bytes)(B, gamma, V, dt)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     return workspace, need
@@ -284,7 +291,8 @@ def _verify_device_params(entry, target_logits, draft_logits, draft_tokens, u_ac
     _expect(draft_lens, (B,), torch.int32, "draft_lens", optional=True)
     _expect(top_k, (B,), torch.int32, "top_k", optional=True)
     _expect(top_p, (B,), torch.float32, "top_p", optional=True)
-    workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace)
+    workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace,
+                                 filtered=entry == "spec_verify_filtered")
     if workspace.numel() < need:
         raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     dbg = None

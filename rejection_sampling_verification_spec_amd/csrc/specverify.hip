@@ -453,32 +453,66 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
 // renormalised rows: K2 and K3 treat z < tau as probability zero and use the
 // kept mass in place of the row sum.
 //
-// k_filter_rows: one 512-thread workgroup per row.  A token's mass is
-// e(z) = 2^(z c - M) with the row's integer M from K1, held as the fixed-point
-// integer floor(e * 2^fs), fs = 61 - ceil(log2 V), so that every sum is exact,
-// independent of the order of the additions, and a whole row fits 64 bits.
-//   pass 1   (count, mass) histogram over 2048 bins of y = z c - M, each 1/32
-//            of a binary order of magnitude, down to y = -64, and one bin below.
-//            The bin index is monotone in z, so equal logits share a bin.
-//   resolve  a scan of the bins from the top finds the bin where the count
-//            reaches k (top-k) or the mass reaches top_p * kept mass (top-p).
-//            That bin covers an interval of order-preserving 32-bit keys; its
-//            logits are gathered into LDS in one more pass, sorted, and scanned
-//            group by group.  A bin holding more than kFCap logits is first
-//            split by 2048-way histograms of the key (one pass each, at most
-//            three: a key interval shrinks 2048-fold per pass).
-// The result per row is (tau, kept mass); rows of requests without a filter
-// are not touched.
-constexpr int kFBlock = 512;
+// Three kernels between K1 and K2.  A token's mass is e(z) = 2^(z c - M) with
+// the row's integer M from K1; exact sums use the fixed-point integer
+// floor(e * 2^fs), fs = 61 - ceil(log2 V), so that they do not depend on the
+// order of the additions and a whole row fits 64 bits.
+//   FA  k_filter_levels (K1's chunks): counts and estimated masses of the
+//       logits in levels 0..15, level l holding y = z c - M in (-l-1, -l].
+//   FB  k_filter_gather (K1's chunks): from the row's level totals, the levels
+//       [l0, l1] that hold the k-th largest logit (exact counts) and the top-p
+//       crossing (estimated masses with a 1e-4 margin; the row's total is K1's
+//       sum) are chosen; logits above l0 add their exact mass, logits in
+//       [l0, l1] are appended to the row's candidate list.
+//   FC  k_filter_resolve (one workgroup per row): sorts the candidates and
+//       scans them group by group from the exact prefix above them.
+// A row takes FC's general path when the chosen levels reach below level 15,
+// hold more than kFCap logits, or do not contain the crossing:
+//   pass 1   exact (count, fixed-point mass) histogram over 2048 bins of y,
+//            each 1/32 of a binary order of magnitude, down to y = -64, and
+//            one bin below;
+//   resolve  the bin where the count reaches k or the mass reaches
+//            top_p * kept mass is found by a scan; its logits are gathered in
+//            one more pass (a bin holding more than kFCap logits is first split
+//            by 2048-way histograms of the order-preserving 32-bit key, one
+//            pass each, at most three), sorted, and scanned group by group.
+// Both paths apply the same definition; they can differ only where a top-p
+// crossing lies within the rounding of the masses (about 1e-7 of the kept
+// mass).  The result per row is (tau, kept mass); rows of requests without a
+// filter are not touched.
+constexpr int kFBlock = 512;  // FC workgroup
 constexpr int kFWaves = kFBlock / kWave;
-constexpr int kFBins = 2048;   // y bins; index kFBins collects y <= -64
-constexpr int kFCap = 2048;    // logits resolved exactly in LDS
-static_assert(SV_FILTER_MAX_V == (1 << 20), "fs >= 41 keeps a row's truncation below 2^-21");
+constexpr int kLBlock = 256;  // FA / FB workgroups
+constexpr int kFBins = 2048;  // general path: y bins; index kFBins collects y <= -64
+constexpr int kFCap = 4096;   // logits sorted and scanned in LDS
+constexpr int kLevels = 16;   // FA levels of one binary order of magnitude below 2^M
+// a chunk of at most SV_FILTER_MAX_V logits leaves each FA column at most 2^12
+// logits: the 16-bit count field and the 48-bit mass field cannot overflow
+static_assert(SV_FILTER_MAX_V / kLBlock <= (1 << 12), "FA column bound");
 
 struct alignas(16) FilterStats {
   double s_kept;  // sum of 2^(z c - M) over the kept tokens
   float tau;      // tokens with z >= tau are kept
   int pad;
+};
+
+// The levels FB gathers for one row, and the counts around them.
+struct alignas(16) RowPlan {
+  int l0, l1;
+  unsigned count_above;  // logits in levels < l0
+  unsigned count_in;     // logits in levels [l0, l1]
+  int general;           // 1: the resolve kernel takes the general path
+  int pad[3];
+};
+
+// Device buffers of the filter kernels (all inside the workspace).
+struct FilterWork {
+  unsigned *lv_cnt;           // [slots][NS][kLevels]
+  double *lv_mass;            // [slots][NS][kLevels]
+  unsigned long long *above;  // [slots][NS] exact mass above the gathered levels
+  unsigned *ncand;            // [slots] candidates appended
+  unsigned *cand;             // [slots][kFCap] their order keys
+  RowPlan *plan;              // [slots]
 };
 
 // Whether request b filters, with its k (0: none) and p (1: none).  Values
@@ -509,7 +543,7 @@ struct DecideShared {
 // draft, find the first rejection.  Every workgroup of a request computes the
 // same result (the arithmetic is deterministic); only the `writer` workgroup
 // stores the outputs and the sampling parameters.  Returns them in sh.sp.
-template <int DT>
+template <int DT, bool FILT>
 __device__ __forceinline__ void decide_request(
     const void *__restrict__ target, const void *__restrict__ draft,
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
@@ -526,7 +560,7 @@ __device__ __forceinline__ void decide_request(
   const float c = greedy ? 0.0f : temp_scale(T);
   int fk;
   float fp;
-  const bool filtered = !greedy && fst && request_filter(topk, topp, b, V, fk, fp);
+  const bool filtered = FILT && !greedy && request_filter(topk, topp, b, V, fk, fp);
   sv_debug dbg = dbg_in;
   if (!writer) memset(&dbg, 0, sizeof dbg);
   double *sh_s = sh.s;
@@ -575,7 +609,7 @@ __device__ __forceinline__ void decide_request(
       }
       if (!greedy) {
         float tau = -INFINITY;
-        if (filtered) {  // the kept mass replaces the row sum
+        if (FILT && filtered) {  // the kept mass replaces the row sum
           const FilterStats f = fst[static_cast<long>(b) * rows + r];
           s = f.s_kept;
           tau = f.tau;
@@ -611,7 +645,7 @@ __device__ __forceinline__ void decide_request(
         const double sp_ = sh_s[tid], sq_ = sh_s[gamma + 1 + tid];
         // a token cut by the filter has probability zero; q(x) = 0 accepts
         // when p(x) > 0 and rejects otherwise
-        const bool pin = zpx >= sh.tau[tid], qin = zqx >= sh.tau[gamma + 1 + tid];
+        const bool pin = !FILT || zpx >= sh.tau[tid], qin = !FILT || zqx >= sh.tau[gamma + 1 + tid];
         double a;
         if (!qin) {
           a = pin ? 1.0 : 0.0;
@@ -690,13 +724,17 @@ __device__ __forceinline__ void decide_request(
 // request) finds the sub-chunk whose prefix crosses u*Z and then the token in it.
 constexpr int kLaneElems = kSub / kWave;  // 32
 
+// FILT: the request may be filtered (top-k / top-p); tokens below the cut carry
+// no mass.  Unfiltered launches compile without the compares.
+template <bool FILT>
 __device__ __forceinline__ void residual_value(const SelParams &sp, float zp, float zq, float &w,
                                                float &p) {
-  // -inf -> 0; tokens cut by a top-k / top-p filter carry no mass
-  const float ep = zp >= sp.tau_p ? __builtin_amdgcn_exp2f(fmaf(zp, sp.c, sp.negMp)) : 0.0f;
+  float ep = __builtin_amdgcn_exp2f(fmaf(zp, sp.c, sp.negMp));  // -inf -> 0
+  if (FILT && !(zp >= sp.tau_p)) ep = 0.0f;
   p = ep;
   if (sp.mode == 1) {
-    const float eq = zq >= sp.tau_q ? __builtin_amdgcn_exp2f(fmaf(zq, sp.c, sp.negMq)) : 0.0f;
+    float eq = __builtin_amdgcn_exp2f(fmaf(zq, sp.c, sp.negMq));
+    if (FILT && !(zq >= sp.tau_q)) eq = 0.0f;
     w = fmaxf(0.0f, fmaf(-eq, sp.r, ep));
   } else {
     w = ep;
@@ -818,7 +856,7 @@ __device__ __forceinline__ void load_lane_raw(const void *row, bool aligned, lon
 // stores it; then every wave writes the masses of SPW consecutive 2048-token
 // sub-chunks of the row pair to sample, loading sub-chunk t+1 while it reduces
 // sub-chunk t.
-template <int DT>
+template <int DT, bool FILT>
 __global__ __launch_bounds__(kBlock) void k2_decide_mass(
     const void *__restrict__ target, const void *__restrict__ draft,
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
@@ -834,7 +872,7 @@ __global__ __launch_bounds__(kBlock) void k2_decide_mass(
   // greedy requests need the decision only (workgroup 0)
   if (wg > 0 && !(request_T(temps, scalar_T, b) > 0.0f)) return;
   __shared__ DecideShared sh;
-  decide_request<DT>(target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V, NS, part, zx,
+  decide_request<DT, FILT>(target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V, NS, part, zx,
                      topk, topp, fst, accepted_count, out_tokens, sel, dbg, b, wg == 0, sh);
   const SelParams sp = sh.sp;
   const int first = (wg * kWaves + static_cast<int>(threadIdx.x) / kWave) * SPW;
@@ -862,7 +900,7 @@ __global__ __launch_bounds__(kBlock) void k2_decide_mass(
 #pragma unroll
       for (int e = 0; e < Elem<DT>::kVec; ++e) {
         float w, p;
-        residual_value(sp, zp[e], sp.mode == 1 ? zq[e] : 0.0f, w, p);
+        residual_value<FILT>(sp, zp[e], sp.mode == 1 ? zq[e] : 0.0f, w, p);
         aw[e & 7] += w;
         ap[e & 7] += p;
       }
@@ -890,7 +928,7 @@ __global__ __launch_bounds__(kBlock) void k2_decide_mass(
 // whose inclusive prefix exceeds u*Z; then wave w scans tokens
 // [512 w, 512 w + 512) of that sub-chunk, 8 contiguous tokens per lane, and the
 // lowest token with mass whose running prefix exceeds u*Z is emitted.
-template <int DT>
+template <int DT, bool FILT>
 __global__ __launch_bounds__(kBlock) void k3_select(
     const void *__restrict__ target, const void *__restrict__ draft,
     const float *__restrict__ u_sample, int gamma, int V, int NSUB,
@@ -966,7 +1004,7 @@ __global__ __launch_bounds__(kBlock) void k3_select(
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float w, p;
-    residual_value(sp, zp[e], sp.mode == 1 ? zq[e] : 0.0f, w, p);
+    residual_value<FILT>(sp, zp[e], sp.mode == 1 ? zq[e] : 0.0f, w, p);
     vals[e] = use_p ? p : w;
     lsum += static_cast<double>(vals[e]);
   }
@@ -1042,17 +1080,33 @@ __device__ __forceinline__ unsigned long long fixed_mass(float z, float c, float
   return sh > -24 ? (mant >> -sh) : 0ull;
 }
 
-struct FilterShared {
-  unsigned cnt0[kFBins + 1];
-  unsigned long long mass0[kFBins + 1];
-  unsigned cnt1[kFBins];
-  unsigned long long mass1[kFBins];  // sub-bin masses, then the gathered logits' masses
-  unsigned cand[kFCap];              // keys of the gathered logits
+// LDS shared by the scans of both filter kernels.
+struct FilterScratch {
   unsigned long long red[2 * kFWaves];
   unsigned long long pick_c, pick_m, res_m;
-  unsigned klo, khi, ncand;
+  unsigned klo, khi, nkeys;
   int pick;
 };
+
+struct GeneralShared {
+  unsigned cnt0[kFBins + 1];
+  unsigned long long mass0[kFBins + 1];
+  union {
+    struct {  // sub-bin histogram of a crowded bin
+      unsigned cnt1[kFBins];
+      unsigned long long mass1[kFBins];
+    } h;
+    unsigned keys[kFCap];  // gathered logits (order keys)
+  } u;
+  FilterScratch sc;
+};
+
+// Level of a logit (monotone in z): l for y = z c - M in (-l-1, -l],
+// l < kLevels; kLevels for y <= -kLevels and -inf.
+__device__ __forceinline__ int level_of(float z, float c, float negM) {
+  const float ny = -fmaf(z, c, negM);
+  return ny < static_cast<float>(kLevels) ? (ny > 0.0f ? static_cast<int>(ny) : 0) : kLevels;
+}
 
 __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int lane) {
 #pragma unroll
@@ -1097,7 +1151,7 @@ __device__ __forceinline__ void wg_excl_scan2(unsigned long long &a, unsigned lo
 // bin is returned.
 __device__ int find_cross(const unsigned *cnt, const unsigned long long *mass, int n, bool by_mass,
                           unsigned long long target, unsigned long long &before_c,
-                          unsigned long long &before_m, FilterShared &sh) {
+                          unsigned long long &before_m, FilterScratch &sh) {
   const int per = (n + kFBlock - 1) / kFBlock;
   const int j0 = threadIdx.x * per, j1 = min(n, j0 + per);
   unsigned long long lc = 0, lm = 0;
@@ -1137,33 +1191,60 @@ __device__ int find_cross(const unsigned *cnt, const unsigned long long *mass, i
   return j;
 }
 
-// Calls f(z) for every logit of the row: U 16-byte loads in flight per thread,
-// widened one vector at a time.
+// Calls f(z) for every logit of the vectors [vb, ve) of a row (16-byte
+// vectors; the row's last vector may be partial).  Whole vectors of an aligned
+// row stream with U loads per thread per step, the next step's loads issued
+// before the current step is processed; the partial tail, and every logit of
+// an unaligned row, are read one by one.  keep(m) is asked with the largest
+// logit m of each whole vector; a vector for which it answers false is skipped
+// (for a test that is monotone in the logit this skips exactly the vectors
+// none of whose logits would pass it).
+template <int DT, int BS, int U, typename K, typename F>
+__device__ __forceinline__ void for_each_logit(const void *row, bool aligned, int V, long vb, long ve, K &&keep,
+                                               F &&f) {
+  constexpr int kV = Elem<DT>::kVec;
+  constexpr long kStep = static_cast<long>(U) * BS;
+  const char *r = static_cast<const char *>(row);
+  const long e_end = min(ve * kV, static_cast<long>(V));
+  long e_tail = vb * kV;  // first logit left to the one-by-one loop
+  if (aligned) {
+    const long vw = min(ve, static_cast<long>(V) / kV);  // whole vectors in range
+    auto load = [&](long v0, u32x4 *dst) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const long v = v0 + static_cast<long>(u) * BS;
+        dst[u] = v < vw ? *reinterpret_cast<const u32x4 *>(r + v * kV * Elem<DT>::kBytes) : neg_inf_vec<DT>();
+      }
+    };
+    u32x4 cur[U], nxt[U];
+    long v0 = vb + threadIdx.x;
+    if (v0 < vw) load(v0, cur);
+    for (; v0 < vw; v0 += kStep) {
+      if (v0 + kStep < vw) load(v0 + kStep, nxt);
+#pragma unroll 1
+      for (int u = 0; u < U; ++u) {
+        if (v0 + static_cast<long>(u) * BS >= vw) break;
+        float x[kV];
+        widen_vec<DT>(cur[u], x);
+        float m = x[0];
+#pragma unroll
+        for (int e = 1; e < kV; ++e) m = fmaxf(m, x[e]);
+        if (!keep(m)) continue;
+#pragma unroll
+        for (int e = 0; e < kV; ++e) f(x[e]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+    e_tail = max(vb, vw) * kV;
+  }
+  for (long e = e_tail + threadIdx.x; e < e_end; e += BS) f(load_one<DT>(row, e));
+}
+
 template <int DT, typename F>
 __device__ __forceinline__ void for_each_logit(const void *row, bool aligned, int V, F &&f) {
-  constexpr int kV = Elem<DT>::kVec;
-  constexpr int U = 4;
-  const char *r = static_cast<const char *>(row);
-  const long nvec = (static_cast<long>(V) + kV - 1) / kV;
-  for (long v0 = threadIdx.x; v0 < nvec; v0 += U * kFBlock) {
-    u32x4 raw[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long e0 = (v0 + static_cast<long>(u) * kFBlock) * kV;
-      raw[u] = (aligned && e0 + kV <= V) ? *reinterpret_cast<const u32x4 *>(r + e0 * Elem<DT>::kBytes)
-                                         : pack_guarded<DT>(r, e0, V);
-    }
-#pragma unroll 1
-    for (int u = 0; u < U; ++u) {
-      const long e0 = (v0 + static_cast<long>(u) * kFBlock) * kV;
-      if (e0 >= V) break;
-      float x[kV];
-      widen_vec<DT>(raw[u], x);
-#pragma unroll
-      for (int e = 0; e < kV; ++e)
-        if (e0 + e < V) f(x[e]);
-    }
-  }
+  for_each_logit<DT, kFBlock, 4>(row, aligned, V, 0, (static_cast<long>(V) + Elem<DT>::kVec - 1) / Elem<DT>::kVec,
+                                 [](float) { return true; }, static_cast<F &&>(f));
 }
 
 // The key interval of y bin j: every key in [lo, hi] maps to bin j and no
@@ -1187,98 +1268,45 @@ __device__ __forceinline__ void bin_key_range(int j, float c, float negM, unsign
   hi = a;
 }
 
-// The threshold for one criterion: the first group of equal logits, from the
-// top, whose inclusive count (by_mass false) or mass (by_mass true) reaches
-// `target`.  Returns its value; `kept` receives the mass of all logits >= it.
-template <int DT>
-__device__ float resolve_cut(const void *row, bool aligned, int V, float c, float negM, int fs,
-                             bool by_mass, unsigned long long target, unsigned long long &kept,
-                             FilterShared &sh) {
+// Sorts keys[0, n) in descending order (bitonic, padded to a power of two
+// with 0, which is below every non-NaN key).
+__device__ void sort_keys_desc(unsigned *keys, int n) {
   const int tid = threadIdx.x;
-  unsigned long long bc, bm;
-  const int j = find_cross(sh.cnt0, sh.mass0, kFBins + 1, by_mass, target, bc, bm, sh);
-  unsigned count = sh.cnt0[j];
-  if (tid == 0) bin_key_range(j, c, negM, sh.klo, sh.khi);
-  __syncthreads();
-  unsigned klo = sh.klo, khi = sh.khi;
-  unsigned long long before_c = bc, before_m = bm;
-
-  // split a crowded bin by the key until it fits the LDS buffer
-  while (count > static_cast<unsigned>(kFCap)) {
-    const unsigned range = khi - klo;
-    const int shb = range >= static_cast<unsigned>(kFBins) ? (32 - __clz(range)) - 11 : 0;
-    for (int i = tid; i < kFBins; i += kFBlock) {
-      sh.cnt1[i] = 0;
-      sh.mass1[i] = 0;
-    }
-    __syncthreads();
-    for_each_logit<DT>(row, aligned, V, [&](float z) {
-      const unsigned key = order_key(z);
-      if (key >= klo && key <= khi) {
-        const unsigned s = (khi - key) >> shb;
-        atomicAdd(&sh.cnt1[s], 1u);
-        const unsigned long long m = fixed_mass(z, c, negM, fs);
-        if (m) atomicAdd(&sh.mass1[s], m);
-      }
-    });
-    __syncthreads();
-    const unsigned long long rel = target - (by_mass ? before_m : before_c);
-    unsigned long long sc, sm;
-    const int s = find_cross(sh.cnt1, sh.mass1, kFBins, by_mass, rel, sc, sm, sh);
-    before_c += sc;
-    before_m += sm;
-    count = sh.cnt1[s];
-    const unsigned long long smass = sh.mass1[s];
-    const long long top = static_cast<long long>(khi) - (static_cast<long long>(s) << shb);
-    const long long bot = static_cast<long long>(khi) - (static_cast<long long>(s + 1) << shb) + 1;
-    khi = static_cast<unsigned>(top);
-    klo = bot > static_cast<long long>(klo) ? static_cast<unsigned>(bot) : klo;
-    if (shb == 0) {  // one key: the whole group is one value
-      kept = before_m + smass;
-      __syncthreads();
-      return key_value(khi);
-    }
-    __syncthreads();
-  }
-
-  // gather the bin's logits, sort them by key (descending)
-  if (tid == 0) sh.ncand = 0;
-  __syncthreads();
-  for_each_logit<DT>(row, aligned, V, [&](float z) {
-    const unsigned key = order_key(z);
-    if (key >= klo && key <= khi) {
-      const unsigned slot = atomicAdd(&sh.ncand, 1u);
-      if (slot < static_cast<unsigned>(kFCap)) sh.cand[slot] = key;
-    }
-  });
-  __syncthreads();
-  const int n = min(static_cast<int>(sh.ncand), kFCap);
   int N = 2;
   while (N < n) N <<= 1;
-  for (int i = n + tid; i < N; i += kFBlock) sh.cand[i] = 0u;  // below every non-NaN key
+  for (int i = n + tid; i < N; i += kFBlock) keys[i] = 0u;
   __syncthreads();
   for (int size = 2; size <= N; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = tid; i < N / 2; i += kFBlock) {
         const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
-        const unsigned a = sh.cand[lo], b = sh.cand[hi];
+        const unsigned a = keys[lo], b = keys[hi];
         if (((lo & size) == 0) == (a < b)) {
-          sh.cand[lo] = b;
-          sh.cand[hi] = a;
+          keys[lo] = b;
+          keys[hi] = a;
         }
       }
       __syncthreads();
     }
   }
+}
 
-  // inclusive mass prefix in sorted order; the first group end meeting the target
+// Scan of sorted keys[0, n) (descending) that continue a prefix with count
+// before_c and mass before_m: the first end of a group of equal keys whose
+// inclusive count (by_mass false) or mass (by_mass true) reaches `target`.
+// Returns its value; `kept` receives the inclusive mass there.
+__device__ float scan_sorted(const unsigned *keys, int n, unsigned long long before_c,
+                             unsigned long long before_m, bool by_mass, unsigned long long target,
+                             float c, float negM, int fs, unsigned long long &kept, bool &found,
+                             FilterScratch &sh) {
   constexpr int kPer = kFCap / kFBlock;
+  const int tid = threadIdx.x;
   const int i0 = tid * kPer;
   unsigned long long m[kPer];
   unsigned long long lsum = 0;
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    m[q] = (i0 + q < n) ? fixed_mass(key_value(sh.cand[i0 + q]), c, negM, fs) : 0ull;
+    m[q] = (i0 + q < n) ? fixed_mass(key_value(keys[i0 + q]), c, negM, fs) : 0ull;
     lsum += m[q];
   }
   unsigned long long ex = lsum, dummy = 0, tot, tdummy;
@@ -1293,7 +1321,7 @@ __device__ float resolve_cut(const void *row, bool aligned, int V, float c, floa
     const int i = i0 + q;
     if (i < n) {
       run += m[q];
-      const bool group_end = (i == n - 1) || sh.cand[i + 1] != sh.cand[i];
+      const bool group_end = (i == n - 1) || keys[i + 1] != keys[i];
       const unsigned long long crit = by_mass ? run : before_c + static_cast<unsigned long long>(i) + 1;
       if (mine < 0 && group_end && crit >= target) {
         mine = i;
@@ -1307,82 +1335,390 @@ __device__ float resolve_cut(const void *row, bool aligned, int V, float c, floa
   if (mine >= 0 && mine == pick) sh.res_m = mine_m;
   __syncthreads();
   float tau;
-  if (pick == 0x7fffffff) {  // not reached for consistent sums: keep the whole bin
-    tau = n > 0 ? key_value(sh.cand[n - 1]) : key_value(klo);
+  found = pick != 0x7fffffff;
+  if (!found) {  // not reached: keep all n
+    tau = key_value(keys[n > 0 ? n - 1 : 0]);
     kept = before_m + tot;
   } else {
-    tau = key_value(sh.cand[pick]);
+    tau = key_value(keys[pick]);
     kept = sh.res_m;
   }
   __syncthreads();
   return tau;
 }
 
+// The threshold for one criterion: the first group of equal logits, from the
+// top, whose inclusive count (by_mass false) or mass (by_mass true) reaches
+// `target`.  Returns its value; `kept` receives the mass of all logits >= it.
 template <int DT>
-__global__ __launch_bounds__(kFBlock) void k_filter_rows(
-    const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
-    const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
-    int gamma, int V, int NS, int fs, const Partial *__restrict__ part, FilterStats *__restrict__ fst) {
-  const int rows = 2 * gamma + 1;
-  const int slot = blockIdx.x;
-  const int b = slot / rows, r = slot - b * rows;
-  const float T = temps[b];
-  int k;
-  float p;
-  if (!(T > 0.0f) || !request_filter(topk, topp, b, V, k, p)) return;  // uniform per workgroup
+__device__ float resolve_cut(const void *row, bool aligned, int V, float c, float negM, int fs,
+                             bool by_mass, unsigned long long target, unsigned long long &kept,
+                             GeneralShared &sh) {
+  const int tid = threadIdx.x;
+  unsigned long long bc, bm;
+  const int j = find_cross(sh.cnt0, sh.mass0, kFBins + 1, by_mass, target, bc, bm, sh.sc);
+  unsigned count = sh.cnt0[j];
+  if (tid == 0) bin_key_range(j, c, negM, sh.sc.klo, sh.sc.khi);
+  __syncthreads();
+  unsigned klo = sh.sc.klo, khi = sh.sc.khi;
+  unsigned long long before_c = bc, before_m = bm;
+
+  // split a crowded bin by the key until it fits the LDS buffer
+  while (count > static_cast<unsigned>(kFCap)) {
+    const unsigned range = khi - klo;
+    const int shb = range >= static_cast<unsigned>(kFBins) ? (32 - __clz(range)) - 11 : 0;
+    for (int i = tid; i < kFBins; i += kFBlock) {
+      sh.u.h.cnt1[i] = 0;
+      sh.u.h.mass1[i] = 0;
+    }
+    __syncthreads();
+    for_each_logit<DT>(row, aligned, V, [&](float z) {
+      const unsigned key = order_key(z);
+      if (key >= klo && key <= khi) {
+        const unsigned s = (khi - key) >> shb;
+        atomicAdd(&sh.u.h.cnt1[s], 1u);
+        const unsigned long long m = fixed_mass(z, c, negM, fs);
+        if (m) atomicAdd(&sh.u.h.mass1[s], m);
+      }
+    });
+    __syncthreads();
+    const unsigned long long rel = target - (by_mass ? before_m : before_c);
+    unsigned long long sc, sm;
+    const int s = find_cross(sh.u.h.cnt1, sh.u.h.mass1, kFBins, by_mass, rel, sc, sm, sh.sc);
+    before_c += sc;
+    before_m += sm;
+    count = sh.u.h.cnt1[s];
+    const unsigned long long smass = sh.u.h.mass1[s];
+    const long long top = static_cast<long long>(khi) - (static_cast<long long>(s) << shb);
+    const long long bot = static_cast<long long>(khi) - (static_cast<long long>(s + 1) << shb) + 1;
+    khi = static_cast<unsigned>(top);
+    klo = bot > static_cast<long long>(klo) ? static_cast<unsigned>(bot) : klo;
+    if (shb == 0) {  // one key: the whole group is one value
+      kept = before_m + smass;
+      __syncthreads();
+      return key_value(khi);
+    }
+    __syncthreads();
+  }
+
+  // gather the bin's logits, sort them, scan
+  if (tid == 0) sh.sc.nkeys = 0;
+  __syncthreads();
+  for_each_logit<DT>(row, aligned, V, [&](float z) {
+    const unsigned key = order_key(z);
+    if (key >= klo && key <= khi) {
+      const unsigned slot = atomicAdd(&sh.sc.nkeys, 1u);
+      if (slot < static_cast<unsigned>(kFCap)) sh.u.keys[slot] = key;
+    }
+  });
+  __syncthreads();
+  const int n = min(static_cast<int>(sh.sc.nkeys), kFCap);
+  sort_keys_desc(sh.u.keys, n);
+  bool found;
+  return scan_sorted(sh.u.keys, n, before_c, before_m, by_mass, target, c, negM, fs, kept, found, sh.sc);
+}
+
+// Row selection shared by the filter kernels: request b's row r (target rows
+// 0..gamma, then draft rows), or nullptr when the row is not filtered (greedy
+// request, no active filter, or a row beyond the request's draft length).
+template <int DT>
+__device__ __forceinline__ const void *filtered_row(const void *target, const void *draft, const float *temps,
+                                                    const int32_t *lens, const int32_t *topk, const float *topp,
+                                                    int gamma, int V, int b, int r, float &T, int &k, float &p) {
+  T = temps[b];
+  if (!(T > 0.0f) || !request_filter(topk, topp, b, V, k, p)) return nullptr;
   const int g = request_len(lens, gamma, b);
   const bool is_target = r <= gamma;
   const int i = is_target ? r : r - gamma - 1;
-  if (is_target ? i > g : i >= g) return;
-  const void *row = is_target
-                        ? static_cast<const void *>(static_cast<const char *>(target) +
-                                                    (static_cast<long>(b) * (gamma + 1) + i) * V *
-                                                        Elem<DT>::kBytes)
-                        : static_cast<const void *>(static_cast<const char *>(draft) +
-                                                    (static_cast<long>(b) * gamma + i) * V * Elem<DT>::kBytes);
-  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-  // the row's M, as K2 merges it
-  int M = kEmptyM;
-  double s = 0.0;
+  if (is_target ? i > g : i >= g) return nullptr;
+  return is_target ? static_cast<const void *>(static_cast<const char *>(target) +
+                                               (static_cast<long>(b) * (gamma + 1) + i) * V * Elem<DT>::kBytes)
+                   : static_cast<const void *>(static_cast<const char *>(draft) +
+                                               (static_cast<long>(b) * gamma + i) * V * Elem<DT>::kBytes);
+}
+
+// The row's M (and K1's row sum s), merged in chunk order as K2 merges them.
+__device__ __forceinline__ void row_scale(const Partial *part, long slot, int NS, int &M, double &s) {
+  M = kEmptyM;
+  s = 0.0;
   float mx = -INFINITY;
   for (int j = 0; j < NS; ++j) {
-    const Partial q = part[static_cast<long>(slot) * NS + j];
+    const Partial q = part[slot * NS + j];
     merge_sm(M, s, mx, q.mi, q.s, q.mx);
   }
+}
+
+// FA: level histogram of one chunk of a row (K1's chunking).  Every thread
+// counts into its own LDS column (plain read-modify-write: no atomics, no bank
+// conflicts), one 64-bit word per level: the count in bits 48..63 and the
+// level's mass estimate in bits 0..47 as sum of round(e * 2^(l + 24)), a value
+// in (2^23, 2^24] for a logit of level l.  Logits below level kLevels - 1 are
+// not counted.
+template <int DT>
+__global__ __launch_bounds__(kLBlock) void k_filter_levels(
+    const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
+    const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
+    int gamma, int V, int NS, int chunk_vecs, const Partial *__restrict__ part, FilterWork fw) {
+  const int rows = 2 * gamma + 1;
+  const long slot = blockIdx.x / NS;
+  const int j = static_cast<int>(blockIdx.x - slot * NS);
+  const int b = static_cast<int>(slot / rows), r = static_cast<int>(slot - static_cast<long>(b) * rows);
+  float T, p;
+  int k;
+  const void *row = filtered_row<DT>(target, draft, temps, lens, topk, topp, gamma, V, b, r, T, k, p);
+  if (!row) return;  // uniform per workgroup
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  int M;
+  double s;
+  row_scale(part, slot, NS, M, s);
   const float c = temp_scale(T), negM = -static_cast<float>(M);
-  __shared__ FilterShared sh;
-  const int tid = threadIdx.x;
-  for (int j = tid; j <= kFBins; j += kFBlock) {
-    sh.cnt0[j] = 0;
-    sh.mass0[j] = 0;
-  }
-  __syncthreads();
-  for_each_logit<DT>(row, aligned, V, [&](float z) {
-    const int j = ybin(z, c, negM);
-    atomicAdd(&sh.cnt0[j], 1u);
-    const unsigned long long m = fixed_mass(z, c, negM, fs);
-    if (m) atomicAdd(&sh.mass0[j], m);
+  __shared__ unsigned long long lw[kLevels * kLBlock];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+#pragma unroll
+  for (int l = 0; l < kLevels; ++l) lw[l * kLBlock + tid] = 0ull;  // each thread clears its own column
+  const long nvec = (static_cast<long>(V) + Elem<DT>::kVec - 1) / Elem<DT>::kVec;
+  const long vb = static_cast<long>(j) * chunk_vecs, ve = min(vb + chunk_vecs, nvec);
+  for_each_logit<DT, kLBlock, 8>(row, aligned, V, vb, ve,
+                                 [&](float m) { return level_of(m, c, negM) < kLevels; }, [&](float z) {
+    const float y = fmaf(z, c, negM);
+    const int l = level_of(z, c, negM);
+    if (l < kLevels) {
+      const unsigned q = static_cast<unsigned>(
+          __builtin_amdgcn_exp2f(y + static_cast<float>(l + 24)) + 0.5f);  // e * 2^(l + 24), rounded
+      lw[l * kLBlock + tid] += (1ull << 48) + q;
+    }
   });
   __syncthreads();
-  unsigned long long total = 0;
-  {
-    unsigned long long lm = 0, lc = 0, tc;
-    for (int j = tid; j <= kFBins; j += kFBlock) lm += sh.mass0[j];
-    wg_excl_scan2(lm, lc, total, tc, sh.red);
+  const long o = (slot * NS + j) * kLevels;
+  for (int l = wave; l < kLevels; l += kLBlock / kWave) {  // fixed order: deterministic
+    // a column holds at most V / 256 <= 2^12 logits, so a lane's four columns
+    // keep both fields in range; the fields are then summed apart
+    unsigned long long w = 0;
+    for (int t = lane; t < kLBlock; t += kWave) w += lw[l * kLBlock + t];
+    unsigned cs = static_cast<unsigned>(w >> 48);
+    unsigned long long ms = w & ((1ull << 48) - 1);
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) {  // integer sums: any order
+      cs += __shfl_xor(cs, d);
+      ms += __shfl_xor(ms, d);
+    }
+    if (lane == 0) {
+      fw.lv_cnt[o + l] = cs;
+      fw.lv_mass[o + l] = ldexp(static_cast<double>(ms), -(l + 24));
+    }
   }
-  float tau = -INFINITY;
-  unsigned long long kept = total;
-  if (k > 0) tau = resolve_cut<DT>(row, aligned, V, c, negM, fs, false, static_cast<unsigned long long>(k), kept, sh);
+  if (j == 0 && tid == 0) fw.ncand[slot] = 0u;
+}
+
+// The levels [l0, l1] whose logits FB gathers, from the row's level counts and
+// fp32-estimated masses (inclusive prefixes lc[], lm[] over levels 0..kLevels-1)
+// and K1's row sum s: the level of the k-th largest logit (exact counts) and
+// the levels that can hold the top-p crossing (a 1e-4 margin on the estimated
+// masses).  general = 1 when those levels reach below level kLevels - 1 or hold
+// more than kFCap logits.
+__device__ RowPlan choose_levels(const unsigned *lc, const double *lm, double s, int k, float p) {
+  constexpr double kEps = 1e-4;
+  RowPlan rp;
+  int lk = kLevels, l0 = 0, l1 = kLevels;
+  if (k > 0) {
+    lk = 0;
+    while (lk < kLevels && lc[lk] < static_cast<unsigned>(k)) ++lk;
+  }
   if (p < 1.0f) {
-    double t = ceil(static_cast<double>(p) * static_cast<double>(kept));
-    if (t < 1.0) t = 1.0;
-    unsigned long long tgt = static_cast<unsigned long long>(t);
-    if (tgt > kept) tgt = kept;
-    unsigned long long kept_p;
-    const float tau_p = resolve_cut<DT>(row, aligned, V, c, negM, fs, true, tgt, kept_p, sh);
-    if (tau_p > tau) {
-      tau = tau_p;
-      kept = kept_p;
+    const bool klev = k > 0 && lk < kLevels;
+    const double fk_lo = klev ? (lk > 0 ? lm[lk - 1] : 0.0) : s, fk_hi = klev ? lm[lk] : s;
+    const double t_lo = static_cast<double>(p) * fk_lo * (1.0 - kEps);
+    const double t_hi = static_cast<double>(p) * fk_hi * (1.0 + kEps);
+    int lf = 0;
+    while (lf < kLevels && lm[lf] * (1.0 + kEps) < t_lo) ++lf;
+    int ll = lf;
+    while (ll < kLevels && lm[ll] * (1.0 - kEps) < t_hi) ++ll;
+    l0 = lf;
+    l1 = k > 0 ? lk : ll;
+    if (l0 > l1) l0 = l1;
+  } else {
+    l0 = l1 = lk;
+  }
+  rp.l0 = l0;
+  rp.l1 = l1;
+  rp.count_above = l0 > 0 ? lc[(l0 < kLevels ? l0 : kLevels) - 1] : 0u;
+  rp.count_in = l1 < kLevels ? lc[l1] - rp.count_above : 0u;
+  rp.general = (l1 >= kLevels || rp.count_in > static_cast<unsigned>(kFCap)) ? 1 : 0;
+  return rp;
+}
+
+// FB: one chunk of a row again.  Logits above level l0 add their exact
+// fixed-point mass to the chunk's sum; logits in levels [l0, l1] are appended
+// to the row's candidate list.
+template <int DT>
+__global__ __launch_bounds__(kLBlock) void k_filter_gather(
+    const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
+    const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
+    int gamma, int V, int NS, int chunk_vecs, int fs, const Partial *__restrict__ part, FilterWork fw) {
+  const int rows = 2 * gamma + 1;
+  const long slot = blockIdx.x / NS;
+  const int j = static_cast<int>(blockIdx.x - slot * NS);
+  const int b = static_cast<int>(slot / rows), r = static_cast<int>(slot - static_cast<long>(b) * rows);
+  float T, p;
+  int k;
+  const void *row = filtered_row<DT>(target, draft, temps, lens, topk, topp, gamma, V, b, r, T, k, p);
+  if (!row) return;  // uniform per workgroup
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  int M;
+  double s;
+  row_scale(part, slot, NS, M, s);
+  const float c = temp_scale(T), negM = -static_cast<float>(M);
+  __shared__ unsigned sc[kLevels];
+  __shared__ double sm[kLevels];
+  __shared__ RowPlan srp;
+  __shared__ unsigned long long red[kLBlock / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  if (tid < kLevels) {  // the row's levels, chunks merged in order
+    unsigned cs = 0;
+    double ms = 0.0;
+    for (int q = 0; q < NS; ++q) {
+      cs += fw.lv_cnt[(slot * NS + q) * kLevels + tid];
+      ms += fw.lv_mass[(slot * NS + q) * kLevels + tid];
+    }
+    sc[tid] = cs;
+    sm[tid] = ms;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int l = 1; l < kLevels; ++l) {
+      sc[l] += sc[l - 1];
+      sm[l] += sm[l - 1];
+    }
+    srp = choose_levels(sc, sm, s, k, p);
+    if (j == 0) fw.plan[slot] = srp;
+  }
+  __syncthreads();
+  const RowPlan rp = srp;
+  if (rp.general) return;  // uniform per workgroup
+  const long nvec = (static_cast<long>(V) + Elem<DT>::kVec - 1) / Elem<DT>::kVec;
+  const long vb = static_cast<long>(j) * chunk_vecs, ve = min(vb + chunk_vecs, nvec);
+  unsigned long long above = 0;
+  unsigned *cand = fw.cand + slot * kFCap;
+  for_each_logit<DT, kLBlock, 8>(row, aligned, V, vb, ve,
+                                 [&](float m) { return level_of(m, c, negM) <= rp.l1; }, [&](float z) {
+    const int l = level_of(z, c, negM);
+    if (l < rp.l0) {
+      above += fixed_mass(z, c, negM, fs);
+    } else if (l <= rp.l1) {
+      const unsigned q = atomicAdd(&fw.ncand[slot], 1u);
+      if (q < static_cast<unsigned>(kFCap)) cand[q] = order_key(z);
+    }
+  });
+  // exact chunk sum (integer: the order of the additions does not matter)
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) above += __shfl_xor(above, d);
+  if (lane == 0) red[wave] = above;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long t = 0;
+    for (int w = 0; w < kLBlock / kWave; ++w) t += red[w];
+    fw.above[slot * NS + j] = t;
+  }
+}
+
+// FC: one workgroup per row.  Sorts the gathered logits and scans them from
+// the exact prefix above them; rows the plan marked, or whose crossing the
+// scan does not find (a margin exceeded), take the general path.
+template <int DT>
+__global__ __launch_bounds__(kFBlock) void k_filter_resolve(
+    const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
+    const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
+    int gamma, int V, int NS, int fs, const Partial *__restrict__ part, FilterWork fw,
+    FilterStats *__restrict__ fst) {
+  const int rows = 2 * gamma + 1;
+  const long slot = blockIdx.x;
+  const int b = static_cast<int>(slot / rows), r = static_cast<int>(slot - static_cast<long>(b) * rows);
+  float T, p;
+  int k;
+  const void *row = filtered_row<DT>(target, draft, temps, lens, topk, topp, gamma, V, b, r, T, k, p);
+  if (!row) return;  // uniform per workgroup
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  int M;
+  double s;
+  row_scale(part, slot, NS, M, s);
+  const float c = temp_scale(T), negM = -static_cast<float>(M);
+  __shared__ GeneralShared sh;
+  const int tid = threadIdx.x;
+  const RowPlan rp = fw.plan[slot];
+  float tau = -INFINITY;
+  unsigned long long kept = 0;
+  bool done = false;
+  if (!rp.general) {
+    const int n = min(static_cast<int>(fw.ncand[slot]), kFCap);
+    unsigned *keys = sh.u.keys;
+    for (int i = tid; i < n; i += kFBlock) keys[i] = fw.cand[slot * kFCap + i];
+    unsigned long long before_m = 0;
+    for (int q = 0; q < NS; ++q) before_m += fw.above[slot * NS + q];
+    sort_keys_desc(keys, n);  // begins with a barrier after its padding stores
+    const unsigned long long before_c = rp.count_above;
+    bool ok = true;
+    if (k > 0) {
+      bool found;
+      tau = scan_sorted(keys, n, before_c, before_m, false, static_cast<unsigned long long>(k), c, negM, fs,
+                        kept, found, sh.sc);
+      ok = found;
+    }
+    if (ok && p < 1.0f) {
+      // top-p of the top-k mass, or of the row's mass (K1's sum, in the same units)
+      const double base = k > 0 ? static_cast<double>(kept) : ldexp(s, fs);
+      double t = ceil(static_cast<double>(p) * base);
+      if (t < 1.0) t = 1.0;
+      const unsigned long long tgt = static_cast<unsigned long long>(t);
+      if (before_m >= tgt) {
+        ok = false;  // the crossing lies above the gathered levels
+      } else {
+        bool found;
+        unsigned long long kept_p;
+        const float tau_p = scan_sorted(keys, n, before_c, before_m, true, tgt, c, negM, fs, kept_p, found, sh.sc);
+        ok = found;
+        if (found && tau_p > tau) {
+          tau = tau_p;
+          kept = kept_p;
+        }
+      }
+    }
+    done = ok;
+    __syncthreads();
+  }
+  if (!done) {  // general path
+    for (int jb = tid; jb <= kFBins; jb += kFBlock) {
+      sh.cnt0[jb] = 0;
+      sh.mass0[jb] = 0;
+    }
+    __syncthreads();
+    for_each_logit<DT>(row, aligned, V, [&](float z) {
+      const int jb = ybin(z, c, negM);
+      atomicAdd(&sh.cnt0[jb], 1u);
+      const unsigned long long m = fixed_mass(z, c, negM, fs);
+      if (m) atomicAdd(&sh.mass0[jb], m);
+    });
+    __syncthreads();
+    unsigned long long total = 0;
+    {
+      unsigned long long lm = 0, lc = 0, tc;
+      for (int jb = tid; jb <= kFBins; jb += kFBlock) lm += sh.mass0[jb];
+      wg_excl_scan2(lm, lc, total, tc, sh.sc.red);
+    }
+    tau = -INFINITY;
+    kept = total;
+    if (k > 0)
+      tau = resolve_cut<DT>(row, aligned, V, c, negM, fs, false, static_cast<unsigned long long>(k), kept, sh);
+    if (p < 1.0f) {
+      double t = ceil(static_cast<double>(p) * static_cast<double>(kept));
+      if (t < 1.0) t = 1.0;
+      unsigned long long tgt = static_cast<unsigned long long>(t);
+      if (tgt > kept) tgt = kept;
+      unsigned long long kept_p;
+      const float tau_p = resolve_cut<DT>(row, aligned, V, c, negM, fs, true, tgt, kept_p, sh);
+      if (tau_p > tau) {
+        tau = tau_p;
+        kept = kept_p;
+      }
     }
   }
   if (tid == 0) {
@@ -1599,6 +1935,8 @@ struct Plan {
   int rows, NS, chunk_vecs, NSUB, SPW, NW;
   long k1_groups, k3_groups;
   size_t part_off, zx_off, sel_off, sums_off, fst_off, total;
+  // filtered calls: buffers of the filter kernels after `total`
+  size_t lvc_off, lvm_off, above_off, ncand_off, cand_off, plan_off, ftotal;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -1646,6 +1984,20 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P) {
   P->fst_off = off;
   off = align_up(off + sizeof(FilterStats) * static_cast<size_t>(slots));
   P->total = off;
+  const size_t chunks = static_cast<size_t>(P->k1_groups);
+  P->lvc_off = off;
+  off = align_up(off + sizeof(unsigned) * chunks * kLevels);
+  P->lvm_off = off;
+  off = align_up(off + sizeof(double) * chunks * kLevels);
+  P->above_off = off;
+  off = align_up(off + sizeof(unsigned long long) * chunks);
+  P->ncand_off = off;
+  off = align_up(off + sizeof(unsigned) * static_cast<size_t>(slots));
+  P->cand_off = off;
+  off = align_up(off + sizeof(unsigned) * static_cast<size_t>(slots) * kFCap);
+  P->plan_off = off;
+  off = align_up(off + sizeof(RowPlan) * static_cast<size_t>(slots));
+  P->ftotal = off;
   return true;
 }
 
@@ -1706,20 +2058,43 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
                                static_cast<hipEvent_t>(dbg.k1_events[1]));
   if (e != hipSuccess) return SV_EHIP;
   if (fst) {
-    hipLaunchKernelGGL((k_filter_rows<DT>), dim3(static_cast<unsigned>(static_cast<long>(B) * P.rows)),
-                       dim3(kFBlock), 0, st, target, draft, temps, lens, topk, topp, gamma, V, P.NS,
-                       filter_frac_bits(V), part, fst);
+    FilterWork fw;
+    fw.lv_cnt = reinterpret_cast<unsigned *>(base + P.lvc_off);
+    fw.lv_mass = reinterpret_cast<double *>(base + P.lvm_off);
+    fw.above = reinterpret_cast<unsigned long long *>(base + P.above_off);
+    fw.ncand = reinterpret_cast<unsigned *>(base + P.ncand_off);
+    fw.cand = reinterpret_cast<unsigned *>(base + P.cand_off);
+    fw.plan = reinterpret_cast<RowPlan *>(base + P.plan_off);
+    const int fs = filter_frac_bits(V);
+    const dim3 cgrid(static_cast<unsigned>(P.k1_groups)), rgrid(static_cast<unsigned>(static_cast<long>(B) * P.rows));
+    hipLaunchKernelGGL((k_filter_levels<DT>), cgrid, dim3(kLBlock), 0, st, target, draft, temps, lens, topk, topp,
+                       gamma, V, P.NS, P.chunk_vecs, part, fw);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    hipLaunchKernelGGL((k_filter_gather<DT>), cgrid, dim3(kLBlock), 0, st, target, draft, temps, lens, topk, topp,
+                       gamma, V, P.NS, P.chunk_vecs, fs, part, fw);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    hipLaunchKernelGGL((k_filter_resolve<DT>), rgrid, dim3(kFBlock), 0, st, target, draft, temps, lens, topk, topp,
+                       gamma, V, P.NS, fs, part, fw, fst);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
   }
   // greedy-only batches need the decision alone: one workgroup per request
   const int nw = all_greedy ? 1 : P.NW;
-  hipLaunchKernelGGL((k2_decide_mass<DT>), dim3(static_cast<unsigned>(static_cast<long>(B) * nw)),
-                     dim3(kBlock), 0, st, target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V,
-                     P.NS, P.NSUB, nw, P.SPW, part, zx, topk, topp, fst, count, out, sel, sums, dbg);
+  if (fst)
+    hipLaunchKernelGGL((k2_decide_mass<DT, true>), dim3(static_cast<unsigned>(static_cast<long>(B) * nw)),
+                       dim3(kBlock), 0, st, target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V,
+                       P.NS, P.NSUB, nw, P.SPW, part, zx, topk, topp, fst, count, out, sel, sums, dbg);
+  else
+    hipLaunchKernelGGL((k2_decide_mass<DT, false>), dim3(static_cast<unsigned>(static_cast<long>(B) * nw)),
+                       dim3(kBlock), 0, st, target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V,
+                       P.NS, P.NSUB, nw, P.SPW, part, zx, topk, topp, fst, count, out, sel, sums, dbg);
   if (hipGetLastError() != hipSuccess) return SV_EHIP;
   if (!all_greedy) {
-    hipLaunchKernelGGL((k3_select<DT>), dim3(B), dim3(kBlock), 0, st, target, draft, u_sample, gamma, V,
-                       P.NSUB, sel, sums, out, dbg.residual_mass);
+    if (fst)
+      hipLaunchKernelGGL((k3_select<DT, true>), dim3(B), dim3(kBlock), 0, st, target, draft, u_sample, gamma,
+                         V, P.NSUB, sel, sums, out, dbg.residual_mass);
+    else
+      hipLaunchKernelGGL((k3_select<DT, false>), dim3(B), dim3(kBlock), 0, st, target, draft, u_sample, gamma,
+                         V, P.NSUB, sel, sums, out, dbg.residual_mass);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
   }
   return SV_OK;
@@ -1738,7 +2113,8 @@ int dispatch(const void *target, const void *draft, const int32_t *tokens, const
   if (!target || !u_sample || !count || !out) return SV_EINVAL;
   if (gamma > 0 && !tokens) return SV_EINVAL;
   if (gamma > 0 && !all_greedy && (!draft || !u_accept)) return SV_EINVAL;
-  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0 || ws_bytes < P.total) return SV_EWORKSPACE;
+  const size_t need = (topk || topp) ? P.ftotal : P.total;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0 || ws_bytes < need) return SV_EWORKSPACE;
   if (dbg && ((dbg->k1_events[0] == nullptr) != (dbg->k1_events[1] == nullptr))) return SV_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == SV_BF16)
@@ -1778,6 +2154,12 @@ int spec_verify_ex(const void *target_logits, const void *draft_logits, const in
   return dispatch(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, 0.0f,
                   false, draft_lens, nullptr, nullptr, B, gamma, V, dtype, accepted_count, out_tokens,
                   workspace, workspace_bytes, stream, dbg);
+}
+
+size_t spec_verify_filtered_workspace_bytes(int B, int gamma, int V, int dtype) {
+  Plan P;
+  if (!make_plan(B, gamma, V, dtype, &P) || V > SV_FILTER_MAX_V) return 0;
+  return P.ftotal;
 }
 
 int spec_verify_filtered(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,

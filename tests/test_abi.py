@@ -135,3 +135,9 @@ def test_filtered_host_argument_checks(lib):
     assert call(B=0) == sv.binding.SV_EINVAL
     ws = f(1, 1, 1, 1, 1, 1, None, 1, None, 2, 3, 10, sv.SV_F32, 1, 1, 256, 16, None, None)
     assert ws == sv.binding.SV_EWORKSPACE
+    # a workspace sized for the unfiltered call is too small for a filtered one
+    plain = sv.spec_verify_workspace_bytes(2, 3, 10, sv.SV_F32)
+    assert sv.spec_verify_filtered_workspace_bytes(2, 3, 10, sv.SV_F32) > plain
+    assert f(1, 1, 1, 1, 1, 1, None, 1, None, 2, 3, 10, sv.SV_F32, 1, 1, 256, plain, None, None) == \
+        sv.binding.SV_EWORKSPACE
+    assert sv.spec_verify_filtered_workspace_bytes(2, 3, (1 << 20) + 1, sv.SV_F32) == 0
