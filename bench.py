@@ -79,11 +79,18 @@ PROFILE_COMMANDS = {
 
 
 def _kernel_short(name: str) -> str:
+    """Kernel name with its template arguments spelled out (element type, request kind, filtering)."""
     import re
-    m = re.search(r"::(k\w+)<", name)
-    if m:
-        return m.group(1)
-    return name.split("(")[0][:60]
+    m = re.search(r"::(k\w+)<([^>]*)>", name)
+    if not m:
+        return name.split("(")[0][:60]
+    kname, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
+    tags = [{"0": "f32", "1": "bf16"}.get(args[0], args[0])]
+    if kname == "k1_row_stats" and len(args) == 3:
+        tags.append({"0": "per-request T", "1": "stochastic", "2": "greedy"}.get(args[2], args[2]))
+    elif len(args) == 2 and args[1] in ("true", "false"):
+        tags.append("filtered" if args[1] == "true" else "plain")
+    return f"{kname}<{', '.join(tags)}>"
 
 
 def _find_csv(d, suffix):
@@ -111,9 +118,15 @@ def summarize_profile(root: str):
         n = _kernel_short(r["Name"])
         lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
-        if n == "k1_row_stats":
+        if n == "k1_row_stats<bf16, stochastic>":
             k1_avg_ns = float(r["AverageNs"])
-    lines += ["", "The copy kernels are the benchmark's set-up (input copies), outside the timed region.", ""]
+    lines += ["", "Which call runs which kernels: the timed steps (spec_verify, T = 1) run "
+              "k1_row_stats<bf16, stochastic>, k2_decide_mass<bf16, plain> and k3_select<bf16, plain>; "
+              "the K1 timing pass (spec_verify_ex) runs k1_row_stats<bf16, per-request T>; the filtered "
+              "measurement (spec_verify_filtered, T = 0.7, top_p = 0.9 with and without top_k = 50) runs "
+              "k1_row_stats<bf16, per-request T>, k_filter_levels, k_filter_gather, k_filter_resolve and the "
+              "filtered k2 / k3; the draft-side sampling measurement runs k_sample_rows.  The copy kernels "
+              "are the benchmark's set-up (input copies), outside the timed region.", ""]
     open(os.path.join(out_dir, "kernels_B64_g5_V128256_bf16.md"), "w").write("\n".join(lines))
 
     def pmc_medians(d):
@@ -131,10 +144,11 @@ def summarize_profile(root: str):
     copy_kib = (1 << 30) / 1024
     f_fetch = copy_kib / cfetch[copy_name]
     f_write = copy_kib / cwrite[copy_name]
-    k1_bytes = (fetch["k1_row_stats"] * f_fetch + write["k1_row_stats"] * f_write) * 1024
+    K1 = "k1_row_stats<bf16, stochastic>"
+    k1_bytes = (fetch[K1] * f_fetch + write[K1] * f_write) * 1024
     bytes_alg = 64 * 11 * 128256 * 2
     rec = {"kernel": "k1_row_stats", "mode": "stochastic", "kernel_source_sha256_16": source_hash(),
-           "fetch_kib_per_dispatch": fetch["k1_row_stats"], "write_kib_per_dispatch": write["k1_row_stats"],
+           "fetch_kib_per_dispatch": fetch[K1], "write_kib_per_dispatch": write[K1],
            "copy_kernel": copy_name, "copy_fetch_kib": cfetch[copy_name], "copy_write_kib": cwrite[copy_name],
            "fetch_scale": f_fetch, "write_scale": f_write, "hbm_bytes_per_launch": round(k1_bytes),
            "bytes_alg_per_launch": bytes_alg, "traffic_over_alg": k1_bytes / bytes_alg,
@@ -153,7 +167,7 @@ def summarize_profile(root: str):
     lines += ["", f"Calibration: the plain 1 GiB device copy ({copy_name}) reads {cfetch[copy_name]:.1f} KiB "
               f"and writes {cwrite[copy_name]:.1f} KiB by these counters, so FETCH_SIZE is scaled by "
               f"{f_fetch:.4f} and WRITE_SIZE by {f_write:.4f} to give bytes.",
-              "", f"k1_row_stats: {k1_bytes / 1e6:.2f} MB per launch against {bytes_alg / 1e6:.2f} MB algorithmic "
+              "", f"{K1}: {k1_bytes / 1e6:.2f} MB per launch against {bytes_alg / 1e6:.2f} MB algorithmic "
               f"(ratio {k1_bytes / bytes_alg:.4f}).", ""]
     open(os.path.join(out_dir, "hbm_traffic_B64_g5_V128256_bf16.md"), "w").write("\n".join(lines))
     print(json.dumps(rec, indent=2))
