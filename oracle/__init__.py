@@ -8,4 +8,5 @@ shares no code with it.
 The arithmetic lives in ``spec_verify_oracle.c`` (single-threaded fp64 C, built
 by ``oracle.build.build()``); this package only marshals numpy arrays to it.
 """
-from .oracle import OracleResult, build, load, run_workload, sample, spec_verify  # noqa: F401
+from .oracle import (OracleResult, TreeResult, build, load, run_workload, sample, spec_verify,  # noqa: F401
+                     spec_verify_tree)

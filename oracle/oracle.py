@@ -44,6 +44,17 @@ class _Args(ctypes.Structure):
     ]
 
 
+class _TreeArgs(ctypes.Structure):
+    _fields_ = [
+        ("target", ctypes.c_void_p), ("draft", ctypes.c_void_p), ("dtype", ctypes.c_int),
+        ("parent", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("num_nodes", ctypes.c_void_p),
+        ("u_accept", ctypes.c_void_p), ("u_sample", ctypes.c_void_p), ("temperature", ctypes.c_void_p),
+        ("B", ctypes.c_int), ("max_nodes", ctypes.c_int), ("V", ctypes.c_int),
+        ("accepted_count", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("out_nodes", ctypes.c_void_p),
+        ("flags", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -51,6 +62,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.oracle_spec_verify.argtypes = [ctypes.POINTER(_Args)]
     lib.oracle_spec_verify.restype = ctypes.c_int
+    lib.oracle_spec_verify_tree.argtypes = [ctypes.POINTER(_TreeArgs)]
+    lib.oracle_spec_verify_tree.restype = ctypes.c_int
     return lib
 
 
@@ -160,3 +173,45 @@ def sample(logits, u, temperature, dtype: Optional[str] = None, lib: Optional[ct
     res = spec_verify(logits.reshape(R, 1, V), np.zeros((R, 0, V), dtype=logits.dtype), np.zeros((R, 0)),
                       np.zeros((R, 0)), u, temperature, dtype=dtype, trace=True, lib=lib)
     return res.out_tokens[:, 0].copy(), res
+
+
+@dataclass
+class TreeResult:
+    accepted_count: np.ndarray  # [B] int32: nodes on the accepted path
+    out_tokens: np.ndarray      # [B, max_nodes+1] int32: path tokens, then the drawn token, -1 after
+    out_nodes: np.ndarray       # [B, max_nodes] int32: path node indices, -1 after
+    flags: np.ndarray           # [B] int32: bit0 accept band, bit1 CDF band, bit2 zero-mass fallback
+
+
+def spec_verify_tree(target, draft, parent, tokens, u_accept, u_sample, temperature, num_nodes=None,
+                     dtype: Optional[str] = None, lib: Optional[ctypes.CDLL] = None) -> TreeResult:
+    """Tree verification on host arrays.
+
+    target: [B, max_nodes+1, V] (row j = target at position j; position 0 is the
+    verified prefix, position n+1 is node n); draft: [B, max_nodes, V] (row j = q
+    at position j); parent, tokens, u_accept: [B, max_nodes]; u_sample: [B].
+    """
+    if dtype is None:
+        dtype = "bf16" if np.asarray(target).dtype == np.uint16 else "f32"
+    store = np.uint16 if dtype == "bf16" else np.float32
+    target = np.ascontiguousarray(target, dtype=store)
+    B, n1, V = target.shape
+    Nmax = n1 - 1
+    draft = np.ascontiguousarray(draft, dtype=store).reshape(B, Nmax, V) if Nmax > 0 else None
+    par = np.ascontiguousarray(parent, dtype=np.int32).reshape(B, Nmax)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, Nmax)
+    ua = np.ascontiguousarray(u_accept, dtype=np.float32).reshape(B, Nmax)
+    us = np.ascontiguousarray(u_sample, dtype=np.float32).reshape(B)
+    if np.isscalar(temperature):
+        temperature = np.full(B, temperature, dtype=np.float32)
+    temps = np.ascontiguousarray(temperature, dtype=np.float32).reshape(B)
+    nn = None if num_nodes is None else np.ascontiguousarray(num_nodes, dtype=np.int32).reshape(B)
+    res = TreeResult(accepted_count=np.zeros(B, np.int32), out_tokens=np.full((B, Nmax + 1), -7, np.int32),
+                     out_nodes=np.full((B, Nmax), -7, np.int32), flags=np.zeros(B, np.int32))
+    args = _TreeArgs(_ptr(target), _ptr(draft), 1 if dtype == "bf16" else 0, _ptr(par), _ptr(tok), _ptr(nn),
+                     _ptr(ua), _ptr(us), _ptr(temps), B, Nmax, V, _ptr(res.accepted_count), _ptr(res.out_tokens),
+                     _ptr(res.out_nodes), _ptr(res.flags))
+    rc = (lib or load()).oracle_spec_verify_tree(ctypes.byref(args))
+    if rc != 0:
+        raise ValueError(f"oracle_spec_verify_tree rejected its arguments (code {rc})")
+    return res

@@ -370,3 +370,123 @@ int oracle_spec_verify(const oracle_args *a)
     free(w);
     return 0;
 }
+
+/* ================================================================== tree verification */
+/* Verification of a tree of drafts (several candidates per position).
+ *
+ * The pages draw the tree (P4, section Eagleツリー推測の原理: several candidate
+ * paths verified together) but verify it with a lossy probability threshold,
+ * so the lossless rule used here is a reading: the children of a position were
+ * drawn independently from that position's draft distribution q, and they are
+ * tested in increasing node index, each against the current target: the first
+ * child against p, and after a rejection the next child against the modified
+ * distribution max(0, p_cur - q) / sum (P1 section 修正分布の定義 applied again,
+ * with the position's q).  The first accepted child is emitted and verification
+ * continues at its position; if every child is rejected, or the position has no
+ * child, the token is drawn from the current target by the inverse CDF (R5)
+ * with u_sample.  One child per position is exactly the linear method.  T == 0
+ * accepts the first child equal to the target arg-max and emits the arg-max
+ * otherwise.
+ *
+ * Layout: node n (0 <= n < N_b) has parent[n] in [-1, n) (-1: the verified
+ * prefix) and token[n].  Position 0 is the prefix, position n + 1 is node n.
+ * target [B][max_nodes + 1][V]: row j is the target at position j.
+ * draft  [B][max_nodes][V]: row j is the q the children of position j were drawn
+ * from (a position with children is the prefix or a node n < N_b - 1, so j < N_b).
+ */
+static void verify_tree_request(const oracle_tree_args *a, int b, double *p, double *q, double *cur)
+{
+    const int Nmax = a->max_nodes, V = a->V, dt = a->dtype;
+    const int N = a->num_nodes ? a->num_nodes[b] : Nmax;
+    const double T = (double)a->temperature[b];
+    const int32_t *parent = a->parent + (size_t)b * Nmax;
+    const int32_t *token = a->tokens + (size_t)b * Nmax;
+    int32_t *out = a->out_tokens + (size_t)b * (Nmax + 1);
+    int32_t *onodes = a->out_nodes + (size_t)b * Nmax;
+    for (int i = 0; i <= Nmax; ++i) out[i] = -1;
+    for (int i = 0; i < Nmax; ++i) onodes[i] = -1;
+    int flags = 0;
+    int depth = 0, pos = 0;
+    for (;;) {
+        row_t rp = {a->target, dt, ((size_t)b * (size_t)(Nmax + 1) + (size_t)pos) * (size_t)V, V};
+        if (T == 0.0) {
+            int am = argmax_lowest(&rp), hit = -1;
+            for (int n = pos; n < N; ++n)
+                if (parent[n] == pos - 1 && token[n] == am) { hit = n; break; }
+            if (hit < 0) { out[depth] = am; break; }
+            out[depth] = am;
+            onodes[depth] = hit;
+            ++depth;
+            pos = hit + 1;
+            continue;
+        }
+        softmax_t sp = softmax_stats(&rp, T, 0, 1.0);
+        for (int v = 0; v < V; ++v) { p[v] = prob(&rp, &sp, v); cur[v] = p[v]; }
+        int hit = -1, have_q = 0;
+        for (int n = pos; n < N && hit < 0; ++n) {
+            if (parent[n] != pos - 1) continue;
+            if (!have_q) {
+                row_t rq = {a->draft, dt, ((size_t)b * (size_t)Nmax + (size_t)pos) * (size_t)V, V};
+                softmax_t sq = softmax_stats(&rq, T, 0, 1.0);
+                for (int v = 0; v < V; ++v) q[v] = prob(&rq, &sq, v);
+                have_q = 1;
+            }
+            const int x = token[n];
+            const double an = accept_probability(cur[x], q[x]);
+            const double u = (double)a->u_accept[(size_t)b * Nmax + n];
+            if (fabs(u - an) < BAND) flags |= 1;
+            if (u < an) { hit = n; break; }
+            /* rejected: the next child is tested against max(0, cur - q) / sum */
+            double Z = 0.0;
+            for (int v = 0; v < V; ++v) {
+                double d = cur[v] - q[v];
+                cur[v] = d > 0.0 ? d : 0.0;
+                Z += cur[v];
+            }
+            if (Z == 0.0) { /* fallback to the position's p, as in the linear case */
+                for (int v = 0; v < V; ++v) cur[v] = p[v];
+                flags |= 4;
+            } else {
+                for (int v = 0; v < V; ++v) cur[v] /= Z;
+            }
+        }
+        if (hit >= 0) {
+            out[depth] = token[hit];
+            onodes[depth] = hit;
+            ++depth;
+            pos = hit + 1;
+            continue;
+        }
+        double Zc, margin;
+        out[depth] = inverse_cdf(cur, V, (double)a->u_sample[b], &Zc, &margin);
+        if (margin < BAND) flags |= 2;
+        break;
+    }
+    a->accepted_count[b] = depth;
+    if (a->flags) a->flags[b] = flags;
+}
+
+int oracle_spec_verify_tree(const oracle_tree_args *a)
+{
+    if (!a || !a->target || !a->parent || !a->tokens || !a->u_sample || !a->temperature || !a->out_tokens ||
+        !a->out_nodes || !a->accepted_count)
+        return -1;
+    if (a->B < 1 || a->max_nodes < 0 || a->V < 1) return -1;
+    if (a->dtype != ORACLE_F32 && a->dtype != ORACLE_BF16) return -1;
+    for (int b = 0; b < a->B; ++b) {
+        const float T = a->temperature[b];
+        const int N = a->num_nodes ? a->num_nodes[b] : a->max_nodes;
+        if (!(T >= 0.0f) || isinf(T)) return -1;
+        if (N < 0 || N > a->max_nodes) return -1;
+        if (T > 0.0f && N > 0 && (!a->draft || !a->u_accept)) return -1;
+        for (int n = 0; n < N; ++n) {
+            const int pa = a->parent[(size_t)b * a->max_nodes + n], x = a->tokens[(size_t)b * a->max_nodes + n];
+            if (pa < -1 || pa >= n || x < 0 || x >= a->V) return -1;
+        }
+    }
+    double *buf = (double *)malloc(sizeof(double) * 3 * (size_t)a->V);
+    if (!buf) return -2;
+    for (int b = 0; b < a->B; ++b) verify_tree_request(a, b, buf, buf + a->V, buf + 2 * (size_t)a->V);
+    free(buf);
+    return 0;
+}

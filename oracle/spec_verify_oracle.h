@@ -46,4 +46,25 @@ typedef struct {
 /* 0 on success, -1 invalid arguments, -2 out of memory. */
 int oracle_spec_verify(const oracle_args *a);
 
+/* Tree of drafts (see the comment above verify_tree_request). */
+typedef struct {
+    const void *target;          /* [B][max_nodes+1][V]: row j = target at position j   */
+    const void *draft;           /* [B][max_nodes][V]: row j = q at position j           */
+    int dtype;
+    const int32_t *parent;       /* [B][max_nodes], -1 = the prefix, else < n            */
+    const int32_t *tokens;       /* [B][max_nodes]                                       */
+    const int32_t *num_nodes;    /* [B] or NULL (= max_nodes)                            */
+    const float *u_accept;       /* [B][max_nodes], one per node                         */
+    const float *u_sample;       /* [B]                                                  */
+    const float *temperature;    /* [B], 0 = greedy                                      */
+    int B, max_nodes, V;
+    int32_t *accepted_count;     /* out [B]: nodes on the accepted path                  */
+    int32_t *out_tokens;         /* out [B][max_nodes+1]: path tokens, then the drawn one */
+    int32_t *out_nodes;          /* out [B][max_nodes]: path node indices, -1 after      */
+    int32_t *flags;              /* out [B] or NULL: bit0 accept band, bit1 CDF band,
+                                    bit2 zero-mass fallback                              */
+} oracle_tree_args;
+
+int oracle_spec_verify_tree(const oracle_tree_args *a);
+
 #endif

@@ -14,6 +14,7 @@ import pytest
 import oracle
 from tests import test_oracle_filter_pins as fpins
 from tests import test_oracle_pins as pins
+from tests import test_oracle_tree_pins as tpins
 
 SRC = oracle.oracle.SRC
 
@@ -42,6 +43,14 @@ MUTANTS = {
     "prob_ignores_cut": ("if (z < st->tau) return 0.0;", "if (0) return 0.0;"),
     "sum_ignores_cut": ("if (z >= st.tau) st.s += exp((z - st.m) / T);", "st.s += exp((z - st.m) / T);"),
     "topp_first_group_kept_only": ("if (cum >= target) {", "if (1) {"),
+    "tree_residual_not_updated": ("cur[v] = d > 0.0 ? d : 0.0;\n                Z += cur[v];",
+                                  "Z += d > 0.0 ? d : 0.0;"),
+    "tree_residual_from_p": ("double d = cur[v] - q[v];", "double d = p[v] - q[v];"),
+    "tree_target_row_shifted": ("row_t rp = {a->target, dt, ((size_t)b * (size_t)(Nmax + 1) + (size_t)pos) * (size_t)V, V};",
+                                "row_t rp = {a->target, dt, ((size_t)b * (size_t)(Nmax + 1) + (size_t)(pos > 0 ? pos - 1 : 0)) * (size_t)V, V};"),
+    "tree_last_sibling_first": ("for (int n = pos; n < N && hit < 0; ++n) {", "for (int n = N - 1; n >= pos && hit < 0; --n) {"),
+    "tree_greedy_no_descent": ("if (parent[n] == pos - 1 && token[n] == am) { hit = n; break; }",
+                               "if (parent[n] == -1 && token[n] == am) { hit = n; break; }"),
 }
 
 PIN_TESTS = [
@@ -61,6 +70,10 @@ PIN_TESTS = [
     (fpins.test_f2_exact_integration_gives_filtered_target, {"seed": 0, "top_k": 6, "top_p": 0.9}),
     (fpins.test_f4_three_token_top_p_cut, {}),
     (fpins.test_f4_ties_at_the_top_k_cut_are_kept, {}),
+    (tpins.test_tr1_chain_is_the_linear_method, {"dtype": "f32", "T": 1.0}),
+    (tpins.test_tr2_exact_integration_first_token_is_p, {"m": 3, "seed": 0}),
+    (tpins.test_tr3_sibling_order_and_residual_chain, {}),
+    (tpins.test_tr4_greedy_tree, {}),
 ]
 
 
@@ -75,6 +88,9 @@ class _MutantOracle:
 
     def run_workload(self, w, trace=True):
         return oracle.run_workload(w, trace=trace, lib=self._lib)
+
+    def spec_verify_tree(self, *a, **k):
+        return oracle.spec_verify_tree(*a, lib=self._lib, **k)
 
 
 def test_mutation_sources_apply():
