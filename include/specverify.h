@@ -173,6 +173,55 @@ int spec_verify_filtered(const void *target_logits, const void *draft_logits,
                          void *workspace, size_t workspace_bytes, void *stream,
                          const sv_debug *dbg);
 
+/* Largest tree and vocabulary accepted by spec_verify_tree. */
+#define SV_TREE_MAX_NODES 256
+#define SV_TREE_MAX_V (1 << 20)
+
+/* Tree (multi-candidate) verification.  The pages draw a tree of drafts (P4,
+ * section Eagleツリー推測の原理: several candidate paths verified together) but
+ * verify it with a lossy probability threshold; the rule here is a reading that
+ * keeps every emitted token distributed as the target:
+ *   - node n (0 <= n < N_b) has parent node_parent[b][n] in [-1, n) (-1: the
+ *     verified prefix) and token node_tokens[b][n]; position 0 is the prefix
+ *     and position n + 1 is node n;
+ *   - the children of a position are independent draws from that position's
+ *     draft distribution q; they are tested in increasing node index, the
+ *     first against p, each later one against max(0, p_cur - q) / sum, the
+ *     modified distribution left by the previous rejection (P1 section
+ *     修正分布の定義 applied again), with u_accept[b][n] (strict <, R2 for q = 0);
+ *   - the first accepted child is emitted and the walk continues at its
+ *     position; when every child is rejected, or the position has none, the
+ *     token is drawn from the current target by the inverse CDF (step 4's
+ *     rule) with u_sample[b]; a zero residual mass falls back to the
+ *     position's p;
+ *   - T == 0 follows the first child equal to the lowest-index arg-max of the
+ *     target and emits the arg-max where none does.
+ * A tree in which every position has at most one child is exactly the linear
+ * method.
+ * target_logits: DEVICE [B][max_nodes + 1][V], row j = target at position j.
+ * draft_logits:  DEVICE [B][max_nodes][V], row j = q at position j (rows of
+ *                positions without children are read but not used: finite).
+ * node_parent, node_tokens, u_accept: DEVICE [B][max_nodes].
+ * num_nodes:     DEVICE [B] node count N_b (clamped to [0, max_nodes]), or NULL
+ *                (= max_nodes).
+ * u_sample:      DEVICE [B]; temperature: DEVICE [B] (0 = greedy).
+ * Outputs: accepted_count[b] = nodes on the accepted path; out_tokens
+ * [B][max_nodes + 1]: the path's tokens then the drawn token, -1 after;
+ * out_nodes [B][max_nodes]: the path's node indices, -1 after.
+ * A parent outside [-1, n) makes the node nobody's child; a token outside
+ * [0, V) is rejected when tested and never dereferenced.  0 <= max_nodes <=
+ * SV_TREE_MAX_NODES, V <= SV_TREE_MAX_V.  The workspace is sized by
+ * spec_verify_tree_workspace_bytes. */
+size_t spec_verify_tree_workspace_bytes(int B, int max_nodes, int V, int dtype);
+
+int spec_verify_tree(const void *target_logits, const void *draft_logits,
+                     const int32_t *node_parent, const int32_t *node_tokens,
+                     const int32_t *num_nodes, const float *u_accept,
+                     const float *u_sample, const float *temperature, int B,
+                     int max_nodes, int V, int dtype, int32_t *accepted_count,
+                     int32_t *out_tokens, int32_t *out_nodes, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
 /* Draft-side sampling: one token per row of softmax(logits[r] / T_r), drawn by
  * the inverse CDF in vocabulary order with the supplied uniform u[r]: the
  * smallest v with u*Z < w[0] + ... + w[v] (the categorical draw that drafting

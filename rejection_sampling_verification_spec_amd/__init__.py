@@ -21,6 +21,8 @@ from .binding import (  # noqa: F401
     spec_verify_ex,
     spec_verify_filtered,
     spec_verify_filtered_workspace_bytes,
+    spec_verify_tree,
+    spec_verify_tree_workspace_bytes,
     spec_verify_strerror,
     spec_verify_workspace_bytes,
 )

@@ -18,6 +18,8 @@ SV_F32 = 0
 SV_BF16 = 1
 SV_GAMMA_MAX = 32
 SV_FILTER_MAX_V = 1 << 20
+SV_TREE_MAX_NODES = 256
+SV_TREE_MAX_V = 1 << 20
 
 SV_OK = 0
 SV_EINVAL = -1
@@ -30,6 +32,8 @@ EXPORTED_SYMBOLS = (
     "spec_verify_ex",
     "spec_verify_filtered",
     "spec_verify_filtered_workspace_bytes",
+    "spec_verify_tree",
+    "spec_verify_tree_workspace_bytes",
     "spec_sample_workspace_bytes",
     "spec_sample",
     "spec_gamma_policy_init",
@@ -118,6 +122,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_filtered.restype = i32
     lib.spec_verify_filtered_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.spec_verify_filtered_workspace_bytes.restype = sz
+    lib.spec_verify_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_tree.restype = i32
+    lib.spec_verify_tree_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spec_verify_tree_workspace_bytes.restype = sz
     lib.spec_sample_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_sample_workspace_bytes.restype = sz
     lib.spec_sample.argtypes = [vp, vp, ctypes.c_float, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -322,6 +330,62 @@ def _verify_device_params(entry, target_logits, draft_logits, draft_tokens, u_ac
     if rc != SV_OK:
         raise SpecVerifyError(rc, entry)
     return accepted_count, out_tokens
+
+
+def spec_verify_tree_workspace_bytes(B: int, max_nodes: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_verify_tree_workspace_bytes(B, max_nodes, V, dtype))
+
+
+def spec_verify_tree(target_logits, draft_logits, node_parent, node_tokens, u_accept, u_sample, temperature,
+                     num_nodes=None, accepted_count=None, out_tokens=None, out_nodes=None, workspace=None,
+                     stream=None):
+    """Tree verification (see ``spec_verify_tree`` in include/specverify.h).
+
+    target_logits [B, N+1, V], draft_logits [B, N, V] (bf16 or fp32); node_parent,
+    node_tokens [B, N] int32; u_accept [B, N], u_sample [B], temperature [B] float32;
+    num_nodes [B] int32 or None.  Returns (accepted_count [B], out_tokens [B, N+1],
+    out_nodes [B, N]).
+    """
+    import torch
+    lib = load_library()
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, max_nodes + 1, V]")
+    B, n1, V = target_logits.shape
+    N = n1 - 1
+    dt = _dtype_code(target_logits)
+    _check_device(target_logits, draft_logits, node_parent, node_tokens, u_accept, u_sample, temperature,
+                  num_nodes)
+    dev = target_logits.device
+    _expect(target_logits, (B, N + 1, V), target_logits.dtype, "target_logits")
+    _expect(draft_logits, (B, N, V), target_logits.dtype, "draft_logits", optional=N == 0)
+    _expect(node_parent, (B, N), torch.int32, "node_parent", optional=N == 0)
+    _expect(node_tokens, (B, N), torch.int32, "node_tokens", optional=N == 0)
+    _expect(u_accept, (B, N), torch.float32, "u_accept", optional=N == 0)
+    _expect(u_sample, (B,), torch.float32, "u_sample")
+    _expect(temperature, (B,), torch.float32, "temperature")
+    _expect(num_nodes, (B,), torch.int32, "num_nodes", optional=True)
+    if accepted_count is None:
+        accepted_count = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+    if out_nodes is None:
+        out_nodes = torch.empty((B, max(N, 1)), dtype=torch.int32, device=dev)
+    _expect(accepted_count, (B,), torch.int32, "accepted_count")
+    _expect(out_tokens, (B, N + 1), torch.int32, "out_tokens")
+    need = spec_verify_tree_workspace_bytes(B, N, V, dt)
+    if need == 0:
+        raise SpecVerifyError(SV_EINVAL, "spec_verify_tree_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    rc = lib.spec_verify_tree(_ptr(target_logits), _ptr(draft_logits), _ptr(node_parent), _ptr(node_tokens),
+                              _ptr(num_nodes), _ptr(u_accept), _ptr(u_sample), _ptr(temperature), B, N, V, dt,
+                              _ptr(accepted_count), _ptr(out_tokens), _ptr(out_nodes), _ptr(workspace),
+                              workspace.numel(), _stream(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_tree")
+    return accepted_count, out_tokens, out_nodes[:, :N]
 
 
 def spec_sample_workspace_bytes(R: int, V: int, dtype: int) -> int:

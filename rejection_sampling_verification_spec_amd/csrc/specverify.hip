@@ -1730,6 +1730,307 @@ __global__ __launch_bounds__(kFBlock) void k_filter_resolve(
   }
 }
 
+// ================================================================== tree verification
+// A tree of drafts per request: node n (n < N_b) has parent[n] in [-1, n)
+// (-1: the verified prefix) and token[n]; position 0 is the prefix and
+// position n + 1 is node n.  Target row j and draft row j are the target and
+// the draft distribution at position j (the layout of the linear call with
+// gamma = max_nodes, so K1 computes every row's statistics unchanged).
+//
+// The pages draw such trees but verify them with a lossy threshold; the rule
+// here is a reading that stays lossless: the children of a position are
+// independent draws from its draft distribution q, tested in node order, the
+// first against p and each later one against max(0, p_cur - q) / sum, the
+// modified distribution of the previous rejection.  With p_j the target after
+// j rejections, p_j = max(0, p - c_j q) / Z_j where c_0 = 0, Z_0 = 1 and
+// c_{j+1} = c_j + Z_j (the recursion unrolled), so one pass over the row pair
+// per rejection gives Z_{j+1}.  An accepted child moves to its position; if
+// every child is rejected, or there is none, the token is drawn from p_j by
+// the inverse CDF with u_sample.  T == 0 follows the first child equal to the
+// target arg-max.
+//
+// k_tree_walk: one 512-thread workgroup per request walks its tree.  Row
+// statistics come from K1's partials; the acceptance ratio is fp64 from the
+// two gathered logits; each rejection costs one pass over the position's two
+// rows (2048-token sub-chunk masses kept in LDS for the final draw).
+constexpr int kTBlock = 512;
+constexpr int kTWaves = kTBlock / kWave;
+constexpr int kTMaxSub = SV_TREE_MAX_V / kSub;
+
+struct TreeShared {
+  int parent[SV_TREE_MAX_NODES];
+  int token[SV_TREE_MAX_NODES];
+  double sub[kTMaxSub];       // sub-chunk masses of the current distribution
+  double red[2 + kTWaves];
+  double W;                   // their sum
+  int pick, last;             // selection results
+};
+
+// (M, s) of a stochastic row, or (max, lowest arg-max) of a greedy one, from
+// K1's chunk partials merged in chunk order.
+__device__ __forceinline__ void merged_row(const Partial *part, long slot, int NS, bool greedy, int &M, double &s,
+                                           int &arg) {
+  M = kEmptyM;
+  s = 0.0;
+  float mx = -INFINITY, v = -INFINITY;
+  int ix = 0x7fffffff;
+  for (int j = 0; j < NS; ++j) {
+    const Partial q = part[slot * NS + j];
+    if (greedy) merge_arg(v, ix, q.mx, q.mi);
+    else merge_sm(M, s, mx, q.mi, q.s, q.mx);
+  }
+  arg = ix;
+}
+
+// Masses of w = max(0, e_p - r e_q) (or e_p when !use_q) over 2048-token
+// sub-chunks of the position's rows, into sh.sub; their sum into sh.W.
+template <int DT>
+__device__ void tree_masses(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c,
+                            float negMp, float negMq, float r, bool use_q, TreeShared &sh) {
+  constexpr int kN = kLaneElems / Elem<DT>::kVec;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  for (int j = wave; j < NSUB; j += kTWaves) {
+    u32x4 tp[kN], dq[kN];
+    load_lane_raw<DT>(trow, aligned, static_cast<long>(j) * kSub, lane, V, tp);
+    if (use_q) load_lane_raw<DT>(drow, aligned, static_cast<long>(j) * kSub, lane, V, dq);
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+      float zp[Elem<DT>::kVec], zq[Elem<DT>::kVec];
+      widen_vec<DT>(tp[u], zp);
+      if (use_q) widen_vec<DT>(dq[u], zq);
+#pragma unroll
+      for (int e = 0; e < Elem<DT>::kVec; ++e) {
+        const float ep = __builtin_amdgcn_exp2f(fmaf(zp[e], c, negMp));
+        acc += use_q ? fmaxf(0.0f, fmaf(-__builtin_amdgcn_exp2f(fmaf(zq[e], c, negMq)), r, ep)) : ep;
+      }
+    }
+    const double ws = wave_sum(static_cast<double>(acc));
+    if (lane == 0) sh.sub[j] = ws;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double W = 0.0;
+    for (int j = 0; j < NSUB; ++j) W += sh.sub[j];  // fixed order
+    sh.W = W;
+  }
+  __syncthreads();
+}
+
+// Inverse CDF over the masses in sh.sub (of the same w as tree_masses): the
+// lowest token with mass whose running prefix exceeds u * W; if rounding
+// leaves none, the last token with mass.
+template <int DT>
+__device__ int tree_select(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c, float negMp,
+                           float negMq, float r, bool use_q, float u, TreeShared &sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  if (tid == 0) {
+    const double target = static_cast<double>(u) * sh.W;
+    double run = 0.0;
+    int sub = -1, lastm = -1;
+    double base = 0.0, base_last = 0.0;
+    for (int j = 0; j < NSUB; ++j) {
+      const double m = sh.sub[j];
+      if (m > 0.0) {
+        if (sub < 0 && target < run + m) {
+          sub = j;
+          base = run;
+        }
+        lastm = j;
+        base_last = run;
+      }
+      run += m;
+    }
+    if (sub < 0) {
+      sub = lastm >= 0 ? lastm : 0;
+      base = lastm >= 0 ? base_last : 0.0;
+    }
+    sh.pick = sub;
+    sh.red[0] = base;
+    sh.red[1] = target;
+  }
+  __syncthreads();
+  const int sub = sh.pick;
+  const double base = sh.red[0], target = sh.red[1];
+  __syncthreads();
+  // four contiguous tokens per thread, in token order through waves and lanes
+  constexpr int kPer = kSub / kTBlock;
+  const long first = static_cast<long>(sub) * kSub + static_cast<long>(tid) * kPer;
+  float w[kPer];
+  double lsum = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const long t = first + e;
+    if (t < V) {
+      const float ep = __builtin_amdgcn_exp2f(fmaf(load_one<DT>(trow, t), c, negMp));
+      w[e] = use_q ? fmaxf(0.0f, fmaf(-__builtin_amdgcn_exp2f(fmaf(load_one<DT>(drow, t), c, negMq)), r, ep)) : ep;
+    } else {
+      w[e] = 0.0f;
+    }
+    lsum += static_cast<double>(w[e]);
+  }
+  const double incl = wave_scan(lsum, lane);
+  if (lane == kWave - 1) sh.red[2 + wave] = incl;  // red[2 .. 2 + kTWaves) is free after the broadcast
+  __syncthreads();
+  double before = base;
+  for (int q = 0; q < wave; ++q) before += sh.red[2 + q];
+  if (tid == 0) {
+    sh.pick = 0x7fffffff;
+    sh.last = -1;
+  }
+  __syncthreads();
+  double acc = before + (incl - lsum);
+  int cand = -1, lastp = -1;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    if (w[e] > 0.0f) {
+      lastp = static_cast<int>(first + e);
+      acc += static_cast<double>(w[e]);
+      if (cand < 0 && target < acc) cand = static_cast<int>(first + e);
+    }
+  }
+  if (cand >= 0) atomicMin(&sh.pick, cand);
+  if (lastp >= 0) atomicMax(&sh.last, lastp);
+  __syncthreads();
+  int tok = sh.pick;
+  if (tok == 0x7fffffff) tok = sh.last >= 0 ? sh.last : static_cast<int>(static_cast<long>(sub) * kSub);
+  __syncthreads();
+  return tok;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kTBlock) void k_tree_walk(
+    const void *__restrict__ target, const void *__restrict__ draft, const int32_t *__restrict__ parent,
+    const int32_t *__restrict__ tokens, const int32_t *__restrict__ num_nodes, const float *__restrict__ u_accept,
+    const float *__restrict__ u_sample, const float *__restrict__ temps, int Nmax, int V, int NS,
+    const Partial *__restrict__ part, int32_t *__restrict__ count, int32_t *__restrict__ out_tokens,
+    int32_t *__restrict__ out_nodes) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int rows = 2 * Nmax + 1;
+  const int N = request_len(num_nodes, Nmax, b);
+  const float T = temps[b];
+  const bool greedy = !(T > 0.0f);
+  const float c = greedy ? 0.0f : temp_scale(T);
+  const int NSUB = (V + kSub - 1) / kSub;
+  __shared__ TreeShared sh;
+  __shared__ int s_hit, s_arg, s_Mp, s_Mq;
+  __shared__ double s_sp, s_sq;
+  for (int n = tid; n < Nmax; n += kTBlock) {
+    int pa = -2, x = -1;
+    if (n < N) {
+      pa = parent[static_cast<long>(b) * Nmax + n];
+      x = tokens[static_cast<long>(b) * Nmax + n];
+      if (pa < -1 || pa >= n) pa = -2;  // not a valid child of anything
+    }
+    sh.parent[n] = pa;
+    sh.token[n] = x;
+  }
+  for (int t = tid; t <= Nmax; t += kTBlock) out_tokens[static_cast<long>(b) * (Nmax + 1) + t] = -1;
+  for (int t = tid; t < Nmax; t += kTBlock) out_nodes[static_cast<long>(b) * Nmax + t] = -1;
+  __syncthreads();
+  const size_t eb = Elem<DT>::kBytes;
+  int pos = 0, depth = 0;
+  for (;;) {
+    const void *trow = static_cast<const char *>(target) + (static_cast<long>(b) * (Nmax + 1) + pos) * V * eb;
+    const void *drow = pos < Nmax ? static_cast<const char *>(draft) + (static_cast<long>(b) * Nmax + pos) * V * eb
+                                  : nullptr;  // position Nmax has no child
+    const bool al = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;
+    if (tid == 0) {
+      int M, arg;
+      double s;
+      merged_row(part, static_cast<long>(b) * rows + pos, NS, greedy, M, s, arg);
+      s_Mp = M;
+      s_sp = s;
+      s_arg = arg;
+    }
+    __syncthreads();
+    int hit = -1;
+    if (greedy) {
+      if (tid == 0) {
+        for (int n = pos; n < N && hit < 0; ++n)
+          if (sh.parent[n] == pos - 1 && sh.token[n] == s_arg) hit = n;
+        s_hit = hit;
+      }
+      __syncthreads();
+      hit = s_hit;
+      if (hit < 0) {
+        if (tid == 0) out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = s_arg;
+        break;
+      }
+    } else {
+      const int Mp = s_Mp;
+      const double sp = s_sp;
+      const float negMp = -static_cast<float>(Mp);
+      double cc = 0.0, Z = 1.0;  // current target: max(0, p - cc q) / Z
+      bool have_q = false, masses_current = false;
+      int Mq = 0;
+      double sq = 1.0;
+      for (int n = pos; n < N; ++n) {
+        if (sh.parent[n] != pos - 1) continue;  // uniform: LDS read by every thread
+        if (!have_q) {
+          if (tid == 0) {
+            int arg;
+            merged_row(part, static_cast<long>(b) * rows + Nmax + 1 + pos, NS, false, s_Mq, s_sq, arg);
+          }
+          __syncthreads();
+          Mq = s_Mq;
+          sq = s_sq;
+          have_q = true;
+        }
+        if (tid == 0) {
+          const int x = sh.token[n];
+          bool acc = false;
+          if (x >= 0 && x < V) {  // an id outside the vocabulary is rejected, never dereferenced
+            const double cd = static_cast<double>(c);
+            const double px = exp2(static_cast<double>(load_one<DT>(trow, x)) * cd - Mp) / sp;
+            const double qx = exp2(static_cast<double>(load_one<DT>(drow, x)) * cd - Mq) / sq;
+            const double num = fmax(0.0, px - cc * qx), den = Z * qx;
+            const double a = den > 0.0 ? fmin(1.0, num / den) : (num > 0.0 ? 1.0 : 0.0);
+            acc = static_cast<double>(u_accept[static_cast<long>(b) * Nmax + n]) < a;
+          }
+          s_hit = acc ? n : -1;
+        }
+        __syncthreads();
+        hit = s_hit;
+        __syncthreads();
+        if (hit >= 0) break;
+        // rejected: the next target is max(0, p - (cc + Z) q) / Z'
+        cc += Z;
+        const float r = static_cast<float>(cc * sp / sq);
+        tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, true, sh);
+        const double W = sh.W;
+        if (W > 0.0) {
+          Z = W / sp;
+          masses_current = true;
+        } else {  // zero residual mass: back to the position's p
+          cc = 0.0;
+          Z = 1.0;
+          masses_current = false;
+        }
+      }
+      if (hit < 0) {
+        // every child rejected, or none: draw from the current target
+        const bool use_q = cc > 0.0;
+        const float r = use_q ? static_cast<float>(cc * sp / sq) : 0.0f;
+        if (!masses_current) tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q, sh);
+        const int tok = tree_select<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q,
+                                        u_sample[b], sh);
+        if (tid == 0) out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = tok;
+        break;
+      }
+    }
+    // accepted node `hit`: emit it and move to its position
+    if (tid == 0) {
+      out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = sh.token[hit];
+      out_nodes[static_cast<long>(b) * Nmax + depth] = hit;
+    }
+    ++depth;
+    pos = hit + 1;
+    __syncthreads();
+  }
+  if (tid == 0) count[b] = depth;
+}
+
 // ================================================================== single-pass sampler
 // Draft-side sampling, one token per row of softmax(z/T), in one kernel: a
 // 1024-thread workgroup per row.  Wave w streams sub-chunks w, w+16, ... of
@@ -1945,8 +2246,8 @@ constexpr int kK1U = 8;                 // 16-byte vectors per thread per K1 til
 constexpr long kK1TargetGroups = 2816;  // about 11 workgroups per CU on 256 CUs
 constexpr long kK3TargetWaves = 2048;   // waves of the mass pass (8 per CU)
 
-bool make_plan(int B, int gamma, int V, int dtype, Plan *P) {
-  if (B < 1 || gamma < 0 || gamma > SV_GAMMA_MAX || V < 1) return false;
+bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV_GAMMA_MAX) {
+  if (B < 1 || gamma < 0 || gamma > gamma_limit || V < 1) return false;
   if (dtype != SV_F32 && dtype != SV_BF16) return false;
   const int vec = dtype == SV_BF16 ? 8 : 4;
   P->rows = 2 * gamma + 1;
@@ -2171,6 +2472,51 @@ int spec_verify_filtered(const void *target_logits, const void *draft_logits, co
   return dispatch(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, 0.0f,
                   false, draft_lens, top_k, top_p, B, gamma, V, dtype, accepted_count, out_tokens,
                   workspace, workspace_bytes, stream, dbg);
+}
+
+size_t spec_verify_tree_workspace_bytes(int B, int max_nodes, int V, int dtype) {
+  Plan P;
+  if (max_nodes < 0 || V > SV_TREE_MAX_V || !make_plan(B, max_nodes, V, dtype, &P, SV_TREE_MAX_NODES)) return 0;
+  return P.total;
+}
+
+// Row statistics of every tree position by K1 (the linear layout with
+// gamma = max_nodes and draft lengths = node counts), then one workgroup per
+// request walks its tree.
+int spec_verify_tree(const void *target_logits, const void *draft_logits, const int32_t *node_parent,
+                     const int32_t *node_tokens, const int32_t *num_nodes, const float *u_accept,
+                     const float *u_sample, const float *temperature, int B, int max_nodes, int V, int dtype,
+                     int32_t *accepted_count, int32_t *out_tokens, int32_t *out_nodes, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  Plan P;
+  if (max_nodes < 0 || V > SV_TREE_MAX_V || !make_plan(B, max_nodes, V, dtype, &P, SV_TREE_MAX_NODES))
+    return SV_EINVAL;
+  if (!target_logits || !u_sample || !temperature || !accepted_count || !out_tokens) return SV_EINVAL;
+  if (max_nodes > 0 && (!draft_logits || !node_parent || !node_tokens || !u_accept || !out_nodes))
+    return SV_EINVAL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < P.total)
+    return SV_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char *base = static_cast<char *>(workspace);
+  Partial *part = reinterpret_cast<Partial *>(base + P.part_off);
+  float *zx = reinterpret_cast<float *>(base + P.zx_off);
+  hipError_t e;
+  if (dtype == SV_BF16) {
+    e = launch_k1<SV_BF16>(target_logits, draft_logits, node_tokens, temperature, 0.0f, num_nodes, max_nodes, V, P,
+                           part, zx, st, nullptr, nullptr);
+    if (e != hipSuccess) return SV_EHIP;
+    hipLaunchKernelGGL((k_tree_walk<SV_BF16>), dim3(B), dim3(kTBlock), 0, st, target_logits, draft_logits,
+                       node_parent, node_tokens, num_nodes, u_accept, u_sample, temperature, max_nodes, V, P.NS,
+                       part, accepted_count, out_tokens, out_nodes);
+  } else {
+    e = launch_k1<SV_F32>(target_logits, draft_logits, node_tokens, temperature, 0.0f, num_nodes, max_nodes, V, P,
+                          part, zx, st, nullptr, nullptr);
+    if (e != hipSuccess) return SV_EHIP;
+    hipLaunchKernelGGL((k_tree_walk<SV_F32>), dim3(B), dim3(kTBlock), 0, st, target_logits, draft_logits,
+                       node_parent, node_tokens, num_nodes, u_accept, u_sample, temperature, max_nodes, V, P.NS,
+                       part, accepted_count, out_tokens, out_nodes);
+  }
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 size_t spec_sample_workspace_bytes(int R, int V, int dtype) {

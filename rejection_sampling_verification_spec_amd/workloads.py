@@ -298,3 +298,112 @@ def from_logits(target_f32: np.ndarray, draft_f32: np.ndarray, draft_tokens, u_a
                     temperature=np.ascontiguousarray(temps, dtype=np.float32).reshape(B),
                     lens=None if lens is None else np.ascontiguousarray(lens, dtype=np.int32),
                     scalar_temperature=scalar_T)
+
+
+# --------------------------------------------------------------------------- trees of drafts
+def tree_parents(width: int, depth: int) -> np.ndarray:
+    """Parent of each node of a full tree with `width` children per node and `depth` levels, nodes
+    numbered level by level (-1: the verified prefix).  Parents precede their children."""
+    parents, level = [], [-1]
+    for _ in range(depth):
+        nxt = []
+        for pa in level:
+            for _ in range(width):
+                parents.append(pa)
+                nxt.append(len(parents) - 1)
+        level = nxt
+    return np.array(parents, dtype=np.int32)
+
+
+@dataclass
+class TreeWorkload:
+    name: str
+    B: int
+    N: int                     # max_nodes: the padding stride of the node dimension
+    V: int
+    dtype: str
+    target: np.ndarray         # [B, N+1, V]: row j = target at position j (0: prefix, n+1: node n)
+    draft: np.ndarray          # [B, N, V]: row j = the draft distribution at position j
+    parent: np.ndarray         # [B, N] int32
+    tokens: np.ndarray         # [B, N] int32
+    u_accept: np.ndarray       # [B, N] float32
+    u_sample: np.ndarray       # [B] float32
+    temperature: np.ndarray    # [B] float32
+    num_nodes: Optional[np.ndarray] = None  # [B] int32, None = N
+    meta: dict = field(default_factory=dict)
+
+    def node_counts(self) -> np.ndarray:
+        return np.full(self.B, self.N, np.int32) if self.num_nodes is None else self.num_nodes
+
+    def bytes_alg(self) -> int:
+        """Logit bytes the row statistics read: every target row of a used position and, for
+        stochastic requests, every draft row of a position that can have children."""
+        n = self.node_counts().astype(np.int64)
+        stoch = (self.temperature > 0).astype(np.int64)
+        return int(((n + 1) + stoch * n).sum()) * self.V * (2 if self.dtype == BF16 else 4)
+
+    def to_torch(self, device):
+        import torch
+
+        def logits(a):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            return (t.view(torch.bfloat16) if self.dtype == BF16 else t).to(device)
+
+        def plain(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+        return dict(target=logits(self.target), draft=logits(self.draft), parent=plain(self.parent),
+                    tokens=plain(self.tokens), u_accept=plain(self.u_accept), u_sample=plain(self.u_sample),
+                    temperature=plain(self.temperature),
+                    num_nodes=None if self.num_nodes is None else plain(self.num_nodes))
+
+
+def build_tree(name: str, seed: int, B: int, width: int, depth: int, V: int, dtype: str, *,
+               target_scale: float, zipf: bool, sigma: float, temps, num_nodes=None,
+               block_elems: int = 1 << 23) -> TreeWorkload:
+    """Seeded tree workload.  Draw order: target noise (+ Zipf bias), draft noise, node tokens
+    (children of a position drawn independently from softmax(z_q / T) by Gumbel-max; at T = 0 the
+    children are the draft row's largest logits, in order), then u_accept and u_sample."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    par1 = tree_parents(width, depth)
+    N = par1.size
+    temps = np.full(B, temps, np.float32) if np.isscalar(temps) else np.asarray(temps, np.float32)
+    zp = rng.standard_normal((B, N + 1, V), dtype=np.float32)
+    zp *= np.float32(target_scale)
+    if zipf:
+        zp += _zipf_bias_rows(rng, B * (N + 1), V).reshape(B, N + 1, V)
+    zq = rng.standard_normal((B, N, V), dtype=np.float32)
+    zq *= np.float32(sigma)
+    zq += zp[:, :N, :]
+    target = _cast(zp, dtype)
+    del zp
+    draft = _cast(zq, dtype)
+    del zq
+    parent = np.tile(par1, (B, 1))
+    tokens = np.zeros((B, N), np.int32)
+    # greedy requests: the children of a position are its draft row's largest logits
+    for b in np.nonzero(temps == 0)[0]:
+        for j in range(N):
+            kids = np.nonzero(par1 == j - 1)[0]
+            if kids.size:
+                z = _as_f64(draft[b, j], dtype)
+                top = np.argsort(-z, kind="stable")[:kids.size]
+                tokens[b, kids] = top
+    # stochastic requests: independent draws, rows visited in (request, node) order
+    rows = [(b, n) for b in np.nonzero(temps > 0)[0] for n in range(N)]
+    per = max(1, block_elems // V)
+    for s0 in range(0, len(rows), per):
+        blk = rows[s0:s0 + per]
+        bi = np.array([r[0] for r in blk])
+        ni = np.array([r[1] for r in blk])
+        z = _as_f64(draft[bi, par1[ni] + 1], dtype)
+        u = rng.random((len(blk), V))
+        with np.errstate(divide="ignore"):
+            g = -np.log(-np.log(u))
+        tokens[bi, ni] = np.argmax(z / temps[bi].astype(np.float64)[:, None] + g, axis=1)
+    u_accept = rng.random((B, N), dtype=np.float32)
+    u_sample = rng.random(B, dtype=np.float32)
+    nn = None if num_nodes is None else np.asarray(num_nodes, np.int32)
+    return TreeWorkload(name=name, B=B, N=N, V=V, dtype=dtype, target=target, draft=draft, parent=parent,
+                        tokens=tokens, u_accept=u_accept, u_sample=u_sample, temperature=temps, num_nodes=nn,
+                        meta=dict(seed=seed, width=width, depth=depth))

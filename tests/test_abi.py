@@ -46,6 +46,8 @@ def test_constants_match_header():
     assert int(re.search(r"#define SV_GAMMA_MAX (\d+)", text).group(1)) == binding.SV_GAMMA_MAX
     assert re.search(r"#define SV_FILTER_MAX_V \(1 << (\d+)\)", text).group(1) == "20"
     assert binding.SV_FILTER_MAX_V == 1 << 20
+    assert int(re.search(r"#define SV_TREE_MAX_NODES (\d+)", text).group(1)) == binding.SV_TREE_MAX_NODES
+    assert re.search(r"#define SV_TREE_MAX_V \(1 << (\d+)\)", text).group(1) == "20"
     for name in ("SV_OK", "SV_EINVAL", "SV_EWORKSPACE", "SV_EHIP"):
         assert int(re.search(name + r"\s*=\s*(-?\d+)", text).group(1)) == getattr(binding, name)
 
@@ -141,3 +143,27 @@ def test_filtered_host_argument_checks(lib):
     assert f(1, 1, 1, 1, 1, 1, None, 1, None, 2, 3, 10, sv.SV_F32, 1, 1, 256, plain, None, None) == \
         sv.binding.SV_EWORKSPACE
     assert sv.spec_verify_filtered_workspace_bytes(2, 3, (1 << 20) + 1, sv.SV_F32) == 0
+
+
+def test_tree_host_argument_checks(lib):
+    f = lib.spec_verify_tree
+
+    def call(B=2, N=3, V=10, dt=sv.SV_F32, wsb=1 << 20, **kw):
+        a = dict(t=1, d=1, par=1, tok=1, nn=None, ua=1, us=1, T=1, cnt=1, out=1, nodes=1, ws=256)
+        a.update(kw)
+        return f(a["t"], a["d"], a["par"], a["tok"], a["nn"], a["ua"], a["us"], a["T"], B, N, V, dt, a["cnt"],
+                 a["out"], a["nodes"], a["ws"], wsb, None)
+
+    E = sv.binding.SV_EINVAL
+    assert call(B=0) == E
+    assert call(N=-1) == E
+    assert call(N=sv.binding.SV_TREE_MAX_NODES + 1) == E
+    assert call(V=sv.binding.SV_TREE_MAX_V + 1) == E
+    assert call(dt=3) == E
+    for name in ("t", "us", "T", "cnt", "out", "d", "par", "tok", "ua", "nodes"):
+        assert call(**{name: None}) == E, name
+    assert call(ws=None) == sv.binding.SV_EWORKSPACE
+    assert call(ws=100) == sv.binding.SV_EWORKSPACE
+    assert call(wsb=8) == sv.binding.SV_EWORKSPACE
+    assert sv.spec_verify_tree_workspace_bytes(8, 84, 128256, sv.SV_BF16) > 0
+    assert sv.spec_verify_tree_workspace_bytes(8, sv.binding.SV_TREE_MAX_NODES + 1, 100, sv.SV_BF16) == 0
