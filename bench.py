@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0: enough for 1.2 GB)")
     ap.add_argument("--mode", choices=["stochastic", "greedy"], default="stochastic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tree", action="store_true", help="skip the tree-verification measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly instead of graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -125,7 +126,9 @@ def summarize_profile(root: str):
               "the K1 timing pass (spec_verify_ex) runs k1_row_stats<bf16, per-request T>; the filtered "
               "measurement (spec_verify_filtered, T = 0.7, top_p = 0.9 with and without top_k = 50) runs "
               "k1_row_stats<bf16, per-request T>, k_filter_levels, k_filter_gather, k_filter_resolve and the "
-              "filtered k2 / k3; the draft-side sampling measurement runs k_sample_rows.  The copy kernels "
+              "filtered k2 / k3; the tree measurement (spec_verify_tree, 8 trees of width 4 and depth 3) runs "
+              "k1_row_stats<bf16, per-request T> and k_tree_walk; the draft-side sampling measurement runs "
+              "k_sample_rows.  The copy kernels "
               "are the benchmark's set-up (input copies), outside the timed region.", ""]
     open(os.path.join(out_dir, "kernels_B64_g5_V128256_bf16.md"), "w").write("\n".join(lines))
 
@@ -395,6 +398,53 @@ def main():
                                "alpha_hat": round(float(fc.float().mean()) / gamma, 4)}
         log(f"[bench] spec_verify_filtered {filtered}")
 
+    # tree verification: 8 trees of width 4 and depth 3 (84 nodes) over the same vocabulary, T = 0.7
+    tree = {}
+    if not greedy and not args.no_tree:
+        t0 = time.perf_counter()
+        tw = W.build_tree("B8_w4_d3_V128256_bf16_T0.7", 3000, 8, 4, 3, V, "bf16", target_scale=4.0, zipf=True,
+                          sigma=0.5, temps=0.7)
+        log(f"[bench] generated {tw.name} in {time.perf_counter() - t0:.1f}s")
+        tt = tw.to_torch(dev)
+        tcopies = max(2, math.ceil(1.2e9 / ((tt["target"].numel() + tt["draft"].numel()) * 2)))
+        ttg = [tt["target"]] + [tt["target"].clone() for _ in range(tcopies - 1)]
+        tdr = [tt["draft"]] + [tt["draft"].clone() for _ in range(tcopies - 1)]
+        tws = torch.empty(sv.spec_verify_tree_workspace_bytes(tw.B, tw.N, V, sv.SV_BF16), dtype=torch.uint8,
+                          device=dev)
+        tc = torch.empty(tw.B, dtype=torch.int32, device=dev)
+        to = torch.empty((tw.B, tw.N + 1), dtype=torch.int32, device=dev)
+        tn = torch.empty((tw.B, tw.N), dtype=torch.int32, device=dev)
+
+        def tstep(c):
+            sv.spec_verify_tree(ttg[c], tdr[c], tt["parent"], tt["tokens"], tt["u_accept"], tt["u_sample"],
+                                tt["temperature"], accepted_count=tc, out_tokens=to, out_nodes=tn, workspace=tws,
+                                stream=stream)
+
+        with torch.cuda.stream(stream):
+            tstep(0)
+        torch.cuda.synchronize()
+        rc, ro = tc.cpu().clone(), to.cpu().clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in range(tcopies):
+                tstep(c)
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // (4 * tcopies))
+        s0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                g.replay()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - s0) / (reps * tcopies)
+        assert torch.equal(tc.cpu(), rc) and torch.equal(to.cpu(), ro), "tree replay differs"
+        emitted = float(rc.sum()) + tw.B
+        tree = {"workload": tw.name, "us_per_call": round(per * 1e6, 3), "nodes_per_s": round(tw.B * tw.N / per, 1),
+                "emitted_tokens_per_s": round(emitted / per, 1), "mean_accepted_path": round(float(rc.float().mean()), 3),
+                "GBps_alg": round(tw.bytes_alg() / per / 1e9, 1)}
+        log(f"[bench] spec_verify_tree {tree}")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -436,6 +486,7 @@ def main():
                   "alpha_hat": round(float(ref_count.float().mean()) / gamma, 4),
                   "spec_sample": sample,
                   "spec_verify_filtered": filtered,
+                  "spec_verify_tree": tree,
                   "kernel_source_sha256_16": source_hash()},
     }
     print(json.dumps(rec), flush=True)

@@ -1789,10 +1789,21 @@ __device__ void tree_masses(const void *trow, const void *drow, bool aligned, in
                             float negMp, float negMq, float r, bool use_q, TreeShared &sh) {
   constexpr int kN = kLaneElems / Elem<DT>::kVec;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  // each wave takes sub-chunks wave, wave + kTWaves, ...; bf16 rows load the
+  // next one while the current one is reduced (fp32 rows, twice the registers
+  // per sub-chunk, load one at a time)
+  constexpr bool kAhead = DT == SV_BF16;
+  u32x4 tp[kN], dq[kN], tn[kN], dn[kN];
+  if (kAhead && wave < NSUB) {
+    load_lane_raw<DT>(trow, aligned, static_cast<long>(wave) * kSub, lane, V, tp);
+    if (use_q) load_lane_raw<DT>(drow, aligned, static_cast<long>(wave) * kSub, lane, V, dq);
+  }
   for (int j = wave; j < NSUB; j += kTWaves) {
-    u32x4 tp[kN], dq[kN];
-    load_lane_raw<DT>(trow, aligned, static_cast<long>(j) * kSub, lane, V, tp);
-    if (use_q) load_lane_raw<DT>(drow, aligned, static_cast<long>(j) * kSub, lane, V, dq);
+    const int jn = kAhead ? j + kTWaves : j;
+    if (jn < NSUB) {
+      load_lane_raw<DT>(trow, aligned, static_cast<long>(jn) * kSub, lane, V, kAhead ? tn : tp);
+      if (use_q) load_lane_raw<DT>(drow, aligned, static_cast<long>(jn) * kSub, lane, V, kAhead ? dn : dq);
+    }
     float acc = 0.0f;
 #pragma unroll
     for (int u = 0; u < kN; ++u) {
@@ -1807,6 +1818,13 @@ __device__ void tree_masses(const void *trow, const void *drow, bool aligned, in
     }
     const double ws = wave_sum(static_cast<double>(acc));
     if (lane == 0) sh.sub[j] = ws;
+    if (kAhead) {
+#pragma unroll
+      for (int u = 0; u < kN; ++u) {
+        tp[u] = tn[u];
+        dq[u] = dn[u];
+      }
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
