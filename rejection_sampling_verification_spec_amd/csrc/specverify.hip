@@ -1756,10 +1756,17 @@ __global__ __launch_bounds__(kFBlock) void k_filter_resolve(
 constexpr int kTBlock = 512;
 constexpr int kTWaves = kTBlock / kWave;
 constexpr int kTMaxSub = SV_TREE_MAX_V / kSub;
+static_assert(SV_TREE_MAX_NODES <= kTBlock, "one thread per node in the child compaction");
 
 struct TreeShared {
   int parent[SV_TREE_MAX_NODES];
   int token[SV_TREE_MAX_NODES];
+  int child[SV_TREE_MAX_NODES];    // children of the current position, in node order
+  float czp[SV_TREE_MAX_NODES];    // their target and draft logits, and uniforms
+  float czq[SV_TREE_MAX_NODES];
+  float cu[SV_TREE_MAX_NODES];
+  int wcnt[kTWaves];
+  int nchild;
   double sub[kTMaxSub];       // sub-chunk masses of the current distribution
   double red[2 + kTWaves];
   double W;                   // their sum
@@ -1947,12 +1954,18 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
   for (int t = tid; t < Nmax; t += kTBlock) out_nodes[static_cast<long>(b) * Nmax + t] = -1;
   __syncthreads();
   const size_t eb = Elem<DT>::kBytes;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
   int pos = 0, depth = 0;
   for (;;) {
     const void *trow = static_cast<const char *>(target) + (static_cast<long>(b) * (Nmax + 1) + pos) * V * eb;
     const void *drow = pos < Nmax ? static_cast<const char *>(draft) + (static_cast<long>(b) * Nmax + pos) * V * eb
                                   : nullptr;  // position Nmax has no child
     const bool al = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;
+    // the position's children in node order (a block-wide compaction), and the
+    // row statistics (target by thread 0, draft by the first lane of wave 1)
+    const bool is_child = tid < N && tid >= pos && sh.parent[tid] == pos - 1;
+    const unsigned long long mask = __ballot(is_child);
+    if (lane == 0) sh.wcnt[wave] = __popcll(mask);
     if (tid == 0) {
       int M, arg;
       double s;
@@ -1961,12 +1974,31 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
       s_sp = s;
       s_arg = arg;
     }
+    if (tid == kWave && !greedy && pos < N) {
+      int arg;
+      merged_row(part, static_cast<long>(b) * rows + Nmax + 1 + pos, NS, false, s_Mq, s_sq, arg);
+    }
+    __syncthreads();
+    int nchild = 0, before = 0;
+    for (int w = 0; w < kTWaves; ++w) {
+      if (w < wave) before += sh.wcnt[w];
+      nchild += sh.wcnt[w];
+    }
+    if (is_child) sh.child[before + __popcll(mask & ((1ull << lane) - 1ull))] = tid;
+    __syncthreads();
+    if (!greedy && tid < nchild) {  // gather each child's two logits and its uniform
+      const int n = sh.child[tid], x = sh.token[n];
+      const bool ok = x >= 0 && x < V;  // an id outside the vocabulary is rejected, never dereferenced
+      sh.czp[tid] = ok ? load_one<DT>(trow, x) : 0.0f;
+      sh.czq[tid] = ok ? load_one<DT>(drow, x) : 0.0f;
+      sh.cu[tid] = ok ? u_accept[static_cast<long>(b) * Nmax + n] : 2.0f;  // 2 rejects
+    }
     __syncthreads();
     int hit = -1;
     if (greedy) {
       if (tid == 0) {
-        for (int n = pos; n < N && hit < 0; ++n)
-          if (sh.parent[n] == pos - 1 && sh.token[n] == s_arg) hit = n;
+        for (int j = 0; j < nchild && hit < 0; ++j)
+          if (sh.token[sh.child[j]] == s_arg) hit = sh.child[j];
         s_hit = hit;
       }
       __syncthreads();
@@ -1979,34 +2011,18 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
       const int Mp = s_Mp;
       const double sp = s_sp;
       const float negMp = -static_cast<float>(Mp);
+      const int Mq = nchild > 0 ? s_Mq : 0;
+      const double sq = nchild > 0 ? s_sq : 1.0;
       double cc = 0.0, Z = 1.0;  // current target: max(0, p - cc q) / Z
-      bool have_q = false, masses_current = false;
-      int Mq = 0;
-      double sq = 1.0;
-      for (int n = pos; n < N; ++n) {
-        if (sh.parent[n] != pos - 1) continue;  // uniform: LDS read by every thread
-        if (!have_q) {
-          if (tid == 0) {
-            int arg;
-            merged_row(part, static_cast<long>(b) * rows + Nmax + 1 + pos, NS, false, s_Mq, s_sq, arg);
-          }
-          __syncthreads();
-          Mq = s_Mq;
-          sq = s_sq;
-          have_q = true;
-        }
+      bool masses_current = false;
+      for (int j = 0; j < nchild; ++j) {
         if (tid == 0) {
-          const int x = sh.token[n];
-          bool acc = false;
-          if (x >= 0 && x < V) {  // an id outside the vocabulary is rejected, never dereferenced
-            const double cd = static_cast<double>(c);
-            const double px = exp2(static_cast<double>(load_one<DT>(trow, x)) * cd - Mp) / sp;
-            const double qx = exp2(static_cast<double>(load_one<DT>(drow, x)) * cd - Mq) / sq;
-            const double num = fmax(0.0, px - cc * qx), den = Z * qx;
-            const double a = den > 0.0 ? fmin(1.0, num / den) : (num > 0.0 ? 1.0 : 0.0);
-            acc = static_cast<double>(u_accept[static_cast<long>(b) * Nmax + n]) < a;
-          }
-          s_hit = acc ? n : -1;
+          const double cd = static_cast<double>(c);
+          const double px = exp2(static_cast<double>(sh.czp[j]) * cd - Mp) / sp;
+          const double qx = exp2(static_cast<double>(sh.czq[j]) * cd - Mq) / sq;
+          const double num = fmax(0.0, px - cc * qx), den = Z * qx;
+          const double a = den > 0.0 ? fmin(1.0, num / den) : (num > 0.0 ? 1.0 : 0.0);
+          s_hit = static_cast<double>(sh.cu[j]) < a ? sh.child[j] : -1;
         }
         __syncthreads();
         hit = s_hit;
