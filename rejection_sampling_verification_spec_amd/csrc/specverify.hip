@@ -13,26 +13,34 @@
 //   [P4] "LLM推測デコーディング最適化実踐", section 検証アルゴリズムの実装
 //        (gamma+1 target rows, bonus draw from the last one)
 //
-// Four launches on the caller's stream, no host synchronisation, no
-// device-wide fences (each kernel boundary is the only cross-workgroup sync):
+// Three launches on the caller's stream for the verify step, no host
+// synchronisation, no device-wide fences (each kernel boundary is the only
+// cross-workgroup sync):
 //
-//   K1  row_stats  one workgroup per (request, logit row, vocabulary chunk).
-//                  Streams the chunk once (16-byte non-temporal loads, next tile
-//                  prefetched) and produces, for a stochastic row, (M, s) with M
-//                  an integer upper bound of max(z)*log2(e)/T and
-//                  s = sum 2^(z*c - M); for a greedy row, the maximum and its
-//                  lowest index.  Integer M makes every rescale between partial
-//                  sums an exact power of two (ldexp).
-//   K2  decide     one workgroup per request.  Merges the chunk partials of each
-//                  row in a fixed order, evaluates a_i = min(1, p_i(x_i)/q_i(x_i))
-//                  in fp64 from the two gathered logits, finds the first
-//                  rejection with a wave ballot, writes accepted_count and the
-//                  accepted prefix, and prepares the one row pair to sample.
-//   K3a mass       re-reads the selected target row (and draft row after a
-//                  rejection) and writes the mass of w = max(0, p - q) (or p for
-//                  the bonus) per 2048-token sub-chunk, one wave each.
-//   K3b select     one wave per request: the sub-chunk whose prefix crosses u*Z,
-//                  then the token inside it.
+//   K1  k1_row_stats    one workgroup per (request, logit row, vocabulary chunk).
+//                       Streams the chunk once (16-byte non-temporal loads, next
+//                       tile prefetched) and produces, for a stochastic row,
+//                       (M, s) with M an integer upper bound of max(z)*log2(e)/T
+//                       and s = sum 2^(z*c - M); for a greedy row, the maximum
+//                       and its lowest index.  Integer M makes every rescale
+//                       between partial sums an exact power of two (ldexp).
+//   K2  k2_decide_mass  NW workgroups per request.  Each merges the chunk
+//                       partials of every row in a fixed order, evaluates
+//                       a_i = min(1, p_i(x_i)/q_i(x_i)) in fp64 from the two
+//                       gathered logits and finds the first rejection with a
+//                       wave ballot (workgroup 0 stores the outputs); then its
+//                       waves write the mass of w = max(0, p - q) (or p for the
+//                       bonus) of the selected row pair per 2048-token sub-chunk.
+//   K3  k3_select       one workgroup per request: the sub-chunk whose prefix
+//                       crosses u*Z, then the token inside it.
+//
+// Extensions, on the same row statistics:
+//   top-k / top-p       k_filter_levels, k_filter_gather, k_filter_resolve
+//                       between K1 and K2 find each filtered row's cut; K2 and
+//                       K3 are instantiated with the cut compares.
+//   tree of drafts      K1 over every tree position, then k_tree_walk (one
+//                       workgroup per request).
+//   draft-side sampling k_sample_rows (one workgroup per row).
 //
 // Numerics: bf16 -> fp32 widening is exact; exponentials are v_exp_f32 of
 // fma(z, c, -M); per-thread partial sums are fp32 over at most 64 terms and
