@@ -241,6 +241,19 @@ int spec_sample(const void *logits, const float *u, float temperature,
                 int32_t *tokens, void *workspace, size_t workspace_bytes,
                 void *stream);
 
+/* Draft-side sampling from filtered rows: one token per row of softmax(logits[r]
+ * / T_r) truncated by top_k[r] / top_p[r] under the rule of spec_verify_filtered
+ * (the sampler a serving system runs before filtered verification), by the
+ * same inverse CDF with u[r].  temperatures: DEVICE [R] (0 = arg-max, which no
+ * filter changes); top_k, top_p: DEVICE [R] or NULL, out-of-range values switch
+ * the filter off for that row.  V <= SV_FILTER_MAX_V.  The workspace is sized by
+ * spec_sample_filtered_workspace_bytes. */
+size_t spec_sample_filtered_workspace_bytes(int R, int V, int dtype);
+int spec_sample_filtered(const void *logits, const float *u, const float *temperatures,
+                         const int32_t *top_k, const float *top_p, int R, int V, int dtype,
+                         int32_t *tokens, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
 /* ---- Adaptive draft length (host only, no GPU work) ----------------------
  * Policies that pick the next gamma from the accepted counts of past steps
  * (P3 section vLLM は利用者が書く表で、SGLang は実行中に観測した受理の長さで

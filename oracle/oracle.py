@@ -164,14 +164,16 @@ def run_workload(w, trace: bool = True, lib: Optional[ctypes.CDLL] = None) -> Or
                        top_k=getattr(w, "top_k", None), top_p=getattr(w, "top_p", None))
 
 
-def sample(logits, u, temperature, dtype: Optional[str] = None, lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
-    """One token per row of softmax(logits / T) by inverse CDF with the uniforms u.
+def sample(logits, u, temperature, dtype: Optional[str] = None, lib: Optional[ctypes.CDLL] = None,
+           top_k=None, top_p=None) -> np.ndarray:
+    """One token per row of softmax(logits / T) (optionally top-k / top-p filtered)
+    by inverse CDF with the uniforms u.
 
     This is the oracle's verify step with no drafts (every row is a bonus row)."""
     logits = np.asarray(logits)
     R, V = logits.shape
     res = spec_verify(logits.reshape(R, 1, V), np.zeros((R, 0, V), dtype=logits.dtype), np.zeros((R, 0)),
-                      np.zeros((R, 0)), u, temperature, dtype=dtype, trace=True, lib=lib)
+                      np.zeros((R, 0)), u, temperature, dtype=dtype, trace=True, lib=lib, top_k=top_k, top_p=top_p)
     return res.out_tokens[:, 0].copy(), res
 
 

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     SpecVerifyError,
     load_library,
     spec_sample,
+    spec_sample_filtered_workspace_bytes,
     spec_sample_workspace_bytes,
     spec_verify,
     spec_verify_ex,

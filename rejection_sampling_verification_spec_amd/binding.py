@@ -34,6 +34,8 @@ EXPORTED_SYMBOLS = (
     "spec_verify_filtered_workspace_bytes",
     "spec_verify_tree",
     "spec_verify_tree_workspace_bytes",
+    "spec_sample_filtered",
+    "spec_sample_filtered_workspace_bytes",
     "spec_sample_workspace_bytes",
     "spec_sample",
     "spec_gamma_policy_init",
@@ -126,6 +128,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_tree.restype = i32
     lib.spec_verify_tree_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.spec_verify_tree_workspace_bytes.restype = sz
+    lib.spec_sample_filtered.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
+    lib.spec_sample_filtered.restype = i32
+    lib.spec_sample_filtered_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spec_sample_filtered_workspace_bytes.restype = sz
     lib.spec_sample_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_sample_workspace_bytes.restype = sz
     lib.spec_sample.argtypes = [vp, vp, ctypes.c_float, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -392,11 +398,17 @@ def spec_sample_workspace_bytes(R: int, V: int, dtype: int) -> int:
     return int(load_library().spec_sample_workspace_bytes(R, V, dtype))
 
 
-def spec_sample(logits, u, temperature, tokens=None, workspace=None, stream=None):
+def spec_sample_filtered_workspace_bytes(R: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_sample_filtered_workspace_bytes(R, V, dtype))
+
+
+def spec_sample(logits, u, temperature, tokens=None, workspace=None, stream=None, top_k=None, top_p=None):
     """One token per row of softmax(logits / T) by inverse CDF with the uniforms ``u``.
 
     logits: device [R, V] bf16/fp32; u: device [R] fp32; temperature: float, or a
-    device fp32 tensor [R] of per-row temperatures (0 = arg-max).  Returns tokens [R] int32.
+    device fp32 tensor [R] of per-row temperatures (0 = arg-max).  ``top_k`` /
+    ``top_p``: optional device tensors [R] (int32 / fp32) that truncate each row
+    first (spec_sample_filtered).  Returns tokens [R] int32.
     """
     import torch
     lib = load_library()
@@ -404,6 +416,26 @@ def spec_sample(logits, u, temperature, tokens=None, workspace=None, stream=None
         raise ValueError("logits must be [R, V]")
     R, V = int(logits.shape[0]), int(logits.shape[1])
     dt = _dtype_code(logits)
+    if top_k is not None or top_p is not None:
+        temps = temperature if isinstance(temperature, torch.Tensor) else \
+            torch.full((R,), float(temperature), dtype=torch.float32, device=logits.device)
+        _check_device(logits, u, temps, top_k, top_p)
+        _expect(logits, (R, V), None, "logits")
+        _expect(u, (R,), torch.float32, "u")
+        _expect(temps, (R,), torch.float32, "temperature")
+        _expect(top_k, (R,), torch.int32, "top_k", optional=True)
+        _expect(top_p, (R,), torch.float32, "top_p", optional=True)
+        if tokens is None:
+            tokens = torch.empty(R, dtype=torch.int32, device=logits.device)
+        _expect(tokens, (R,), torch.int32, "tokens")
+        need = spec_sample_filtered_workspace_bytes(R, V, dt)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+        rc = lib.spec_sample_filtered(_ptr(logits), _ptr(u), _ptr(temps), _ptr(top_k), _ptr(top_p), R, V, dt,
+                                      _ptr(tokens), _ptr(workspace), workspace.numel(), _stream(stream))
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, "spec_sample_filtered")
+        return tokens
     per_row = isinstance(temperature, torch.Tensor)
     _check_device(logits, u, temperature if per_row else None)
     _expect(logits, (R, V), None, "logits")

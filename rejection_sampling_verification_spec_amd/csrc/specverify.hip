@@ -2597,6 +2597,29 @@ int spec_sample(const void *logits, const float *u, float temperature, const flo
                   counts, tokens, workspace, P.total, stream, nullptr);
 }
 
+size_t spec_sample_filtered_workspace_bytes(int R, int V, int dtype) {
+  Plan P;
+  if (!make_plan(R, 0, V, dtype, &P) || V > SV_FILTER_MAX_V) return 0;
+  return P.ftotal + align_up(sizeof(int32_t) * static_cast<size_t>(R));
+}
+
+// Filtered sampling is the filtered verify step with no drafts: every row is a
+// bonus row of its filtered distribution.  The per-row counts (always 0) go to
+// the tail of the workspace.
+int spec_sample_filtered(const void *logits, const float *u, const float *temperatures, const int32_t *top_k,
+                         const float *top_p, int R, int V, int dtype, int32_t *tokens, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  Plan P;
+  if (!make_plan(R, 0, V, dtype, &P) || V > SV_FILTER_MAX_V) return SV_EINVAL;
+  if (!logits || !u || !temperatures || !tokens) return SV_EINVAL;
+  const size_t need = P.ftotal + align_up(sizeof(int32_t) * static_cast<size_t>(R));
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < need)
+    return SV_EWORKSPACE;
+  int32_t *counts = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + P.ftotal);
+  return dispatch(logits, nullptr, nullptr, nullptr, u, temperatures, 0.0f, false, nullptr, top_k, top_p, R, 0, V,
+                  dtype, counts, tokens, workspace, P.ftotal, stream, nullptr);
+}
+
 const char *spec_verify_strerror(int code) {
   switch (code) {
     case SV_OK: return "success";

@@ -167,3 +167,13 @@ def test_tree_host_argument_checks(lib):
     assert call(wsb=8) == sv.binding.SV_EWORKSPACE
     assert sv.spec_verify_tree_workspace_bytes(8, 84, 128256, sv.SV_BF16) > 0
     assert sv.spec_verify_tree_workspace_bytes(8, sv.binding.SV_TREE_MAX_NODES + 1, 100, sv.SV_BF16) == 0
+
+
+def test_sample_filtered_host_argument_checks(lib):
+    f = lib.spec_sample_filtered
+    E = sv.binding.SV_EINVAL
+    assert f(1, 1, None, 1, None, 4, 10, sv.SV_F32, 1, 256, 1 << 20, None) == E      # temperatures required
+    assert f(1, 1, 1, 1, None, 4, (1 << 20) + 1, sv.SV_F32, 1, 256, 1 << 30, None) == E
+    assert f(None, 1, 1, 1, None, 4, 10, sv.SV_F32, 1, 256, 1 << 20, None) == E
+    assert f(1, 1, 1, 1, None, 4, 10, sv.SV_F32, 1, 256, 16, None) == sv.binding.SV_EWORKSPACE
+    assert sv.spec_sample_filtered_workspace_bytes(4, 10, sv.SV_F32) > sv.spec_sample_workspace_bytes(4, 10, sv.SV_F32)

@@ -79,3 +79,36 @@ def test_sample_integrates_to_softmax():
     counts = np.bincount(g, minlength=V)
     assert np.all(np.abs(counts - N * p) <= 2.0), (counts, N * p)
     assert np.all(np.diff(g) >= 0)   # inverse CDF is monotone in u
+
+
+@pytest.mark.parametrize("R,V,dtype,k,p", [
+    (64, 1000, "f32", 20, None), (64, 32000, "bf16", None, 0.9), (320, 128256, "bf16", 50, 0.9),
+    (48, 9000, "f32", "mixed", "mixed"),
+])
+def test_sample_filtered_parity(R, V, dtype, k, p):
+    """spec_sample with top_k / top_p (spec_sample_filtered) against the oracle's filtered rows."""
+    import oracle
+
+    import rejection_sampling_verification_spec_amd as sv
+    seed = R * 7919 + V
+    store, u = _case(seed, R, V, dtype, 0.7)
+    rng = np.random.default_rng(seed + 2)
+    T = rng.choice(np.array([0.0, 0.6, 1.0], np.float32), size=R) if k == "mixed" else np.full(R, 0.7, np.float32)
+    ks = (rng.choice(np.array([0, 1, 10, 400, V], np.int32), size=R) if k == "mixed"
+          else None if k is None else np.full(R, k, np.int32))
+    ps = (rng.choice(np.array([1.0, 0.95, 0.8, 0.3], np.float32), size=R) if p == "mixed"
+          else None if p is None else np.full(R, p, np.float32))
+    dev = torch.device("cuda:0")
+    lt = torch.from_numpy(np.ascontiguousarray(store))
+    lt = (lt.view(torch.bfloat16) if dtype == "bf16" else lt).to(dev)
+    say(f"spec_sample filtered R={R} V={V} {dtype} k={k} p={p}")
+    tok = sv.spec_sample(lt, torch.from_numpy(u).to(dev), torch.from_numpy(T).to(dev),
+                         top_k=None if ks is None else torch.from_numpy(ks).to(dev),
+                         top_p=None if ps is None else torch.from_numpy(ps).to(dev))
+    torch.cuda.synchronize()
+    g = tok.cpu().numpy()
+    o, tr = oracle.sample(store, u, T, dtype=dtype, top_k=ks, top_p=ps)
+    ok = tr.flags == 0
+    assert ok.sum() >= R - max(1, R // 16)
+    np.testing.assert_array_equal(g[ok], o[ok])
+    np.testing.assert_array_equal(g[T == 0], o[T == 0])
