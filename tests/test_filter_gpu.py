@@ -209,3 +209,43 @@ def test_filtered_deterministic():
     np.testing.assert_array_equal(a.out, b.out)
     for k in a.dbg:
         np.testing.assert_array_equal(a.dbg[k], b.dbg[k])
+
+
+def test_filtered_graph_replay_and_side_stream():
+    """Filtered verification captured in a HIP graph equals the eager call on every replay, with the
+    workspace scribbled between replays (the filter kernels clear what they need themselves)."""
+    import rejection_sampling_verification_spec_amd as sv
+    w = with_filter(W.make_random(36, 12, 4, 20000, "bf16", temps=0.7, zipf=True), top_k=40, top_p=0.9)
+    redraw_filtered_drafts(w, 37)
+    dev = torch.device("cuda:0")
+    t = w.to_torch(dev)
+    count = torch.empty(w.B, dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.gamma + 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(sv.spec_verify_filtered_workspace_bytes(w.B, w.gamma, w.V, sv.SV_BF16), dtype=torch.uint8,
+                     device=dev)
+    s = torch.cuda.Stream()
+
+    def call():
+        sv.spec_verify_filtered(t["target"], t["draft"], t["draft_tokens"], t["u_accept"], t["u_sample"],
+                                t["temperature"], None, top_k=t["top_k"], top_p=t["top_p"], accepted_count=count,
+                                out_tokens=out, workspace=ws, stream=s)
+
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    ref = (count.cpu().clone(), out.cpu().clone())
+    g0 = gpu_run(w)
+    np.testing.assert_array_equal(ref[0].numpy(), g0.count)
+    np.testing.assert_array_equal(ref[1].numpy(), g0.out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for rep in range(3):
+        count.fill_(-5)
+        out.fill_(-5)
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"filtered graph replay {rep}")
+        assert torch.equal(count.cpu(), ref[0]) and torch.equal(out.cpu(), ref[1])

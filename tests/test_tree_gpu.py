@@ -143,3 +143,43 @@ def test_tree_deterministic():
     b = gpu_tree(w)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+def test_tree_graph_replay_and_side_stream():
+    import rejection_sampling_verification_spec_amd as sv
+    w = W.build_tree("graph", 75, 6, 3, 2, 7000, "bf16", target_scale=3.0, zipf=True, sigma=0.6,
+                     temps=np.array([1.0, 0.0, 0.7, 1.0, 0.7, 1.0], np.float32))
+    ref = gpu_tree(w)
+    dev = torch.device("cuda:0")
+    t = w.to_torch(dev)
+    cnt = torch.empty(w.B, dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.N + 1), dtype=torch.int32, device=dev)
+    nodes = torch.empty((w.B, w.N), dtype=torch.int32, device=dev)
+    ws = torch.empty(sv.spec_verify_tree_workspace_bytes(w.B, w.N, w.V, sv.SV_BF16), dtype=torch.uint8, device=dev)
+    s = torch.cuda.Stream()
+
+    def call():
+        sv.spec_verify_tree(t["target"], t["draft"], t["parent"], t["tokens"], t["u_accept"], t["u_sample"],
+                            t["temperature"], accepted_count=cnt, out_tokens=out, out_nodes=nodes, workspace=ws,
+                            stream=s)
+
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(cnt.cpu().numpy(), ref[0])
+    np.testing.assert_array_equal(out.cpu().numpy(), ref[1])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for rep in range(3):
+        cnt.fill_(-5)
+        out.fill_(-5)
+        nodes.fill_(-5)
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"tree graph replay {rep}")
+        np.testing.assert_array_equal(cnt.cpu().numpy(), ref[0])
+        np.testing.assert_array_equal(out.cpu().numpy(), ref[1])
+        np.testing.assert_array_equal(nodes.cpu().numpy(), ref[2])
