@@ -35,7 +35,7 @@
 //                       crosses u*Z, then the token inside it.
 //
 // Extensions, on the same row statistics:
-//   top-k / top-p       k_filter_levels, k_filter_gather, k_filter_resolve
+//   top-k / top-p       k_filter_capture, k_filter_resolve
 //                       between K1 and K2 find each filtered row's cut; K2 and
 //                       K3 are instantiated with the cut compares.
 //   tree of drafts      K1 over every tree position, then k_tree_walk (one
@@ -316,12 +316,14 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
     const void *__restrict__ target, const void *__restrict__ draft,
     const int32_t *__restrict__ tokens, const float *__restrict__ temps, float scalar_T,
     const int32_t *__restrict__ lens, int gamma, int V, int NCH, int chunk_vecs,
-    Partial *__restrict__ part, float *__restrict__ zx) {
+    Partial *__restrict__ part, float *__restrict__ zx, unsigned *__restrict__ row_counter) {
   constexpr int kV = Elem<DT>::kVec;
   const int rows = 2 * gamma + 1;
   const int wgid = blockIdx.x;
   const int slot = wgid / NCH;
   const int j = wgid - slot * NCH;
+  // a per-row counter of the kernels that follow (filtered calls), cleared here
+  if (row_counter && j == 0 && threadIdx.x == 0) row_counter[slot] = 0u;
   const int b = slot / rows;
   const int r = slot - b * rows;
   const int g = request_len(lens, gamma, b);
@@ -461,21 +463,23 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
 // renormalised rows: K2 and K3 treat z < tau as probability zero and use the
 // kept mass in place of the row sum.
 //
-// Three kernels between K1 and K2.  A token's mass is e(z) = 2^(z c - M) with
+// Two kernels between K1 and K2.  A token's mass is e(z) = 2^(z c - M) with
 // the row's integer M from K1; exact sums use the fixed-point integer
 // floor(e * 2^fs), fs = 61 - ceil(log2 V), so that they do not depend on the
 // order of the additions and a whole row fits 64 bits.
-//   FA  k_filter_levels (K1's chunks): counts and estimated masses of the
-//       logits in levels 0..15, level l holding y = z c - M in (-l-1, -l].
-//   FB  k_filter_gather (K1's chunks): from the row's level totals, the levels
-//       [l0, l1] that hold the k-th largest logit (exact counts) and the top-p
-//       crossing (estimated masses with a 1e-4 margin; the row's total is K1's
-//       sum) are chosen; logits above l0 add their exact mass, logits in
-//       [l0, l1] are appended to the row's candidate list.
-//   FC  k_filter_resolve (one workgroup per row): sorts the candidates and
-//       scans them group by group from the exact prefix above them.
-// A row takes FC's general path when the chosen levels reach below level 15,
-// hold more than kFCap logits, or do not contain the crossing:
+//   FG  k_filter_capture (K1's chunks): appends the order key of every logit
+//       within 16 binary orders of magnitude of 2^M (y = z c - M > -16) to the
+//       row's candidate list (wave-aggregated slot reservations); a vector
+//       whose largest logit is below that is skipped after one test.
+//   FC  k_filter_resolve (one workgroup per row): an exact (count, fixed-point
+//       mass) histogram of the candidates over 1/32-order bins finds the bin
+//       holding the k-th largest logit or the top-p crossing (the candidates
+//       are every logit above the window's floor, so the prefixes from the top
+//       are exact); that bin's candidates are sorted and scanned group by
+//       group.  The top-p target is top_p times the exact top-k mass, or times
+//       K1's row sum without top-k.
+// A row takes FC's general path when it captured more than kGCap logits, or
+// when the k-th logit or the crossing lies below the window:
 //   pass 1   exact (count, fixed-point mass) histogram over 2048 bins of y,
 //            each 1/32 of a binary order of magnitude, down to y = -64, and
 //            one bin below;
@@ -490,13 +494,11 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
 // filter are not touched.
 constexpr int kFBlock = 512;  // FC workgroup
 constexpr int kFWaves = kFBlock / kWave;
-constexpr int kLBlock = 256;  // FA / FB workgroups
+constexpr int kLBlock = 256;  // FG workgroup
 constexpr int kFBins = 2048;  // general path: y bins; index kFBins collects y <= -64
 constexpr int kFCap = 4096;   // logits sorted and scanned in LDS
-constexpr int kLevels = 16;   // FA levels of one binary order of magnitude below 2^M
-// a chunk of at most SV_FILTER_MAX_V logits leaves each FA column at most 2^12
-// logits: the 16-bit count field and the 48-bit mass field cannot overflow
-static_assert(SV_FILTER_MAX_V / kLBlock <= (1 << 12), "FA column bound");
+constexpr int kLevels = 16;   // the capture window: levels of one binary order of magnitude below 2^M
+constexpr int kGCap = 8192;   // logits a row may capture
 
 struct alignas(16) FilterStats {
   double s_kept;  // sum of 2^(z c - M) over the kept tokens
@@ -504,23 +506,10 @@ struct alignas(16) FilterStats {
   int pad;
 };
 
-// The levels FB gathers for one row, and the counts around them.
-struct alignas(16) RowPlan {
-  int l0, l1;
-  unsigned count_above;  // logits in levels < l0
-  unsigned count_in;     // logits in levels [l0, l1]
-  int general;           // 1: the resolve kernel takes the general path
-  int pad[3];
-};
-
-// Device buffers of the filter kernels (all inside the workspace).
+// Device buffers of the filter kernels (inside the workspace).
 struct FilterWork {
-  unsigned *lv_cnt;           // [slots][NS][kLevels]
-  double *lv_mass;            // [slots][NS][kLevels]
-  unsigned long long *above;  // [slots][NS] exact mass above the gathered levels
-  unsigned *ncand;            // [slots] candidates appended
-  unsigned *cand;             // [slots][kFCap] their order keys
-  RowPlan *plan;              // [slots]
+  unsigned *ncand;  // [slots] logits captured (cleared by K1)
+  unsigned *cand;   // [slots][kGCap] their order keys
 };
 
 // Whether request b filters, with its k (0: none) and p (1: none).  Values
@@ -1456,17 +1445,21 @@ __device__ __forceinline__ void row_scale(const Partial *part, long slot, int NS
   }
 }
 
-// FA: level histogram of one chunk of a row (K1's chunking).  Every thread
-// counts into its own LDS column (plain read-modify-write: no atomics, no bank
-// conflicts), one 64-bit word per level: the count in bits 48..63 and the
-// level's mass estimate in bits 0..47 as sum of round(e * 2^(l + 24)), a value
-// in (2^23, 2^24] for a logit of level l.  Logits below level kLevels - 1 are
-// not counted.
+// FG: one chunk of a row (K1's chunking).  Every logit with y > -kLevels is a
+// candidate.  Each wave gathers its candidates in its own LDS region (slots
+// from a ballot: no atomics), then reserves its range of the row's list with
+// one atomic and copies them out.  A wave that finds more than kWaveCap
+// candidates pushes the row's count past kGCap (the general path).
+constexpr int kWaveCap = 512;
+
 template <int DT>
-__global__ __launch_bounds__(kLBlock) void k_filter_levels(
+__global__ __launch_bounds__(kLBlock) void k_filter_capture(
     const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
     const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
     int gamma, int V, int NS, int chunk_vecs, const Partial *__restrict__ part, FilterWork fw) {
+  constexpr int kV = Elem<DT>::kVec;
+  constexpr int U = 8;
+  constexpr long kStep = static_cast<long>(U) * kLBlock;
   const int rows = 2 * gamma + 1;
   const long slot = blockIdx.x / NS;
   const int j = static_cast<int>(blockIdx.x - slot * NS);
@@ -1480,158 +1473,92 @@ __global__ __launch_bounds__(kLBlock) void k_filter_levels(
   double s;
   row_scale(part, slot, NS, M, s);
   const float c = temp_scale(T), negM = -static_cast<float>(M);
-  __shared__ unsigned long long lw[kLevels * kLBlock];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-#pragma unroll
-  for (int l = 0; l < kLevels; ++l) lw[l * kLBlock + tid] = 0ull;  // each thread clears its own column
-  const long nvec = (static_cast<long>(V) + Elem<DT>::kVec - 1) / Elem<DT>::kVec;
+  __shared__ unsigned wbuf[kLBlock / kWave][kWaveCap];
+  unsigned wcount = 0;  // the same in every lane of the wave
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  auto offer = [&](float z) {  // called by every lane of the wave together
+    const bool in = level_of(z, c, negM) < kLevels;
+    const unsigned long long mask = __ballot(in);
+    if (in) {
+      const unsigned q = wcount + static_cast<unsigned>(__popcll(mask & lt));
+      if (q < static_cast<unsigned>(kWaveCap)) wbuf[wave][q] = order_key(z);
+    }
+    wcount += static_cast<unsigned>(__popcll(mask));
+  };
+  const char *rb = static_cast<const char *>(row);
+  const long nvec = (static_cast<long>(V) + kV - 1) / kV;
   const long vb = static_cast<long>(j) * chunk_vecs, ve = min(vb + chunk_vecs, nvec);
-  for_each_logit<DT, kLBlock, 8>(row, aligned, V, vb, ve,
-                                 [&](float m) { return level_of(m, c, negM) < kLevels; }, [&](float z) {
-    const float y = fmaf(z, c, negM);
-    const int l = level_of(z, c, negM);
-    if (l < kLevels) {
-      const unsigned q = static_cast<unsigned>(
-          __builtin_amdgcn_exp2f(y + static_cast<float>(l + 24)) + 0.5f);  // e * 2^(l + 24), rounded
-      lw[l * kLBlock + tid] += (1ull << 48) + q;
-    }
-  });
-  __syncthreads();
-  const long o = (slot * NS + j) * kLevels;
-  for (int l = wave; l < kLevels; l += kLBlock / kWave) {  // fixed order: deterministic
-    // a column holds at most V / 256 <= 2^12 logits, so a lane's four columns
-    // keep both fields in range; the fields are then summed apart
-    unsigned long long w = 0;
-    for (int t = lane; t < kLBlock; t += kWave) w += lw[l * kLBlock + t];
-    unsigned cs = static_cast<unsigned>(w >> 48);
-    unsigned long long ms = w & ((1ull << 48) - 1);
+  const long vw = aligned ? min(ve, static_cast<long>(V) / kV) : vb;  // whole 16-byte vectors
+  // whole vectors: the same trip count in every lane; out-of-range vectors read as -inf
+  for (long base = vb; base < vw; base += kStep) {
+    u32x4 raw[U];
 #pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1) {  // integer sums: any order
-      cs += __shfl_xor(cs, d);
-      ms += __shfl_xor(ms, d);
+    for (int u = 0; u < U; ++u) {
+      const long v = base + static_cast<long>(u) * kLBlock + tid;
+      raw[u] = v < vw ? *reinterpret_cast<const u32x4 *>(rb + v * kV * Elem<DT>::kBytes) : neg_inf_vec<DT>();
     }
-    if (lane == 0) {
-      fw.lv_cnt[o + l] = cs;
-      fw.lv_mass[o + l] = ldexp(static_cast<double>(ms), -(l + 24));
-    }
-  }
-  if (j == 0 && tid == 0) fw.ncand[slot] = 0u;
-}
-
-// The levels [l0, l1] whose logits FB gathers, from the row's level counts and
-// fp32-estimated masses (inclusive prefixes lc[], lm[] over levels 0..kLevels-1)
-// and K1's row sum s: the level of the k-th largest logit (exact counts) and
-// the levels that can hold the top-p crossing (a 1e-4 margin on the estimated
-// masses).  general = 1 when those levels reach below level kLevels - 1 or hold
-// more than kFCap logits.
-__device__ RowPlan choose_levels(const unsigned *lc, const double *lm, double s, int k, float p) {
-  constexpr double kEps = 1e-4;
-  RowPlan rp;
-  int lk = kLevels, l0 = 0, l1 = kLevels;
-  if (k > 0) {
-    lk = 0;
-    while (lk < kLevels && lc[lk] < static_cast<unsigned>(k)) ++lk;
-  }
-  if (p < 1.0f) {
-    const bool klev = k > 0 && lk < kLevels;
-    const double fk_lo = klev ? (lk > 0 ? lm[lk - 1] : 0.0) : s, fk_hi = klev ? lm[lk] : s;
-    const double t_lo = static_cast<double>(p) * fk_lo * (1.0 - kEps);
-    const double t_hi = static_cast<double>(p) * fk_hi * (1.0 + kEps);
-    int lf = 0;
-    while (lf < kLevels && lm[lf] * (1.0 + kEps) < t_lo) ++lf;
-    int ll = lf;
-    while (ll < kLevels && lm[ll] * (1.0 - kEps) < t_hi) ++ll;
-    l0 = lf;
-    l1 = k > 0 ? lk : ll;
-    if (l0 > l1) l0 = l1;
-  } else {
-    l0 = l1 = lk;
-  }
-  rp.l0 = l0;
-  rp.l1 = l1;
-  rp.count_above = l0 > 0 ? lc[(l0 < kLevels ? l0 : kLevels) - 1] : 0u;
-  rp.count_in = l1 < kLevels ? lc[l1] - rp.count_above : 0u;
-  rp.general = (l1 >= kLevels || rp.count_in > static_cast<unsigned>(kFCap)) ? 1 : 0;
-  return rp;
-}
-
-// FB: one chunk of a row again.  Logits above level l0 add their exact
-// fixed-point mass to the chunk's sum; logits in levels [l0, l1] are appended
-// to the row's candidate list.
-template <int DT>
-__global__ __launch_bounds__(kLBlock) void k_filter_gather(
-    const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
-    const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
-    int gamma, int V, int NS, int chunk_vecs, int fs, const Partial *__restrict__ part, FilterWork fw) {
-  const int rows = 2 * gamma + 1;
-  const long slot = blockIdx.x / NS;
-  const int j = static_cast<int>(blockIdx.x - slot * NS);
-  const int b = static_cast<int>(slot / rows), r = static_cast<int>(slot - static_cast<long>(b) * rows);
-  float T, p;
-  int k;
-  const void *row = filtered_row<DT>(target, draft, temps, lens, topk, topp, gamma, V, b, r, T, k, p);
-  if (!row) return;  // uniform per workgroup
-  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-  int M;
-  double s;
-  row_scale(part, slot, NS, M, s);
-  const float c = temp_scale(T), negM = -static_cast<float>(M);
-  __shared__ unsigned sc[kLevels];
-  __shared__ double sm[kLevels];
-  __shared__ RowPlan srp;
-  __shared__ unsigned long long red[kLBlock / kWave];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  if (tid < kLevels) {  // the row's levels, chunks merged in order
-    unsigned cs = 0;
-    double ms = 0.0;
-    for (int q = 0; q < NS; ++q) {
-      cs += fw.lv_cnt[(slot * NS + q) * kLevels + tid];
-      ms += fw.lv_mass[(slot * NS + q) * kLevels + tid];
-    }
-    sc[tid] = cs;
-    sm[tid] = ms;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    for (int l = 1; l < kLevels; ++l) {
-      sc[l] += sc[l - 1];
-      sm[l] += sm[l - 1];
-    }
-    srp = choose_levels(sc, sm, s, k, p);
-    if (j == 0) fw.plan[slot] = srp;
-  }
-  __syncthreads();
-  const RowPlan rp = srp;
-  if (rp.general) return;  // uniform per workgroup
-  const long nvec = (static_cast<long>(V) + Elem<DT>::kVec - 1) / Elem<DT>::kVec;
-  const long vb = static_cast<long>(j) * chunk_vecs, ve = min(vb + chunk_vecs, nvec);
-  unsigned long long above = 0;
-  unsigned *cand = fw.cand + slot * kFCap;
-  for_each_logit<DT, kLBlock, 8>(row, aligned, V, vb, ve,
-                                 [&](float m) { return level_of(m, c, negM) <= rp.l1; }, [&](float z) {
-    const int l = level_of(z, c, negM);
-    if (l < rp.l0) {
-      above += fixed_mass(z, c, negM, fs);
-    } else if (l <= rp.l1) {
-      const unsigned q = atomicAdd(&fw.ncand[slot], 1u);
-      if (q < static_cast<unsigned>(kFCap)) cand[q] = order_key(z);
-    }
-  });
-  // exact chunk sum (integer: the order of the additions does not matter)
+#pragma unroll 1
+    for (int u = 0; u < U; ++u) {
+      float x[kV];
+      widen_vec<DT>(raw[u], x);
+      float m = x[0];
 #pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) above += __shfl_xor(above, d);
-  if (lane == 0) red[wave] = above;
-  __syncthreads();
-  if (tid == 0) {
-    unsigned long long t = 0;
-    for (int w = 0; w < kLBlock / kWave; ++w) t += red[w];
-    fw.above[slot * NS + j] = t;
+      for (int e = 1; e < kV; ++e) m = fmaxf(m, x[e]);
+      if (!__ballot(level_of(m, c, negM) < kLevels)) continue;  // no lane of the wave has a candidate
+#pragma unroll
+      for (int e = 0; e < kV; ++e) offer(x[e]);
+    }
+  }
+  // the rest one by one (a partial last vector, or a row that is not aligned)
+  const long e0 = max(vb, vw) * kV, e1 = min(ve * kV, static_cast<long>(V));
+  for (long eb = e0; eb < e1; eb += kLBlock) {
+    const long e = eb + tid;
+    offer(e < e1 ? load_one<DT>(row, e) : -INFINITY);
+  }
+  // reserve the wave's range of the row's list and copy it out
+  unsigned *cnt = fw.ncand + slot;
+  unsigned *cand = fw.cand + slot * kGCap;
+  unsigned base = 0;
+  if (lane == 0 && wcount > 0)
+    base = atomicAdd(cnt, wcount <= static_cast<unsigned>(kWaveCap) ? wcount : static_cast<unsigned>(kGCap) + 1u);
+  base = static_cast<unsigned>(__shfl(static_cast<int>(base), 0));
+  if (wcount <= static_cast<unsigned>(kWaveCap)) {
+    for (unsigned i = lane; i < wcount; i += kWave)
+      if (base + i < static_cast<unsigned>(kGCap)) cand[base + i] = wbuf[wave][i];
   }
 }
 
-// FC: one workgroup per row.  Sorts the gathered logits and scans them from
-// the exact prefix above them; rows the plan marked, or whose crossing the
-// scan does not find (a margin exceeded), take the general path.
+// The cut for one criterion from a row's candidate list, whose histogram is in
+// sh.cnt0 / sh.mass0: the bin that reaches the target, its candidates sorted
+// and scanned from the prefix above it.  ok is false when that bin holds more
+// than kFCap candidates or the scan does not reach the target.
+__device__ float list_cut(const unsigned *cand, int n, float c, float negM, int fs, bool by_mass,
+                          unsigned long long target, unsigned long long &kept, bool &ok, GeneralShared &sh) {
+  const int tid = threadIdx.x;
+  unsigned long long bc, bm;
+  const int jb = find_cross(sh.cnt0, sh.mass0, kFBins + 1, by_mass, target, bc, bm, sh.sc);
+  if (sh.cnt0[jb] > static_cast<unsigned>(kFCap)) {  // uniform
+    ok = false;
+    return -INFINITY;
+  }
+  if (tid == 0) sh.sc.nkeys = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kFBlock) {
+    const unsigned key = cand[i];
+    if (ybin(key_value(key), c, negM) == jb) {
+      const unsigned q = atomicAdd(&sh.sc.nkeys, 1u);
+      if (q < static_cast<unsigned>(kFCap)) sh.u.keys[q] = key;
+    }
+  }
+  __syncthreads();
+  const int m = min(static_cast<int>(sh.sc.nkeys), kFCap);
+  sort_keys_desc(sh.u.keys, m);
+  return scan_sorted(sh.u.keys, m, bc, bm, by_mass, target, c, negM, fs, kept, ok, sh.sc);
+}
+
+// FC: one workgroup per row.  Resolves the cut from the row's candidates, or
+// by the general path.
 template <int DT>
 __global__ __launch_bounds__(kFBlock) void k_filter_resolve(
     const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
@@ -1652,24 +1579,37 @@ __global__ __launch_bounds__(kFBlock) void k_filter_resolve(
   const float c = temp_scale(T), negM = -static_cast<float>(M);
   __shared__ GeneralShared sh;
   const int tid = threadIdx.x;
-  const RowPlan rp = fw.plan[slot];
   float tau = -INFINITY;
   unsigned long long kept = 0;
   bool done = false;
-  if (!rp.general) {
-    const int n = min(static_cast<int>(fw.ncand[slot]), kFCap);
-    unsigned *keys = sh.u.keys;
-    for (int i = tid; i < n; i += kFBlock) keys[i] = fw.cand[slot * kFCap + i];
-    unsigned long long before_m = 0;
-    for (int q = 0; q < NS; ++q) before_m += fw.above[slot * NS + q];
-    sort_keys_desc(keys, n);  // begins with a barrier after its padding stores
-    const unsigned long long before_c = rp.count_above;
+  const unsigned ncap = fw.ncand[slot];
+  if (ncap <= static_cast<unsigned>(kGCap)) {
+    // exact histogram of the candidates: every logit with y > -kLevels
+    const int n = static_cast<int>(ncap);
+    const unsigned *cand = fw.cand + slot * kGCap;
+    for (int jb = tid; jb <= kFBins; jb += kFBlock) {
+      sh.cnt0[jb] = 0;
+      sh.mass0[jb] = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kFBlock) {
+      const float z = key_value(cand[i]);
+      const int jb = ybin(z, c, negM);
+      atomicAdd(&sh.cnt0[jb], 1u);
+      const unsigned long long m = fixed_mass(z, c, negM, fs);
+      if (m) atomicAdd(&sh.mass0[jb], m);
+    }
+    __syncthreads();
+    unsigned long long total_m = 0;
+    {
+      unsigned long long lm = 0, lc = 0, tc;
+      for (int jb = tid; jb <= kFBins; jb += kFBlock) lm += sh.mass0[jb];
+      wg_excl_scan2(lm, lc, total_m, tc, sh.sc.red);
+    }
     bool ok = true;
     if (k > 0) {
-      bool found;
-      tau = scan_sorted(keys, n, before_c, before_m, false, static_cast<unsigned long long>(k), c, negM, fs,
-                        kept, found, sh.sc);
-      ok = found;
+      if (static_cast<unsigned>(k) > ncap) ok = false;  // the k-th logit lies below the window
+      else tau = list_cut(cand, n, c, negM, fs, false, static_cast<unsigned long long>(k), kept, ok, sh);
     }
     if (ok && p < 1.0f) {
       // top-p of the top-k mass, or of the row's mass (K1's sum, in the same units)
@@ -1677,14 +1617,12 @@ __global__ __launch_bounds__(kFBlock) void k_filter_resolve(
       double t = ceil(static_cast<double>(p) * base);
       if (t < 1.0) t = 1.0;
       const unsigned long long tgt = static_cast<unsigned long long>(t);
-      if (before_m >= tgt) {
-        ok = false;  // the crossing lies above the gathered levels
+      if (total_m < tgt) {
+        ok = false;  // the crossing lies below the window
       } else {
-        bool found;
         unsigned long long kept_p;
-        const float tau_p = scan_sorted(keys, n, before_c, before_m, true, tgt, c, negM, fs, kept_p, found, sh.sc);
-        ok = found;
-        if (found && tau_p > tau) {
+        const float tau_p = list_cut(cand, n, c, negM, fs, true, tgt, kept_p, ok, sh);
+        if (ok && tau_p > tau) {
           tau = tau_p;
           kept = kept_p;
         }
@@ -2279,7 +2217,7 @@ struct Plan {
   long k1_groups, k3_groups;
   size_t part_off, zx_off, sel_off, sums_off, fst_off, total;
   // filtered calls: buffers of the filter kernels after `total`
-  size_t lvc_off, lvm_off, above_off, ncand_off, cand_off, plan_off, ftotal;
+  size_t ncand_off, cand_off, ftotal;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -2327,19 +2265,10 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV
   P->fst_off = off;
   off = align_up(off + sizeof(FilterStats) * static_cast<size_t>(slots));
   P->total = off;
-  const size_t chunks = static_cast<size_t>(P->k1_groups);
-  P->lvc_off = off;
-  off = align_up(off + sizeof(unsigned) * chunks * kLevels);
-  P->lvm_off = off;
-  off = align_up(off + sizeof(double) * chunks * kLevels);
-  P->above_off = off;
-  off = align_up(off + sizeof(unsigned long long) * chunks);
   P->ncand_off = off;
   off = align_up(off + sizeof(unsigned) * static_cast<size_t>(slots));
   P->cand_off = off;
-  off = align_up(off + sizeof(unsigned) * static_cast<size_t>(slots) * kFCap);
-  P->plan_off = off;
-  off = align_up(off + sizeof(RowPlan) * static_cast<size_t>(slots));
+  off = align_up(off + sizeof(unsigned) * static_cast<size_t>(slots) * kGCap);
   P->ftotal = off;
   return true;
 }
@@ -2349,14 +2278,15 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV
 template <int DT, int KIND>
 hipError_t launch_k1_kind(const void *target, const void *draft, const int32_t *tokens, const float *temps,
                           float scalar_T, const int32_t *lens, int gamma, int V, const Plan &P,
-                          Partial *part, float *zx, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                          Partial *part, float *zx, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
+                          unsigned *row_counter) {
   const dim3 grid(static_cast<unsigned>(P.k1_groups)), block(kBlock);
   if (ev0 && ev1) {
     hipExtLaunchKernelGGL((k1_row_stats<DT, kK1U, KIND>), grid, block, 0, st, ev0, ev1, 0, target, draft,
-                          tokens, temps, scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, part, zx);
+                          tokens, temps, scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, part, zx, row_counter);
   } else {
     hipLaunchKernelGGL((k1_row_stats<DT, kK1U, KIND>), grid, block, 0, st, target, draft, tokens, temps,
-                       scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, part, zx);
+                       scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, part, zx, row_counter);
   }
   return hipGetLastError();
 }
@@ -2364,15 +2294,16 @@ hipError_t launch_k1_kind(const void *target, const void *draft, const int32_t *
 template <int DT>
 hipError_t launch_k1(const void *target, const void *draft, const int32_t *tokens, const float *temps,
                      float scalar_T, const int32_t *lens, int gamma, int V, const Plan &P, Partial *part,
-                     float *zx, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                     float *zx, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
+                     unsigned *row_counter = nullptr) {
   if (temps)
     return launch_k1_kind<DT, kMixed>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx,
-                                      st, ev0, ev1);
+                                      st, ev0, ev1, row_counter);
   if (scalar_T > 0.0f)
     return launch_k1_kind<DT, kStochasticOnly>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P,
-                                               part, zx, st, ev0, ev1);
+                                               part, zx, st, ev0, ev1, row_counter);
   return launch_k1_kind<DT, kGreedyOnly>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx,
-                                         st, ev0, ev1);
+                                         st, ev0, ev1, row_counter);
 }
 
 // fractional bits of the filter's fixed-point masses: V * 2^(fs + 1) <= 2^62
@@ -2396,25 +2327,19 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
   sv_debug dbg;
   memset(&dbg, 0, sizeof dbg);
   if (dbgp) dbg = *dbgp;
+  unsigned *ncand = fst ? reinterpret_cast<unsigned *>(base + P.ncand_off) : nullptr;
   hipError_t e = launch_k1<DT>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx, st,
                                static_cast<hipEvent_t>(dbg.k1_events[0]),
-                               static_cast<hipEvent_t>(dbg.k1_events[1]));
+                               static_cast<hipEvent_t>(dbg.k1_events[1]), ncand);
   if (e != hipSuccess) return SV_EHIP;
   if (fst) {
     FilterWork fw;
-    fw.lv_cnt = reinterpret_cast<unsigned *>(base + P.lvc_off);
-    fw.lv_mass = reinterpret_cast<double *>(base + P.lvm_off);
-    fw.above = reinterpret_cast<unsigned long long *>(base + P.above_off);
-    fw.ncand = reinterpret_cast<unsigned *>(base + P.ncand_off);
+    fw.ncand = ncand;
     fw.cand = reinterpret_cast<unsigned *>(base + P.cand_off);
-    fw.plan = reinterpret_cast<RowPlan *>(base + P.plan_off);
     const int fs = filter_frac_bits(V);
     const dim3 cgrid(static_cast<unsigned>(P.k1_groups)), rgrid(static_cast<unsigned>(static_cast<long>(B) * P.rows));
-    hipLaunchKernelGGL((k_filter_levels<DT>), cgrid, dim3(kLBlock), 0, st, target, draft, temps, lens, topk, topp,
+    hipLaunchKernelGGL((k_filter_capture<DT>), cgrid, dim3(kLBlock), 0, st, target, draft, temps, lens, topk, topp,
                        gamma, V, P.NS, P.chunk_vecs, part, fw);
-    if (hipGetLastError() != hipSuccess) return SV_EHIP;
-    hipLaunchKernelGGL((k_filter_gather<DT>), cgrid, dim3(kLBlock), 0, st, target, draft, temps, lens, topk, topp,
-                       gamma, V, P.NS, P.chunk_vecs, fs, part, fw);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
     hipLaunchKernelGGL((k_filter_resolve<DT>), rgrid, dim3(kFBlock), 0, st, target, draft, temps, lens, topk, topp,
                        gamma, V, P.NS, fs, part, fw, fst);
