@@ -125,8 +125,8 @@ def summarize_profile(root: str):
               "k1_row_stats<bf16, stochastic>, k2_decide_mass<bf16, plain> and k3_select<bf16, plain>; "
               "the K1 timing pass (spec_verify_ex) runs k1_row_stats<bf16, per-request T>; the filtered "
               "measurement (spec_verify_filtered, T = 0.7, top_p = 0.9 with and without top_k = 50) runs "
-              "k1_row_stats<bf16, per-request T>, k_filter_capture, k_filter_resolve and the "
-              "filtered k2 / k3; the tree measurement (spec_verify_tree, 8 trees of width 4 and depth 3) runs "
+              "k1_row_stats<bf16, per-request T>, k_filter_capture, k_filter_deep_count (with top_k = 50), "
+              "k_filter_resolve, k_filter_general and the filtered k2 / k3; the tree measurement (spec_verify_tree, 8 trees of width 4 and depth 3) runs "
               "k1_row_stats<bf16, per-request T> and k_tree_walk; the draft-side sampling measurement runs "
               "k_sample_rows.  The copy kernels "
               "are the benchmark's set-up (input copies), outside the timed region.", ""]

@@ -35,8 +35,9 @@
 //                       crosses u*Z, then the token inside it.
 //
 // Extensions, on the same row statistics:
-//   top-k / top-p       k_filter_capture, k_filter_resolve
-//                       between K1 and K2 find each filtered row's cut; K2 and
+//   top-k / top-p       k_filter_capture, k_filter_deep_count, k_filter_resolve,
+//                       k_filter_general between K1 and K2 find each filtered
+//                       row's cut; K2 and
 //                       K3 are instantiated with the cut compares.
 //   tree of drafts      K1 over every tree position, then k_tree_walk (one
 //                       workgroup per request).
@@ -276,11 +277,11 @@ __device__ __forceinline__ void fold_tile(const u32x4 *v, float c, int &M, doubl
 // Every lane loads (indices are clamped into the chunk, so the code is straight
 // line and the compiler can wait for exactly the older tile); lanes past v1
 // then hold -inf.
-template <int DT, int U>
+template <int DT, int U, int BS = kBlock>
 __device__ __forceinline__ void load_tile(const u32x4 *rv, int t0, int v1, int tid, u32x4 *dst) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int vi = t0 + u * kBlock + tid;
+    const int vi = t0 + u * BS + tid;
     const u32x4 x = load_nt(rv + min(vi, v1 - 1));
     dst[u] = (vi < v1) ? x : neg_inf_vec<DT>();
   }
@@ -289,18 +290,18 @@ __device__ __forceinline__ void load_tile(const u32x4 *rv, int t0, int v1, int t
 // Streams the vectors [v0, v1) of a row in tiles of U vectors per thread with
 // two register buffers: the next tile is in flight while the current one is
 // folded.  fold(tile, t0) sees each tile once, in order.
-template <int DT, int U, typename Fold>
+template <int DT, int U, int BS = kBlock, typename Fold>
 __device__ __forceinline__ void stream_chunk(const u32x4 *rv, int v0, int v1, int tid, Fold &&fold) {
-  constexpr int kTileVecs = U * kBlock;
+  constexpr int kTileVecs = U * BS;
   if (v0 >= v1) return;
   u32x4 a[U], b[U];
-  load_tile<DT, U>(rv, v0, v1, tid, a);
+  load_tile<DT, U, BS>(rv, v0, v1, tid, a);
   for (int t0 = v0;;) {
-    load_tile<DT, U>(rv, t0 + kTileVecs, v1, tid, b);
+    load_tile<DT, U, BS>(rv, t0 + kTileVecs, v1, tid, b);
     fold(a, t0);
     t0 += kTileVecs;
     if (t0 >= v1) break;
-    load_tile<DT, U>(rv, t0 + kTileVecs, v1, tid, a);
+    load_tile<DT, U, BS>(rv, t0 + kTileVecs, v1, tid, a);
     fold(b, t0);
     t0 += kTileVecs;
     if (t0 >= v1) break;
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
 // renormalised rows: K2 and K3 treat z < tau as probability zero and use the
 // kept mass in place of the row sum.
 //
-// Two kernels between K1 and K2.  A token's mass is e(z) = 2^(z c - M) with
+// Four kernels between K1 and K2.  A token's mass is e(z) = 2^(z c - M) with
 // the row's integer M from K1; exact sums use the fixed-point integer
 // floor(e * 2^fs), fs = 61 - ceil(log2 V), so that they do not depend on the
 // order of the additions and a whole row fits 64 bits.
@@ -471,15 +472,21 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
 //       within 16 binary orders of magnitude of 2^M (y = z c - M > -16) to the
 //       row's candidate list (wave-aggregated slot reservations); a vector
 //       whose largest logit is below that is skipped after one test.
+//   FD  k_filter_deep_count (K1's chunks of the top-k rows that captured
+//       fewer than k logits, whose k-th logit lies below the window): counts of
+//       the logits in the bands between the floors y = -18, -20, ..., -40.
 //   FC  k_filter_resolve (one workgroup per row): an exact (count, fixed-point
 //       mass) histogram of the candidates over 1/32-order bins finds the bin
 //       holding the k-th largest logit or the top-p crossing (the candidates
 //       are every logit above the window's floor, so the prefixes from the top
 //       are exact); that bin's candidates are sorted and scanned group by
 //       group.  The top-p target is top_p times the exact top-k mass, or times
-//       K1's row sum without top-k.
-// A row takes FC's general path when it captured more than kGCap logits, or
-// when the k-th logit or the crossing lies below the window:
+//       K1's row sum without top-k.  For a row FD counted, the list is first
+//       replaced by a deeper one: the shallowest floor that holds the k-th
+//       logit with at most kFCap logits, captured by one pass over the row.
+//   FE  k_filter_general (one workgroup per row FC could not resolve: more
+//       than kGCap logits captured, a crowded bin, a top-p crossing below the
+//       window, or no deeper floor that qualifies):
 //   pass 1   exact (count, fixed-point mass) histogram over 2048 bins of y,
 //            each 1/32 of a binary order of magnitude, down to y = -64, and
 //            one bin below;
@@ -499,6 +506,7 @@ constexpr int kFBins = 2048;  // general path: y bins; index kFBins collects y <
 constexpr int kFCap = 4096;   // logits sorted and scanned in LDS
 constexpr int kLevels = 16;   // the capture window: levels of one binary order of magnitude below 2^M
 constexpr int kGCap = 8192;   // logits a row may capture
+constexpr int kDeep = 12;     // deeper floors y = -18, -20, ..., -40 (FD, FC)
 
 struct alignas(16) FilterStats {
   double s_kept;  // sum of 2^(z c - M) over the kept tokens
@@ -508,8 +516,9 @@ struct alignas(16) FilterStats {
 
 // Device buffers of the filter kernels (inside the workspace).
 struct FilterWork {
-  unsigned *ncand;  // [slots] logits captured (cleared by K1)
-  unsigned *cand;   // [slots][kGCap] their order keys
+  unsigned *ncand;   // [slots] logits captured (cleared by K1)
+  unsigned *cand;    // [slots][kGCap] their order keys
+  unsigned *dcount;  // [slots][NS][kDeep + 1] FD's per-chunk counts above the floors
 };
 
 // Whether request b filters, with its k (0: none) and p (1: none).  Values
@@ -1094,6 +1103,10 @@ struct GeneralShared {
       unsigned long long mass1[kFBins];
     } h;
     unsigned keys[kFCap];  // gathered logits (order keys)
+    struct {  // deeper windows: the row's band counts, then capture counts
+      unsigned tot[kDeep + 1];
+      unsigned wc[kFWaves];
+    } d;
   } u;
   FilterScratch sc;
 };
@@ -1191,56 +1204,47 @@ __device__ int find_cross(const unsigned *cnt, const unsigned long long *mass, i
 // Calls f(z) for every logit of the vectors [vb, ve) of a row (16-byte
 // vectors; the row's last vector may be partial).  Whole vectors of an aligned
 // row stream with U loads per thread per step, the next step's loads issued
-// before the current step is processed; the partial tail, and every logit of
-// an unaligned row, are read one by one.  keep(m) is asked with the largest
-// logit m of each whole vector; a vector for which it answers false is skipped
-// (for a test that is monotone in the logit this skips exactly the vectors
-// none of whose logits would pass it).
+// before the current step is processed (stream_chunk: every lane issues every
+// load, indices clamped into the range, so the compiler waits for exactly the
+// older step).  The partial tail, and every logit of an
+// unaligned row, are read one by one.  keep(m) is asked with the largest logit
+// m of each whole vector; a vector for which it answers false is skipped (for
+// a test that is monotone in the logit this skips exactly the vectors none of
+// whose logits would pass it).  Lanes leave the loops in decreasing order of
+// their index: lane 0 of a wave is active whenever any lane of it is.
 template <int DT, int BS, int U, typename K, typename F>
 __device__ __forceinline__ void for_each_logit(const void *row, bool aligned, int V, long vb, long ve, K &&keep,
                                                F &&f) {
   constexpr int kV = Elem<DT>::kVec;
-  constexpr long kStep = static_cast<long>(U) * BS;
   const char *r = static_cast<const char *>(row);
   const long e_end = min(ve * kV, static_cast<long>(V));
   long e_tail = vb * kV;  // first logit left to the one-by-one loop
   if (aligned) {
-    const long vw = min(ve, static_cast<long>(V) / kV);  // whole vectors in range
-    auto load = [&](long v0, u32x4 *dst) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const long v = v0 + static_cast<long>(u) * BS;
-        dst[u] = v < vw ? *reinterpret_cast<const u32x4 *>(r + v * kV * Elem<DT>::kBytes) : neg_inf_vec<DT>();
-      }
-    };
-    u32x4 cur[U], nxt[U];
-    long v0 = vb + threadIdx.x;
-    if (v0 < vw) load(v0, cur);
-    for (; v0 < vw; v0 += kStep) {
-      if (v0 + kStep < vw) load(v0 + kStep, nxt);
+    const int vw = static_cast<int>(min(ve, static_cast<long>(V) / kV));  // whole vectors in range
+    const int tid = threadIdx.x;
+    stream_chunk<DT, U, BS>(reinterpret_cast<const u32x4 *>(r), static_cast<int>(vb), vw, tid,
+                            [&](const u32x4 *tile, int t0) {
 #pragma unroll 1
-      for (int u = 0; u < U; ++u) {
-        if (v0 + static_cast<long>(u) * BS >= vw) break;
-        float x[kV];
-        widen_vec<DT>(cur[u], x);
-        float m = x[0];
+                              for (int u = 0; u < U; ++u) {
+                                if (t0 + u * BS + tid >= vw) break;
+                                float x[kV];
+                                widen_vec<DT>(tile[u], x);
+                                float m = x[0];
 #pragma unroll
-        for (int e = 1; e < kV; ++e) m = fmaxf(m, x[e]);
-        if (!keep(m)) continue;
+                                for (int e = 1; e < kV; ++e) m = fmaxf(m, x[e]);
+                                if (!keep(m)) continue;
 #pragma unroll
-        for (int e = 0; e < kV; ++e) f(x[e]);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-    }
-    e_tail = max(vb, vw) * kV;
+                                for (int e = 0; e < kV; ++e) f(x[e]);
+                              }
+                            });
+    e_tail = max(vb, static_cast<long>(vw)) * kV;
   }
   for (long e = e_tail + threadIdx.x; e < e_end; e += BS) f(load_one<DT>(row, e));
 }
 
 template <int DT, typename F>
 __device__ __forceinline__ void for_each_logit(const void *row, bool aligned, int V, F &&f) {
-  for_each_logit<DT, kFBlock, 4>(row, aligned, V, 0, (static_cast<long>(V) + Elem<DT>::kVec - 1) / Elem<DT>::kVec,
+  for_each_logit<DT, kFBlock, 8>(row, aligned, V, 0, (static_cast<long>(V) + Elem<DT>::kVec - 1) / Elem<DT>::kVec,
                                  [](float) { return true; }, static_cast<F &&>(f));
 }
 
@@ -1459,7 +1463,6 @@ __global__ __launch_bounds__(kLBlock) void k_filter_capture(
     int gamma, int V, int NS, int chunk_vecs, const Partial *__restrict__ part, FilterWork fw) {
   constexpr int kV = Elem<DT>::kVec;
   constexpr int U = 8;
-  constexpr long kStep = static_cast<long>(U) * kLBlock;
   const int rows = 2 * gamma + 1;
   const long slot = blockIdx.x / NS;
   const int j = static_cast<int>(blockIdx.x - slot * NS);
@@ -1490,26 +1493,24 @@ __global__ __launch_bounds__(kLBlock) void k_filter_capture(
   const long nvec = (static_cast<long>(V) + kV - 1) / kV;
   const long vb = static_cast<long>(j) * chunk_vecs, ve = min(vb + chunk_vecs, nvec);
   const long vw = aligned ? min(ve, static_cast<long>(V) / kV) : vb;  // whole 16-byte vectors
-  // whole vectors: the same trip count in every lane; out-of-range vectors read as -inf
-  for (long base = vb; base < vw; base += kStep) {
-    u32x4 raw[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long v = base + static_cast<long>(u) * kLBlock + tid;
-      raw[u] = v < vw ? *reinterpret_cast<const u32x4 *>(rb + v * kV * Elem<DT>::kBytes) : neg_inf_vec<DT>();
-    }
+  // whole vectors (K1's streaming: non-temporal loads, the next tile in flight
+  // while this one is examined): the same trip count in every lane, and
+  // out-of-range vectors read as -inf
+  stream_chunk<DT, U, kLBlock>(reinterpret_cast<const u32x4 *>(rb), static_cast<int>(vb), static_cast<int>(vw), tid,
+                               [&](const u32x4 *tile, int) {
 #pragma unroll 1
-    for (int u = 0; u < U; ++u) {
-      float x[kV];
-      widen_vec<DT>(raw[u], x);
-      float m = x[0];
+                                 for (int u = 0; u < U; ++u) {
+                                   float x[kV];
+                                   widen_vec<DT>(tile[u], x);
+                                   float m = x[0];
 #pragma unroll
-      for (int e = 1; e < kV; ++e) m = fmaxf(m, x[e]);
-      if (!__ballot(level_of(m, c, negM) < kLevels)) continue;  // no lane of the wave has a candidate
+                                   for (int e = 1; e < kV; ++e) m = fmaxf(m, x[e]);
+                                   // no lane of the wave has a candidate
+                                   if (!__ballot(level_of(m, c, negM) < kLevels)) continue;
 #pragma unroll
-      for (int e = 0; e < kV; ++e) offer(x[e]);
-    }
-  }
+                                   for (int e = 0; e < kV; ++e) offer(x[e]);
+                                 }
+                               });
   // the rest one by one (a partial last vector, or a row that is not aligned)
   const long e0 = max(vb, vw) * kV, e1 = min(ve * kV, static_cast<long>(V));
   for (long eb = e0; eb < e1; eb += kLBlock) {
@@ -1557,123 +1558,392 @@ __device__ float list_cut(const unsigned *cand, int n, float c, float negM, int 
   return scan_sorted(sh.u.keys, m, bc, bm, by_mass, target, c, negM, fs, kept, ok, sh.sc);
 }
 
-// FC: one workgroup per row.  Resolves the cut from the row's candidates, or
-// by the general path.
+// The cut of a row from a list that holds every logit above some floor y = -L
+// (L <= 64): an exact histogram of the list, then the count criterion (top-k)
+// and the mass criterion (top-p of the top-k mass, or of K1's row sum s).
+// Returns false when the list cannot decide the cut; short_list is then true
+// when the k-th logit or the crossing lies below the floor.  list_mass receives
+// the list's fixed-point mass.
+__device__ bool list_resolve(const unsigned *cand, int n, float c, float negM, int fs, int k, float p, double s,
+                             float &tau, unsigned long long &kept, unsigned long long &list_mass, bool &short_list,
+                             GeneralShared &sh) {
+  const int tid = threadIdx.x;
+  tau = -INFINITY;
+  kept = 0;
+  short_list = false;
+  for (int jb = tid; jb <= kFBins; jb += kFBlock) {
+    sh.cnt0[jb] = 0;
+    sh.mass0[jb] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kFBlock) {
+    const float z = key_value(cand[i]);
+    const int jb = ybin(z, c, negM);
+    atomicAdd(&sh.cnt0[jb], 1u);
+    const unsigned long long m = fixed_mass(z, c, negM, fs);
+    if (m) atomicAdd(&sh.mass0[jb], m);
+  }
+  __syncthreads();
+  unsigned long long total_m = 0;
+  {
+    unsigned long long lm = 0, lc = 0, tc;
+    for (int jb = tid; jb <= kFBins; jb += kFBlock) lm += sh.mass0[jb];
+    wg_excl_scan2(lm, lc, total_m, tc, sh.sc.red);
+  }
+  list_mass = total_m;
+  bool ok = true;
+  if (k > 0) {
+    if (k > n) {  // the k-th logit lies below the floor
+      ok = false;
+      short_list = true;
+    } else {
+      tau = list_cut(cand, n, c, negM, fs, false, static_cast<unsigned long long>(k), kept, ok, sh);
+    }
+  }
+  if (ok && p < 1.0f) {
+    // top-p of the top-k mass, or of the row's mass (K1's sum, in the same units)
+    const double base = k > 0 ? static_cast<double>(kept) : ldexp(s, fs);
+    double t = ceil(static_cast<double>(p) * base);
+    if (t < 1.0) t = 1.0;
+    const unsigned long long tgt = static_cast<unsigned long long>(t);
+    if (total_m < tgt) {  // the crossing lies below the floor
+      ok = false;
+      short_list = true;
+    } else {
+      unsigned long long kept_p;
+      const float tau_p = list_cut(cand, n, c, negM, fs, true, tgt, kept_p, ok, sh);
+      if (ok && tau_p > tau) {
+        tau = tau_p;
+        kept = kept_p;
+      }
+    }
+  }
+  __syncthreads();
+  return ok;
+}
+
+__device__ __forceinline__ int deep_level(int j) { return kLevels + 2 * (j + 1); }
+
+// f(z) for every logit of a row, in control flow that is uniform over the
+// workgroup: whole vectors of an aligned row stream as in K1 (out-of-range
+// vectors read as -inf), the rest one by one with -inf past the row's end.
+template <int DT, int U, typename F>
+__device__ __forceinline__ void for_each_logit_uniform(const void *row, bool aligned, int V, F &&f) {
+  constexpr int kV = Elem<DT>::kVec;
+  const int tid = threadIdx.x;
+  const int vw = aligned ? V / kV : 0;
+  stream_chunk<DT, U, kFBlock>(reinterpret_cast<const u32x4 *>(row), 0, vw, tid, [&](const u32x4 *tile, int) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[kV];
+      widen_vec<DT>(tile[u], x);
+#pragma unroll
+      for (int e = 0; e < kV; ++e) f(x[e]);
+    }
+  });
+  for (long eb = static_cast<long>(vw) * kV; eb < V; eb += kFBlock) {
+    const long e = eb + tid;
+    f(e < V ? load_one<DT>(row, e) : -INFINITY);
+  }
+}
+
+// Per-thread counts of the logits of vectors [vb, vw) (whole 16-byte vectors of
+// an aligned row, streamed as in K1) and elements [e0, e1) (one by one) in the
+// bands between the deeper floors: band b holds the logits with
+// floor(-y/2 - 8) = b, clamped to [0, kDeep] (b = 0: above y = -18, the first
+// deeper floor; b = kDeep: at or below y = -40), so that the count above floor
+// j (y > -(18 + 2 j)) is the sum of bands 0..j.  -y/2 - 8 is exact for
+// y > -64, so each band test agrees with the compare y > -L.  A logit costs
+// a handful of operations: its band's one-hot nibble is added to a 64-bit
+// word, which is spread into byte counters once per vector and into 32-bit
+// counters once per tile.
+template <int DT, int BS, int U>
+__device__ __forceinline__ void count_bands(const void *row, int vb, int vw, long e0, long e1, float c, float negM,
+                                            unsigned *cnt) {
+  constexpr int kV = Elem<DT>::kVec;
+  constexpr unsigned long long kLow = 0x0F0F0F0F0F0F0F0Full;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j <= kDeep; ++j) cnt[j] = 0;
+  auto nibble = [&](float z) {
+    const float q = fmaf(fmaf(z, c, negM), -0.5f, -8.0f);
+    const int b = static_cast<int>(fminf(fmaxf(floorf(q), 0.0f), static_cast<float>(kDeep)));
+    return 1ull << (4 * b);
+  };
+  // even bands in the bytes of ev, odd bands in the bytes of od
+  auto spread = [&](unsigned long long nib, unsigned long long &ev, unsigned long long &od) {
+    ev += nib & kLow;
+    od += (nib >> 4) & kLow;
+  };
+  auto flush = [&](unsigned long long ev, unsigned long long od) {
+#pragma unroll
+    for (int j = 0; j <= kDeep; ++j)
+      cnt[j] += static_cast<unsigned>(((j & 1) ? od : ev) >> (8 * (j >> 1))) & 0xFFu;
+  };
+  stream_chunk<DT, U, BS>(reinterpret_cast<const u32x4 *>(row), vb, vw, tid, [&](const u32x4 *tile, int) {
+    unsigned long long ev = 0, od = 0;  // at most U * kV <= 64 per byte
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[kV];
+      widen_vec<DT>(tile[u], x);
+      unsigned long long nib = 0;  // at most kV <= 8 per nibble
+#pragma unroll
+      for (int e = 0; e < kV; ++e) nib += nibble(x[e]);
+      spread(nib, ev, od);
+    }
+    flush(ev, od);
+  });
+  for (long eb = e0; eb < e1; eb += BS) {
+    const long e = eb + tid;
+    if (e < e1) {
+      unsigned long long ev = 0, od = 0;
+      spread(nibble(load_one<DT>(row, e)), ev, od);
+      flush(ev, od);
+    }
+  }
+}
+
+// The floor for the deeper list from the row's band counts band[0..kDeep]:
+// the level count L of the shallowest floor whose logits include the k-th
+// largest, provided that floor holds at most kFCap logits; 0 otherwise.
+__device__ __forceinline__ int choose_floor(const unsigned *band, int k) {
+  unsigned C = 0;  // logits above floor j
+  for (int j = 0; j < kDeep; ++j) {
+    C += band[j];
+    if (C >= static_cast<unsigned>(k)) return C <= static_cast<unsigned>(kFCap) ? deep_level(j) : 0;
+  }
+  return 0;
+}
+
+// Second pass: every logit with y > -L goes to the row's list.  Each wave
+// fills its own part of the list (slots from a ballot, a scalar count), then
+// the parts are packed to the front of the list through LDS.  Returns the
+// list's length, or kGCap + 1 when a wave's part overflowed.
+template <int DT>
+__device__ unsigned deep_capture(const void *row, bool aligned, int V, float c, float negM, int L,
+                                 unsigned *cand, GeneralShared &sh) {
+  constexpr unsigned kPart = kGCap / kFWaves;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const float floor_y = -static_cast<float>(L);
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  unsigned *part = cand + wave * kPart;
+  unsigned wcount = 0;  // the same in every lane of the wave
+  for_each_logit_uniform<DT, 8>(row, aligned, V, [&](float z) {
+    const bool in = fmaf(z, c, negM) > floor_y;
+    const unsigned long long mask = __ballot(in);
+    if (in) {
+      const unsigned q = wcount + static_cast<unsigned>(__popcll(mask & lt));
+      if (q < kPart) part[q] = order_key(z);
+    }
+    wcount += static_cast<unsigned>(__popcll(mask));
+  });
+  if (lane == 0) sh.u.d.wc[wave] = wcount;
+  __syncthreads();
+  unsigned total = 0, before = 0;
+  bool over = false;
+  for (int w = 0; w < kFWaves; ++w) {
+    const unsigned nw = sh.u.d.wc[w];
+    if (w < wave) before += nw;
+    total += nw;
+    over = over || nw > kPart;
+  }
+  __syncthreads();
+  if (over || total > static_cast<unsigned>(kFCap)) return static_cast<unsigned>(kGCap) + 1u;
+  for (unsigned i = lane; i < wcount; i += kWave) sh.u.keys[before + i] = part[i];
+  __syncthreads();
+  for (unsigned i = tid; i < total; i += kFBlock) cand[i] = sh.u.keys[i];
+  __syncthreads();
+  return total;
+}
+
+// Row setup shared by the filter kernels after FG: the row (nullptr when it
+// is not filtered), its alignment, M and K1's row sum.
+struct FilterRow {
+  const void *row;
+  bool aligned;
+  int k;
+  float p, c, negM;
+  double s;
+};
+
+template <int DT>
+__device__ __forceinline__ FilterRow filter_row_setup(const void *target, const void *draft, const float *temps,
+                                                      const int32_t *lens, const int32_t *topk, const float *topp,
+                                                      int gamma, int V, int NS, const Partial *part, long slot) {
+  const int rows = 2 * gamma + 1;
+  const int b = static_cast<int>(slot / rows), r = static_cast<int>(slot - static_cast<long>(b) * rows);
+  FilterRow fr;
+  float T;
+  fr.row = filtered_row<DT>(target, draft, temps, lens, topk, topp, gamma, V, b, r, T, fr.k, fr.p);
+  if (!fr.row) return fr;
+  fr.aligned = (reinterpret_cast<uintptr_t>(fr.row) & 15u) == 0;
+  int M;
+  row_scale(part, slot, NS, M, fr.s);
+  fr.c = temp_scale(T);
+  fr.negM = -static_cast<float>(M);
+  return fr;
+}
+
+// FilterStats.pad after FC: 0 resolved, 1 pending for the general path (FE).
+enum { kFResolved = 0, kFGeneral = 1 };
+
+__device__ __forceinline__ void store_filter_stats(FilterStats *fst, long slot, unsigned long long kept, int fs,
+                                                   float tau, int state) {
+  if (threadIdx.x == 0) {
+    FilterStats f;
+    f.s_kept = ldexp(static_cast<double>(kept), -fs);
+    f.tau = tau;
+    f.pad = state;
+    fst[slot] = f;
+  }
+}
+
+// Whether row `slot` is filtered and FC left it in `state`.  The
+// stats are read only for filtered rows (the others are never written).
+__device__ __forceinline__ bool filter_pending(const float *temps, const int32_t *lens, const int32_t *topk,
+                                               const float *topp, int gamma, int V, long slot,
+                                               const FilterStats *fst, int state) {
+  const int rows = 2 * gamma + 1;
+  const int b = static_cast<int>(slot / rows), r = static_cast<int>(slot - static_cast<long>(b) * rows);
+  int k;
+  float p;
+  if (!(temps[b] > 0.0f) || !request_filter(topk, topp, b, V, k, p)) return false;
+  const int g = request_len(lens, gamma, b);
+  if (r <= gamma ? r > g : r - gamma - 1 >= g) return false;
+  return fst[slot].pad == state;
+}
+
+// Whether top-k row `slot` captured fewer logits than k (its k-th logit lies
+// below the capture window): FD counts it, FC takes a deeper list.
+__device__ __forceinline__ bool needs_deeper(int k, const FilterWork &fw, long slot) {
+  return k > 0 && fw.ncand[slot] < static_cast<unsigned>(k);
+}
+
+// FD: K1's chunks of every top-k row whose k-th logit lies below the capture
+// window (fewer than k logits captured): each chunk's counts above the floors.
+template <int DT>
+__global__ __launch_bounds__(kLBlock) void k_filter_deep_count(
+    const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
+    const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
+    int gamma, int V, int NS, int chunk_vecs, const Partial *__restrict__ part, FilterWork fw) {
+  constexpr int kV = Elem<DT>::kVec;
+  const long slot = blockIdx.x / NS;
+  const int j = static_cast<int>(blockIdx.x - slot * NS);
+  const FilterRow fr = filter_row_setup<DT>(target, draft, temps, lens, topk, topp, gamma, V, NS, part, slot);
+  if (!fr.row || !needs_deeper(fr.k, fw, slot)) return;  // uniform per workgroup
+  // the chunk's whole vectors, then its remaining elements (the capture kernel's split)
+  const long nvec = (static_cast<long>(V) + kV - 1) / kV;
+  const long vb = static_cast<long>(j) * chunk_vecs, ve = min(vb + chunk_vecs, nvec);
+  const long vw = fr.aligned ? min(ve, static_cast<long>(V) / kV) : vb;
+  const long e0 = max(vb, vw) * kV, e1 = min(ve * kV, static_cast<long>(V));
+  unsigned cnt[kDeep + 1];
+  count_bands<DT, kLBlock, 8>(fr.row, static_cast<int>(vb), static_cast<int>(vw), e0, e1, fr.c, fr.negM, cnt);
+  __shared__ unsigned wcnt[kLBlock / kWave][kDeep + 1];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int f = 0; f <= kDeep; ++f) {
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off /= 2)
+      cnt[f] += static_cast<unsigned>(__shfl_xor(static_cast<int>(cnt[f]), off));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int f = 0; f <= kDeep; ++f) wcnt[wave][f] = cnt[f];
+  }
+  __syncthreads();
+  if (threadIdx.x <= kDeep) {
+    unsigned t = 0;
+    for (int w = 0; w < kLBlock / kWave; ++w) t += wcnt[w][threadIdx.x];
+    fw.dcount[(slot * NS + j) * (kDeep + 1) + threadIdx.x] = t;
+  }
+}
+
+// FC: one workgroup per row.  Resolves the cut from the row's captured list,
+// or, for a top-k row whose k-th logit lies below the window, from a deeper
+// list: the floor from FD's counts, a capture pass, the list resolve.  Rows it
+// cannot resolve are left for FE.
 template <int DT>
 __global__ __launch_bounds__(kFBlock) void k_filter_resolve(
     const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
     const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
     int gamma, int V, int NS, int fs, const Partial *__restrict__ part, FilterWork fw,
     FilterStats *__restrict__ fst) {
-  const int rows = 2 * gamma + 1;
   const long slot = blockIdx.x;
-  const int b = static_cast<int>(slot / rows), r = static_cast<int>(slot - static_cast<long>(b) * rows);
-  float T, p;
-  int k;
-  const void *row = filtered_row<DT>(target, draft, temps, lens, topk, topp, gamma, V, b, r, T, k, p);
-  if (!row) return;  // uniform per workgroup
-  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-  int M;
-  double s;
-  row_scale(part, slot, NS, M, s);
-  const float c = temp_scale(T), negM = -static_cast<float>(M);
+  const FilterRow fr = filter_row_setup<DT>(target, draft, temps, lens, topk, topp, gamma, V, NS, part, slot);
+  if (!fr.row) return;  // uniform per workgroup
+  __shared__ GeneralShared sh;
+  float tau = -INFINITY;
+  unsigned long long kept = 0, list_mass;
+  bool done = false, short_list;
+  unsigned *cand = fw.cand + slot * kGCap;
+  unsigned n = fw.ncand[slot];
+  if (needs_deeper(fr.k, fw, slot)) {
+    if (threadIdx.x <= kDeep) {
+      unsigned t = 0;
+      for (int j = 0; j < NS; ++j) t += fw.dcount[(slot * NS + j) * (kDeep + 1) + threadIdx.x];
+      sh.u.d.tot[threadIdx.x] = t;
+    }
+    __syncthreads();
+    const int L = choose_floor(sh.u.d.tot, fr.k);
+    __syncthreads();
+    n = L > 0 ? deep_capture<DT>(fr.row, fr.aligned, V, fr.c, fr.negM, L, cand, sh) : kGCap + 1u;
+  }
+  if (n <= static_cast<unsigned>(kGCap))
+    done = list_resolve(cand, static_cast<int>(n), fr.c, fr.negM, fs, fr.k, fr.p, fr.s, tau, kept, list_mass,
+                        short_list, sh);
+  store_filter_stats(fst, slot, kept, fs, tau, done ? kFResolved : kFGeneral);
+}
+
+// FE: one workgroup per row still pending: the general path.
+template <int DT>
+__global__ __launch_bounds__(kFBlock) void k_filter_general(
+    const void *__restrict__ target, const void *__restrict__ draft, const float *__restrict__ temps,
+    const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
+    int gamma, int V, int NS, int fs, const Partial *__restrict__ part, FilterStats *__restrict__ fst) {
+  const long slot = blockIdx.x;
+  if (!filter_pending(temps, lens, topk, topp, gamma, V, slot, fst, kFGeneral)) return;  // uniform
+  const FilterRow fr = filter_row_setup<DT>(target, draft, temps, lens, topk, topp, gamma, V, NS, part, slot);
+  const void *row = fr.row;
+  const bool aligned = fr.aligned;
+  const int k = fr.k;
+  const float p = fr.p, c = fr.c, negM = fr.negM;
   __shared__ GeneralShared sh;
   const int tid = threadIdx.x;
+  for (int jb = tid; jb <= kFBins; jb += kFBlock) {
+    sh.cnt0[jb] = 0;
+    sh.mass0[jb] = 0;
+  }
+  __syncthreads();
+  for_each_logit<DT>(row, aligned, V, [&](float z) {
+    const int jb = ybin(z, c, negM);
+    atomicAdd(&sh.cnt0[jb], 1u);
+    const unsigned long long m = fixed_mass(z, c, negM, fs);
+    if (m) atomicAdd(&sh.mass0[jb], m);
+  });
+  __syncthreads();
+  unsigned long long total = 0;
+  {
+    unsigned long long lm = 0, lc = 0, tc;
+    for (int jb = tid; jb <= kFBins; jb += kFBlock) lm += sh.mass0[jb];
+    wg_excl_scan2(lm, lc, total, tc, sh.sc.red);
+  }
   float tau = -INFINITY;
-  unsigned long long kept = 0;
-  bool done = false;
-  const unsigned ncap = fw.ncand[slot];
-  if (ncap <= static_cast<unsigned>(kGCap)) {
-    // exact histogram of the candidates: every logit with y > -kLevels
-    const int n = static_cast<int>(ncap);
-    const unsigned *cand = fw.cand + slot * kGCap;
-    for (int jb = tid; jb <= kFBins; jb += kFBlock) {
-      sh.cnt0[jb] = 0;
-      sh.mass0[jb] = 0;
-    }
-    __syncthreads();
-    for (int i = tid; i < n; i += kFBlock) {
-      const float z = key_value(cand[i]);
-      const int jb = ybin(z, c, negM);
-      atomicAdd(&sh.cnt0[jb], 1u);
-      const unsigned long long m = fixed_mass(z, c, negM, fs);
-      if (m) atomicAdd(&sh.mass0[jb], m);
-    }
-    __syncthreads();
-    unsigned long long total_m = 0;
-    {
-      unsigned long long lm = 0, lc = 0, tc;
-      for (int jb = tid; jb <= kFBins; jb += kFBlock) lm += sh.mass0[jb];
-      wg_excl_scan2(lm, lc, total_m, tc, sh.sc.red);
-    }
-    bool ok = true;
-    if (k > 0) {
-      if (static_cast<unsigned>(k) > ncap) ok = false;  // the k-th logit lies below the window
-      else tau = list_cut(cand, n, c, negM, fs, false, static_cast<unsigned long long>(k), kept, ok, sh);
-    }
-    if (ok && p < 1.0f) {
-      // top-p of the top-k mass, or of the row's mass (K1's sum, in the same units)
-      const double base = k > 0 ? static_cast<double>(kept) : ldexp(s, fs);
-      double t = ceil(static_cast<double>(p) * base);
-      if (t < 1.0) t = 1.0;
-      const unsigned long long tgt = static_cast<unsigned long long>(t);
-      if (total_m < tgt) {
-        ok = false;  // the crossing lies below the window
-      } else {
-        unsigned long long kept_p;
-        const float tau_p = list_cut(cand, n, c, negM, fs, true, tgt, kept_p, ok, sh);
-        if (ok && tau_p > tau) {
-          tau = tau_p;
-          kept = kept_p;
-        }
-      }
-    }
-    done = ok;
-    __syncthreads();
-  }
-  if (!done) {  // general path
-    for (int jb = tid; jb <= kFBins; jb += kFBlock) {
-      sh.cnt0[jb] = 0;
-      sh.mass0[jb] = 0;
-    }
-    __syncthreads();
-    for_each_logit<DT>(row, aligned, V, [&](float z) {
-      const int jb = ybin(z, c, negM);
-      atomicAdd(&sh.cnt0[jb], 1u);
-      const unsigned long long m = fixed_mass(z, c, negM, fs);
-      if (m) atomicAdd(&sh.mass0[jb], m);
-    });
-    __syncthreads();
-    unsigned long long total = 0;
-    {
-      unsigned long long lm = 0, lc = 0, tc;
-      for (int jb = tid; jb <= kFBins; jb += kFBlock) lm += sh.mass0[jb];
-      wg_excl_scan2(lm, lc, total, tc, sh.sc.red);
-    }
-    tau = -INFINITY;
-    kept = total;
-    if (k > 0)
-      tau = resolve_cut<DT>(row, aligned, V, c, negM, fs, false, static_cast<unsigned long long>(k), kept, sh);
-    if (p < 1.0f) {
-      double t = ceil(static_cast<double>(p) * static_cast<double>(kept));
-      if (t < 1.0) t = 1.0;
-      unsigned long long tgt = static_cast<unsigned long long>(t);
-      if (tgt > kept) tgt = kept;
-      unsigned long long kept_p;
-      const float tau_p = resolve_cut<DT>(row, aligned, V, c, negM, fs, true, tgt, kept_p, sh);
-      if (tau_p > tau) {
-        tau = tau_p;
-        kept = kept_p;
-      }
+  unsigned long long kept = total;
+  if (k > 0)
+    tau = resolve_cut<DT>(row, aligned, V, c, negM, fs, false, static_cast<unsigned long long>(k), kept, sh);
+  if (p < 1.0f) {
+    double t = ceil(static_cast<double>(p) * static_cast<double>(kept));
+    if (t < 1.0) t = 1.0;
+    unsigned long long tgt = static_cast<unsigned long long>(t);
+    if (tgt > kept) tgt = kept;
+    unsigned long long kept_p;
+    const float tau_p = resolve_cut<DT>(row, aligned, V, c, negM, fs, true, tgt, kept_p, sh);
+    if (tau_p > tau) {
+      tau = tau_p;
+      kept = kept_p;
     }
   }
-  if (tid == 0) {
-    FilterStats f;
-    f.s_kept = ldexp(static_cast<double>(kept), -fs);
-    f.tau = tau;
-    f.pad = 0;
-    fst[slot] = f;
-  }
+  store_filter_stats(fst, slot, kept, fs, tau, kFResolved);
 }
 
 // ================================================================== tree verification
@@ -2217,7 +2487,7 @@ struct Plan {
   long k1_groups, k3_groups;
   size_t part_off, zx_off, sel_off, sums_off, fst_off, total;
   // filtered calls: buffers of the filter kernels after `total`
-  size_t ncand_off, cand_off, ftotal;
+  size_t ncand_off, cand_off, dcount_off, ftotal;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -2269,6 +2539,8 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV
   off = align_up(off + sizeof(unsigned) * static_cast<size_t>(slots));
   P->cand_off = off;
   off = align_up(off + sizeof(unsigned) * static_cast<size_t>(slots) * kGCap);
+  P->dcount_off = off;
+  off = align_up(off + sizeof(unsigned) * static_cast<size_t>(P->k1_groups) * (kDeep + 1));
   P->ftotal = off;
   return true;
 }
@@ -2336,13 +2608,20 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
     FilterWork fw;
     fw.ncand = ncand;
     fw.cand = reinterpret_cast<unsigned *>(base + P.cand_off);
+    fw.dcount = reinterpret_cast<unsigned *>(base + P.dcount_off);
     const int fs = filter_frac_bits(V);
     const dim3 cgrid(static_cast<unsigned>(P.k1_groups)), rgrid(static_cast<unsigned>(static_cast<long>(B) * P.rows));
     hipLaunchKernelGGL((k_filter_capture<DT>), cgrid, dim3(kLBlock), 0, st, target, draft, temps, lens, topk, topp,
                        gamma, V, P.NS, P.chunk_vecs, part, fw);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    // the deeper-window counts only concern top-k requests
+    if (topk)
+      hipLaunchKernelGGL((k_filter_deep_count<DT>), cgrid, dim3(kLBlock), 0, st, target, draft, temps, lens, topk,
+                         topp, gamma, V, P.NS, P.chunk_vecs, part, fw);
     hipLaunchKernelGGL((k_filter_resolve<DT>), rgrid, dim3(kFBlock), 0, st, target, draft, temps, lens, topk, topp,
                        gamma, V, P.NS, fs, part, fw, fst);
+    hipLaunchKernelGGL((k_filter_general<DT>), rgrid, dim3(kFBlock), 0, st, target, draft, temps, lens, topk, topp,
+                       gamma, V, P.NS, fs, part, fst);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
   }
   // greedy-only batches need the decision alone: one workgroup per request

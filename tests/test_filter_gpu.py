@@ -166,6 +166,30 @@ def test_crowded_bins_force_key_refinement():
     assert rep["flagged"] <= 1
 
 
+def test_cut_below_the_capture_window():
+    """One dominant logit per row puts every other logit more than 16 binary orders of
+    magnitude below the maximum: the captured list holds one logit, so the k-th logit or
+    the top-p crossing lies below it.  Rows resolve through a deeper window (the count /
+    mass pass and a second capture) or, when that floor would hold more than 4096
+    logits, through the general path."""
+    rng = np.random.default_rng(8)
+    B, gamma, V = 8, 3, 50000
+    z = (rng.standard_normal((B, gamma + 1, V)) * 2.0).astype(np.float32)
+    z[:, :, 4321] += 30.0
+    z[:, :, 777] += 22.0  # second tier, still outside the 16-order window at T = 1
+    draft = z[:, :gamma] + (rng.standard_normal((B, gamma, V)) * 0.3).astype(np.float32)
+    tokens = np.zeros((B, gamma), np.int32)
+    w = W.from_logits(z, draft, tokens, rng.random((B, gamma)), rng.random(B), 1.0, dtype="bf16",
+                      name="dominant")
+    w.scalar_temperature = None
+    #              deeper window by count ...... general  top-p below the window ...... both
+    w.top_k = np.array([50, 200, 1000, 3000, 6000, 0, 0, 40], np.int32)
+    w.top_p = np.array([1.0, 1.0, 1.0, 0.95, 1.0, 0.99999, 0.9999999, 0.99], np.float32)
+    redraw_filtered_drafts(w, 9)
+    rep = run_and_check(w, debug=True, require_no_flags=False)
+    assert rep["flagged"] <= 2
+
+
 def test_filters_off_equal_unfiltered_entry_point():
     w = W.make_random(33, 16, 3, 9000, "bf16", temps=0.8, zipf=True)
     base = gpu_run(w, debug=True, force_ex=True)
