@@ -521,15 +521,18 @@ struct FilterWork {
   unsigned *dcount;  // [slots][NS][kDeep + 1] FD's per-chunk counts above the floors
 };
 
-// Whether request b filters, with its k (0: none) and p (1: none).  Values
-// outside the documented ranges switch the corresponding filter off.
+// Whether a request with top_k kr and top_p pr filters, with its k (0: none)
+// and p (1: none).  Values outside the documented ranges switch the
+// corresponding filter off.
+__device__ __forceinline__ bool filter_params(int kr, float pr, int V, int &k, float &p) {
+  k = (kr > 0 && kr < V) ? kr : 0;
+  p = (pr > 0.0f && pr < 1.0f) ? pr : 1.0f;
+  return k > 0 || p < 1.0f;
+}
+
 __device__ __forceinline__ bool request_filter(const int32_t *topk, const float *topp, int b, int V,
                                                int &k, float &p) {
-  k = topk ? topk[b] : 0;
-  p = topp ? topp[b] : 1.0f;
-  if (!(k > 0 && k < V)) k = 0;
-  if (!(p > 0.0f && p < 1.0f)) p = 1.0f;
-  return k > 0 || p < 1.0f;
+  return filter_params(topk ? topk[b] : 0, topp ? topp[b] : 1.0f, V, k, p);
 }
 
 // ================================================================== K2
@@ -1111,11 +1114,10 @@ struct GeneralShared {
   FilterScratch sc;
 };
 
-// Level of a logit (monotone in z): l for y = z c - M in (-l-1, -l],
-// l < kLevels; kLevels for y <= -kLevels and -inf.
-__device__ __forceinline__ int level_of(float z, float c, float negM) {
-  const float ny = -fmaf(z, c, negM);
-  return ny < static_cast<float>(kLevels) ? (ny > 0.0f ? static_cast<int>(ny) : 0) : kLevels;
+// Whether a logit lies inside the capture window: y = z c - M > -kLevels (the
+// same fma as every other use of y).
+__device__ __forceinline__ bool in_window(float z, float c, float negM) {
+  return fmaf(z, c, negM) > -static_cast<float>(kLevels);
 }
 
 __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int lane) {
@@ -1426,9 +1428,13 @@ template <int DT>
 __device__ __forceinline__ const void *filtered_row(const void *target, const void *draft, const float *temps,
                                                     const int32_t *lens, const int32_t *topk, const float *topp,
                                                     int gamma, int V, int b, int r, float &T, int &k, float &p) {
+  // the request's four parameters are fetched together (one round trip)
   T = temps[b];
-  if (!(T > 0.0f) || !request_filter(topk, topp, b, V, k, p)) return nullptr;
+  const int kr = topk ? topk[b] : 0;
+  const float pr = topp ? topp[b] : 1.0f;
   const int g = request_len(lens, gamma, b);
+  const bool filters = filter_params(kr, pr, V, k, p);
+  if (!(T > 0.0f) || !filters) return nullptr;
   const bool is_target = r <= gamma;
   const int i = is_target ? r : r - gamma - 1;
   if (is_target ? i > g : i >= g) return nullptr;
@@ -1443,9 +1449,14 @@ __device__ __forceinline__ void row_scale(const Partial *part, long slot, int NS
   M = kEmptyM;
   s = 0.0;
   float mx = -INFINITY;
-  for (int j = 0; j < NS; ++j) {
-    const Partial q = part[slot * NS + j];
-    merge_sm(M, s, mx, q.mi, q.s, q.mx);
+  for (int j0 = 0; j0 < NS; j0 += kK2Batch) {  // partials fetched kK2Batch at a time
+    Partial buf[kK2Batch];
+#pragma unroll
+    for (int u = 0; u < kK2Batch; ++u)
+      if (j0 + u < NS) buf[u] = part[slot * NS + j0 + u];
+#pragma unroll
+    for (int u = 0; u < kK2Batch; ++u)
+      if (j0 + u < NS) merge_sm(M, s, mx, buf[u].mi, buf[u].s, buf[u].mx);
   }
 }
 
@@ -1481,7 +1492,7 @@ __global__ __launch_bounds__(kLBlock) void k_filter_capture(
   unsigned wcount = 0;  // the same in every lane of the wave
   const unsigned long long lt = (1ull << lane) - 1ull;
   auto offer = [&](float z) {  // called by every lane of the wave together
-    const bool in = level_of(z, c, negM) < kLevels;
+    const bool in = in_window(z, c, negM);
     const unsigned long long mask = __ballot(in);
     if (in) {
       const unsigned q = wcount + static_cast<unsigned>(__popcll(mask & lt));
@@ -1506,7 +1517,7 @@ __global__ __launch_bounds__(kLBlock) void k_filter_capture(
 #pragma unroll
                                    for (int e = 1; e < kV; ++e) m = fmaxf(m, x[e]);
                                    // no lane of the wave has a candidate
-                                   if (!__ballot(level_of(m, c, negM) < kLevels)) continue;
+                                   if (!__ballot(in_window(m, c, negM))) continue;
 #pragma unroll
                                    for (int e = 0; e < kV; ++e) offer(x[e]);
                                  }
