@@ -128,7 +128,7 @@ def summarize_profile(root: str):
               "k1_row_stats<bf16, per-request T>, k_filter_capture, k_filter_deep_count (with top_k = 50), "
               "k_filter_resolve, k_filter_general and the filtered k2 / k3; the tree measurement (spec_verify_tree, 8 trees of width 4 and depth 3) runs "
               "k1_row_stats<bf16, per-request T> and k_tree_walk; the draft-side sampling measurement runs "
-              "k_sample_rows.  The copy kernels "
+              "k_sample_stats and k_sample_pick.  The copy kernels "
               "are the benchmark's set-up (input copies), outside the timed region.", ""]
     open(os.path.join(out_dir, "kernels_B64_g5_V128256_bf16.md"), "w").write("\n".join(lines))
 

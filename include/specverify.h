@@ -227,7 +227,9 @@ int spec_verify_tree(const void *target_logits, const void *draft_logits,
  * smallest v with u*Z < w[0] + ... + w[v] (the categorical draw that drafting
  * performs before verification: P2 code sketch, multinomial over
  * softmax(logits / temperature); P4 section 検証アルゴリズムの実装).  T_r == 0
- * gives the lowest-index arg-max.  This runs the verify kernels with no drafts.
+ * gives the lowest-index arg-max.  Two kernels: the per-sub-chunk statistics
+ * (2048 tokens each) over several workgroups per row, then one wave per row
+ * that scans them and reads one sub-chunk again.
  * logits:       DEVICE [R][V] dt, row-major
  * u:            DEVICE [R] in [0, 1)
  * temperature:  host scalar used when `temperatures` is NULL (>= 0, finite)

@@ -41,7 +41,8 @@
 //                       K3 are instantiated with the cut compares.
 //   tree of drafts      K1 over every tree position, then k_tree_walk (one
 //                       workgroup per request).
-//   draft-side sampling k_sample_rows (one workgroup per row).
+//   draft-side sampling k_sample_stats (several workgroups per row), then
+//                       k_sample_pick (one wave per row).
 //
 // Numerics: bf16 -> fp32 widening is exact; exponentials are v_exp_f32 of
 // fma(z, c, -M); per-thread partial sums are fp32 over at most 64 terms and
@@ -2292,17 +2293,24 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
   if (tid == 0) count[b] = depth;
 }
 
-// ================================================================== single-pass sampler
-// Draft-side sampling, one token per row of softmax(z/T), in one kernel: a
-// 1024-thread workgroup per row.  Wave w streams sub-chunks w, w+16, ... of
-// 2048 tokens and leaves each one's (M_j, s_j = sum 2^(z c - M_j)) in LDS, with
-// M_j = ceil(max_j * c) the sub-chunk's own integer reference.  The row's
-// masses are then m_j = s_j * 2^(M_j - M) (exact), the sub-chunk holding u*Z is
-// found by a scan, and only that sub-chunk is read again.  Greedy rows keep the
-// (max, lowest index) of each sub-chunk instead.
-constexpr int kSBlock = 1024;
+// ================================================================== draft-side sampler
+// One token per row of softmax(z/T), in two kernels.
+//   S1 k_sample_stats: kSBlock-thread workgroups, several per row; each wave
+//      takes 2048-token sub-chunks of a row and records (M_j, s_j =
+//      sum 2^(z c - M_j)), M_j = ceil(max_j * c) the sub-chunk's own integer
+//      reference, or for a greedy row its (max, lowest index).
+//   S2 k_sample_pick: one wave per row.  The row's masses are
+//      m_j = s_j * 2^(M_j - M) (exact), the sub-chunk holding u*Z is found by
+//      a scan, and only that sub-chunk is read again.
+constexpr int kSBlock = 256;
 constexpr int kSWaves = kSBlock / kWave;
-constexpr int kSMaxSub = 2048;  // sub-chunk records held in LDS: V <= 2048 * 2048
+constexpr long kSTargetWaves = 4096;  // waves of S1 (16 per CU)
+
+struct alignas(16) SubRecord {
+  double s;  // sum 2^(z c - M_j) over the sub-chunk (stochastic)
+  float mx;  // the sub-chunk's maximum (greedy)
+  int mi;    // M_j (stochastic) or the maximum's lowest index (greedy)
+};
 
 __device__ __forceinline__ float wave_max_f32(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x111, 0xf, 0xf, false)));
@@ -2314,26 +2322,24 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
+// S1: workgroup g of row r (SG workgroups per row); wave w takes sub-chunks
+// g * kSWaves + w, then every SG * kSWaves further.
 template <int DT>
-__global__ __launch_bounds__(kSBlock) void k_sample_rows(const void *__restrict__ logits,
-                                                         const float *__restrict__ u,
-                                                         const float *__restrict__ temps, float scalar_T,
-                                                         int V, int NSUB, int32_t *__restrict__ tokens) {
+__global__ __launch_bounds__(kSBlock) void k_sample_stats(const void *__restrict__ logits,
+                                                          const float *__restrict__ temps, float scalar_T, int V,
+                                                          int NSUB, int SG, SubRecord *__restrict__ rec) {
   constexpr int kN = kLaneElems / Elem<DT>::kVec;
-  const int r = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int r = blockIdx.x / SG, g = blockIdx.x - r * SG;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const float T = temps ? temps[r] : scalar_T;
   const bool greedy = !(T > 0.0f);
   const float c = greedy ? 0.0f : temp_scale(T);
   const char *row = static_cast<const char *>(logits) + static_cast<long>(r) * V * Elem<DT>::kBytes;
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-  __shared__ double sh_s[kSMaxSub];
-  __shared__ float sh_f[kSMaxSub];
-  __shared__ int sh_i[kSMaxSub];
-
-  for (int sub = wave; sub < NSUB; sub += kSWaves) {
+  for (int sub = g * kSWaves + wave; sub < NSUB; sub += SG * kSWaves) {
     u32x4 raw[kN];
     load_lane_raw<DT>(row, aligned, static_cast<long>(sub) * kSub, lane, V, raw);
+    SubRecord rc;
     if (!greedy) {
       float lmx = -INFINITY;
 #pragma unroll
@@ -2363,10 +2369,9 @@ __global__ __launch_bounds__(kSBlock) void k_sample_rows(const void *__restrict_
         const float ls = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
         sw = wave_sum(static_cast<double>(ls));
       }
-      if (lane == 0) {
-        sh_s[sub] = sw;
-        sh_i[sub] = M;
-      }
+      rc.s = sw;
+      rc.mx = wmx;
+      rc.mi = M;
     } else {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
@@ -2389,19 +2394,33 @@ __global__ __launch_bounds__(kSBlock) void k_sample_rows(const void *__restrict_
         const int io = __shfl_xor(bi, off);
         merge_arg(bv, bi, vo, io);
       }
-      if (lane == 0) {
-        sh_f[sub] = bv;
-        sh_i[sub] = bi;
-      }
+      rc.s = 0.0;
+      rc.mx = bv;
+      rc.mi = bi;
     }
+    if (lane == 0) rec[static_cast<long>(r) * NSUB + sub] = rc;
   }
-  __syncthreads();
-  if (wave != 0) return;  // the rest is wave 0's, with no barrier
+}
+
+// S2: one wave per row.
+template <int DT>
+__global__ __launch_bounds__(kWave) void k_sample_pick(const void *__restrict__ logits, const float *__restrict__ u,
+                                                       const float *__restrict__ temps, float scalar_T, int V,
+                                                       int NSUB, const SubRecord *__restrict__ rec,
+                                                       int32_t *__restrict__ tokens) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float T = temps ? temps[r] : scalar_T;
+  const bool greedy = !(T > 0.0f);
+  const float c = greedy ? 0.0f : temp_scale(T);
+  const char *row = static_cast<const char *>(logits) + static_cast<long>(r) * V * Elem<DT>::kBytes;
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  const SubRecord *rr = rec + static_cast<long>(r) * NSUB;
 
   if (greedy) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int j = lane; j < NSUB; j += kWave) merge_arg(bv, bi, sh_f[j], sh_i[j]);
+    for (int j = lane; j < NSUB; j += kWave) merge_arg(bv, bi, rr[j].mx, rr[j].mi);
 #pragma unroll
     for (int off = kWave / 2; off >= 1; off /= 2) {
       const float vo = __shfl_xor(bv, off);
@@ -2413,20 +2432,18 @@ __global__ __launch_bounds__(kSBlock) void k_sample_rows(const void *__restrict_
   }
   // the row's reference exponent and the sub-chunk masses m_j = s_j 2^(M_j - M)
   int M = kEmptyM;
-  for (int j = lane; j < NSUB; j += kWave) M = max(M, sh_i[j]);
+  for (int j = lane; j < NSUB; j += kWave) M = max(M, rr[j].mi);
 #pragma unroll
   for (int off = kWave / 2; off >= 1; off /= 2) M = max(M, __shfl_xor(M, off));
+  auto mass = [&](int j) { return j < NSUB ? ldexp(rr[j].s, rr[j].mi - M) : 0.0; };
   double Z = 0.0;
-  for (int base = 0; base < NSUB; base += kWave) {
-    const int j = base + lane;
-    Z += wave_sum(j < NSUB ? ldexp(sh_s[j], sh_i[j] - M) : 0.0);
-  }
+  for (int base = 0; base < NSUB; base += kWave) Z += wave_sum(mass(base + lane));
   const double target_mass = static_cast<double>(u[r]) * Z;
   int sub = -1;
   double base_mass = 0.0, run = 0.0;
   for (int base = 0; base < NSUB; base += kWave) {
     const int j = base + lane;
-    const double v = j < NSUB ? ldexp(sh_s[j], sh_i[j] - M) : 0.0;
+    const double v = mass(j);
     const double incl = wave_scan(v, lane);
     const unsigned long long hit = __ballot(j < NSUB && v > 0.0 && run + incl > target_mass);
     if (hit) {
@@ -2441,7 +2458,7 @@ __global__ __launch_bounds__(kSBlock) void k_sample_rows(const void *__restrict_
     run = 0.0;
     for (int base = 0; base < NSUB; base += kWave) {
       const int j = base + lane;
-      const double v = j < NSUB ? ldexp(sh_s[j], sh_i[j] - M) : 0.0;
+      const double v = mass(j);
       const double incl = wave_scan(v, lane);
       const unsigned long long has = __ballot(j < NSUB && v > 0.0);
       if (has) {
@@ -2458,7 +2475,7 @@ __global__ __launch_bounds__(kSBlock) void k_sample_rows(const void *__restrict_
   }
   // the token inside the sub-chunk: the same per-token values as the first
   // pass (reference M_sub), rescaled exactly to the row reference
-  const int Ms = sh_i[sub];
+  const int Ms = rr[sub].mi;
   const long first = static_cast<long>(sub) * kSub + static_cast<long>(lane) * kLaneElems;
   float z[kLaneElems];
 #pragma unroll
@@ -2782,9 +2799,8 @@ size_t spec_sample_workspace_bytes(int R, int V, int dtype) {
   return P.total + align_up(sizeof(int32_t) * static_cast<size_t>(R));
 }
 
-// Sampling one token per row is the verify step with no drafts: every row is a
-// bonus row, drawn by the same kernels.  The per-row counts (always 0) go to
-// the tail of the workspace.
+// Sampling one token per row: S1 and S2 above (the same law as the verify
+// step with no drafts, where every row is a bonus row).
 int spec_sample(const void *logits, const float *u, float temperature, const float *temperatures, int R,
                 int V, int dtype, int32_t *tokens, void *workspace, size_t workspace_bytes, void *stream) {
   if (!temperatures && (!(temperature >= 0.0f) || isinf(temperature))) return SV_EINVAL;
@@ -2794,22 +2810,28 @@ int spec_sample(const void *logits, const float *u, float temperature, const flo
   const size_t need = P.total + align_up(sizeof(int32_t) * static_cast<size_t>(R));
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < need)
     return SV_EWORKSPACE;
-  const int nsub = (V + kSub - 1) / kSub;
-  if (nsub <= kSMaxSub) {
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (dtype == SV_BF16)
-      hipLaunchKernelGGL((k_sample_rows<SV_BF16>), dim3(R), dim3(kSBlock), 0, st, logits, u, temperatures,
-                         temperature, V, nsub, tokens);
-    else
-      hipLaunchKernelGGL((k_sample_rows<SV_F32>), dim3(R), dim3(kSBlock), 0, st, logits, u, temperatures,
-                         temperature, V, nsub, tokens);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+  // S1 over every row's sub-chunks (records in the workspace's sub-chunk sum
+  // area, R * NSUB records of 16 bytes), then S2
+  static_assert(sizeof(SubRecord) == sizeof(SubSums), "records share the sub-chunk sum area");
+  SubRecord *rec = reinterpret_cast<SubRecord *>(static_cast<char *>(workspace) + P.sums_off);
+  const long waves_per_row = min(static_cast<long>(P.NSUB), max(static_cast<long>(kSWaves),
+                                                                (kSTargetWaves + R - 1) / R));
+  const int SG = static_cast<int>((waves_per_row + kSWaves - 1) / kSWaves);
+  if (static_cast<long>(R) * SG > (1L << 32) / kSBlock - 1) return SV_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 g1(static_cast<unsigned>(static_cast<long>(R) * SG));
+  if (dtype == SV_BF16) {
+    hipLaunchKernelGGL((k_sample_stats<SV_BF16>), g1, dim3(kSBlock), 0, st, logits, temperatures, temperature, V,
+                       P.NSUB, SG, rec);
+    hipLaunchKernelGGL((k_sample_pick<SV_BF16>), dim3(R), dim3(kWave), 0, st, logits, u, temperatures,
+                       temperature, V, P.NSUB, rec, tokens);
+  } else {
+    hipLaunchKernelGGL((k_sample_stats<SV_F32>), g1, dim3(kSBlock), 0, st, logits, temperatures, temperature, V,
+                       P.NSUB, SG, rec);
+    hipLaunchKernelGGL((k_sample_pick<SV_F32>), dim3(R), dim3(kWave), 0, st, logits, u, temperatures,
+                       temperature, V, P.NSUB, rec, tokens);
   }
-  // rows longer than the LDS records: the verify kernels with no drafts
-  int32_t *counts = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + P.total);
-  return dispatch(logits, nullptr, nullptr, nullptr, u, temperatures, temperature,
-                  temperatures == nullptr && temperature == 0.0f, nullptr, nullptr, nullptr, R, 0, V, dtype,
-                  counts, tokens, workspace, P.total, stream, nullptr);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 size_t spec_sample_filtered_workspace_bytes(int R, int V, int dtype) {

@@ -49,7 +49,7 @@ def _case(seed, R, V, dtype, T, scale=3.0, zipf=True):
     (1, 1, "f32", 1.0), (7, 5, "bf16", 0.8), (64, 1000, "f32", 1.0), (300, 4099, "bf16", 0.6),
     (64, 128256, "bf16", 1.0), (320, 128256, "bf16", 0.7), (33, 152064, "bf16", "mixed"),
     (5, 70001, "f32", "mixed"), (16, 3000, "bf16", 0.0),
-    (2, 4194305, "bf16", 1.0),   # longer than the single-pass kernel's LDS records: verify kernels
+    (2, 4194305, "bf16", 1.0),   # a long row: 2049 sub-chunk records per row
 ])
 def test_sample_parity(R, V, dtype, T):
     import oracle
