@@ -566,11 +566,14 @@ __device__ __forceinline__ void decide_request(
   const int rows = 2 * gamma + 1;
   const int g = request_len(lens, gamma, b);
   const float T = request_T(temps, scalar_T, b);
+  // the filter parameters are fetched together with T (one round trip)
+  const int fkr = FILT && topk ? topk[b] : 0;
+  const float fpr = FILT && topp ? topp[b] : 1.0f;
   const bool greedy = !(T > 0.0f);
   const float c = greedy ? 0.0f : temp_scale(T);
   int fk;
   float fp;
-  const bool filtered = FILT && !greedy && request_filter(topk, topp, b, V, fk, fp);
+  const bool filtered = FILT && filter_params(fkr, fpr, V, fk, fp) && !greedy;
   sv_debug dbg = dbg_in;
   if (!writer) memset(&dbg, 0, sizeof dbg);
   double *sh_s = sh.s;
@@ -599,6 +602,10 @@ __device__ __forceinline__ void decide_request(
     const bool needed = is_target ? (i <= g) : (!greedy && i < g);
     if (needed) {
       const Partial *pp = part + (static_cast<long>(b) * rows + r) * NS;
+      // the row's filter statistics (written for every filtered row), fetched
+      // together with the partials
+      FilterStats fsr;
+      if (FILT && filtered) fsr = fst[static_cast<long>(b) * rows + r];
       int M = kEmptyM;
       double s = 0.0;
       float mx = -INFINITY;
@@ -620,9 +627,8 @@ __device__ __forceinline__ void decide_request(
       if (!greedy) {
         float tau = -INFINITY;
         if (FILT && filtered) {  // the kept mass replaces the row sum
-          const FilterStats f = fst[static_cast<long>(b) * rows + r];
-          s = f.s_kept;
-          tau = f.tau;
+          s = fsr.s_kept;
+          tau = fsr.tau;
         }
         sh_M[r] = M;
         sh_s[r] = s;
