@@ -166,28 +166,44 @@ def test_crowded_bins_force_key_refinement():
     assert rep["flagged"] <= 1
 
 
-def test_cut_below_the_capture_window():
+@pytest.mark.parametrize("V,dtype,ragged", [(50000, "bf16", False), (32003, "f32", False), (20001, "bf16", True)],
+                         ids=["V50000_bf16", "V32003_f32_unaligned", "V20001_bf16_unaligned_ragged"])
+def test_cut_below_the_capture_window(V, dtype, ragged):
     """One dominant logit per row puts every other logit more than 16 binary orders of
-    magnitude below the maximum: the captured list holds one logit, so the k-th logit or
-    the top-p crossing lies below it.  Rows resolve through a deeper window (the count /
-    mass pass and a second capture) or, when that floor would hold more than 4096
-    logits, through the general path."""
-    rng = np.random.default_rng(8)
-    B, gamma, V = 8, 3, 50000
-    z = (rng.standard_normal((B, gamma + 1, V)) * 2.0).astype(np.float32)
-    z[:, :, 4321] += 30.0
-    z[:, :, 777] += 22.0  # second tier, still outside the 16-order window at T = 1
+    magnitude below the maximum: the captured list holds one logit, so the k-th logit
+    or the top-p crossing lies below it.  Rows resolve through a deeper window
+    (the band counts and a second capture) or, when that floor would hold more than
+    4096 logits, through the general path.  Odd V makes every row after the first
+    start off a 16-byte boundary (the one-by-one paths); ragged draft lengths leave
+    padding rows that must not be read."""
+    rng = np.random.default_rng(8 + V)
+    B, gamma = 8, 3
+    z = (rng.standard_normal((B, gamma + 1, V)) * 2.0 - 10.0).astype(np.float32)
+    for b in range(B):  # a tier of 60 logits 11.2 to 12.8 nats below the top, outside the window
+        for i in range(gamma + 1):
+            tier = rng.choice(V, 60, replace=False)
+            z[b, i, tier] = (12.0 - rng.uniform(11.2, 12.8, 60)).astype(np.float32)
+    z[:, :, 4321] = 12.0
     draft = z[:, :gamma] + (rng.standard_normal((B, gamma, V)) * 0.3).astype(np.float32)
     tokens = np.zeros((B, gamma), np.int32)
-    w = W.from_logits(z, draft, tokens, rng.random((B, gamma)), rng.random(B), 1.0, dtype="bf16",
-                      name="dominant")
+    lens = np.array([3, 1, 0, 2, 3, 3, 2, 1], np.int32) if ragged else None
+    # the token at the end is drawn in the last 4e-4 of the CDF: one of the kept tier
+    u_s = np.minimum(1.0 - rng.random(B) * 4e-4, 1.0 - 2.0 ** -24).astype(np.float32)
+    w = W.from_logits(z, draft, tokens, rng.random((B, gamma)), u_s, 1.0, dtype=dtype,
+                      name="dominant", lens=lens)
     w.scalar_temperature = None
+    if ragged:  # padding rows poisoned
+        nan = W.BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+        for b in range(B):
+            w.target[b, lens[b] + 1:] = nan
+            w.draft[b, lens[b]:] = nan
     #              deeper window by count ...... general  top-p below the window ...... both
     w.top_k = np.array([50, 200, 1000, 3000, 6000, 0, 0, 40], np.int32)
     w.top_p = np.array([1.0, 1.0, 1.0, 0.95, 1.0, 0.99999, 0.9999999, 0.99], np.float32)
     redraw_filtered_drafts(w, 9)
     rep = run_and_check(w, debug=True, require_no_flags=False)
-    assert rep["flagged"] <= 2
+    # the top-p rows' cuts and some tail draws sit within the rounding bands
+    assert rep["flagged"] <= 4
 
 
 def test_filters_off_equal_unfiltered_entry_point():

@@ -112,3 +112,41 @@ def test_sample_filtered_parity(R, V, dtype, k, p):
     assert ok.sum() >= R - max(1, R // 16)
     np.testing.assert_array_equal(g[ok], o[ok])
     np.testing.assert_array_equal(g[T == 0], o[T == 0])
+
+
+@pytest.mark.parametrize("V,dtype", [(50000, "bf16"), (32003, "f32")])
+def test_sample_filtered_cut_below_the_window(V, dtype):
+    """Rows with one dominant logit and a tier of 60 logits 11.2 to 12.8 nats below it:
+    every other logit lies more than 16 binary orders of magnitude below the top (the
+    capture window holds one logit), so the top-k cut is found through the deeper
+    window (or the general path for large k).  The uniforms sit in the last 4e-4 of the
+    CDF, where the drawn token is one of the kept tier in vocabulary order: a cut off by
+    one logit moves the draw."""
+    import oracle
+
+    import rejection_sampling_verification_spec_amd as sv
+    R = 48
+    rng = np.random.default_rng(V + 3)
+    z = (rng.standard_normal((R, V)) * 2.0 - 10.0).astype(np.float32)
+    for r in range(R):
+        tier = rng.choice(V, 60, replace=False)
+        z[r, tier] = (12.0 - rng.uniform(11.2, 12.8, 60)).astype(np.float32)
+    z[:, 4321] = 12.0
+    store = W.bf16_bits_from_f32(z) if dtype == "bf16" else z
+    u = (1.0 - rng.random(R) * 4e-4).astype(np.float32)
+    u = np.minimum(u, np.float32(1.0) - np.float32(2.0 ** -24)).astype(np.float32)
+    ks = rng.choice(np.array([20, 40, 55, 200, 3000], np.int32), size=R)
+    T = np.full(R, 1.0, np.float32)
+    dev = torch.device("cuda:0")
+    lt = torch.from_numpy(np.ascontiguousarray(store))
+    lt = (lt.view(torch.bfloat16) if dtype == "bf16" else lt).to(dev)
+    say(f"spec_sample filtered, dominant rows, V={V} {dtype}")
+    tok = sv.spec_sample(lt, torch.from_numpy(u).to(dev), torch.from_numpy(T).to(dev),
+                         top_k=torch.from_numpy(ks).to(dev))
+    torch.cuda.synchronize()
+    g = tok.cpu().numpy()
+    o, tr = oracle.sample(store, u, T, dtype=dtype, top_k=ks)
+    ok = tr.flags == 0   # a tail token's interval is a few 1e-6 of the mass: some draws sit in the band
+    assert ok.sum() >= R // 2
+    np.testing.assert_array_equal(g[ok], o[ok])
+    assert np.count_nonzero(ok & (o != 4321)) >= R // 3   # the checked draws are mostly tier tokens
