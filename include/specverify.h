@@ -49,7 +49,10 @@
  *     check returns SV_EINVAL / SV_EWORKSPACE and touches nothing.  A failed
  *     launch returns SV_EHIP.  Values that live in device memory (uniforms in
  *     [0, 1), per-request T >= 0 and finite) are the caller's contract and are
- *     not checked; memory safety does not depend on them: a draft length
+ *     not checked; memory safety does not depend on them.  For T > 0 every
+ *     row's scaled maximum |max(z) * log2(e) / T| must stay below 2^28 (for
+ *     example T >= 1e-5 with |z| <= 1000; the tests run T from 1e-3 to 50 with
+ *     logits up to about 150 in magnitude).  A draft length
  *     outside [0, gamma] is clamped to that range, and a draft token id outside
  *     [0, V) is treated as rejected at its position.  Logits must be finite on
  *     every row that the method reads (padding rows of ragged requests are

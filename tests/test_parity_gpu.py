@@ -166,6 +166,20 @@ def test_zero_residual_mass_fallback():
     np.testing.assert_array_equal(g.out, o.out_tokens)
 
 
+@pytest.mark.parametrize("dtype,temps,scale", [
+    ("f32", 1e-3, 3.0),                                              # nearly one-hot rows
+    ("bf16", 1e-2, 40.0),                                            # logits up to about +-150
+    ("f32", 50.0, 3.0),                                              # nearly uniform rows
+    ("bf16", np.array([1e-3, 0.05, 1.0, 20.0, 0.0, 3.0, 0.2, 7.0], np.float32), 8.0),
+], ids=["T1e-3_f32", "T1e-2_bf16_large_logits", "T50_f32", "mixed_extremes_bf16"])
+def test_extreme_temperatures(dtype, temps, scale):
+    """Temperatures from 1e-3 to 50 (and greedy rows among them), with logits up to
+    about 150 in magnitude: y = z log2(e) / T - M reaches -1e5 and the integer M 1e5."""
+    w = W.make_random(4242, 8, 4, 5003, dtype, temps=temps, target_scale=scale, sigma=0.5, zipf=True)
+    rep = run_and_check(w, debug=True, require_no_flags=False)
+    assert rep["flagged"] <= 1
+
+
 def test_identical_rows_accept_all():
     w = W.make_random(77, 8, 6, 20000, "bf16", temps=0.9, zipf=True)
     w.draft[:] = w.target[:, :6]
