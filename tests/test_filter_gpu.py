@@ -289,3 +289,43 @@ def test_filtered_graph_replay_and_side_stream():
         torch.cuda.synchronize()
         say(f"filtered graph replay {rep}")
         assert torch.equal(count.cpu(), ref[0]) and torch.equal(out.cpu(), ref[1])
+
+
+def _fuzz_case(seed):
+    """A small random filtered batch: shape, dtype, temperature, filter values and the
+    logit law (Gaussian, integer ties, one dominant token, nearly flat) all drawn."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 9))
+    gamma = int(rng.integers(0, 7))
+    V = int(rng.choice([1, 2, 3, 17, 64, 257, 1000, 4099, 5000]))
+    dtype = str(rng.choice(["f32", "bf16"]))
+    law = str(rng.choice(["normal", "ties", "dominant", "flat"]))
+    shape = (B, gamma + 1, V)
+    if law == "normal":
+        z = rng.standard_normal(shape) * rng.uniform(0.5, 4.0)
+    elif law == "ties":
+        z = rng.integers(0, 5, size=shape).astype(np.float64)
+    elif law == "dominant":
+        z = rng.standard_normal(shape) * 2.0
+        z[..., int(rng.integers(0, V))] += rng.uniform(8.0, 30.0)
+    else:
+        z = rng.standard_normal(shape) * 0.1
+    z = z.astype(np.float32)
+    noise = rng.standard_normal((B, gamma, V)).astype(np.float32) * np.float32(rng.uniform(0.0, 1.0))
+    draft = z[:, :gamma] + noise
+    T = rng.choice(np.array([0.0, 0.3, 1.0, 2.0], np.float32), size=B)
+    lens = rng.integers(0, gamma + 1, size=B).astype(np.int32) if gamma > 0 and rng.random() < 0.5 else None
+    w = W.from_logits(z, draft, np.zeros((B, gamma), np.int32), rng.random((B, gamma)), rng.random(B), T,
+                      dtype=dtype, lens=lens, name=f"fuzz{seed}_{law}")
+    w.scalar_temperature = None
+    w.top_k = rng.choice(np.array([0, 1, 2, 5, max(V - 1, 0), V, int(rng.integers(1, V + 1))], np.int32), size=B)
+    w.top_p = rng.choice(np.array([1.0, 0.5, 0.9, 0.99, 0.999], np.float32), size=B)
+    redraw_filtered_drafts(w, seed + 1)
+    return w
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_filtered_fuzz(seed):
+    w = _fuzz_case(1000 + seed)
+    rep = run_and_check(w, debug=True, require_no_flags=False)
+    assert rep["flagged"] <= max(1, w.B // 2)

@@ -2,7 +2,8 @@
 
 Bar: accepted counts, emitted tokens and path nodes bit-exact on every request
 the oracle does not flag (an acceptance uniform within 1e-6 of its threshold,
-u_sample within 1e-6 of a CDF break, or the zero-mass fallback); greedy
+u_sample within 1e-6 of a CDF break, both bands in units of the current
+target's unnormalised mass, or the zero-mass fallback); greedy
 requests fully bit-exact.
 """
 import zlib
@@ -183,3 +184,36 @@ def test_tree_graph_replay_and_side_stream():
         np.testing.assert_array_equal(cnt.cpu().numpy(), ref[0])
         np.testing.assert_array_equal(out.cpu().numpy(), ref[1])
         np.testing.assert_array_equal(nodes.cpu().numpy(), ref[2])
+
+
+def _tree_fuzz_case(seed):
+    """A small random tree batch: parents drawn node by node (any earlier node or the
+    prefix), ragged node counts, per-request T (greedy included), tokens half the time
+    the target arg-max at the parent position (so greedy and stochastic paths grow)."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 7))
+    N = int(rng.integers(1, 24))
+    V = int(rng.choice([1, 7, 100, 1000, 3001]))
+    dtype = str(rng.choice(["f32", "bf16"]))
+    zp = (rng.standard_normal((B, N + 1, V)) * rng.uniform(0.5, 3.0)).astype(np.float32)
+    zq = (zp[:, :N] + rng.standard_normal((B, N, V)).astype(np.float32) * np.float32(rng.uniform(0.0, 1.0)))
+    parent = np.stack([np.array([int(rng.integers(-1, n)) for n in range(N)], np.int32) for _ in range(B)])
+    cast = (lambda a: W.bf16_bits_from_f32(a)) if dtype == "bf16" else (lambda a: a)
+    target, draft = cast(zp), cast(zq.astype(np.float32))
+    tgt64 = W._as_f64(target, dtype)
+    tokens = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    for b in range(B):
+        for n in range(N):
+            if rng.random() < 0.5:
+                tokens[b, n] = int(np.argmax(tgt64[b, parent[b, n] + 1]))
+    temps = rng.choice(np.array([0.0, 0.5, 1.0, 1.5], np.float32), size=B)
+    num_nodes = rng.integers(0, N + 1, size=B).astype(np.int32)
+    return W.TreeWorkload(name=f"treefuzz{seed}", B=B, N=N, V=V, dtype=dtype, target=target, draft=draft,
+                          parent=parent, tokens=tokens, u_accept=rng.random((B, N)).astype(np.float32),
+                          u_sample=rng.random(B).astype(np.float32), temperature=temps, num_nodes=num_nodes)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_tree_fuzz(seed):
+    w = _tree_fuzz_case(2000 + seed)
+    check(w, max_flagged=max(1, w.B // 2))
