@@ -291,13 +291,13 @@ def test_filtered_graph_replay_and_side_stream():
         assert torch.equal(count.cpu(), ref[0]) and torch.equal(out.cpu(), ref[1])
 
 
-def _fuzz_case(seed):
+def _fuzz_case(seed, V=None):
     """A small random filtered batch: shape, dtype, temperature, filter values and the
     logit law (Gaussian, integer ties, one dominant token, nearly flat) all drawn."""
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 9))
     gamma = int(rng.integers(0, 7))
-    V = int(rng.choice([1, 2, 3, 17, 64, 257, 1000, 4099, 5000]))
+    V = int(rng.choice([1, 2, 3, 17, 64, 257, 1000, 4099, 5000])) if V is None else V
     dtype = str(rng.choice(["f32", "bf16"]))
     law = str(rng.choice(["normal", "ties", "dominant", "flat"]))
     shape = (B, gamma + 1, V)

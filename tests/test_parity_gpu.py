@@ -269,14 +269,14 @@ def test_graph_replay_matches_eager():
         assert torch.equal(count.cpu(), ref[0]) and torch.equal(out.cpu(), ref[1])
 
 
-def _verify_fuzz_case(seed):
+def _verify_fuzz_case(seed, V=None):
     """A small random batch of spec_verify_ex: shape, dtype, ragged lengths, per-request T
     (greedy included) and the logit law (Gaussian, integer ties, one dominant token,
     nearly flat) all drawn; draft tokens half from the draft arg-max, half at random."""
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 9))
     gamma = int(rng.integers(0, 9))
-    V = int(rng.choice([1, 2, 5, 64, 999, 4099]))
+    V = int(rng.choice([1, 2, 5, 64, 999, 4099])) if V is None else V
     dtype = str(rng.choice(["f32", "bf16"]))
     law = str(rng.choice(["normal", "ties", "dominant", "flat"]))
     shape = (B, gamma + 1, V)
