@@ -35,10 +35,10 @@
 //                       crosses u*Z, then the token inside it.
 //
 // Extensions, on the same row statistics:
-//   top-k / top-p       k_filter_capture, k_filter_deep_count, k_filter_resolve,
-//                       k_filter_general between K1 and K2 find each filtered
-//                       row's cut; K2 and
-//                       K3 are instantiated with the cut compares.
+//   top-k / top-p       k_filter_capture, k_filter_deep_count, k_filter_resolve
+//                       and k_filter_general between K1 and K2 find each
+//                       filtered row's cut; K2 and K3 are instantiated with
+//                       the cut compares.
 //   tree of drafts      K1 over every tree position, then k_tree_walk (one
 //                       workgroup per request).
 //   draft-side sampling k_sample_stats (several workgroups per row), then
