@@ -506,7 +506,7 @@ constexpr int kLBlock = 256;  // FG workgroup
 constexpr int kFBins = 2048;  // general path: y bins; index kFBins collects y <= -64
 constexpr int kFCap = 4096;   // logits sorted and scanned in LDS
 constexpr int kLevels = 16;   // the capture window: levels of one binary order of magnitude below 2^M
-constexpr int kGCap = 8192;   // logits a row may capture
+constexpr int kGCap = 32768;  // logits a row may capture (T = 1.2 rows of a 128K vocabulary fit)
 constexpr int kDeep = 12;     // deeper floors y = -18, -20, ..., -40 (FD, FC)
 
 struct alignas(16) FilterStats {
@@ -1472,7 +1472,7 @@ __device__ __forceinline__ void row_scale(const Partial *part, long slot, int NS
 // from a ballot: no atomics), then reserves its range of the row's list with
 // one atomic and copies them out.  A wave that finds more than kWaveCap
 // candidates pushes the row's count past kGCap (the general path).
-constexpr int kWaveCap = 512;
+constexpr int kWaveCap = 2048;
 
 template <int DT>
 __global__ __launch_bounds__(kLBlock) void k_filter_capture(

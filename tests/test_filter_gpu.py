@@ -241,6 +241,17 @@ def test_filtered_serving_shape(top_k, top_p):
     assert rep["flagged"] <= 2
 
 
+@pytest.mark.parametrize("T", [1.2, 2.5])
+def test_filtered_flat_rows(T):
+    """Serving-size rows at a high temperature: at T = 1.2 the capture window holds up to
+    about 25000 logits (the long list), at T = 2.5 nearly the whole row (the general path)."""
+    w = with_filter(W.build(f"B4_g2_V128256_bf16_T{T}_zipf", 2100, 4, 2, 128256, "bf16", target_scale=4.0,
+                            zipf=True, sigma=0.5, temps=T), top_p=0.9)
+    redraw_filtered_drafts(w, 2101)
+    rep = run_and_check(w, debug=True, require_no_flags=False)
+    assert rep["flagged"] <= 1
+
+
 def test_filtered_deterministic():
     w = with_filter(W.make_random(35, 16, 4, 30000, "bf16", temps=0.7, zipf=True), top_k=200, top_p=0.9)
     a = gpu_run(w, debug=True)
