@@ -276,33 +276,41 @@ __device__ __forceinline__ void fold_tile(const u32x4 *v, float c, int &M, doubl
 
 // U vectors per thread of the tile starting at vector t0 of the chunk [.., v1).
 // Every lane loads (indices are clamped into the chunk, so the code is straight
-// line and the compiler can wait for exactly the older tile); lanes past v1
-// then hold -inf.
-template <int DT, int U, int BS = kBlock>
+// line and the compiler can wait for exactly the older tile); with MASK, lanes
+// past v1 then hold -inf, else they hold a copy of the chunk's last vector and
+// the fold masks them itself (mask_tile).
+template <int DT, int U, int BS = kBlock, bool MASK = true>
 __device__ __forceinline__ void load_tile(const u32x4 *rv, int t0, int v1, int tid, u32x4 *dst) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int vi = t0 + u * BS + tid;
     const u32x4 x = load_nt(rv + min(vi, v1 - 1));
-    dst[u] = (vi < v1) ? x : neg_inf_vec<DT>();
+    dst[u] = (!MASK || vi < v1) ? x : neg_inf_vec<DT>();
   }
+}
+
+// The vectors of a tile loaded without MASK, those past v1 replaced by -inf.
+template <int DT, int U, int BS = kBlock>
+__device__ __forceinline__ void mask_tile(const u32x4 *src, int t0, int v1, int tid, u32x4 *dst) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) dst[u] = (t0 + u * BS + tid < v1) ? src[u] : neg_inf_vec<DT>();
 }
 
 // Streams the vectors [v0, v1) of a row in tiles of U vectors per thread with
 // two register buffers: the next tile is in flight while the current one is
 // folded.  fold(tile, t0) sees each tile once, in order.
-template <int DT, int U, int BS = kBlock, typename Fold>
+template <int DT, int U, int BS = kBlock, bool MASK = true, typename Fold>
 __device__ __forceinline__ void stream_chunk(const u32x4 *rv, int v0, int v1, int tid, Fold &&fold) {
   constexpr int kTileVecs = U * BS;
   if (v0 >= v1) return;
   u32x4 a[U], b[U];
-  load_tile<DT, U, BS>(rv, v0, v1, tid, a);
+  load_tile<DT, U, BS, MASK>(rv, v0, v1, tid, a);
   for (int t0 = v0;;) {
-    load_tile<DT, U, BS>(rv, t0 + kTileVecs, v1, tid, b);
+    load_tile<DT, U, BS, MASK>(rv, t0 + kTileVecs, v1, tid, b);
     fold(a, t0);
     t0 += kTileVecs;
     if (t0 >= v1) break;
-    load_tile<DT, U, BS>(rv, t0 + kTileVecs, v1, tid, a);
+    load_tile<DT, U, BS, MASK>(rv, t0 + kTileVecs, v1, tid, a);
     fold(b, t0);
     t0 += kTileVecs;
     if (t0 >= v1) break;
@@ -373,7 +381,16 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
     int M = kEmptyM;
     double s = 0.0;
     float mx = -INFINITY;
-    stream_chunk<DT, U>(rv, v0, v1, tid, [&](const u32x4 *tile, int) { fold_tile<DT, U>(tile, c, M, s, mx); });
+    // only a tile that reaches past v1 is masked (the chunk's last one)
+    stream_chunk<DT, U, kBlock, false>(rv, v0, v1, tid, [&](const u32x4 *tile, int t0) {
+      if (t0 + U * kBlock <= v1) {  // uniform per workgroup
+        fold_tile<DT, U>(tile, c, M, s, mx);
+      } else {
+        u32x4 m[U];
+        mask_tile<DT, U>(tile, t0, v1, tid, m);
+        fold_tile<DT, U>(m, c, M, s, mx);
+      }
+    });
     for (long e = se0 + tid; e < se1; e += kBlock) {
       const float z = load_one<DT>(row, e);
       fold_values<1>(&z, c, M, s, mx);
@@ -2537,15 +2554,18 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV
   P->rows = 2 * gamma + 1;
   const long slots = static_cast<long>(B) * P->rows;
   // split each row into NS chunks of whole K1 tiles: enough workgroups to fill
-  // the chip, no chunk shorter than one tile
+  // the chip, no chunk shorter than one tile.  Chunk lengths are whole tiles,
+  // so that only the row's last chunk ends in a partial (masked) tile.
   const long vecs = (V + vec - 1) / vec;
   const long tile = static_cast<long>(kK1U) * kBlock;
   const long tiles_per_row = (vecs + tile - 1) / tile;
   long NS = (kK1TargetGroups + slots / 2) / slots;
   if (NS < 1) NS = 1;
   if (NS > tiles_per_row) NS = tiles_per_row;
+  const long tiles_per_chunk = (tiles_per_row + NS - 1) / NS;
+  P->chunk_vecs = static_cast<int>(tiles_per_chunk * tile);
+  NS = (tiles_per_row + tiles_per_chunk - 1) / tiles_per_chunk;  // every chunk non-empty
   P->NS = static_cast<int>(NS);
-  P->chunk_vecs = static_cast<int>((vecs + NS - 1) / NS);
   P->k1_groups = slots * NS;
   P->NSUB = (V + kSub - 1) / kSub;
   // sub-chunks per wave in the mass pass: pipeline two per wave when the batch
