@@ -298,13 +298,20 @@ __device__ __forceinline__ void mask_tile(const u32x4 *src, int t0, int v1, int 
 
 // Streams the vectors [v0, v1) of a row in tiles of U vectors per thread with
 // two register buffers: the next tile is in flight while the current one is
-// folded.  fold(tile, t0) sees each tile once, in order.
-template <int DT, int U, int BS = kBlock, bool MASK = true, typename Fold>
-__device__ __forceinline__ void stream_chunk(const u32x4 *rv, int v0, int v1, int tid, Fold &&fold) {
+// folded.  fold(tile, t0) sees each tile once, in order.  With PRE the first
+// tile has already been loaded (load_tile with the same MASK) into `pre`.
+template <int DT, int U, int BS, bool MASK, bool PRE, typename Fold>
+__device__ __forceinline__ void stream_chunk_impl(const u32x4 *rv, int v0, int v1, int tid, const u32x4 *pre,
+                                                  Fold &&fold) {
   constexpr int kTileVecs = U * BS;
   if (v0 >= v1) return;
   u32x4 a[U], b[U];
-  load_tile<DT, U, BS, MASK>(rv, v0, v1, tid, a);
+  if constexpr (PRE) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = pre[u];
+  } else {
+    load_tile<DT, U, BS, MASK>(rv, v0, v1, tid, a);
+  }
   for (int t0 = v0;;) {
     load_tile<DT, U, BS, MASK>(rv, t0 + kTileVecs, v1, tid, b);
     fold(a, t0);
@@ -315,6 +322,19 @@ __device__ __forceinline__ void stream_chunk(const u32x4 *rv, int v0, int v1, in
     t0 += kTileVecs;
     if (t0 >= v1) break;
   }
+}
+
+template <int DT, int U, int BS = kBlock, bool MASK = true, typename Fold>
+__device__ __forceinline__ void stream_chunk(const u32x4 *rv, int v0, int v1, int tid, Fold &&fold) {
+  stream_chunk_impl<DT, U, BS, MASK, false>(rv, v0, v1, tid, nullptr, fold);
+}
+
+// K1's streaming: unmasked tiles (its folds mask the last one themselves);
+// with PRE the first tile is already in `pre`.
+template <int DT, int U, bool PRE, typename Fold>
+__device__ __forceinline__ void stream_chunk_k1(const u32x4 *rv, int v0, int v1, int tid, const u32x4 *pre,
+                                                Fold &&fold) {
+  stream_chunk_impl<DT, U, kBlock, false, PRE>(rv, v0, v1, tid, pre, fold);
 }
 
 // Which request kinds a K1 instantiation handles: the uniform entry point knows
@@ -336,13 +356,8 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   if (row_counter && j == 0 && threadIdx.x == 0) row_counter[slot] = 0u;
   const int b = slot / rows;
   const int r = slot - b * rows;
-  const int g = request_len(lens, gamma, b);
-  const float T = request_T(temps, scalar_T, b);
   const bool is_target = r <= gamma;
   const int i = is_target ? r : r - gamma - 1;
-  const bool greedy = KIND == kGreedyOnly ? true : (KIND == kStochasticOnly ? false : !(T > 0.0f));
-  if (is_target ? (i > g) : (greedy || i >= g)) return;
-
   const char *row =
       is_target ? static_cast<const char *>(target) +
                       (static_cast<long>(b) * (gamma + 1) + i) * V * Elem<DT>::kBytes
@@ -352,13 +367,28 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   const int nvec = aligned ? V / kV : 0;  // whole aligned vectors of the row
   const int v0 = min(j * chunk_vecs, nvec);
   const int v1 = min(v0 + chunk_vecs, nvec);
+  const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
+  const int tid = threadIdx.x;
+  // With per-request temperatures and lengths, whether this row is needed (and
+  // how) is known only once temps[b] and lens[b] have arrived; the chunk's first
+  // tile is requested before them, so that the two latencies overlap.  A row
+  // that turns out not to be needed (a greedy request's draft row, a row past
+  // the request's length) has then read one tile for nothing.
+  constexpr bool kPre = KIND == kMixed;
+  u32x4 pre[U];
+  if constexpr (kPre) {
+    if (v0 < v1) load_tile<DT, U, kBlock, false>(rv, v0, v1, tid, pre);
+  }
+  const int g = request_len(lens, gamma, b);
+  const float T = request_T(temps, scalar_T, b);
+  const bool greedy = KIND == kGreedyOnly ? true : (KIND == kStochasticOnly ? false : !(T > 0.0f));
+  if (is_target ? (i > g) : (greedy || i >= g)) return;
+
   // elements read one by one: the tail after the last whole vector (last
   // chunk), or this chunk's share of a row that is not 16-byte aligned
   const long se0 = aligned ? (j == NCH - 1 ? static_cast<long>(nvec) * kV : V)
                            : min(static_cast<long>(j) * chunk_vecs * kV, static_cast<long>(V));
   const long se1 = aligned ? V : min(static_cast<long>(j + 1) * chunk_vecs * kV, static_cast<long>(V));
-  const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
-  const int tid = threadIdx.x;
   // the logit at this position's draft token, picked up by the chunk that owns it
   // (stochastic rows i < g only; ids outside [0, V) are never dereferenced)
   if (tid == 0 && !greedy && i < g) {
@@ -376,13 +406,17 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   __shared__ float sh_mx[kWaves];
   __shared__ int sh_mi[kWaves];
 
-  if (!greedy) {
-    const float c = temp_scale(T);
-    int M = kEmptyM;
-    double s = 0.0;
-    float mx = -INFINITY;
-    // only a tile that reaches past v1 is masked (the chunk's last one)
-    stream_chunk<DT, U, kBlock, false>(rv, v0, v1, tid, [&](const u32x4 *tile, int t0) {
+  // One streaming loop for both kinds of row (the preloaded tile and the two
+  // register buffers are shared); the fold is chosen per workgroup.
+  const float c = greedy ? 0.0f : temp_scale(T);
+  int M = kEmptyM;  // stochastic: (M, s, max)
+  double s = 0.0;
+  float mx = -INFINITY;
+  float bv = -INFINITY;  // greedy: the maximum and its lowest index; a thread's
+  int bi = 0x7fffffff;   // elements come in increasing index order, so a strict > keeps the first
+  stream_chunk_k1<DT, U, kPre>(rv, v0, v1, tid, pre, [&](const u32x4 *tile, int t0) {
+    if (!greedy) {
+      // only a tile that reaches past v1 is masked (the chunk's last one)
       if (t0 + U * kBlock <= v1) {  // uniform per workgroup
         fold_tile<DT, U>(tile, c, M, s, mx);
       } else {
@@ -390,7 +424,26 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
         mask_tile<DT, U>(tile, t0, v1, tid, m);
         fold_tile<DT, U>(m, c, M, s, mx);
       }
-    });
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {  // lanes past v1 are skipped
+        const int vi = t0 + u * kBlock + tid;
+        if (vi < v1) {
+          float x[kV];
+          widen_vec<DT>(tile[u], x);
+#pragma unroll
+          for (int e = 0; e < kV; ++e) {
+            if (x[e] > bv || bi == 0x7fffffff) {
+              bv = x[e];
+              bi = vi * kV + e;
+            }
+          }
+        }
+      }
+    }
+  });
+
+  if (!greedy) {
     for (long e = se0 + tid; e < se1; e += kBlock) {
       const float z = load_one<DT>(row, e);
       fold_values<1>(&z, c, M, s, mx);
@@ -420,27 +473,6 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
       part[wgid] = pr;
     }
   } else {
-    // lowest index of the maximum; a thread's elements are visited in
-    // increasing index order, so a strict > keeps the first occurrence
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    stream_chunk<DT, U>(rv, v0, v1, tid, [&](const u32x4 *tile, int t0) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int vi = t0 + u * kBlock + tid;
-        if (vi < v1) {
-          float x[kV];
-          widen_vec<DT>(tile[u], x);
-#pragma unroll
-          for (int e = 0; e < kV; ++e) {
-            if (x[e] > bv || bi == 0x7fffffff) {
-              bv = x[e];
-              bi = vi * kV + e;
-            }
-          }
-        }
-      }
-    });
     for (long e = se0 + tid; e < se1; e += kBlock) {
       const float z = load_one<DT>(row, e);
       if (z > bv || bi == 0x7fffffff) {
