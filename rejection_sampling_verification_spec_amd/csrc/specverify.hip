@@ -370,19 +370,24 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   const u32x4 *rv = reinterpret_cast<const u32x4 *>(row);
   const int tid = threadIdx.x;
   // With per-request temperatures and lengths, whether this row is needed (and
-  // how) is known only once temps[b] and lens[b] have arrived; the chunk's first
-  // tile is requested before them, so that the two latencies overlap.  A row
-  // that turns out not to be needed (a greedy request's draft row, a row past
-  // the request's length) has then read one tile for nothing.
+  // how) is known only once temps[b] and lens[b] have arrived.  A target row's
+  // first tile is requested before them, so that the two latencies overlap: a
+  // target row is needed unless it lies past a ragged request's length.  A
+  // draft row is also unneeded for every greedy request, so its first tile
+  // waits for the parameters (requested early, a mixed batch with greedy or
+  // short requests read a tile for nothing in about half of its workgroups).
   constexpr bool kPre = KIND == kMixed;
   u32x4 pre[U];
   if constexpr (kPre) {
-    if (v0 < v1) load_tile<DT, U, kBlock, false>(rv, v0, v1, tid, pre);
+    if (is_target && v0 < v1) load_tile<DT, U, kBlock, false>(rv, v0, v1, tid, pre);
   }
   const int g = request_len(lens, gamma, b);
   const float T = request_T(temps, scalar_T, b);
   const bool greedy = KIND == kGreedyOnly ? true : (KIND == kStochasticOnly ? false : !(T > 0.0f));
   if (is_target ? (i > g) : (greedy || i >= g)) return;
+  if constexpr (kPre) {
+    if (!is_target && v0 < v1) load_tile<DT, U, kBlock, false>(rv, v0, v1, tid, pre);
+  }
 
   // elements read one by one: the tail after the last whole vector (last
   // chunk), or this chunk's share of a row that is not 16-byte aligned
