@@ -796,19 +796,26 @@ constexpr int kLaneElems = kSub / kWave;  // 32
 
 // FILT: the request may be filtered (top-k / top-p); tokens below the cut carry
 // no mass.  Unfiltered launches compile without the compares.
-template <bool FILT>
-__device__ __forceinline__ void residual_value(const SelParams &sp, float zp, float zq, float &w,
-                                               float &p) {
+// USEQ: the residual at a rejection (sp.mode == 1); otherwise the bonus row.
+template <bool FILT, bool USEQ>
+__device__ __forceinline__ void residual_value_of(const SelParams &sp, float zp, float zq, float &w, float &p) {
   float ep = __builtin_amdgcn_exp2f(fmaf(zp, sp.c, sp.negMp));  // -inf -> 0
   if (FILT && !(zp >= sp.tau_p)) ep = 0.0f;
   p = ep;
-  if (sp.mode == 1) {
+  if constexpr (USEQ) {
     float eq = __builtin_amdgcn_exp2f(fmaf(zq, sp.c, sp.negMq));
     if (FILT && !(zq >= sp.tau_q)) eq = 0.0f;
     w = fmaxf(0.0f, fmaf(-eq, sp.r, ep));
   } else {
     w = ep;
   }
+}
+
+template <bool FILT>
+__device__ __forceinline__ void residual_value(const SelParams &sp, float zp, float zq, float &w,
+                                               float &p) {
+  if (sp.mode == 1) residual_value_of<FILT, true>(sp, zp, zq, w, p);
+  else residual_value_of<FILT, false>(sp, zp, zq, w, p);
 }
 
 // The 32 logits of one lane in a sub-chunk starting at token `base`.
@@ -921,6 +928,72 @@ __device__ __forceinline__ void load_lane_raw(const void *row, bool aligned, lon
   }
 }
 
+// One lane's 32 tokens of a sub-chunk that lies wholly inside a 16-byte aligned
+// row, in the interleaved layout of load_lane_raw, with no guards.
+template <int DT>
+__device__ __forceinline__ void load_lane_fast(const void *row, long base, int lane, u32x4 *raw) {
+  constexpr int kV = Elem<DT>::kVec;
+  const u32x4 *r = reinterpret_cast<const u32x4 *>(static_cast<const char *>(row) + base * Elem<DT>::kBytes);
+#pragma unroll
+  for (int u = 0; u < kLaneElems / kV; ++u) raw[u] = r[u * kWave + lane];
+}
+
+// The masses of the wave's SPW consecutive sub-chunks [first, ...) of the row
+// pair to sample (USEQ: residual at a rejection, else the bonus row), loading
+// sub-chunk t+1 while sub-chunk t is reduced.  FAST: every one of them lies
+// wholly inside an aligned row.
+template <int DT, bool FILT, bool FAST, bool USEQ>
+__device__ __forceinline__ void mass_pass(const RowPair &rp, const SelParams &sp, int first, int SPW, int NSUB,
+                                          int V, int lane, SubSums *__restrict__ out) {
+  constexpr int kN = kLaneElems / Elem<DT>::kVec;
+  auto load = [&](const void *row, int sub, u32x4 *dst) {
+    if constexpr (FAST) load_lane_fast<DT>(row, static_cast<long>(sub) * kSub, lane, dst);
+    else load_lane_raw<DT>(row, rp.aligned, static_cast<long>(sub) * kSub, lane, V, dst);
+  };
+  u32x4 tc[kN], dc[kN], tn[kN], dn[kN];
+  load(rp.trow, first, tc);
+  if constexpr (USEQ) load(rp.drow, first, dc);
+  for (int t = 0; t < SPW; ++t) {
+    const int sub = first + t;
+    if (sub >= NSUB) break;
+    if (t + 1 < SPW && sub + 1 < NSUB) {
+      load(rp.trow, sub + 1, tn);
+      if constexpr (USEQ) load(rp.drow, sub + 1, dn);
+    }
+    float aw[8], ap[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) aw[e] = ap[e] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+      float zp[Elem<DT>::kVec], zq[Elem<DT>::kVec];
+      widen_vec<DT>(tc[u], zp);
+      if constexpr (USEQ) widen_vec<DT>(dc[u], zq);
+#pragma unroll
+      for (int e = 0; e < Elem<DT>::kVec; ++e) {
+        float w, p;
+        residual_value_of<FILT, USEQ>(sp, zp[e], USEQ ? zq[e] : 0.0f, w, p);
+        aw[e & 7] += w;
+        ap[e & 7] += p;
+      }
+    }
+    const float lw = ((aw[0] + aw[1]) + (aw[2] + aw[3])) + ((aw[4] + aw[5]) + (aw[6] + aw[7]));
+    const float lp = ((ap[0] + ap[1]) + (ap[2] + ap[3])) + ((ap[4] + ap[5]) + (ap[6] + ap[7]));
+    const double sw = wave_sum(static_cast<double>(lw));
+    const double spp = wave_sum(static_cast<double>(lp));
+    if (lane == 0) {
+      SubSums ss;
+      ss.w = sw;
+      ss.p = spp;
+      out[sub] = ss;
+    }
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+      tc[u] = tn[u];
+      if constexpr (USEQ) dc[u] = dn[u];
+    }
+  }
+}
+
 // K2 (decide) fused with K3a (mass): NW workgroups per request.  Each one
 // recomputes the request's decision (cheap and deterministic) and workgroup 0
 // stores it; then every wave writes the masses of SPW consecutive 2048-token
@@ -936,7 +1009,6 @@ __global__ __launch_bounds__(kBlock) void k2_decide_mass(
     const FilterStats *__restrict__ fst, int32_t *__restrict__ accepted_count,
     int32_t *__restrict__ out_tokens, SelParams *__restrict__ sel, SubSums *__restrict__ sums,
     sv_debug dbg) {
-  constexpr int kN = kLaneElems / Elem<DT>::kVec;
   const int b = blockIdx.x / NW;
   const int wg = blockIdx.x - b * NW;
   // greedy requests need the decision only (workgroup 0)
@@ -949,47 +1021,16 @@ __global__ __launch_bounds__(kBlock) void k2_decide_mass(
   if (sp.mode == 0 || first >= NSUB) return;  // uniform per wave; no barrier below
   const int lane = threadIdx.x & (kWave - 1);
   const RowPair rp = selected_rows<DT>(target, draft, gamma, V, b, sp);
-  u32x4 tc[kN], dc[kN], tn[kN], dn[kN];
-  load_lane_raw<DT>(rp.trow, rp.aligned, static_cast<long>(first) * kSub, lane, V, tc);
-  if (sp.mode == 1) load_lane_raw<DT>(rp.drow, rp.aligned, static_cast<long>(first) * kSub, lane, V, dc);
-  for (int t = 0; t < SPW; ++t) {
-    const int sub = first + t;
-    if (sub >= NSUB) break;
-    if (t + 1 < SPW && sub + 1 < NSUB) {
-      load_lane_raw<DT>(rp.trow, rp.aligned, static_cast<long>(sub + 1) * kSub, lane, V, tn);
-      if (sp.mode == 1) load_lane_raw<DT>(rp.drow, rp.aligned, static_cast<long>(sub + 1) * kSub, lane, V, dn);
-    }
-    float aw[8], ap[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) aw[e] = ap[e] = 0.0f;
-#pragma unroll
-    for (int u = 0; u < kN; ++u) {
-      float zp[Elem<DT>::kVec], zq[Elem<DT>::kVec];
-      widen_vec<DT>(tc[u], zp);
-      if (sp.mode == 1) widen_vec<DT>(dc[u], zq);
-#pragma unroll
-      for (int e = 0; e < Elem<DT>::kVec; ++e) {
-        float w, p;
-        residual_value<FILT>(sp, zp[e], sp.mode == 1 ? zq[e] : 0.0f, w, p);
-        aw[e & 7] += w;
-        ap[e & 7] += p;
-      }
-    }
-    const float lw = ((aw[0] + aw[1]) + (aw[2] + aw[3])) + ((aw[4] + aw[5]) + (aw[6] + aw[7]));
-    const float lp = ((ap[0] + ap[1]) + (ap[2] + ap[3])) + ((ap[4] + ap[5]) + (ap[6] + ap[7]));
-    const double sw = wave_sum(static_cast<double>(lw));
-    const double spp = wave_sum(static_cast<double>(lp));
-    if (lane == 0) {
-      SubSums ss;
-      ss.w = sw;
-      ss.p = spp;
-      sums[static_cast<long>(b) * NSUB + sub] = ss;
-    }
-#pragma unroll
-    for (int u = 0; u < kN; ++u) {
-      tc[u] = tn[u];
-      dc[u] = dn[u];
-    }
+  SubSums *out = sums + static_cast<long>(b) * NSUB;
+  // the wave's sub-chunks lie wholly inside an aligned row: straight-line
+  // loads, so that the arithmetic on each vector can start as it arrives
+  const bool fast = rp.aligned && static_cast<long>(min(first + SPW, NSUB)) * kSub <= static_cast<long>(V);
+  if (sp.mode == 1) {
+    if (fast) mass_pass<DT, FILT, true, true>(rp, sp, first, SPW, NSUB, V, lane, out);
+    else mass_pass<DT, FILT, false, true>(rp, sp, first, SPW, NSUB, V, lane, out);
+  } else {
+    if (fast) mass_pass<DT, FILT, true, false>(rp, sp, first, SPW, NSUB, V, lane, out);
+    else mass_pass<DT, FILT, false, false>(rp, sp, first, SPW, NSUB, V, lane, out);
   }
 }
 
@@ -2077,49 +2118,63 @@ __device__ __forceinline__ void merged_row(const Partial *part, long slot, int N
   arg = ix;
 }
 
-// Masses of w = max(0, e_p - r e_q) (or e_p when !use_q) over 2048-token
+// Masses of w = max(0, e_p - r e_q) (or e_p without USEQ) over 2048-token
 // sub-chunks of the position's rows, into sh.sub; their sum into sh.W.
-template <int DT>
-__device__ void tree_masses(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c,
-                            float negMp, float negMq, float r, bool use_q, TreeShared &sh) {
+template <int DT, bool USEQ>
+__device__ __forceinline__ float tree_lane_mass(const u32x4 *tp, const u32x4 *dq, float c, float negMp, float negMq,
+                                                float r) {
+  constexpr int kN = kLaneElems / Elem<DT>::kVec;
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kN; ++u) {
+    float zp[Elem<DT>::kVec], zq[Elem<DT>::kVec];
+    widen_vec<DT>(tp[u], zp);
+    if constexpr (USEQ) widen_vec<DT>(dq[u], zq);
+#pragma unroll
+    for (int e = 0; e < Elem<DT>::kVec; ++e) {
+      const float ep = __builtin_amdgcn_exp2f(fmaf(zp[e], c, negMp));
+      if constexpr (USEQ) acc += fmaxf(0.0f, fmaf(-__builtin_amdgcn_exp2f(fmaf(zq[e], c, negMq)), r, ep));
+      else acc += ep;
+    }
+  }
+  return acc;
+}
+
+template <int DT, bool USEQ>
+__device__ __forceinline__ void tree_masses_of(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c,
+                               float negMp, float negMq, float r, TreeShared &sh) {
   constexpr int kN = kLaneElems / Elem<DT>::kVec;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  // each wave takes sub-chunks wave, wave + kTWaves, ...; bf16 rows load the
-  // next one while the current one is reduced (fp32 rows, twice the registers
-  // per sub-chunk, load one at a time)
-  constexpr bool kAhead = DT == SV_BF16;
-  u32x4 tp[kN], dq[kN], tn[kN], dn[kN];
-  if (kAhead && wave < NSUB) {
-    load_lane_raw<DT>(trow, aligned, static_cast<long>(wave) * kSub, lane, V, tp);
-    if (use_q) load_lane_raw<DT>(drow, aligned, static_cast<long>(wave) * kSub, lane, V, dq);
-  }
-  for (int j = wave; j < NSUB; j += kTWaves) {
-    const int jn = kAhead ? j + kTWaves : j;
-    if (jn < NSUB) {
-      load_lane_raw<DT>(trow, aligned, static_cast<long>(jn) * kSub, lane, V, kAhead ? tn : tp);
-      if (use_q) load_lane_raw<DT>(drow, aligned, static_cast<long>(jn) * kSub, lane, V, kAhead ? dn : dq);
-    }
-    float acc = 0.0f;
-#pragma unroll
-    for (int u = 0; u < kN; ++u) {
-      float zp[Elem<DT>::kVec], zq[Elem<DT>::kVec];
-      widen_vec<DT>(tp[u], zp);
-      if (use_q) widen_vec<DT>(dq[u], zq);
-#pragma unroll
-      for (int e = 0; e < Elem<DT>::kVec; ++e) {
-        const float ep = __builtin_amdgcn_exp2f(fmaf(zp[e], c, negMp));
-        acc += use_q ? fmaxf(0.0f, fmaf(-__builtin_amdgcn_exp2f(fmaf(zq[e], c, negMq)), r, ep)) : ep;
-      }
-    }
-    const double ws = wave_sum(static_cast<double>(acc));
-    if (lane == 0) sh.sub[j] = ws;
-    if (kAhead) {
+  // Sub-chunks wholly inside an aligned row: wave w takes w, w + kTWaves, ...
+  // with straight-line loads, the next one requested while the current one is
+  // reduced (its index clamped to the last such sub-chunk, so that the loads are
+  // unconditional and each wait covers exactly the older sub-chunk).
+  const int nfast = aligned ? min(NSUB, V / kSub) : 0;
+  if (wave < nfast) {
+    u32x4 tp[kN], dq[kN], tn[kN], dn[kN];
+    load_lane_fast<DT>(trow, static_cast<long>(wave) * kSub, lane, tp);
+    if constexpr (USEQ) load_lane_fast<DT>(drow, static_cast<long>(wave) * kSub, lane, dq);
+    for (int j = wave; j < nfast; j += kTWaves) {
+      const long jn = min(j + kTWaves, nfast - 1);
+      load_lane_fast<DT>(trow, jn * kSub, lane, tn);
+      if constexpr (USEQ) load_lane_fast<DT>(drow, jn * kSub, lane, dn);
+      const double ws = wave_sum(static_cast<double>(tree_lane_mass<DT, USEQ>(tp, dq, c, negMp, negMq, r)));
+      if (lane == 0) sh.sub[j] = ws;
 #pragma unroll
       for (int u = 0; u < kN; ++u) {
         tp[u] = tn[u];
-        dq[u] = dn[u];
+        if constexpr (USEQ) dq[u] = dn[u];
       }
     }
+  }
+  // the rest (a partial last sub-chunk, or every sub-chunk of a row that is not
+  // aligned): guarded loads, one sub-chunk at a time
+  for (int j = nfast + wave; j < NSUB; j += kTWaves) {
+    u32x4 tp[kN], dq[kN];
+    load_lane_raw<DT>(trow, aligned, static_cast<long>(j) * kSub, lane, V, tp);
+    if constexpr (USEQ) load_lane_raw<DT>(drow, aligned, static_cast<long>(j) * kSub, lane, V, dq);
+    const double ws = wave_sum(static_cast<double>(tree_lane_mass<DT, USEQ>(tp, dq, c, negMp, negMq, r)));
+    if (lane == 0) sh.sub[j] = ws;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -2130,11 +2185,18 @@ __device__ void tree_masses(const void *trow, const void *drow, bool aligned, in
   __syncthreads();
 }
 
+template <int DT>
+__device__ __forceinline__ void tree_masses(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c,
+                            float negMp, float negMq, float r, bool use_q, TreeShared &sh) {
+  if (use_q) tree_masses_of<DT, true>(trow, drow, aligned, V, NSUB, c, negMp, negMq, r, sh);
+  else tree_masses_of<DT, false>(trow, drow, aligned, V, NSUB, c, negMp, negMq, r, sh);
+}
+
 // Inverse CDF over the masses in sh.sub (of the same w as tree_masses): the
 // lowest token with mass whose running prefix exceeds u * W; if rounding
 // leaves none, the last token with mass.
 template <int DT>
-__device__ int tree_select(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c, float negMp,
+__device__ __forceinline__ int tree_select(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c, float negMp,
                            float negMq, float r, bool use_q, float u, TreeShared &sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   if (tid == 0) {
