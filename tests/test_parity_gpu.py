@@ -63,6 +63,9 @@ SHAPES = [
     (3, 31, 64, "bf16"), (2, 32, 1000, "f32"), (5, 8, 1000, "bf16"), (4, 1, 4099, "f32"),
     (3, 5, 4099, "bf16"), (2, 4, 16384, "bf16"), (2, 4, 16385, "f32"), (3, 2, 40000, "bf16"),
     (2, 3, 70001, "f32"), (6, 0, 3000, "bf16"),
+    # sub-chunk boundaries: one whole 2048-token sub-chunk, one plus a single
+    # token, three whole ones
+    (3, 3, 2048, "bf16"), (3, 3, 2049, "bf16"), (2, 2, 6144, "f32"),
 ]
 
 

@@ -69,6 +69,7 @@ CASES = [
     (8, 1, 6, 4096, "f32", 1.3),             # a chain
     (5, 5, 1, 20000, "f32", 1.0),            # one level of five siblings
     (8, 2, 2, 3000, "bf16", "mixed"),
+    (4, 3, 2, 8192, "bf16", 1.0),            # whole 2048-token sub-chunks only
 ]
 
 
