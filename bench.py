@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--mode", choices=["stochastic", "greedy"], default="stochastic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tree", action="store_true", help="skip the tree-verification measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations' timings and the cold-latency distribution")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly instead of graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -67,11 +69,11 @@ def parse():
 
 # --------------------------------------------------------------------------- profile summaries
 PROFILE_COMMANDS = {
-    "kt": "rocprofv3 --kernel-trace --stats -d DIR/kt -o kt --output-format csv -- python3 bench.py",
+    "kt": "rocprofv3 --kernel-trace --stats -d DIR/kt -o kt --output-format csv -- python3 bench.py --no-configs",
     "pmc_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -d DIR/pmc_FETCH_SIZE -o pmc --output-format csv -- "
-                      "python3 bench.py --steps 14 --warmup 7 --no-cpu-baseline --eager",
+                      "python3 bench.py --steps 14 --warmup 7 --no-cpu-baseline --eager --no-configs",
     "pmc_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -d DIR/pmc_WRITE_SIZE -o pmc --output-format csv -- "
-                      "python3 bench.py --steps 14 --warmup 7 --no-cpu-baseline --eager",
+                      "python3 bench.py --steps 14 --warmup 7 --no-cpu-baseline --eager --no-configs",
     "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -d DIR/copy_FETCH_SIZE -o pmc --output-format csv -- "
                        "python3 bench.py --copy-calibration",
     "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -d DIR/copy_WRITE_SIZE -o pmc --output-format csv -- "
@@ -187,6 +189,80 @@ def copy_calibration():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
+
+
+def time_config(sv, W, torch, math, cfg, greedy, dev, stream, reps_target=100):
+    """Throughput of spec_verify (uniform T) or spec_verify_ex (per-request T and lengths) on one of
+    the configurations, inputs rotated over enough copies to exceed the last-level cache where that
+    fits in 1.2 GB (at most 64 copies: the smallest configurations run from cache, and say so)."""
+    t0 = time.perf_counter()
+    w = W.make_config(cfg, greedy=greedy)
+    gen_s = time.perf_counter() - t0
+    t = w.to_torch(dev)
+    elt = 2 if w.dtype == "bf16" else 4
+    copy_bytes = (t["target"].numel() + t["draft"].numel()) * elt
+    copies = min(64, max(2, math.ceil(1.2e9 / copy_bytes)))
+    tg = [t["target"]] + [t["target"].clone() for _ in range(copies - 1)]
+    dr = [t["draft"]] + [t["draft"].clone() for _ in range(copies - 1)]
+    dt = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
+    ws = torch.empty(sv.spec_verify_workspace_bytes(w.B, w.gamma, w.V, dt), dtype=torch.uint8, device=dev)
+    cnt = torch.empty(w.B, dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.gamma + 1), dtype=torch.int32, device=dev)
+    uniform = w.lens is None and w.scalar_temperature is not None
+
+    def one(c):
+        if uniform:
+            sv.spec_verify(tg[c], dr[c], t["draft_tokens"], t["u_accept"], t["u_sample"], float(w.scalar_temperature),
+                           accepted_count=cnt, out_tokens=out, workspace=ws, stream=stream)
+        else:
+            sv.spec_verify_ex(tg[c], dr[c], t["draft_tokens"], t["u_accept"], t["u_sample"], t["temperature"],
+                              t.get("lens"), accepted_count=cnt, out_tokens=out, workspace=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        one(0)
+    torch.cuda.synchronize()
+    rc, ro = cnt.cpu().clone(), out.cpu().clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in range(copies):
+            one(c)
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, reps_target // copies)
+    s0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            g.replay()
+    torch.cuda.synchronize()
+    per = (time.perf_counter() - s0) / (reps * copies)
+    assert torch.equal(cnt.cpu(), rc) and torch.equal(out.cpu(), ro), f"config {cfg} replay differs"
+    return {"workload": w.name, "entry": "spec_verify" if uniform else "spec_verify_ex",
+            "us_per_call": round(per * 1e6, 3), "positions_per_s": round(w.positions() / per, 1),
+            "GBps_alg": round(w.bytes_alg() / per / 1e9, 1), "bytes_alg": w.bytes_alg(),
+            "copies_rotated": copies, "cache_warm": copies * copy_bytes < 512e6,
+            "alpha_hat": round(float(rc.float().sum()) / max(1, w.positions()), 4),
+            "generate_s": round(gen_s, 1)}
+
+
+def cold_latency(torch, np, one_call, stream, dev, n=41):
+    """Per-call latency with the last-level cache flushed before each call (a 512 MB fill that the
+    events exclude): median, p10 and p90 over n calls."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ts = []
+    for k in range(n):
+        with torch.cuda.stream(stream):
+            flush.fill_(k & 0xff)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            one_call(k)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    del flush
+    q = np.percentile(np.array(ts), [10, 50, 90])
+    return {"p10_us": round(float(q[0]), 2), "median_us": round(float(q[1]), 2), "p90_us": round(float(q[2]), 2),
+            "calls": n}
 
 
 def main():
@@ -445,6 +521,17 @@ def main():
                 "GBps_alg": round(tw.bytes_alg() / per / 1e9, 1)}
         log(f"[bench] spec_verify_tree {tree}")
 
+    # cold per-call latency of the timed call, and the other configurations' throughput
+    latency, configs = None, {}
+    if not args.no_configs:
+        latency = cold_latency(torch, np, lambda k: step(k % copies, stream), stream, dev)
+        log(f"[bench] cold latency {latency}")
+        runs = [(0, False), (1, False), (2, False), (4, False)] + ([(3, True)] if not greedy else [])
+        for cfg, gr in runs:
+            key = f"config{cfg}" + ("_greedy" if gr else "")
+            configs[key] = time_config(sv, W, torch, math, cfg, gr, dev, stream)
+            log(f"[bench] {key} {configs[key]}")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -487,6 +574,8 @@ def main():
                   "spec_sample": sample,
                   "spec_verify_filtered": filtered,
                   "spec_verify_tree": tree,
+                  "cold_latency": latency,
+                  "configs": configs,
                   "kernel_source_sha256_16": source_hash()},
     }
     print(json.dumps(rec), flush=True)
