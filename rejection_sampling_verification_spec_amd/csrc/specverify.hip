@@ -1568,6 +1568,7 @@ __device__ __forceinline__ void row_scale(const Partial *part, long slot, int NS
 // one atomic and copies them out.  A wave that finds more than kWaveCap
 // candidates pushes the row's count past kGCap (the general path).
 constexpr int kWaveCap = 2048;
+constexpr unsigned kStageVecs = 128;  // 16-byte vectors a wave stages before it offers them (2 KB)
 
 template <int DT>
 __global__ __launch_bounds__(kLBlock) void k_filter_capture(
@@ -1602,6 +1603,29 @@ __global__ __launch_bounds__(kLBlock) void k_filter_capture(
     }
     wcount += static_cast<unsigned>(__popcll(mask));
   };
+  // Vectors that hold a candidate are rare on most rows, so a lane whose
+  // vector's maximum passes the window test copies the raw vector into the
+  // wave's staging area (one 16-byte LDS store), and the wave offers the
+  // staged logits together, 64 at a time, once the area is half full: one
+  // ballot round per 64 staged logits instead of one per logit of every
+  // vector round with a candidate somewhere in the wave.
+  __shared__ u32x4 stage[kLBlock / kWave][kStageVecs];
+  unsigned nst = 0;  // vectors staged by the wave (the same in every lane)
+  auto flush = [&]() {
+    __builtin_amdgcn_wave_barrier();  // the stores above come first
+    const unsigned n = nst * static_cast<unsigned>(kV);
+    for (unsigned i0 = 0; i0 < n; i0 += kWave) {
+      const unsigned i = i0 + static_cast<unsigned>(lane);
+      float z = -INFINITY;
+      if (i < n) {
+        if constexpr (DT == SV_F32) z = reinterpret_cast<const float *>(stage[wave])[i];
+        else z = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(stage[wave])[i]) << 16);
+      }
+      offer(z);
+    }
+    __builtin_amdgcn_wave_barrier();  // the loads above complete before the area is reused
+    nst = 0;
+  };
   const char *rb = static_cast<const char *>(row);
   const long nvec = (static_cast<long>(V) + kV - 1) / kV;
   const long vb = static_cast<long>(j) * chunk_vecs, ve = min(vb + chunk_vecs, nvec);
@@ -1611,19 +1635,22 @@ __global__ __launch_bounds__(kLBlock) void k_filter_capture(
   // out-of-range vectors read as -inf
   stream_chunk<DT, U, kLBlock>(reinterpret_cast<const u32x4 *>(rb), static_cast<int>(vb), static_cast<int>(vw), tid,
                                [&](const u32x4 *tile, int) {
-#pragma unroll 1
+#pragma unroll
                                  for (int u = 0; u < U; ++u) {
                                    float x[kV];
                                    widen_vec<DT>(tile[u], x);
                                    float m = x[0];
 #pragma unroll
                                    for (int e = 1; e < kV; ++e) m = fmaxf(m, x[e]);
-                                   // no lane of the wave has a candidate
-                                   if (!__ballot(in_window(m, c, negM))) continue;
-#pragma unroll
-                                   for (int e = 0; e < kV; ++e) offer(x[e]);
+                                   const bool hit = in_window(m, c, negM);
+                                   const unsigned long long F = __ballot(hit);
+                                   if (!F) continue;  // no lane of the wave has a candidate
+                                   if (hit) stage[wave][nst + static_cast<unsigned>(__popcll(F & lt))] = tile[u];
+                                   nst += static_cast<unsigned>(__popcll(F));
+                                   if (nst > kStageVecs - kWave) flush();
                                  }
                                });
+  if (nst) flush();
   // the rest one by one (a partial last vector, or a row that is not aligned)
   const long e0 = max(vb, vw) * kV, e1 = min(ve * kV, static_cast<long>(V));
   for (long eb = e0; eb < e1; eb += kLBlock) {
