@@ -562,6 +562,7 @@ constexpr int kFCap = 4096;   // logits sorted and scanned in LDS
 constexpr int kLevels = 16;   // the capture window: levels of one binary order of magnitude below 2^M
 constexpr int kGCap = 32768;  // logits a row may capture (T = 1.2 rows of a 128K vocabulary fit)
 constexpr int kDeep = 12;     // deeper floors y = -18, -20, ..., -40 (FD, FC)
+constexpr unsigned kStageVecs = 128;  // 16-byte vectors a wave stages before it offers them (2 KB)
 
 struct alignas(16) FilterStats {
   double s_kept;  // sum of 2^(z c - M) over the kept tokens
@@ -1212,6 +1213,7 @@ struct GeneralShared {
       unsigned tot[kDeep + 1];
       unsigned wc[kFWaves];
     } d;
+    u32x4 stage[kFWaves][kStageVecs];  // deeper capture: each wave's staged vectors
   } u;
   FilterScratch sc;
 };
@@ -1568,7 +1570,6 @@ __device__ __forceinline__ void row_scale(const Partial *part, long slot, int NS
 // one atomic and copies them out.  A wave that finds more than kWaveCap
 // candidates pushes the row's count past kGCap (the general path).
 constexpr int kWaveCap = 2048;
-constexpr unsigned kStageVecs = 128;  // 16-byte vectors a wave stages before it offers them (2 KB)
 
 template <int DT>
 __global__ __launch_bounds__(kLBlock) void k_filter_capture(
@@ -1764,29 +1765,6 @@ __device__ bool list_resolve(const unsigned *cand, int n, float c, float negM, i
 
 __device__ __forceinline__ int deep_level(int j) { return kLevels + 2 * (j + 1); }
 
-// f(z) for every logit of a row, in control flow that is uniform over the
-// workgroup: whole vectors of an aligned row stream as in K1 (out-of-range
-// vectors read as -inf), the rest one by one with -inf past the row's end.
-template <int DT, int U, typename F>
-__device__ __forceinline__ void for_each_logit_uniform(const void *row, bool aligned, int V, F &&f) {
-  constexpr int kV = Elem<DT>::kVec;
-  const int tid = threadIdx.x;
-  const int vw = aligned ? V / kV : 0;
-  stream_chunk<DT, U, kFBlock>(reinterpret_cast<const u32x4 *>(row), 0, vw, tid, [&](const u32x4 *tile, int) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float x[kV];
-      widen_vec<DT>(tile[u], x);
-#pragma unroll
-      for (int e = 0; e < kV; ++e) f(x[e]);
-    }
-  });
-  for (long eb = static_cast<long>(vw) * kV; eb < V; eb += kFBlock) {
-    const long e = eb + tid;
-    f(e < V ? load_one<DT>(row, e) : -INFINITY);
-  }
-}
-
 // Per-thread counts of the logits of vectors [vb, vw) (whole 16-byte vectors of
 // an aligned row, streamed as in K1) and elements [e0, e1) (one by one) in the
 // bands between the deeper floors: band b holds the logits with
@@ -1856,9 +1834,11 @@ __device__ __forceinline__ int choose_floor(const unsigned *band, int k) {
 }
 
 // Second pass: every logit with y > -L goes to the row's list.  Each wave
-// fills its own part of the list (slots from a ballot, a scalar count), then
-// the parts are packed to the front of the list through LDS.  Returns the
-// list's length, or kGCap + 1 when a wave's part overflowed.
+// fills its own part of the list (slots from a ballot, a scalar count; the
+// vectors that can hold such a logit are first staged in LDS and offered 64
+// logits at a time), then the parts are packed to the front of the list
+// through LDS.  Returns the list's length, or kGCap + 1 when a wave's part
+// overflowed.
 template <int DT>
 __device__ unsigned deep_capture(const void *row, bool aligned, int V, float c, float negM, int L,
                                  unsigned *cand, GeneralShared &sh) {
@@ -1868,7 +1848,7 @@ __device__ unsigned deep_capture(const void *row, bool aligned, int V, float c, 
   const unsigned long long lt = (1ull << lane) - 1ull;
   unsigned *part = cand + wave * kPart;
   unsigned wcount = 0;  // the same in every lane of the wave
-  for_each_logit_uniform<DT, 8>(row, aligned, V, [&](float z) {
+  auto offer = [&](float z) {  // called by every lane of the wave together
     const bool in = fmaf(z, c, negM) > floor_y;
     const unsigned long long mask = __ballot(in);
     if (in) {
@@ -1876,7 +1856,50 @@ __device__ unsigned deep_capture(const void *row, bool aligned, int V, float c, 
       if (q < kPart) part[q] = order_key(z);
     }
     wcount += static_cast<unsigned>(__popcll(mask));
+  };
+  // as in the capture kernel: a vector whose maximum passes the floor is staged
+  // in LDS, and the wave offers the staged logits 64 per ballot round
+  constexpr int kV = Elem<DT>::kVec;
+  unsigned nst = 0;
+  auto flush = [&]() {
+    __builtin_amdgcn_wave_barrier();
+    const unsigned n = nst * static_cast<unsigned>(kV);
+    for (unsigned i0 = 0; i0 < n; i0 += kWave) {
+      const unsigned i = i0 + static_cast<unsigned>(lane);
+      float z = -INFINITY;
+      if (i < n) {
+        if constexpr (DT == SV_F32) z = reinterpret_cast<const float *>(sh.u.stage[wave])[i];
+        else z = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(sh.u.stage[wave])[i]) << 16);
+      }
+      offer(z);
+    }
+    __builtin_amdgcn_wave_barrier();
+    nst = 0;
+  };
+  const int vw = aligned ? V / kV : 0;  // whole 16-byte vectors
+  stream_chunk<DT, 8, kFBlock>(reinterpret_cast<const u32x4 *>(row), 0, vw, tid, [&](const u32x4 *tile, int) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float x[kV];
+      widen_vec<DT>(tile[u], x);
+      float m = x[0];
+#pragma unroll
+      for (int e = 1; e < kV; ++e) m = fmaxf(m, x[e]);
+      const bool hit = fmaf(m, c, negM) > floor_y;  // fma is monotonic in z for c > 0
+      const unsigned long long F = __ballot(hit);
+      if (!F) continue;
+      if (hit) sh.u.stage[wave][nst + static_cast<unsigned>(__popcll(F & lt))] = tile[u];
+      nst += static_cast<unsigned>(__popcll(F));
+      if (nst > kStageVecs - kWave) flush();
+    }
   });
+  if (nst) flush();
+  // the rest one by one (a partial last vector, or a row that is not aligned)
+  for (long eb = static_cast<long>(vw) * kV; eb < V; eb += kFBlock) {
+    const long e = eb + tid;
+    offer(e < V ? load_one<DT>(row, e) : -INFINITY);
+  }
+  __syncthreads();  // every wave is done with its staging area, which wc overlaps
   if (lane == 0) sh.u.d.wc[wave] = wcount;
   __syncthreads();
   unsigned total = 0, before = 0;
