@@ -1992,6 +1992,13 @@ __global__ __launch_bounds__(kLBlock) void k_filter_deep_count(
   constexpr int kV = Elem<DT>::kVec;
   const long slot = blockIdx.x / NS;
   const int j = static_cast<int>(blockIdx.x - slot * NS);
+  {  // most rows need no deeper count: decide that from top_k and the captured
+     // count alone (one round trip) before the rest of the row's set-up
+    const int b = static_cast<int>(slot / (2 * gamma + 1));
+    const int kr = topk[b];
+    const unsigned nc = fw.ncand[slot];
+    if (!(kr > 0 && kr < V && nc < static_cast<unsigned>(kr))) return;  // uniform per workgroup
+  }
   const FilterRow fr = filter_row_setup<DT>(target, draft, temps, lens, topk, topp, gamma, V, NS, part, slot);
   if (!fr.row || !needs_deeper(fr.k, fw, slot)) return;  // uniform per workgroup
   // the chunk's whole vectors, then its remaining elements (the capture kernel's split)
