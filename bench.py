@@ -43,7 +43,14 @@ def log(msg):
 
 
 def source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source with comments and blank space removed, so that
+    stored counters stay valid across edits that change no code."""
+    import re
+    text = open(KERNEL_SRC, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+    text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+    code = " ".join(text.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def parse():

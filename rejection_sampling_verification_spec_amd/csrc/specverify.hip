@@ -374,8 +374,8 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   // first tile is requested before them, so that the two latencies overlap: a
   // target row is needed unless it lies past a ragged request's length.  A
   // draft row is also unneeded for every greedy request, so its first tile
-  // waits for the parameters (requested early, a mixed batch with greedy or
-  // short requests read a tile for nothing in about half of its workgroups).
+  // waits for the parameters: requested early as well, it was read for nothing
+  // in about half of the workgroups of a batch with greedy and short requests.
   constexpr bool kPre = KIND == kMixed;
   u32x4 pre[U];
   if constexpr (kPre) {
