@@ -241,6 +241,16 @@ def test_filtered_serving_shape(top_k, top_p):
     assert rep["flagged"] <= 2
 
 
+def test_filtered_largest_vocabulary():
+    """V = 2^20, the largest the filtered entry point accepts (fixed-point masses with
+    41 fractional bits), top_k = 100 and top_p = 0.9."""
+    w = with_filter(W.build("B2_g2_V1048576_bf16_T0.7_zipf", 2200, 2, 2, 1 << 20, "bf16", target_scale=4.0,
+                            zipf=True, sigma=0.5, temps=0.7), top_k=100, top_p=0.9)
+    redraw_filtered_drafts(w, 2201)
+    rep = run_and_check(w, debug=True, require_no_flags=False)
+    assert rep["flagged"] <= 1
+
+
 @pytest.mark.parametrize("T", [1.2, 2.5])
 def test_filtered_flat_rows(T):
     """Serving-size rows at a high temperature: at T = 1.2 the capture window holds up to

@@ -86,6 +86,22 @@ def test_random_shapes(B, gamma, V, dtype, mode):
     run_and_check(w, debug=False, require_no_flags=False)
 
 
+@pytest.mark.parametrize("dtype,mode", [("bf16", "uniform"), ("f32", "mixed")])
+def test_large_vocabulary(dtype, mode):
+    """V = 2^20 + 3: 513 sub-chunks per row (the selection scans the sub-chunk masses
+    in nine batches of 64; the last sub-chunk holds three tokens) and many K1 chunks
+    per row."""
+    V = (1 << 20) + 3
+    seed = 4100 + (mode == "mixed")
+    if mode == "uniform":
+        w = W.make_random(seed, 3, 3, V, dtype, temps=1.0, target_scale=4.0, sigma=0.5, zipf=True)
+    else:
+        w = W.make_random(seed, 4, 3, V, dtype, temps=np.array([0.0, 0.7, 1.0, 1.3], np.float32),
+                          lens=np.array([3, 1, 3, 2], np.int32), target_scale=4.0, sigma=0.8, zipf=True)
+    say(f"large vocabulary {dtype} {mode} V={V}")
+    run_and_check(w, debug=True, require_no_flags=False)
+
+
 def test_greedy_ties_lowest_index():
     rng = np.random.default_rng(0)
     B, gamma, V = 16, 4, 5000

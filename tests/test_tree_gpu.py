@@ -139,6 +139,14 @@ def test_tree_serving_shape():
     check(w, max_flagged=1)
 
 
+def test_tree_largest_vocabulary():
+    """V = 2^20, the largest the tree entry point accepts: 512 sub-chunk masses per
+    position, all kept in LDS."""
+    w = W.build_tree("B2_w2_d2_V1048576_f32", 3100, 2, 2, 2, 1 << 20, "f32", target_scale=3.0, zipf=True,
+                     sigma=0.6, temps=1.0)
+    check(w, max_flagged=1)
+
+
 def test_tree_deterministic():
     w = W.build_tree("det", 74, 6, 3, 3, 9000, "bf16", target_scale=3.0, zipf=True, sigma=0.6, temps=1.0)
     a = gpu_tree(w)
