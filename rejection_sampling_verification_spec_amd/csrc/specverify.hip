@@ -586,11 +586,6 @@ __device__ __forceinline__ bool filter_params(int kr, float pr, int V, int &k, f
   return k > 0 || p < 1.0f;
 }
 
-__device__ __forceinline__ bool request_filter(const int32_t *topk, const float *topp, int b, int V,
-                                               int &k, float &p) {
-  return filter_params(topk ? topk[b] : 0, topp ? topp[b] : 1.0f, V, k, p);
-}
-
 // ================================================================== K2
 constexpr int kK2Batch = 8;  // chunk partials fetched together per row
 
@@ -1947,7 +1942,8 @@ __device__ __forceinline__ FilterRow filter_row_setup(const void *target, const 
   return fr;
 }
 
-// FilterStats.pad after FC: 0 resolved, 1 pending for the general path (FE).
+// FilterStats.pad after FC, for every row: 0 resolved (or not filtered), 1 pending for the
+// general path (FE).
 enum { kFResolved = 0, kFGeneral = 1 };
 
 __device__ __forceinline__ void store_filter_stats(FilterStats *fst, long slot, unsigned long long kept, int fs,
@@ -1959,21 +1955,6 @@ __device__ __forceinline__ void store_filter_stats(FilterStats *fst, long slot, 
     f.pad = state;
     fst[slot] = f;
   }
-}
-
-// Whether row `slot` is filtered and FC left it in `state`.  The
-// stats are read only for filtered rows (the others are never written).
-__device__ __forceinline__ bool filter_pending(const float *temps, const int32_t *lens, const int32_t *topk,
-                                               const float *topp, int gamma, int V, long slot,
-                                               const FilterStats *fst, int state) {
-  const int rows = 2 * gamma + 1;
-  const int b = static_cast<int>(slot / rows), r = static_cast<int>(slot - static_cast<long>(b) * rows);
-  int k;
-  float p;
-  if (!(temps[b] > 0.0f) || !request_filter(topk, topp, b, V, k, p)) return false;
-  const int g = request_len(lens, gamma, b);
-  if (r <= gamma ? r > g : r - gamma - 1 >= g) return false;
-  return fst[slot].pad == state;
 }
 
 // Whether top-k row `slot` captured fewer logits than k (its k-th logit lies
@@ -2040,7 +2021,10 @@ __global__ __launch_bounds__(kFBlock) void k_filter_resolve(
     FilterStats *__restrict__ fst) {
   const long slot = blockIdx.x;
   const FilterRow fr = filter_row_setup<DT>(target, draft, temps, lens, topk, topp, gamma, V, NS, part, slot);
-  if (!fr.row) return;  // uniform per workgroup
+  if (!fr.row) {  // uniform per workgroup: marked resolved, so that FE needs one load to skip it
+    store_filter_stats(fst, slot, 0ull, fs, -INFINITY, kFResolved);
+    return;
+  }
   __shared__ GeneralShared sh;
   float tau = -INFINITY;
   unsigned long long kept = 0, list_mass;
@@ -2071,7 +2055,7 @@ __global__ __launch_bounds__(kFBlock) void k_filter_general(
     const int32_t *__restrict__ lens, const int32_t *__restrict__ topk, const float *__restrict__ topp,
     int gamma, int V, int NS, int fs, const Partial *__restrict__ part, FilterStats *__restrict__ fst) {
   const long slot = blockIdx.x;
-  if (!filter_pending(temps, lens, topk, topp, gamma, V, slot, fst, kFGeneral)) return;  // uniform
+  if (fst[slot].pad != kFGeneral) return;  // uniform; FC stores every row's state
   const FilterRow fr = filter_row_setup<DT>(target, draft, temps, lens, topk, topp, gamma, V, NS, part, slot);
   const void *row = fr.row;
   const bool aligned = fr.aligned;
