@@ -2685,7 +2685,6 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 constexpr int kK1U = 8;                 // 16-byte vectors per thread per K1 tile
 constexpr long kK1TargetGroups = 2816;  // about 11 workgroups per CU on 256 CUs
-constexpr long kK3TargetWaves = 2048;   // waves of the mass pass (8 per CU)
 
 bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV_GAMMA_MAX) {
   if (B < 1 || gamma < 0 || gamma > gamma_limit || V < 1) return false;
@@ -2708,10 +2707,9 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV
   P->NS = static_cast<int>(NS);
   P->k1_groups = slots * NS;
   P->NSUB = (V + kSub - 1) / kSub;
-  // sub-chunks per wave in the mass pass: pipeline two per wave when the batch
-  // still gives about 2048 waves, else one
-  const long subs = static_cast<long>(B) * P->NSUB;
-  P->SPW = subs >= 2 * kK3TargetWaves ? 2 : 1;
+  // sub-chunks per wave in the mass pass: one (two, the second prefetched,
+  // measured slower at B = 64 and at B = 128)
+  P->SPW = 1;
   P->NW = (P->NSUB + kWaves * P->SPW - 1) / (kWaves * P->SPW);
   P->k3_groups = static_cast<long>(B) * P->NW;
   // 1-D grids: work-items per launch must stay below 2^32
