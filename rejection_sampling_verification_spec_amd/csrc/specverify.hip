@@ -259,15 +259,22 @@ __device__ __forceinline__ void fold_tile(const u32x4 *v, float c, int &M, doubl
   if (tmx > -INFINITY) {
     const float Mf = ceilf(tmx * c);
     const float nM = -Mf;
+    static_assert(U * kV >= 8, "a tile fills the eight accumulators");
     float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float x[kV];
       widen_vec<DT>(v[u], x);
 #pragma unroll
-      for (int e = 0; e < kV; ++e) acc[(u * kV + e) & 7] += __builtin_amdgcn_exp2f(fmaf(x[e], c, nM));
+      for (int e = 0; e < kV; ++e) {
+        // the first eight terms start the accumulators (no add of zero)
+        const int i = u * kV + e;
+        const float t = __builtin_amdgcn_exp2f(fmaf(x[e], c, nM));
+        if (i < 8)
+          acc[i] = t;
+        else
+          acc[i & 7] += t;
+      }
     }
     const float ts = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     merge_sm(M, s, mx, static_cast<int>(Mf), static_cast<double>(ts), tmx);
@@ -958,7 +965,7 @@ __device__ __forceinline__ void mass_pass(const RowPair &rp, const SelParams &sp
     }
     float aw[8], ap[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) aw[e] = ap[e] = 0.0f;
+    for (int e = Elem<DT>::kVec; e < 8; ++e) aw[e] = ap[e] = 0.0f;  // unused by 4-wide vectors
 #pragma unroll
     for (int u = 0; u < kN; ++u) {
       float zp[Elem<DT>::kVec], zq[Elem<DT>::kVec];
@@ -968,8 +975,13 @@ __device__ __forceinline__ void mass_pass(const RowPair &rp, const SelParams &sp
       for (int e = 0; e < Elem<DT>::kVec; ++e) {
         float w, p;
         residual_value_of<FILT, USEQ>(sp, zp[e], USEQ ? zq[e] : 0.0f, w, p);
-        aw[e & 7] += w;
-        ap[e & 7] += p;
+        if (u == 0) {  // the first vector's terms start the sums (no add of zero)
+          aw[e & 7] = w;
+          ap[e & 7] = p;
+        } else {
+          aw[e & 7] += w;
+          ap[e & 7] += p;
+        }
       }
     }
     const float lw = ((aw[0] + aw[1]) + (aw[2] + aw[3])) + ((aw[4] + aw[5]) + (aw[6] + aw[7]));
