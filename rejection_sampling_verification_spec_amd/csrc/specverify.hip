@@ -242,9 +242,9 @@ __device__ __forceinline__ void fold_values(const float *x, float c, int &M, dou
   }
 }
 
-// The same for a tile held as U raw 16-byte vectors; the vectors are widened
-// twice (once for the maximum, once for the sum) instead of being kept widened,
-// which halves the registers the tile occupies.
+// The same for a tile held as U raw 16-byte vectors, widened once for the
+// maximum and again for the sum (the compiler may keep the first widening in
+// registers instead of repeating it).
 template <int DT, int U>
 __device__ __forceinline__ void fold_tile(const u32x4 *v, float c, int &M, double &s, float &mx) {
   constexpr int kV = Elem<DT>::kVec;
