@@ -10,6 +10,7 @@ candidate; rounding is half away from zero; the windowed acceptance rate of a
 step is its mean accepted count divided by the draft length used.
 """
 import math
+from collections import deque
 
 
 def _round_half_away(x):
@@ -66,21 +67,30 @@ class Ema:
 
 
 class RateWindow:
+    """Windowed acceptance rate.  The rule as stated: keep the acceptance rates of
+    the most recent `window` steps; when their mean exceeds `raise_above` the draft
+    length grows by one, when it falls below `lower_below` it shrinks by one, and
+    it never leaves [lo, hi]."""
+
     def __init__(self, window=100, raise_above=0.85, lower_below=0.65, lo=2, hi=8, start=5):
-        self.window, self.raise_above, self.lower_below = window, raise_above, lower_below
+        self.rates = deque(maxlen=window)          # the most recent rates, oldest first
+        self.raise_above, self.lower_below = raise_above, lower_below
         self.lo, self.hi, self.gamma = lo, hi, start
-        self.history = []
 
     def next(self, batch):
         return self.gamma
 
+    def _mean_rate(self):
+        total = 0.0
+        for r in self.rates:                       # oldest first
+            total += r
+        return total / len(self.rates)
+
     def observe(self, counts, gamma_used):
-        if gamma_used == 0:
+        if gamma_used == 0:                        # no drafts: no rate to record
             return
-        self.history.append(sum(int(c) for c in counts) / len(counts) / gamma_used)
-        self.history = self.history[-self.window:]
-        avg = sum(self.history) / len(self.history)
-        if avg > self.raise_above:
-            self.gamma = min(self.gamma + 1, self.hi)
-        elif avg < self.lower_below:
-            self.gamma = max(self.gamma - 1, self.lo)
+        step_rate = sum(int(c) for c in counts) / len(counts) / gamma_used
+        self.rates.append(step_rate)
+        m = self._mean_rate()
+        step = 1 if m > self.raise_above else (-1 if m < self.lower_below else 0)
+        self.gamma = min(max(self.gamma + step, self.lo), self.hi)

@@ -20,9 +20,11 @@ GAMMA_MAX = 32
 
 def build(extra_flags=(), src: str = SRC, out: str = LIB) -> str:
     """Compile the oracle with gcc (plain -O2, no fast-math, no contraction)."""
+    tmp = f"{out}.tmp{os.getpid()}"
     cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
-           "-shared", "-fPIC", "-I", HERE, *extra_flags, "-o", out, src, "-lm"]
+           "-shared", "-fPIC", "-I", HERE, *extra_flags, "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True, cwd=HERE)
+    os.replace(tmp, out)   # atomic: a concurrent loader sees the old or the new library, whole
     return out
 
 
@@ -182,7 +184,8 @@ class TreeResult:
     accepted_count: np.ndarray  # [B] int32: nodes on the accepted path
     out_tokens: np.ndarray      # [B, max_nodes+1] int32: path tokens, then the drawn token, -1 after
     out_nodes: np.ndarray       # [B, max_nodes] int32: path node indices, -1 after
-    flags: np.ndarray           # [B] int32: bit0 accept band, bit1 CDF band, bit2 zero-mass fallback
+    flags: np.ndarray           # [B] int32: bit0 accept band, bit1 CDF band, bit2 zero-mass fallback,
+                                #   bit4 a band in units of the current target's unnormalised mass only
 
 
 def spec_verify_tree(target, draft, parent, tokens, u_accept, u_sample, temperature, num_nodes=None,

@@ -65,17 +65,23 @@
  *   R12 ragged requests use rows 0..gamma_b only.
  *
  * Near-boundary flags (for parity comparison, not part of the method):
- *   bit 0  some decided position i has |u_i - a_i| < 1e-6 (in a tree, after
- *          rejections, the band is divided by the current target's unnormalised
- *          mass, as for bit 1)
- *   bit 1  the sampled token's CDF interval [C(v-1), C(v)) has u*Z within 1e-6
- *          of one of its ends, in probability units: Z is the unnormalised
- *          mass drawn from (sum of max(0, p - q) for a residual, 1 for p), so
- *          a residual of mass below 1e-6 is always flagged.  A kernel that
- *          forms p - q in fp32 carries an absolute error of a few 1e-8 per
- *          token; relative to a tiny Z the normalised CDF is ill-conditioned.
+ *   bit 0  some decided position i has |u_i - a_i| < 1e-6
+ *   bit 1  u_sample lies within 1e-6 of an end of the sampled token's interval
+ *          [C(v-1), C(v)) of the normalised CDF C = P / Z (P 修正分布の定義:
+ *          the residual is sampled after normalisation)
  *   bit 2  the zero-residual-mass fallback was used
  *   bit 3  a top-p cut lies within 1e-6 (of the kept mass) of a value group
+ *   bit 4  not bit 1, but the same distance measured in probability units,
+ *          (u - C(v-1)) * Z or (C(v) - u) * Z, is below 1e-6: the residual's
+ *          mass Z = sum of max(0, p - q) is so small that a break of its CDF
+ *          moves by more than 1e-6 of Z when p - q is formed in single
+ *          precision (an absolute error of a few 1e-8 per token).  Never set
+ *          for a draw from p (Z = 1).
+ * In a tree, a position's current target after rejections is
+ * max(0, p - c q) / Z_j; bits 0 and 1 use the normalised bands above, and
+ * bit 4 marks a uniform outside them but within 1e-6 once the distance is
+ * multiplied by the current target's unnormalised mass (the product of the
+ * normalisers Z_j so far).
  */
 #include <math.h>
 #include <stddef.h>
@@ -340,7 +346,8 @@ static void verify_request(const oracle_args *a, int b, double *w)
         double m;
         out[k] = inverse_cdf(w, V, (double)a->u_sample[b], &Zrep, &m);
         cdf_margin = m;
-        if (m * Zrep < BAND) flags |= 2;  /* in probability units (Zrep <= 1) */
+        if (m < BAND) flags |= 2;              /* normalised CDF band */
+        else if (m * Zrep < BAND) flags |= 16; /* the same band in probability units */
         if (acc_margin < BAND) flags |= 1;
     }
     if (tr && tr->residual_mass) tr->residual_mass[b] = Zrep;
@@ -429,7 +436,7 @@ static void verify_tree_request(const oracle_tree_args *a, int b, double *p, dou
         softmax_t sp = softmax_stats(&rp, T, 0, 1.0);
         for (int v = 0; v < V; ++v) { p[v] = prob(&rp, &sp, v); cur[v] = p[v]; }
         /* cur's unnormalised mass in probability units (the product of the
-         * normalisers so far): the flags' bands are taken in these units */
+         * normalisers so far): bit 4 measures the bands in these units */
         double scale = 1.0;
         int hit = -1, have_q = 0;
         for (int n = pos; n < N && hit < 0; ++n) {
@@ -443,7 +450,8 @@ static void verify_tree_request(const oracle_tree_args *a, int b, double *p, dou
             const int x = token[n];
             const double an = accept_probability(cur[x], q[x]);
             const double u = (double)a->u_accept[(size_t)b * Nmax + n];
-            if (fabs(u - an) * scale < BAND) flags |= 1;
+            if (fabs(u - an) < BAND) flags |= 1;
+            else if (fabs(u - an) * scale < BAND) flags |= 16;
             if (u < an) { hit = n; break; }
             /* rejected: the next child is tested against max(0, cur - q) / sum */
             double Z = 0.0;
@@ -470,7 +478,8 @@ static void verify_tree_request(const oracle_tree_args *a, int b, double *p, dou
         }
         double Zc, margin;
         out[depth] = inverse_cdf(cur, V, (double)a->u_sample[b], &Zc, &margin);
-        if (margin * scale < BAND) flags |= 2;
+        if (margin < BAND) flags |= 2;
+        else if (margin * scale < BAND) flags |= 16;
         break;
     }
     a->accepted_count[b] = depth;

@@ -20,8 +20,9 @@ typedef struct {
     double *row_sum;       /* [B*(2*gamma+1)] sum_v exp((z - max)/T)                 */
     int32_t *row_argmax;   /* [B*(gamma+1)] greedy target rows                       */
     double *residual_mass; /* [B] mass of the sampled distribution (NaN if greedy)   */
-    int32_t *flags;        /* [B] bit0 accept band, bit1 CDF band, bit2 fallback,
-                              bit3 a top-p cut within the band                      */
+    int32_t *flags;        /* [B] bit0 accept band, bit1 normalised CDF band,
+                              bit2 fallback, bit3 a top-p cut within the band,
+                              bit4 CDF band in probability units only          */
     double *accept_margin; /* [B] min |u_i - a_i| over decided positions             */
     double *cdf_margin;    /* [B] distance of u_sample from its CDF interval's ends  */
 } oracle_trace;
@@ -62,7 +63,8 @@ typedef struct {
     int32_t *out_tokens;         /* out [B][max_nodes+1]: path tokens, then the drawn one */
     int32_t *out_nodes;          /* out [B][max_nodes]: path node indices, -1 after      */
     int32_t *flags;              /* out [B] or NULL: bit0 accept band, bit1 CDF band,
-                                    bit2 zero-mass fallback                              */
+                                    bit2 zero-mass fallback, bit4 a band in units of
+                                    the current target's unnormalised mass only     */
 } oracle_tree_args;
 
 int oracle_spec_verify_tree(const oracle_tree_args *a);

@@ -1,7 +1,8 @@
 """Thin ctypes binding of libspecverify (include/specverify.h).
 
 Argument marshalling only: shapes and dtypes are read off torch tensors, their
-device pointers and torch's current HIP stream are handed to the C ABI, and
+device pointers and the HIP stream (the ``stream`` argument, else torch's
+current stream) are handed to the C ABI, and
 every step of the verify path runs in the library's HIP kernels.  There is no
 fallback: if the compiled library is missing the calls raise ``LibraryMissing``.
 """
@@ -242,6 +243,17 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context for the binding's own allocations and fills: with a ``stream``,
+    they are made on that stream (torch's allocator then ties the blocks to it,
+    and a fill is ordered before the kernels that read it); otherwise on the
+    current stream, which is where the kernels run."""
+    import contextlib
+
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def spec_verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature: float,
                 accepted_count=None, out_tokens=None, workspace=None, stream=None):
     """Uniform batch (one temperature, gamma drafts per request).  Returns (accepted_count, out_tokens)."""
@@ -249,10 +261,11 @@ def spec_verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample, t
     B, gamma, V = _shapes(target_logits)
     dt = _dtype_code(target_logits)
     _check_device(target_logits, draft_logits, draft_tokens, u_accept, u_sample)
-    accepted_count, out_tokens = _outputs(B, gamma, target_logits.device, accepted_count, out_tokens)
-    _check_all(target_logits, draft_logits, draft_tokens, u_accept, u_sample, accepted_count, out_tokens,
-               greedy_only=float(temperature) == 0.0)
-    workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace)
+    with _on(stream):
+        accepted_count, out_tokens = _outputs(B, gamma, target_logits.device, accepted_count, out_tokens)
+        _check_all(target_logits, draft_logits, draft_tokens, u_accept, u_sample, accepted_count, out_tokens,
+                   greedy_only=float(temperature) == 0.0)
+        workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace)
     rc = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
                          _ptr(u_sample), float(temperature), B, gamma, V, dt,
                          _ptr(accepted_count), _ptr(out_tokens), _ptr(workspace),
@@ -297,7 +310,8 @@ def _verify_device_params(entry, target_logits, draft_logits, draft_tokens, u_ac
     dt = _dtype_code(target_logits)
     _check_device(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature, draft_lens,
                   top_k, top_p)
-    accepted_count, out_tokens = _outputs(B, gamma, target_logits.device, accepted_count, out_tokens)
+    with _on(stream):
+        accepted_count, out_tokens = _outputs(B, gamma, target_logits.device, accepted_count, out_tokens)
     _check_all(target_logits, draft_logits, draft_tokens, u_accept, u_sample, accepted_count, out_tokens,
                greedy_only=False)
     import torch
@@ -305,8 +319,9 @@ def _verify_device_params(entry, target_logits, draft_logits, draft_tokens, u_ac
     _expect(draft_lens, (B,), torch.int32, "draft_lens", optional=True)
     _expect(top_k, (B,), torch.int32, "top_k", optional=True)
     _expect(top_p, (B,), torch.float32, "top_p", optional=True)
-    workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace,
-                                 filtered=entry == "spec_verify_filtered")
+    with _on(stream):
+        workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace,
+                                     filtered=entry == "spec_verify_filtered")
     if workspace.numel() < need:
         raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     dbg = None
@@ -370,19 +385,21 @@ def spec_verify_tree(target_logits, draft_logits, node_parent, node_tokens, u_ac
     _expect(u_sample, (B,), torch.float32, "u_sample")
     _expect(temperature, (B,), torch.float32, "temperature")
     _expect(num_nodes, (B,), torch.int32, "num_nodes", optional=True)
-    if accepted_count is None:
-        accepted_count = torch.empty(B, dtype=torch.int32, device=dev)
-    if out_tokens is None:
-        out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
-    if out_nodes is None:
-        out_nodes = torch.empty((B, max(N, 1)), dtype=torch.int32, device=dev)
+    with _on(stream):
+        if accepted_count is None:
+            accepted_count = torch.empty(B, dtype=torch.int32, device=dev)
+        if out_tokens is None:
+            out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+        if out_nodes is None:
+            out_nodes = torch.empty((B, max(N, 1)), dtype=torch.int32, device=dev)
     _expect(accepted_count, (B,), torch.int32, "accepted_count")
     _expect(out_tokens, (B, N + 1), torch.int32, "out_tokens")
     need = spec_verify_tree_workspace_bytes(B, N, V, dt)
     if need == 0:
         raise SpecVerifyError(SV_EINVAL, "spec_verify_tree_workspace_bytes")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace.numel() < need:
         raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     rc = lib.spec_verify_tree(_ptr(target_logits), _ptr(draft_logits), _ptr(node_parent), _ptr(node_tokens),
@@ -417,20 +434,22 @@ def spec_sample(logits, u, temperature, tokens=None, workspace=None, stream=None
     R, V = int(logits.shape[0]), int(logits.shape[1])
     dt = _dtype_code(logits)
     if top_k is not None or top_p is not None:
-        temps = temperature if isinstance(temperature, torch.Tensor) else \
-            torch.full((R,), float(temperature), dtype=torch.float32, device=logits.device)
+        with _on(stream):        # the fill is ordered before the kernels that read it
+            temps = temperature if isinstance(temperature, torch.Tensor) else \
+                torch.full((R,), float(temperature), dtype=torch.float32, device=logits.device)
         _check_device(logits, u, temps, top_k, top_p)
         _expect(logits, (R, V), None, "logits")
         _expect(u, (R,), torch.float32, "u")
         _expect(temps, (R,), torch.float32, "temperature")
         _expect(top_k, (R,), torch.int32, "top_k", optional=True)
         _expect(top_p, (R,), torch.float32, "top_p", optional=True)
-        if tokens is None:
-            tokens = torch.empty(R, dtype=torch.int32, device=logits.device)
-        _expect(tokens, (R,), torch.int32, "tokens")
         need = spec_sample_filtered_workspace_bytes(R, V, dt)
-        if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+        with _on(stream):
+            if tokens is None:
+                tokens = torch.empty(R, dtype=torch.int32, device=logits.device)
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+        _expect(tokens, (R,), torch.int32, "tokens")
         rc = lib.spec_sample_filtered(_ptr(logits), _ptr(u), _ptr(temps), _ptr(top_k), _ptr(top_p), R, V, dt,
                                       _ptr(tokens), _ptr(workspace), workspace.numel(), _stream(stream))
         if rc != SV_OK:
@@ -442,12 +461,13 @@ def spec_sample(logits, u, temperature, tokens=None, workspace=None, stream=None
     _expect(u, (R,), torch.float32, "u")
     if per_row:
         _expect(temperature, (R,), torch.float32, "temperature")
-    if tokens is None:
-        tokens = torch.empty(R, dtype=torch.int32, device=logits.device)
-    _expect(tokens, (R,), torch.int32, "tokens")
     need = spec_sample_workspace_bytes(R, V, dt)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    with _on(stream):
+        if tokens is None:
+            tokens = torch.empty(R, dtype=torch.int32, device=logits.device)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    _expect(tokens, (R,), torch.int32, "tokens")
     rc = lib.spec_sample(_ptr(logits), _ptr(u), 0.0 if per_row else float(temperature),
                          _ptr(temperature) if per_row else None, R, V, dt, _ptr(tokens), _ptr(workspace),
                          workspace.numel(), _stream(stream))

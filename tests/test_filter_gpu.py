@@ -92,12 +92,16 @@ CASES = [
     (8, 5, 32000, "f32", 0.7, 40, 0.95),
     (4, 2, 32003, "bf16", 1.0, 4000, 0.8),     # ragged tail, unaligned rows, k beyond one bin
     (8, 2, 70001, "bf16", 1.0, None, 0.99),    # deep cut: thousands of tokens kept
-    (4, 2, 70001, "f32", 1.0, None, 0.999),    # deep cut among fp32 values, every one inside the band
+    (8, 2, 70001, "f32", 1.0, None, 0.999),    # deep cut among fp32 values on a 1/16 grid
     (12, 0, 4096, "f32", 0.9, 10, 0.7),        # gamma = 0: filtered plain sampling
 ]
-# requests the oracle may flag: a top-p cut among many distinct fp32 logits of
-# mass ~1e-6 each always lies within 1e-6 of a group boundary
-MAX_FLAGGED = {(4, 2, 70001, "f32", 1.0, None, 0.999): 4, (8, 2, 70001, "bf16", 1.0, None, 0.99): 3}
+# requests the oracle may flag: a deep top-p cut among many distinct logits of
+# small mass can lie within 1e-6 of a group boundary.  A cut among tens of
+# thousands of distinct fp32 logits of mass ~1e-6 each always does, so the fp32
+# deep-cut case puts its logits on a 1/16 grid (387 distinct values per row):
+# value groups then hold many tokens and most cuts are decided.
+MAX_FLAGGED = {(8, 2, 70001, "f32", 1.0, None, 0.999): 2, (8, 2, 70001, "bf16", 1.0, None, 0.99): 3}
+GRID = {(8, 2, 70001, "f32", 1.0, None, 0.999): 16}
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}_g{c[1]}_V{c[2]}_{c[3]}_T{c[4]}_k{c[5]}_p{c[6]}"
@@ -107,9 +111,13 @@ def test_filtered_parity_shapes(case):
     seed = zlib.crc32(repr(case).encode()) & 0xffff
     w = with_filter(W.make_random(seed, B, gamma, V, dtype, temps=T, target_scale=3.0, sigma=0.6, zipf=True),
                     top_k=k, top_p=p)
+    if case in GRID:
+        q = np.float32(GRID[case])
+        w.target = (np.round(w.target * q) / q).astype(np.float32)
+        w.draft = (np.round(w.draft * q) / q).astype(np.float32)
     redraw_filtered_drafts(w, seed + 1)
     rep = run_and_check(w, debug=True, require_no_flags=False)
-    assert rep["flagged"] <= MAX_FLAGGED.get(case, max(1, B // 8))
+    assert rep["flagged"] <= MAX_FLAGGED.get(case, B // 8)
 
 
 def test_filtered_per_request_parameters_mixed_batch():
@@ -349,4 +357,4 @@ def _fuzz_case(seed, V=None):
 def test_filtered_fuzz(seed):
     w = _fuzz_case(1000 + seed)
     rep = run_and_check(w, debug=True, require_no_flags=False)
-    assert rep["flagged"] <= max(1, w.B // 2)
+    assert rep["flagged"] <= w.B // 2

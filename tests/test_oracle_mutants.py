@@ -49,6 +49,8 @@ MUTANTS = {
     "tree_target_row_shifted": ("row_t rp = {a->target, dt, ((size_t)b * (size_t)(Nmax + 1) + (size_t)pos) * (size_t)V, V};",
                                 "row_t rp = {a->target, dt, ((size_t)b * (size_t)(Nmax + 1) + (size_t)(pos > 0 ? pos - 1 : 0)) * (size_t)V, V};"),
     "tree_last_sibling_first": ("for (int n = pos; n < N && hit < 0; ++n) {", "for (int n = N - 1; n >= pos && hit < 0; --n) {"),
+    "cdf_band_in_probability_units": ("if (m < BAND) flags |= 2;", "if (m * Zrep < BAND) flags |= 2;"),
+    "cdf_band_normalised_only": ("else if (m * Zrep < BAND) flags |= 16;", "else if (0) flags |= 16;"),
     "tree_greedy_no_descent": ("if (parent[n] == pos - 1 && token[n] == am) { hit = n; break; }",
                                "if (parent[n] == -1 && token[n] == am) { hit = n; break; }"),
 }
@@ -66,6 +68,7 @@ PIN_TESTS = [
     (pins.test_t5_zero_residual_mass_falls_back_to_p, {}),
     (pins.test_t5_inverse_cdf_is_strict_at_exact_breakpoints, {}),
     (pins.test_t5_identical_rows_accept_everything, {}),
+    (pins.test_flag_bits_normalised_band_and_probability_units, {"side": 1.0}),
     (fpins.test_f1_filter_matches_brute_force_definition, {"coarse": True}),
     (fpins.test_f2_exact_integration_gives_filtered_target, {"seed": 0, "top_k": 6, "top_p": 0.9}),
     (fpins.test_f4_three_token_top_p_cut, {}),

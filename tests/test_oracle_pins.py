@@ -467,3 +467,35 @@ def test_oracle_sample_is_inverse_cdf_of_softmax(oracle_mod):
             continue
         cdf = np.cumsum(softmax(z[r].astype(np.float64) / T[r]))
         assert tok[r] == np.searchsorted(cdf, u[r] * cdf[-1], side="right")
+
+
+@pytest.mark.parametrize("side", [1.0, -1.0])
+def test_flag_bits_normalised_band_and_probability_units(oracle_mod, side):
+    """Bit 1 is the 1e-6 band on the normalised residual CDF (P1 section 修正分布の定義
+    normalises the residual before sampling); bit 4 marks a draw outside that band
+    whose distance, multiplied by the residual's mass Z, is below 1e-6.
+
+    p = (0.4, 0.3, 0.3), q = (0.399, 0.299, 0.302): the draft token 2 is rejected
+    (a = 0.3 / 0.302 against u = 0.999) and the residual max(0, p - q) is
+    (1e-3, 1e-3, 0), Z = 2e-3 with one break C near 1/2.  C is evaluated here in
+    fp64 from the stored fp32 logits, and u_sample is placed at normalised
+    distances 5e-7 (bit 1), 1e-4 (bit 4: 1e-4 * Z = 2e-7) and 1e-2 (no flag) on
+    either side of it."""
+    p = np.array([0.4, 0.3, 0.3])
+    q = np.array([0.399, 0.299, 0.302])
+    zp, zq = np.log(p).astype(np.float32), np.log(q).astype(np.float32)
+    pp = softmax(zp.astype(np.float64))
+    qq = softmax(zq.astype(np.float64))
+    w = np.maximum(0.0, pp - qq)
+    Z = w.sum()
+    C = w[0] / Z
+    assert w[2] == 0.0 and abs(Z - 2e-3) < 1e-6
+    for d, want in ((5e-7, 2), (1e-4, 16), (1e-2, 0)):
+        u = np.float32(C + side * d)
+        dist = abs(float(u) - C)
+        assert (2 if dist < 1e-6 else (16 if dist * Z < 1e-6 else 0)) == want
+        r = run(oracle_mod, np.stack([zp, zp])[None], zq[None, None], [[2]], [[0.999]], [u], 1.0)
+        assert r.accepted_count[0] == 0
+        assert r.out_tokens[0, 0] == (1 if side > 0 else 0)
+        assert r.flags[0] == want, (d, side, r.flags[0])
+        np.testing.assert_allclose(r.residual_mass[0], Z, rtol=1e-9)

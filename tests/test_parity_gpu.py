@@ -1,11 +1,13 @@
 """GPU parity: libspecverify (HIP, through the C ABI) against the CPU oracle.
 
 Bar: accepted counts and tokens bit-exact on every request the oracle does not
-flag as near-boundary (|u - a| < 1e-6 at a decided position, u*Z within 1e-6
-of the sampled token's CDF interval ends in probability units, Z the residual's
-unnormalised mass, or the zero-mass fallback); the number
-of flagged requests must be 0 on the five workloads; greedy requests fully
-bit-exact; probabilities within 1e-5 (fp32 logits) / 2e-3 (bf16 logits).
+flag as near-boundary: |u - a| < 1e-6 at a decided position (bit 0), u_sample
+within 1e-6 of the sampled token's interval ends on the normalised CDF (bit 1),
+the zero-mass fallback (bit 2), or the same CDF distance below 1e-6 in
+probability units, i.e. multiplied by the residual's mass Z (bit 4).  The
+number of flagged requests must be 0 on the five workloads; no case may excuse
+more than half of its requests; greedy requests fully bit-exact; probabilities
+within 1e-5 (fp32 logits) / 2e-3 (bf16 logits).
 """
 import json
 import os
@@ -326,4 +328,29 @@ def _verify_fuzz_case(seed, V=None):
 def test_verify_fuzz(seed):
     w = _verify_fuzz_case(3000 + seed)
     rep = run_and_check(w, debug=True, require_no_flags=False)
-    assert rep["flagged"] <= max(1, w.B // 2)
+    assert rep["flagged"] <= w.B // 2
+
+
+def test_non_current_stream_without_workspace():
+    """``stream`` other than the current stream, no workspace and no outputs passed:
+    the binding makes its allocations and fills on that stream."""
+    import oracle
+    import rejection_sampling_verification_spec_amd as sv
+    w = W.make_config(2)
+    dev = torch.device("cuda:0")
+    t = w.to_torch(dev)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    assert torch.cuda.current_stream() != s
+    count, out = sv.spec_verify(t["target"], t["draft"], t["draft_tokens"], t["u_accept"], t["u_sample"],
+                                float(w.scalar_temperature), stream=s)
+    tok = sv.spec_sample(t["target"][:, 0].contiguous(), t["u_sample"], 0.7, stream=s,
+                         top_p=torch.full((w.B,), 0.9, dtype=torch.float32, device=dev))
+    s.synchronize()
+    o = oracle.run_workload(w)
+    ok = o.flags == 0
+    np.testing.assert_array_equal(count.cpu().numpy()[ok], o.accepted_count[ok])
+    np.testing.assert_array_equal(out.cpu().numpy()[ok], o.out_tokens[ok])
+    ref, tr = oracle.sample(w.target[:, 0], w.u_sample, 0.7, dtype=w.dtype, top_p=0.9)
+    okr = tr.flags == 0
+    np.testing.assert_array_equal(tok.cpu().numpy()[okr], ref[okr])
