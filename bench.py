@@ -212,7 +212,7 @@ def time_config(sv, W, torch, math, cfg, greedy, dev, stream, reps_target=100):
     tg = [t["target"]] + [t["target"].clone() for _ in range(copies - 1)]
     dr = [t["draft"]] + [t["draft"].clone() for _ in range(copies - 1)]
     dt = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
-    ws = torch.empty(sv.spec_verify_workspace_bytes(w.B, w.gamma, w.V, dt), dtype=torch.uint8, device=dev)
+    ws = sv.new_workspace(sv.spec_verify_workspace_bytes(w.B, w.gamma, w.V, dt), dev)
     cnt = torch.empty(w.B, dtype=torch.int32, device=dev)
     out = torch.empty((w.B, w.gamma + 1), dtype=torch.int32, device=dev)
     uniform = w.lens is None and w.scalar_temperature is not None
@@ -314,7 +314,7 @@ def main():
     count = torch.empty(B, dtype=torch.int32, device=dev)
     out = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
     need = sv.spec_verify_workspace_bytes(B, gamma, V, sv.SV_BF16)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws = sv.new_workspace(need, dev)
     stream = torch.cuda.Stream()
     log(f"[bench] {copies} input copies ({copies * copy_bytes / 1e9:.2f} GB), workspace {need} B")
 

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     LibraryMissing,
     SpecVerifyError,
     load_library,
+    new_workspace,
     spec_sample,
     spec_sample_filtered_workspace_bytes,
     spec_sample_workspace_bytes,

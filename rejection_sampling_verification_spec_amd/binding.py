@@ -228,11 +228,16 @@ def _outputs(B, gamma, device, accepted_count, out_tokens):
     return accepted_count, out_tokens
 
 
-def _workspace(B, gamma, V, dt, device, workspace, filtered=False):
+def new_workspace(nbytes: int, device):
+    """Device workspace of ``nbytes`` bytes (its contents on entry do not matter)."""
     import torch
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _workspace(B, gamma, V, dt, device, workspace, filtered=False):
     need = (spec_verify_filtered_workspace_bytes if filtered else spec_verify_workspace_bytes)(B, gamma, V, dt)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        workspace = new_workspace(need, device)
     return workspace, need
 
 
@@ -399,7 +404,7 @@ def spec_verify_tree(target_logits, draft_logits, node_parent, node_tokens, u_ac
         raise SpecVerifyError(SV_EINVAL, "spec_verify_tree_workspace_bytes")
     if workspace is None:
         with _on(stream):
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            workspace = new_workspace(need, dev)
     if workspace.numel() < need:
         raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     rc = lib.spec_verify_tree(_ptr(target_logits), _ptr(draft_logits), _ptr(node_parent), _ptr(node_tokens),
@@ -448,7 +453,7 @@ def spec_sample(logits, u, temperature, tokens=None, workspace=None, stream=None
             if tokens is None:
                 tokens = torch.empty(R, dtype=torch.int32, device=logits.device)
             if workspace is None:
-                workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+                workspace = new_workspace(need, logits.device)
         _expect(tokens, (R,), torch.int32, "tokens")
         rc = lib.spec_sample_filtered(_ptr(logits), _ptr(u), _ptr(temps), _ptr(top_k), _ptr(top_p), R, V, dt,
                                       _ptr(tokens), _ptr(workspace), workspace.numel(), _stream(stream))
@@ -466,7 +471,7 @@ def spec_sample(logits, u, temperature, tokens=None, workspace=None, stream=None
         if tokens is None:
             tokens = torch.empty(R, dtype=torch.int32, device=logits.device)
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+            workspace = new_workspace(need, logits.device)
     _expect(tokens, (R,), torch.int32, "tokens")
     rc = lib.spec_sample(_ptr(logits), _ptr(u), 0.0 if per_row else float(temperature),
                          _ptr(temperature) if per_row else None, R, V, dt, _ptr(tokens), _ptr(workspace),

@@ -261,8 +261,7 @@ def test_graph_replay_matches_eager():
     t = w.to_torch(dev)
     count = torch.empty(w.B, dtype=torch.int32, device=dev)
     out = torch.empty((w.B, w.gamma + 1), dtype=torch.int32, device=dev)
-    ws = torch.empty(sv.spec_verify_workspace_bytes(w.B, w.gamma, w.V, sv.SV_BF16), dtype=torch.uint8,
-                     device=dev)
+    ws = sv.new_workspace(sv.spec_verify_workspace_bytes(w.B, w.gamma, w.V, sv.SV_BF16), dev)
     s = torch.cuda.Stream()
 
     def call():
