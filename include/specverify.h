@@ -78,7 +78,9 @@ enum {
     SV_OK = 0,
     SV_EINVAL = -1,     /* bad pointer, size, dtype or temperature           */
     SV_EWORKSPACE = -2, /* workspace NULL, misaligned (256 B) or too small    */
-    SV_EHIP = -3        /* a HIP launch or runtime call failed                */
+    SV_EHIP = -3,       /* a HIP launch or runtime call failed                */
+    SV_ESCRATCH = -4    /* spec_verify_noalloc: the call needs more scratch
+                           than SV_NOALLOC_SCRATCH_BYTES                     */
 };
 
 /* largest supported draft length gamma */
@@ -308,6 +310,27 @@ int spec_gamma_policy_init(sv_gamma_policy *policy, int kind);
 int spec_gamma_next(const sv_gamma_policy *policy, int batch_size);
 int spec_gamma_observe(sv_gamma_policy *policy, const int32_t *accepted_count,
                        int B, int gamma_used);
+
+/* ---- No-allocation variant ---------------------------------------------
+ * For callers that cannot allocate device memory or take a workspace argument:
+ * code under HIP graph capture that must not call hipMalloc, tight serving
+ * loops, harnesses that forbid allocation.  spec_verify_noalloc computes
+ * exactly what spec_verify computes, with the same kernels, but its scratch
+ * memory is a fixed array inside the library (SV_NOALLOC_SCRATCH_BYTES per
+ * GPU, held until the process ends) instead of a caller's workspace.  Its
+ * device address is looked up once per GPU, on the first call made with that
+ * GPU current.  The call allocates nothing and calls no allocating routine.
+ * Limit: a call whose spec_verify_workspace_bytes(B, gamma, V, dtype) exceeds
+ * SV_NOALLOC_SCRATCH_BYTES returns SV_ESCRATCH and touches nothing.  Every call
+ * on one GPU uses that GPU's one array: calls that overlap on one GPU (two
+ * streams, or two host threads) race and must be serialised by the caller.
+ * Arguments and results are those of spec_verify. */
+#define SV_NOALLOC_SCRATCH_BYTES (4 << 20)
+int spec_verify_noalloc(const void *target_logits, const void *draft_logits,
+                        const int32_t *draft_tokens, const float *u_accept,
+                        const float *u_sample, float temperature, int B, int gamma,
+                        int V, int dtype, int32_t *accepted_count,
+                        int32_t *out_tokens, void *stream);
 
 /* Static description of a return code. */
 const char *spec_verify_strerror(int code);

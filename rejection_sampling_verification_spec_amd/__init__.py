@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     spec_sample_workspace_bytes,
     spec_verify,
     spec_verify_ex,
+    spec_verify_noalloc,
     spec_verify_filtered,
     spec_verify_filtered_workspace_bytes,
     spec_verify_tree,

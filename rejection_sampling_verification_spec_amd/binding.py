@@ -26,6 +26,8 @@ SV_OK = 0
 SV_EINVAL = -1
 SV_EWORKSPACE = -2
 SV_EHIP = -3
+SV_ESCRATCH = -4
+SV_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 EXPORTED_SYMBOLS = (
     "spec_verify_workspace_bytes",
@@ -43,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "spec_gamma_next",
     "spec_gamma_observe",
     "spec_verify_strerror",
+    "spec_verify_noalloc",
 )
 
 SV_GAMMA_BY_BATCH = 0
@@ -143,6 +146,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_gamma_next.restype = i32
     lib.spec_gamma_observe.argtypes = [ctypes.POINTER(SvGammaPolicy), vp, i32, i32]
     lib.spec_gamma_observe.restype = i32
+    lib.spec_verify_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, vp, vp, vp]
+    lib.spec_verify_noalloc.restype = i32
     lib.spec_verify_strerror.argtypes = [i32]
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -277,6 +282,26 @@ def spec_verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample, t
                          workspace.numel(), _stream(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify")
+    return accepted_count, out_tokens
+
+
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature: float,
+                        accepted_count, out_tokens, stream=None):
+    """``spec_verify`` on the library's built-in scratch array: no workspace, and
+    nothing is allocated (the caller passes the outputs).  Calls that overlap on
+    one GPU race; a problem whose workspace would exceed SV_NOALLOC_SCRATCH_BYTES
+    raises SpecVerifyError(SV_ESCRATCH)."""
+    lib = load_library()
+    B, gamma, V = _shapes(target_logits)
+    dt = _dtype_code(target_logits)
+    _check_device(target_logits, draft_logits, draft_tokens, u_accept, u_sample, accepted_count, out_tokens)
+    _check_all(target_logits, draft_logits, draft_tokens, u_accept, u_sample, accepted_count, out_tokens,
+               greedy_only=float(temperature) == 0.0)
+    rc = lib.spec_verify_noalloc(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
+                                 _ptr(u_sample), float(temperature), B, gamma, V, dt, _ptr(accepted_count),
+                                 _ptr(out_tokens), _stream(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_noalloc")
     return accepted_count, out_tokens
 
 

@@ -54,6 +54,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "specverify.h"
 
 namespace {
@@ -2875,6 +2877,30 @@ int dispatch(const void *target, const void *draft, const int32_t *tokens, const
                      B, gamma, V, count, out, ws, P, st, dbg);
 }
 
+// ------------------------------------------------------------------ built-in scratch
+// Scratch of spec_verify_noalloc: one array per GPU (each GPU that loads the
+// code object holds its own copy).  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (nullptr on failure).
+void *scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 // ================================================================== C ABI
@@ -2894,6 +2920,20 @@ int spec_verify(const void *target_logits, const void *draft_logits, const int32
   return dispatch(target_logits, draft_logits, draft_tokens, u_accept, u_sample, nullptr, temperature,
                   temperature == 0.0f, nullptr, nullptr, nullptr, B, gamma, V, dtype, accepted_count,
                   out_tokens, workspace, workspace_bytes, stream, nullptr);
+}
+
+int spec_verify_noalloc(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
+                        const float *u_accept, const float *u_sample, float temperature, int B, int gamma,
+                        int V, int dtype, int32_t *accepted_count, int32_t *out_tokens, void *stream) {
+  if (!(temperature >= 0.0f) || isinf(temperature)) return SV_EINVAL;
+  Plan P;
+  if (!make_plan(B, gamma, V, dtype, &P)) return SV_EINVAL;
+  if (P.total > static_cast<size_t>(SV_NOALLOC_SCRATCH_BYTES)) return SV_ESCRATCH;
+  void *ws = scratch_address();
+  if (!ws) return SV_EHIP;
+  return dispatch(target_logits, draft_logits, draft_tokens, u_accept, u_sample, nullptr, temperature,
+                  temperature == 0.0f, nullptr, nullptr, nullptr, B, gamma, V, dtype, accepted_count,
+                  out_tokens, ws, SV_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int spec_verify_ex(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
@@ -3039,6 +3079,7 @@ const char *spec_verify_strerror(int code) {
     case SV_EINVAL: return "invalid argument (pointer, size, dtype or temperature)";
     case SV_EWORKSPACE: return "workspace missing, not 256-byte aligned, or too small";
     case SV_EHIP: return "HIP launch or runtime call failed";
+    case SV_ESCRATCH: return "problem too large for the built-in scratch of spec_verify_noalloc";
     default: return "unknown error code";
   }
 }
