@@ -1,12 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the verify step (spec_verify) on one MI355X.
 
-Workload: B=64 requests, gamma=5 drafts each, vocabulary V=128256, bf16 logits,
-temperature 1.0 (target logits 4 N(0,1) plus a Zipf-like bias, draft logits =
-target + 0.5 N(0,1), drafts sampled from the draft distribution, seeded
-uniforms).  One step = one spec_verify call over the whole batch: row
+Workload (default): B=64 requests, gamma=5 drafts each, vocabulary V=128256,
+bf16 logits, temperature 1.0 (target logits 4 N(0,1) plus a Zipf-like bias,
+draft logits = target + 0.5 N(0,1), drafts sampled from the draft distribution,
+seeded uniforms).  One step = one spec_verify call over the whole batch: row
 statistics of the 11 logit rows of every request, acceptance and first
-rejection, residual / bonus sampling.
+rejection, residual / bonus sampling.  ``--mode greedy`` runs the same logits at
+T = 0, ``--config N`` another workload (4: the ragged, mixed-temperature batch
+through spec_verify_ex).
 
 Inputs are resident in HBM before timing starts.  Steps rotate over C copies of
 the logits totalling more than 1 GB, so that every call streams its logits
@@ -14,18 +16,19 @@ from HBM and not from the 256 MB last-level cache; C consecutive steps are
 captured in one HIP graph and replayed.
 
 Printed: one JSON line with the metric, the per-step time, the roofline figure
-of the dominant kernel (row statistics, timed with HIP events that the library
-records around it on the launch stream) and the single-threaded CPU oracle's
-rate on the same workload.
+of the step (algorithmic bytes over the step's device time, from HIP events on
+the launch stream around the timed region), the row-statistics kernel's own
+time, the streaming-read ceiling, and the single-threaded CPU oracle's rate on
+the same workloads (pinned to one core).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
 import os
-import platform
 import sys
 import time
 
@@ -34,8 +37,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified draft positions/s + achieved HBM GB/s vs peak (B×(2γ+1)×V logits)"
 HBM_PEAK_GBS = 8000.0
-PROFILE_PMC = os.path.join(ROOT, "profiles", "k1_row_stats_B64_g5_V128256_bf16.pmc.json")
+PROFILES = os.path.join(ROOT, "profiles")
+PROFILE_PMC = os.path.join(PROFILES, "step_B64_g5_V128256_bf16.pmc.json")
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verification_spec_amd", "csrc", "specverify.hip")
+PROBE_LIB = os.path.join(ROOT, "rejection_sampling_verification_spec_amd", "libsvprobe.so")
+STEP_KERNELS = ("k1_row_stats", "k2_decide_mass", "k3_select")
 
 
 def log(msg):
@@ -59,33 +65,51 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0: enough for 1.2 GB)")
-    ap.add_argument("--mode", choices=["stochastic", "greedy"], default="stochastic")
+    ap.add_argument("--config", type=int, default=3, help="workload timed as the step (default 3)")
+    ap.add_argument("--mode", choices=["stochastic", "greedy"], default="stochastic",
+                    help="workload 3 at T = 1 or at T = 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-tree", action="store_true", help="skip the tree-verification measurement")
-    ap.add_argument("--no-configs", action="store_true",
-                    help="skip the other configurations' timings and the cold-latency distribution")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the step only (no sampler, filter, tree, other workloads, cold latency, probe)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU oracle time budget over all workloads")
     ap.add_argument("--eager", action="store_true", help="launch every step eagerly instead of graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--summarize-profile", metavar="DIR",
-                    help="summarise rocprofv3 CSV output under DIR (kt/, pmc_FETCH_SIZE/, pmc_WRITE_SIZE/, "
-                         "copy_FETCH_SIZE/, copy_WRITE_SIZE/) into profiles/")
+                    help="summarise rocprofv3 CSV output under DIR into profiles/")
     return ap.parse_args()
 
 
 # --------------------------------------------------------------------------- profile summaries
+_BENCH = "python3 bench.py"
 PROFILE_COMMANDS = {
-    "kt": "rocprofv3 --kernel-trace --stats -d DIR/kt -o kt --output-format csv -- python3 bench.py --no-configs",
-    "pmc_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -d DIR/pmc_FETCH_SIZE -o pmc --output-format csv -- "
-                      "python3 bench.py --steps 14 --warmup 7 --no-cpu-baseline --eager --no-configs",
-    "pmc_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -d DIR/pmc_WRITE_SIZE -o pmc --output-format csv -- "
-                      "python3 bench.py --steps 14 --warmup 7 --no-cpu-baseline --eager --no-configs",
-    "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE -d DIR/copy_FETCH_SIZE -o pmc --output-format csv -- "
-                       "python3 bench.py --copy-calibration",
-    "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE -d DIR/copy_WRITE_SIZE -o pmc --output-format csv -- "
-                       "python3 bench.py --copy-calibration",
+    "kt": f"rocprofv3 --kernel-trace --stats -d DIR/kt -o kt --output-format csv -- {_BENCH} "
+          "--no-extras --no-cpu-baseline",
+    "kt_greedy": f"rocprofv3 --kernel-trace --stats -d DIR/kt_greedy -o kt --output-format csv -- {_BENCH} "
+                 "--mode greedy --no-extras --no-cpu-baseline",
+    "kt_config4": f"rocprofv3 --kernel-trace --stats -d DIR/kt_config4 -o kt --output-format csv -- {_BENCH} "
+                  "--config 4 --no-extras --no-cpu-baseline",
+    "kt_extras": f"rocprofv3 --kernel-trace --stats -d DIR/kt_extras -o kt --output-format csv -- {_BENCH} "
+                 "--no-cpu-baseline",
+    "pmc_FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -d DIR/pmc_FETCH_SIZE -o pmc --output-format csv -- {_BENCH} "
+                      "--steps 14 --warmup 7 --no-cpu-baseline --eager --no-extras",
+    "pmc_WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -d DIR/pmc_WRITE_SIZE -o pmc --output-format csv -- {_BENCH} "
+                      "--steps 14 --warmup 7 --no-cpu-baseline --eager --no-extras",
+    "copy_FETCH_SIZE": f"rocprofv3 --pmc FETCH_SIZE -d DIR/copy_FETCH_SIZE -o pmc --output-format csv -- {_BENCH} "
+                       "--copy-calibration",
+    "copy_WRITE_SIZE": f"rocprofv3 --pmc WRITE_SIZE -d DIR/copy_WRITE_SIZE -o pmc --output-format csv -- {_BENCH} "
+                       "--copy-calibration",
 }
+TRACE_TITLES = {
+    "kt": "Kernel durations: the timed step, B=64, gamma=5, V=128256 bf16, T=1 (stochastic)",
+    "kt_greedy": "Kernel durations: the timed step, B=64, gamma=5, V=128256 bf16, T=0 (greedy)",
+    "kt_config4": "Kernel durations: the timed step, B=128, ragged gamma_b in 1..7, V=152064 bf16, "
+                  "per-request T in {0, 0.6, 1} (spec_verify_ex)",
+    "kt_extras": "Kernel durations: the default benchmark run (timed step plus the sampler, filtered, tree and "
+                 "other-workload measurements)",
+}
+TRACE_FILES = {"kt": "kernels_B64_g5_V128256_bf16_T1.md", "kt_greedy": "kernels_B64_g5_V128256_bf16_greedy.md",
+               "kt_config4": "kernels_B128_ragged_V152064_bf16_mixedT.md", "kt_extras": "kernels_benchmark_extras.md"}
 
 
 def _kernel_short(name: str) -> str:
@@ -93,7 +117,8 @@ def _kernel_short(name: str) -> str:
     import re
     m = re.search(r"::(k\w+)<([^>]*)>", name)
     if not m:
-        return name.split("(")[0][:60]
+        m2 = re.search(r"\b(k_\w+|k\d\w*)\b", name)
+        return m2.group(1) if m2 else name.split("(")[0][:60]
     kname, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
     tags = [{"0": "f32", "1": "bf16"}.get(args[0], args[0])]
     if kname == "k1_row_stats" and len(args) == 3:
@@ -111,35 +136,48 @@ def _find_csv(d, suffix):
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
+def _bench_line(d):
+    """The JSON line bench.py printed under the profiler (saved next to the trace as bench.json)."""
+    p = os.path.join(d, "bench.json")
+    if os.path.exists(p):
+        for line in open(p):
+            line = line.strip()
+            if line.startswith("{"):
+                return json.loads(line)
+    return None
+
+
 def summarize_profile(root: str):
     import csv
     import statistics
-    out_dir = os.path.join(ROOT, "profiles")
-    os.makedirs(out_dir, exist_ok=True)
-    # kernel trace statistics
-    stats = list(csv.DictReader(open(_find_csv(os.path.join(root, "kt"), "kernel_stats.csv"))))
-    lines = ["# Kernel durations: B=64, gamma=5, V=128256 bf16, T=1 (stochastic)", "",
-             "Command (from the repository root, output under DIR):", "",
-             "    " + PROFILE_COMMANDS["kt"], "",
-             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
-             "|---|---|---|---|---|---|"]
-    k1_avg_ns = None
-    for r in stats:
-        n = _kernel_short(r["Name"])
-        lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
-                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
-        if n == "k1_row_stats<bf16, stochastic>":
-            k1_avg_ns = float(r["AverageNs"])
-    lines += ["", "Which call runs which kernels: the timed steps (spec_verify, T = 1) run "
-              "k1_row_stats<bf16, stochastic>, k2_decide_mass<bf16, plain> and k3_select<bf16, plain>; "
-              "the K1 timing pass (spec_verify_ex) runs k1_row_stats<bf16, per-request T>; the filtered "
-              "measurement (spec_verify_filtered, T = 0.7, top_p = 0.9 with and without top_k = 50) runs "
-              "k1_row_stats<bf16, per-request T>, k_filter_capture, k_filter_deep_count (with top_k = 50), "
-              "k_filter_resolve, k_filter_general and the filtered k2 / k3; the tree measurement (spec_verify_tree, 8 trees of width 4 and depth 3) runs "
-              "k1_row_stats<bf16, per-request T> and k_tree_walk; the draft-side sampling measurement runs "
-              "k_sample_stats and k_sample_pick.  The copy kernels "
-              "are the benchmark's set-up (input copies), outside the timed region.", ""]
-    open(os.path.join(out_dir, "kernels_B64_g5_V128256_bf16.md"), "w").write("\n".join(lines))
+    os.makedirs(PROFILES, exist_ok=True)
+    traces = {}
+    for key, title in TRACE_TITLES.items():
+        d = os.path.join(root, key)
+        if not os.path.isdir(d):
+            continue
+        stats = list(csv.DictReader(open(_find_csv(d, "kernel_stats.csv"))))
+        bl = _bench_line(d)
+        lines = [f"# {title}", "", "Command (from the repository root, output under DIR):", "",
+                 "    " + PROFILE_COMMANDS[key] + " > DIR/" + key + "/bench.json", "",
+                 "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+                 "|---|---|---|---|---|---|"]
+        avg = {}
+        for r in stats:
+            n = _kernel_short(r["Name"])
+            avg[n] = float(r["AverageNs"]) / 1e3
+            lines.append(f"| {n} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+        if bl is not None:
+            lines += ["", f"The same run's benchmark line: {bl['ms_per_step'] * 1e3:.2f} us per step on the host "
+                          f"clock, {bl['extra']['device_us_per_step']:.2f} us per step between the HIP events "
+                          f"({bl['config']['workload']}); step roofline fraction {bl['roofline']['frac']:.4f} "
+                          f"({bl['roofline']['achieved']:.0f} GB/s of algorithmic bytes)."]
+        lines += ["", "The copy kernels are the benchmark's set-up (input copies), outside the timed region.", ""]
+        open(os.path.join(PROFILES, TRACE_FILES[key]), "w").write("\n".join(lines))
+        traces[key] = {"kernel_avg_us": avg, "bench": None if bl is None else
+                       {"ms_per_step": bl["ms_per_step"], "device_us_per_step": bl["extra"]["device_us_per_step"],
+                        "frac": bl["roofline"]["frac"]}}
 
     def pmc_medians(d):
         rows = list(csv.DictReader(open(_find_csv(os.path.join(root, d), "counter_collection.csv"))))
@@ -148,40 +186,45 @@ def summarize_profile(root: str):
             by.setdefault(_kernel_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
         return {k: statistics.median(v) for k, v in by.items()}, {k: len(v) for k, v in by.items()}
 
-    fetch, nf = pmc_medians("pmc_FETCH_SIZE")
-    write, nw = pmc_medians("pmc_WRITE_SIZE")
-    cfetch, _ = pmc_medians("copy_FETCH_SIZE")
-    cwrite, _ = pmc_medians("copy_WRITE_SIZE")
-    copy_name = max(cfetch, key=lambda k: cfetch[k])   # the 1 GiB copy kernel (the fill reads nothing)
-    copy_kib = (1 << 30) / 1024
-    f_fetch = copy_kib / cfetch[copy_name]
-    f_write = copy_kib / cwrite[copy_name]
-    K1 = "k1_row_stats<bf16, stochastic>"
-    k1_bytes = (fetch[K1] * f_fetch + write[K1] * f_write) * 1024
-    bytes_alg = 64 * 11 * 128256 * 2
-    rec = {"kernel": "k1_row_stats", "mode": "stochastic", "kernel_source_sha256_16": source_hash(),
-           "fetch_kib_per_dispatch": fetch[K1], "write_kib_per_dispatch": write[K1],
-           "copy_kernel": copy_name, "copy_fetch_kib": cfetch[copy_name], "copy_write_kib": cwrite[copy_name],
-           "fetch_scale": f_fetch, "write_scale": f_write, "hbm_bytes_per_launch": round(k1_bytes),
-           "bytes_alg_per_launch": bytes_alg, "traffic_over_alg": k1_bytes / bytes_alg,
-           "k1_avg_us_kernel_trace": None if k1_avg_ns is None else k1_avg_ns / 1e3,
-           "commands": {k: PROFILE_COMMANDS[k] for k in ("pmc_FETCH_SIZE", "pmc_WRITE_SIZE", "copy_FETCH_SIZE",
-                                                          "copy_WRITE_SIZE")}}
+    rec = {"kernel_source_sha256_16": source_hash(), "traces": traces}
+    if os.path.isdir(os.path.join(root, "pmc_FETCH_SIZE")):
+        fetch, nf = pmc_medians("pmc_FETCH_SIZE")
+        write, _ = pmc_medians("pmc_WRITE_SIZE")
+        cfetch, _ = pmc_medians("copy_FETCH_SIZE")
+        cwrite, _ = pmc_medians("copy_WRITE_SIZE")
+        copy_name = max(cfetch, key=lambda k: cfetch[k])   # the 1 GiB copy kernel (the fill reads nothing)
+        copy_kib = (1 << 30) / 1024
+        f_fetch, f_write = copy_kib / cfetch[copy_name], copy_kib / cwrite[copy_name]
+        step = [k for k in fetch if k.split("<")[0] in STEP_KERNELS]
+        per = {k: round((fetch[k] * f_fetch + write.get(k, 0.0) * f_write) * 1024) for k in step}
+        step_bytes = sum(per.values())
+        bytes_alg = 64 * 11 * 128256 * 2
+        rec.update({"mode": "stochastic", "copy_kernel": copy_name, "copy_fetch_kib": cfetch[copy_name],
+                    "copy_write_kib": cwrite[copy_name], "fetch_scale": f_fetch, "write_scale": f_write,
+                    "fetch_kib_per_dispatch": {k: fetch[k] for k in step},
+                    "write_kib_per_dispatch": {k: write.get(k) for k in step},
+                    "hbm_bytes_per_launch": per, "hbm_bytes_per_step": step_bytes, "bytes_alg_per_step": bytes_alg,
+                    "traffic_over_alg": step_bytes / bytes_alg,
+                    "commands": {k: PROFILE_COMMANDS[k] for k in ("pmc_FETCH_SIZE", "pmc_WRITE_SIZE",
+                                                                   "copy_FETCH_SIZE", "copy_WRITE_SIZE")}})
+        lines = ["# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE, KiB)", "",
+                 "Workload: B=64, gamma=5, V=128256 bf16, T=1 (stochastic), eager launches.", "",
+                 "Commands (from the repository root, output under DIR):", ""]
+        lines += ["    " + PROFILE_COMMANDS[k] for k in ("pmc_FETCH_SIZE", "pmc_WRITE_SIZE", "copy_FETCH_SIZE",
+                                                           "copy_WRITE_SIZE")]
+        lines += ["", "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | bytes (scaled) |",
+                  "|---|---|---|---|---|"]
+        for k in fetch:
+            b = (fetch[k] * f_fetch + write.get(k, 0.0) * f_write) * 1024
+            lines.append(f"| {k} | {nf[k]} | {fetch[k]:.1f} | {write.get(k, float('nan')):.1f} | {b / 1e6:.2f} MB |")
+        lines += ["", f"Calibration: the plain 1 GiB device copy ({copy_name}) reads {cfetch[copy_name]:.1f} KiB "
+                  f"and writes {cwrite[copy_name]:.1f} KiB by these counters, so FETCH_SIZE is scaled by "
+                  f"{f_fetch:.4f} and WRITE_SIZE by {f_write:.4f} to give bytes.", "",
+                  f"The step (k1_row_stats + k2_decide_mass + k3_select): {step_bytes / 1e6:.2f} MB per step against "
+                  f"{bytes_alg / 1e6:.2f} MB algorithmic (ratio {step_bytes / bytes_alg:.4f}); the excess is "
+                  f"the residual pass re-reading the sampled row pair of each request.", ""]
+        open(os.path.join(PROFILES, "hbm_traffic_B64_g5_V128256_bf16.md"), "w").write("\n".join(lines))
     json.dump(rec, open(PROFILE_PMC, "w"), indent=2)
-    lines = ["# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE, KiB)", "",
-             "Workload: B=64, gamma=5, V=128256 bf16, T=1 (stochastic), eager launches.", "",
-             "Commands (from the repository root, output under DIR):", ""]
-    lines += ["    " + PROFILE_COMMANDS[k] for k in ("pmc_FETCH_SIZE", "pmc_WRITE_SIZE", "copy_FETCH_SIZE",
-                                                       "copy_WRITE_SIZE")]
-    lines += ["", "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) |", "|---|---|---|---|"]
-    for k in fetch:
-        lines.append(f"| {k} | {nf[k]} | {fetch[k]:.1f} | {write.get(k, float('nan')):.1f} |")
-    lines += ["", f"Calibration: the plain 1 GiB device copy ({copy_name}) reads {cfetch[copy_name]:.1f} KiB "
-              f"and writes {cwrite[copy_name]:.1f} KiB by these counters, so FETCH_SIZE is scaled by "
-              f"{f_fetch:.4f} and WRITE_SIZE by {f_write:.4f} to give bytes.",
-              "", f"{K1}: {k1_bytes / 1e6:.2f} MB per launch against {bytes_alg / 1e6:.2f} MB algorithmic "
-              f"(ratio {k1_bytes / bytes_alg:.4f}).", ""]
-    open(os.path.join(out_dir, "hbm_traffic_B64_g5_V128256_bf16.md"), "w").write("\n".join(lines))
     print(json.dumps(rec, indent=2))
 
 
@@ -198,37 +241,12 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
 
 
-def time_config(sv, W, torch, math, cfg, greedy, dev, stream, reps_target=100):
-    """Throughput of spec_verify (uniform T) or spec_verify_ex (per-request T and lengths) on one of
-    the configurations, inputs rotated over enough copies to exceed the last-level cache where that
-    fits in 1.2 GB (at most 64 copies: the smallest configurations run from cache, and say so)."""
-    t0 = time.perf_counter()
-    w = W.make_config(cfg, greedy=greedy)
-    gen_s = time.perf_counter() - t0
-    t = w.to_torch(dev)
-    elt = 2 if w.dtype == "bf16" else 4
-    copy_bytes = (t["target"].numel() + t["draft"].numel()) * elt
-    copies = min(64, max(2, math.ceil(1.2e9 / copy_bytes)))
-    tg = [t["target"]] + [t["target"].clone() for _ in range(copies - 1)]
-    dr = [t["draft"]] + [t["draft"].clone() for _ in range(copies - 1)]
-    dt = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
-    ws = sv.new_workspace(sv.spec_verify_workspace_bytes(w.B, w.gamma, w.V, dt), dev)
-    cnt = torch.empty(w.B, dtype=torch.int32, device=dev)
-    out = torch.empty((w.B, w.gamma + 1), dtype=torch.int32, device=dev)
-    uniform = w.lens is None and w.scalar_temperature is not None
-
-    def one(c):
-        if uniform:
-            sv.spec_verify(tg[c], dr[c], t["draft_tokens"], t["u_accept"], t["u_sample"], float(w.scalar_temperature),
-                           accepted_count=cnt, out_tokens=out, workspace=ws, stream=stream)
-        else:
-            sv.spec_verify_ex(tg[c], dr[c], t["draft_tokens"], t["u_accept"], t["u_sample"], t["temperature"],
-                              t.get("lens"), accepted_count=cnt, out_tokens=out, workspace=ws, stream=stream)
-
+# --------------------------------------------------------------------------- timing helpers
+def graph_time(torch, stream, one, copies, reps_target):
+    """Per-call time of one(c) over the copies, captured in one graph and replayed."""
     with torch.cuda.stream(stream):
         one(0)
     torch.cuda.synchronize()
-    rc, ro = cnt.cpu().clone(), out.cpu().clone()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for c in range(copies):
@@ -242,14 +260,58 @@ def time_config(sv, W, torch, math, cfg, greedy, dev, stream, reps_target=100):
         for _ in range(reps):
             g.replay()
     torch.cuda.synchronize()
-    per = (time.perf_counter() - s0) / (reps * copies)
-    assert torch.equal(cnt.cpu(), rc) and torch.equal(out.cpu(), ro), f"config {cfg} replay differs"
-    return {"workload": w.name, "entry": "spec_verify" if uniform else "spec_verify_ex",
-            "us_per_call": round(per * 1e6, 3), "positions_per_s": round(w.positions() / per, 1),
-            "GBps_alg": round(w.bytes_alg() / per / 1e9, 1), "bytes_alg": w.bytes_alg(),
-            "copies_rotated": copies, "cache_warm": copies * copy_bytes < 512e6,
-            "alpha_hat": round(float(rc.float().sum()) / max(1, w.positions()), 4),
-            "generate_s": round(gen_s, 1)}
+    return (time.perf_counter() - s0) / (reps * copies)
+
+
+def verify_call(sv, w, t, tg, dr, cnt, out, ws, stream):
+    """The step for workload w: spec_verify for a uniform batch, spec_verify_ex otherwise."""
+    uniform = w.lens is None and w.scalar_temperature is not None
+    greedy = uniform and w.scalar_temperature == 0.0
+
+    def one(c):
+        if uniform:
+            sv.spec_verify(tg[c], None if greedy else dr[c], t["draft_tokens"], None if greedy else t["u_accept"],
+                           t["u_sample"], float(w.scalar_temperature), accepted_count=cnt, out_tokens=out,
+                           workspace=ws, stream=stream)
+        else:
+            sv.spec_verify_ex(tg[c], dr[c], t["draft_tokens"], t["u_accept"], t["u_sample"], t["temperature"],
+                              t.get("lens"), accepted_count=cnt, out_tokens=out, workspace=ws, stream=stream)
+    return one, ("spec_verify" if uniform else "spec_verify_ex")
+
+
+def rotate(torch, t, elt, copies=None):
+    cb = (t["target"].numel() + t["draft"].numel()) * elt
+    if copies is None:
+        copies = min(64, max(2, math.ceil(1.2e9 / cb)))
+    return ([t["target"]] + [t["target"].clone() for _ in range(copies - 1)],
+            [t["draft"]] + [t["draft"].clone() for _ in range(copies - 1)], copies, cb)
+
+
+def time_config(sv, W, torch, cfg, greedy, dev, stream, cache, reps_target=100):
+    """Throughput of one of the other workloads (inputs rotated over enough copies to exceed the
+    last-level cache, at most 64: the smallest workloads run from cache, and say so)."""
+    t0 = time.perf_counter()
+    w = W.make_config(cfg, greedy=greedy)
+    gen_s = time.perf_counter() - t0
+    cache[(cfg, greedy)] = w
+    t = w.to_torch(dev)
+    elt = 2 if w.dtype == "bf16" else 4
+    tg, dr, copies, cb = rotate(torch, t, elt)
+    dt = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
+    ws = sv.new_workspace(sv.spec_verify_workspace_bytes(w.B, w.gamma, w.V, dt), dev)
+    cnt = torch.empty(w.B, dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.gamma + 1), dtype=torch.int32, device=dev)
+    one, entry = verify_call(sv, w, t, tg, dr, cnt, out, ws, stream)
+    with torch.cuda.stream(stream):
+        one(0)
+    torch.cuda.synchronize()
+    rc, ro = cnt.cpu().clone(), out.cpu().clone()
+    per = graph_time(torch, stream, one, copies, reps_target)
+    assert torch.equal(cnt.cpu(), rc) and torch.equal(out.cpu(), ro), f"workload {cfg} replay differs"
+    return {"workload": w.name, "entry": entry, "us_per_call": round(per * 1e6, 3),
+            "positions_per_s": round(w.positions() / per, 1), "GBps_alg": round(w.bytes_alg() / per / 1e9, 1),
+            "bytes_alg": w.bytes_alg(), "copies_rotated": copies, "cache_warm": copies * cb < 512e6,
+            "alpha_hat": round(float(rc.float().sum()) / max(1, w.positions()), 4), "generate_s": round(gen_s, 1)}
 
 
 def cold_latency(torch, np, one_call, stream, dev, n=41):
@@ -272,6 +334,96 @@ def cold_latency(torch, np, one_call, stream, dev, n=41):
             "calls": n}
 
 
+def stream_probe(torch, dev, stream, nbytes, steps):
+    """The streaming-read ceiling (libsvprobe): the same bytes per launch as the step's algorithmic
+    bytes, rotated over copies beyond the last-level cache, 2816 workgroups as the row statistics."""
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.sv_stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.sv_stream_probe.restype = ctypes.c_int
+    copies = max(2, math.ceil(1.2e9 / nbytes))
+    bufs = [torch.full((nbytes,), k + 1, dtype=torch.uint8, device=dev) for k in range(copies)]
+    groups = 2816
+    out = torch.empty(groups, dtype=torch.int32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    with torch.cuda.stream(stream):     # torch's events must have been recorded once to be read
+        for a, b in evs:
+            a.record(stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    for k in range(steps + 5):
+        ev = None
+        if k >= 5:
+            a, b = evs[k - 5]
+            ev = (ctypes.c_void_p * 2)(a.cuda_event, b.cuda_event)
+        rc = lib.sv_stream_probe(ctypes.c_void_p(bufs[k % copies].data_ptr()), nbytes, groups,
+                                 ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream), ev)
+        assert rc == 0, rc
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / steps * 1e3
+    del bufs
+    return {"us_per_launch": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
+            "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+            "workgroups": groups, "copies_rotated": copies}
+
+
+# --------------------------------------------------------------------------- CPU oracle leg
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+FLAG_NAMES = ("accept_band", "cdf_band", "zero_mass_fallback", "top_p_cut_band", "cdf_band_prob_units")
+
+
+def cpu_leg(W, budget_s, cache, headline_key):
+    """The single-threaded fp64 oracle, pinned to one core, on every workload: at least one full call
+    each, repeated within the budget; the headline is the benchmark's own workload."""
+    import numpy as np
+
+    import oracle
+    oracle.load()
+    old = os.sched_getaffinity(0)
+    core = max(old)
+    os.sched_setaffinity(0, {core})
+    try:
+        keys = [(0, False), (1, False), (2, False), (3, False), (3, True), (4, False)]
+        per = {}
+        share = budget_s / len(keys)
+        for key in keys:
+            w = cache.get(key) or W.make_config(key[0], greedy=key[1])
+            cache[key] = w
+            tr = oracle.run_workload(w, trace=True)     # flags: not timed
+            flags = tr.flags
+            n, spent = 0, 0.0
+            while n == 0 or spent < share:
+                c0 = time.perf_counter()
+                oracle.run_workload(w, trace=False)
+                spent += time.perf_counter() - c0
+                n += 1
+            name = f"config{key[0]}" + ("_greedy" if key[1] else "")
+            per[name] = {"workload": w.name, "s_per_call": round(spent / n, 4), "calls": n,
+                         "positions_per_s": round(w.positions() * n / spent, 2),
+                         "near_boundary": {"flagged": int((flags != 0).sum()),
+                                           **{b: int(((flags >> i) & 1).sum()) for i, b in enumerate(FLAG_NAMES)}},
+                         "alpha_hat": round(float(np.sum(tr.accepted_count)) / max(1, w.positions()), 4)}
+    finally:
+        os.sched_setaffinity(0, old)
+    head = per[headline_key]
+    return {"value": head["positions_per_s"], "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"{head['calls']} full calls of {head['workload']} "
+                      f"({head['s_per_call']:.3f} s each; single-threaded fp64 C, gcc -O2), pinned to core {core}; "
+                      f"every workload timed the same way under per_config, about {budget_s:.0f} s in all",
+            "cpu_model": cpu_model(), "pinned_core": core, "host_cpus": os.cpu_count(), "per_config": per}
+
+
+# --------------------------------------------------------------------------- main
 def main():
     args = parse()
     if args.summarize_profile:
@@ -295,49 +447,47 @@ def main():
     import rejection_sampling_verification_spec_amd as sv
     from rejection_sampling_verification_spec_amd import workloads as W
 
-    lib = sv.load_library()
+    sv.load_library()
     dev = torch.device("cuda:0")
     greedy = args.mode == "greedy"
+    if greedy and args.config != 3:
+        print("--mode greedy applies to workload 3", file=sys.stderr)
+        sys.exit(2)
+    cache = {}
     t0 = time.perf_counter()
-    w = W.make_config(3, greedy=greedy)
+    w = W.make_config(args.config, greedy=greedy)
+    cache[(args.config, greedy)] = w
     log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")
     B, gamma, V = w.B, w.gamma, w.V
-    T = float(w.scalar_temperature)
     positions = w.positions()
-    bytes_alg = w.bytes_alg()                       # rows the method must read x V x 2 B
-    formula_bytes = B * (2 * gamma + 1) * V * 2     # the metric's B x (2 gamma + 1) x V logits
+    bytes_alg = w.bytes_alg()                       # rows the method must read x V x element size
+    elt = w.elt_bytes()
+    formula_bytes = B * (2 * gamma + 1) * V * elt   # the metric's B x (2 gamma + 1) x V logits
     t = w.to_torch(dev)
-    copy_bytes = (t["target"].numel() + t["draft"].numel()) * 2
-    copies = args.copies or max(2, math.ceil(1.2e9 / copy_bytes))
-    targets = [t["target"]] + [t["target"].clone() for _ in range(copies - 1)]
-    drafts = [t["draft"]] + [t["draft"].clone() for _ in range(copies - 1)]
+    targets, drafts, copies, copy_bytes = rotate(torch, t, elt, args.copies or None)
+    dt = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
     count = torch.empty(B, dtype=torch.int32, device=dev)
     out = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
-    need = sv.spec_verify_workspace_bytes(B, gamma, V, sv.SV_BF16)
+    need = sv.spec_verify_workspace_bytes(B, gamma, V, dt)
     ws = sv.new_workspace(need, dev)
     stream = torch.cuda.Stream()
     log(f"[bench] {copies} input copies ({copies * copy_bytes / 1e9:.2f} GB), workspace {need} B")
+    one, entry = verify_call(sv, w, t, targets, drafts, count, out, ws, stream)
 
-    def step(c, s):
-        return sv.spec_verify(targets[c], None if greedy else drafts[c], t["draft_tokens"],
-                              None if greedy else t["u_accept"], t["u_sample"], T,
-                              accepted_count=count, out_tokens=out, workspace=ws, stream=s)
-
-    # eager reference result
     with torch.cuda.stream(stream):
-        step(0, stream)
+        one(0)
     torch.cuda.synchronize()
     ref_count, ref_out = count.cpu().clone(), out.cpu().clone()
 
-    # HIP graphs: one graph holds `copies` consecutive steps (copy 0, 1, ..., C-1);
-    # a shorter graph covers a remainder so that exactly K steps are timed
+    # HIP graphs: one graph holds `copies` consecutive steps (copy 0, 1, ..., C-1); a
+    # shorter graph covers a remainder so that exactly K steps are timed
     graphs = {}
 
     def chain_graph(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for c in range(n):
-                step(c, stream)
+                one(c)
         return g
 
     if not args.eager:
@@ -351,7 +501,7 @@ def main():
         with torch.cuda.stream(stream):
             if args.eager:
                 for k in range(n):
-                    step(k % copies, stream)
+                    one(k % copies)
                 return
             full, rem = divmod(n, copies)
             for _ in range(full):
@@ -372,83 +522,92 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     h1 = time.perf_counter()
-    dev_ms = e0.elapsed_time(e1)
+    dev_s_per_step = e0.elapsed_time(e1) / 1e3 / args.steps
     host_ms = (h1 - h0) * 1e3
     ms_per_step = host_ms / args.steps
     value = positions * args.steps / (host_ms / 1e3)
     # every copy holds the same logits, so the last replay must reproduce the eager result
     assert torch.equal(count.cpu(), ref_count) and torch.equal(out.cpu(), ref_out), "timed replay differs"
-    log(f"[bench] timed {args.steps} steps: host {host_ms:.3f} ms, device {dev_ms:.3f} ms")
+    log(f"[bench] timed {args.steps} steps: host {host_ms:.3f} ms, device {dev_s_per_step * 1e3 * args.steps:.3f} ms")
 
-    # dominant kernel: row statistics, timed by events the library records around it
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    with torch.cuda.stream(stream):
-        for a, b in evs:
-            a.record(stream)
-            b.record(stream)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for k, (a, b) in enumerate(evs):
-            c = (args.warmup + k) % copies
-            sv.spec_verify_ex(targets[c], drafts[c], t["draft_tokens"], t["u_accept"], t["u_sample"],
-                              t["temperature"], None, accepted_count=count, out_tokens=out, workspace=ws,
-                              stream=stream, k1_events=(a, b))
-    torch.cuda.synchronize()
-    k1_ms = [a.elapsed_time(b) for a, b in evs]
-    k1_avg_s = float(np.mean(k1_ms)) / 1e3
-    achieved = bytes_alg / k1_avg_s / 1e9
+    # the step's roofline: algorithmic bytes over the device time per step (HIP events on the
+    # launch stream around the timed region)
+    achieved = bytes_alg / dev_s_per_step / 1e9
+    pmc = json.load(open(PROFILE_PMC)) if os.path.exists(PROFILE_PMC) else {}
+    pmc_current = pmc.get("kernel_source_sha256_16") == source_hash()
     traffic = None
-    if os.path.exists(PROFILE_PMC):
-        pmc = json.load(open(PROFILE_PMC))
-        if pmc.get("kernel_source_sha256_16") == source_hash() and pmc.get("mode") == args.mode:
-            traffic = pmc.get("hbm_bytes_per_launch")
+    if pmc_current and args.config == 3 and not greedy and pmc.get("mode") == "stochastic":
+        traffic = pmc.get("hbm_bytes_per_step")
+    kernels = STEP_KERNELS[:2] if greedy else STEP_KERNELS
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k1_row_stats", "kernel_avg_us": round(k1_avg_s * 1e6, 3),
-                "bytes_per_launch": bytes_alg}
+                "scope": "whole step: " + " + ".join(kernels), "step_us": round(dev_s_per_step * 1e6, 3),
+                "bytes_per_step": bytes_alg}
+
+    # the row-statistics kernel on its own: event pairs the library records around its dispatch.  They
+    # are accepted through spec_verify_ex, whose per-request-temperature instantiation of the kernel
+    # runs here (every request at the benchmark's temperature); K1 reads every algorithmic byte once
+    if args.config == 3:
+        temps = torch.full((B,), 0.0 if greedy else 1.0, dtype=torch.float32, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        with torch.cuda.stream(stream):
+            for a, b in evs:
+                a.record(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for k in range(args.warmup):      # this instantiation's first calls are not timed
+                sv.spec_verify_ex(targets[k % copies], drafts[k % copies], t["draft_tokens"], t["u_accept"],
+                                  t["u_sample"], temps, None, accepted_count=count, out_tokens=out, workspace=ws,
+                                  stream=stream)
+            for k, (a, b) in enumerate(evs):
+                c = (args.warmup + k) % copies
+                sv.spec_verify_ex(targets[c], drafts[c], t["draft_tokens"], t["u_accept"], t["u_sample"], temps,
+                                  None, accepted_count=count, out_tokens=out, workspace=ws, stream=stream,
+                                  k1_events=(a, b))
+        torch.cuda.synchronize()
+        k1_ms = [a.elapsed_time(b) for a, b in evs]
+        k1_us = float(np.mean(k1_ms)) * 1e3
+        roofline["k1_row_stats"] = {"instantiation": "per-request T (through spec_verify_ex)",
+                                    "avg_us": round(k1_us, 3), "median_us": round(float(np.median(k1_ms)) * 1e3, 3),
+                                    "min_us": round(min(k1_ms) * 1e3, 3),
+                                    "max_us": round(max(k1_ms) * 1e3, 3),
+                                    "achieved_GBps": round(bytes_alg / k1_us / 1e3, 1),
+                                    "frac": round(bytes_alg / k1_us / 1e3 / HBM_PEAK_GBS, 4)}
+    key = {(3, False): "kt", (3, True): "kt_greedy", (4, False): "kt_config4"}.get((args.config, greedy))
+    tr = pmc.get("traces", {}).get(key) if pmc_current else None
+    if tr:
+        roofline["kernel_trace_avg_us"] = {k: round(v, 3) for k, v in tr["kernel_avg_us"].items()
+                                           if k.split("<")[0] in STEP_KERNELS}
+
+    extras = {}
+    if not args.no_extras:
+        extras["stream_probe"] = stream_probe(torch, dev, stream, bytes_alg, 50)
+        log(f"[bench] stream probe {extras['stream_probe']}")
 
     # draft-side sampling (one token per row of softmax(z/T)) on the same draft logits:
-    # 64 rows (one drafting step of the batch) and 320 rows (all five positions)
-    sample = {}
-    if not greedy:
+    # B rows (one drafting step of the batch) and B*gamma rows (all positions)
+    if not args.no_extras and args.config == 3 and not greedy:
+        sample = {}
         for R in (B, B * gamma):
             rows = [d.view(B * gamma, V)[:R] for d in drafts]
             us = t["u_accept"].reshape(-1)[:R].contiguous()
             toks = torch.empty(R, dtype=torch.int32, device=dev)
-            sws = torch.empty(sv.spec_sample_workspace_bytes(R, V, sv.SV_BF16), dtype=torch.uint8, device=dev)
-
-            def sstep(c, R=R, rows=rows, us=us, toks=toks, sws=sws):
-                sv.spec_sample(rows[c], us, T, tokens=toks, workspace=sws, stream=stream)
-
-            with torch.cuda.stream(stream):
-                sstep(0)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for c in range(copies):
-                    sstep(c)
-            with torch.cuda.stream(stream):
-                for _ in range(3):
-                    g.replay()
-            torch.cuda.synchronize()
-            reps = max(1, args.steps // copies)
-            s0 = time.perf_counter()
-            with torch.cuda.stream(stream):
-                for _ in range(reps):
-                    g.replay()
-            torch.cuda.synchronize()
-            per = (time.perf_counter() - s0) / (reps * copies)
+            sws = sv.new_workspace(sv.spec_sample_workspace_bytes(R, V, sv.SV_BF16), dev)
+            per = graph_time(torch, stream, lambda c, rows=rows, us=us, toks=toks, sws=sws:
+                             sv.spec_sample(rows[c], us, 1.0, tokens=toks, workspace=sws, stream=stream),
+                             copies, args.steps)
             sample[f"rows_{R}"] = {"us_per_call": round(per * 1e6, 3), "rows_per_s": round(R / per, 1),
                                    "GBps": round(R * V * 2 / per / 1e9, 1)}
+        extras["spec_sample"] = sample
         log(f"[bench] spec_sample {sample}")
 
-    # top-k / top-p filtered verification on the same logits at T = 0.7 (the pages' vLLM
-    # example: temperature 0.7, top_p 0.9), with and without top_k = 50
-    filtered = {}
-    if not greedy:
+        # top-k / top-p filtered verification on the same logits at T = 0.7 (the pages' vLLM
+        # example: temperature 0.7, top_p 0.9), with and without top_k = 50
+        filtered = {}
         temps07 = torch.full((B,), 0.7, dtype=torch.float32, device=dev)
-        fws = torch.empty(sv.spec_verify_filtered_workspace_bytes(B, gamma, V, sv.SV_BF16), dtype=torch.uint8,
-                          device=dev)
+        fws = sv.new_workspace(sv.spec_verify_filtered_workspace_bytes(B, gamma, V, sv.SV_BF16), dev)
         for label, k, p in (("top_p0.9", None, 0.9), ("top_k50_top_p0.9", 50, 0.9)):
             tk = None if k is None else torch.full((B,), k, dtype=torch.int32, device=dev)
             tp = torch.full((B,), p, dtype=torch.float32, device=dev)
@@ -462,38 +621,21 @@ def main():
                 fstep(0)
             torch.cuda.synchronize()
             fc, fo = count.cpu().clone(), out.cpu().clone()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for c in range(copies):
-                    fstep(c)
-            with torch.cuda.stream(stream):
-                g.replay()
-            torch.cuda.synchronize()
-            reps = max(1, args.steps // copies)
-            s0 = time.perf_counter()
-            with torch.cuda.stream(stream):
-                for _ in range(reps):
-                    g.replay()
-            torch.cuda.synchronize()
-            per = (time.perf_counter() - s0) / (reps * copies)
+            per = graph_time(torch, stream, fstep, copies, args.steps)
             assert torch.equal(count.cpu(), fc) and torch.equal(out.cpu(), fo), "filtered replay differs"
             filtered[label] = {"us_per_call": round(per * 1e6, 3), "positions_per_s": round(positions / per, 1),
                                "alpha_hat": round(float(fc.float().mean()) / gamma, 4)}
+        extras["spec_verify_filtered"] = filtered
         log(f"[bench] spec_verify_filtered {filtered}")
 
-    # tree verification: 8 trees of width 4 and depth 3 (84 nodes) over the same vocabulary, T = 0.7
-    tree = {}
-    if not greedy and not args.no_tree:
+        # tree verification: 8 trees of width 4 and depth 3 (84 nodes) over the same vocabulary, T = 0.7
         t0 = time.perf_counter()
         tw = W.build_tree("B8_w4_d3_V128256_bf16_T0.7", 3000, 8, 4, 3, V, "bf16", target_scale=4.0, zipf=True,
                           sigma=0.5, temps=0.7)
         log(f"[bench] generated {tw.name} in {time.perf_counter() - t0:.1f}s")
         tt = tw.to_torch(dev)
-        tcopies = max(2, math.ceil(1.2e9 / ((tt["target"].numel() + tt["draft"].numel()) * 2)))
-        ttg = [tt["target"]] + [tt["target"].clone() for _ in range(tcopies - 1)]
-        tdr = [tt["draft"]] + [tt["draft"].clone() for _ in range(tcopies - 1)]
-        tws = torch.empty(sv.spec_verify_tree_workspace_bytes(tw.B, tw.N, V, sv.SV_BF16), dtype=torch.uint8,
-                          device=dev)
+        ttg, tdr, tcopies, _ = rotate(torch, tt, 2)
+        tws = sv.new_workspace(sv.spec_verify_tree_workspace_bytes(tw.B, tw.N, V, sv.SV_BF16), dev)
         tc = torch.empty(tw.B, dtype=torch.int32, device=dev)
         to = torch.empty((tw.B, tw.N + 1), dtype=torch.int32, device=dev)
         tn = torch.empty((tw.B, tw.N), dtype=torch.int32, device=dev)
@@ -507,51 +649,33 @@ def main():
             tstep(0)
         torch.cuda.synchronize()
         rc, ro = tc.cpu().clone(), to.cpu().clone()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for c in range(tcopies):
-                tstep(c)
-        with torch.cuda.stream(stream):
-            g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, args.steps // (4 * tcopies))
-        s0 = time.perf_counter()
-        with torch.cuda.stream(stream):
-            for _ in range(reps):
-                g.replay()
-        torch.cuda.synchronize()
-        per = (time.perf_counter() - s0) / (reps * tcopies)
+        per = graph_time(torch, stream, tstep, tcopies, args.steps // 4)
         assert torch.equal(tc.cpu(), rc) and torch.equal(to.cpu(), ro), "tree replay differs"
         emitted = float(rc.sum()) + tw.B
-        tree = {"workload": tw.name, "us_per_call": round(per * 1e6, 3), "nodes_per_s": round(tw.B * tw.N / per, 1),
-                "emitted_tokens_per_s": round(emitted / per, 1), "mean_accepted_path": round(float(rc.float().mean()), 3),
-                "GBps_alg": round(tw.bytes_alg() / per / 1e9, 1)}
-        log(f"[bench] spec_verify_tree {tree}")
+        extras["spec_verify_tree"] = {
+            "workload": tw.name, "us_per_call": round(per * 1e6, 3), "nodes_per_s": round(tw.B * tw.N / per, 1),
+            "emitted_tokens_per_s": round(emitted / per, 1), "mean_accepted_path": round(float(rc.float().mean()), 3),
+            "GBps_alg": round(tw.bytes_alg() / per / 1e9, 1)}
+        log(f"[bench] spec_verify_tree {extras['spec_verify_tree']}")
+        del ttg, tdr, tt
 
-    # cold per-call latency of the timed call, and the other configurations' throughput
-    latency, configs = None, {}
-    if not args.no_configs:
-        latency = cold_latency(torch, np, lambda k: step(k % copies, stream), stream, dev)
-        log(f"[bench] cold latency {latency}")
-        runs = [(0, False), (1, False), (2, False), (4, False)] + ([(3, True)] if not greedy else [])
-        for cfg, gr in runs:
-            key = f"config{cfg}" + ("_greedy" if gr else "")
-            configs[key] = time_config(sv, W, torch, math, cfg, gr, dev, stream)
-            log(f"[bench] {key} {configs[key]}")
+    if not args.no_extras:
+        extras["cold_latency"] = cold_latency(torch, np, lambda k: one(k % copies), stream, dev)
+        log(f"[bench] cold latency {extras['cold_latency']}")
+        configs = {}
+        for cfg, gr in [(0, False), (1, False), (2, False), (3, False), (3, True), (4, False)]:
+            if (cfg, gr) == (args.config, greedy):
+                continue
+            name = f"config{cfg}" + ("_greedy" if gr else "")
+            configs[name] = time_config(sv, W, torch, cfg, gr, dev, stream, cache)
+            log(f"[bench] {name} {configs[name]}")
+        extras["configs"] = configs
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        n, spent = 0, 0.0
-        while spent < args.cpu_seconds or n == 0:
-            c0 = time.perf_counter()
-            oracle.run_workload(w, trace=False)
-            spent += time.perf_counter() - c0
-            n += 1
-        cpu = {"value": round(positions * n / spent, 2), "unit": "positions/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n} full calls of the same B=64 workload (single-threaded fp64 C, gcc -O2), "
-                         f"{spent:.1f} s", "host_cpus": os.cpu_count(), "host": platform.processor() or
-                         platform.machine()}
+        head = f"config{args.config}" + ("_greedy" if greedy else "")
+        cpu = cpu_leg(W, args.cpu_seconds, cache, head)
+        log(f"[bench] cpu baseline {cpu['value']} positions/s on {cpu['cpu_model']}")
 
     rec = {
         "metric": METRIC,
@@ -566,23 +690,19 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "gamma": gamma, "V": V, "input_dtype": "bf16",
-                   "temperature": T, "mode": args.mode, "copies_rotated": copies,
+        "config": {"workload": w.name, "entry": entry, "B": B, "gamma": gamma, "V": V, "input_dtype": w.dtype,
+                   "temperature": "per request" if w.scalar_temperature is None else w.scalar_temperature,
+                   "mode": args.mode, "copies_rotated": copies,
                    "launch": "eager" if args.eager else f"hip graph replay, {copies} steps per graph",
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "extra": {"step_GBps_alg": round(bytes_alg / (ms_per_step / 1e3) / 1e9, 1),
+        "extra": {"device_us_per_step": round(dev_s_per_step * 1e6, 3),
+                  "step_GBps_alg": round(bytes_alg / (ms_per_step / 1e3) / 1e9, 1),
                   "step_GBps_formula": round(formula_bytes / (ms_per_step / 1e3) / 1e9, 1),
                   "bytes_alg": bytes_alg, "bytes_formula": formula_bytes,
-                  "device_ms_per_step": round(dev_ms / args.steps, 5),
-                  "k1_us_min": round(min(k1_ms) * 1e3, 3), "k1_us_max": round(max(k1_ms) * 1e3, 3),
-                  "alpha_hat": round(float(ref_count.float().mean()) / gamma, 4),
-                  "spec_sample": sample,
-                  "spec_verify_filtered": filtered,
-                  "spec_verify_tree": tree,
-                  "cold_latency": latency,
-                  "configs": configs,
+                  "alpha_hat": round(float(ref_count.float().sum()) / max(1, positions), 4),
+                  **extras,
                   "kernel_source_sha256_16": source_hash()},
     }
     print(json.dumps(rec), flush=True)

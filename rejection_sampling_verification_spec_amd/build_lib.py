@@ -14,6 +14,8 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "specverify.hip")
 SOURCES = [SRC, os.path.join(HERE, "csrc", "gamma_policy.cpp")]
 OUT = os.path.join(HERE, "libspecverify.so")
+PROBE_SRC = os.path.join(HERE, "csrc", "stream_probe.hip")
+PROBE_OUT = os.path.join(HERE, "libsvprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -30,10 +32,12 @@ FLAGS = [
 
 
 def build(out: str = OUT, extra=()) -> str:
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *SOURCES]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
+    """Builds libspecverify.so and the benchmark's streaming-read probe, libsvprobe.so."""
+    for srcs, dst in ((SOURCES, out), ([PROBE_SRC], PROBE_OUT)):
+        tmp = dst + ".tmp"
+        cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *srcs]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, dst)
     return out
 
 
