@@ -1,12 +1,22 @@
-"""GPU-vs-oracle comparison helpers (used by the GPU tests only)."""
+"""GPU-vs-oracle comparison helpers (used by the GPU tests only).
+
+A failing comparison writes the case (inputs, GPU outputs, oracle outputs) to
+an .npz file under $SPECVERIFY_DUMP_DIR (default gpurun_out/parity_failures at
+the repository root); ``python -m tests._parity replay FILE.npz`` reruns the
+oracle on it and prints where the two disagree.
+"""
 from __future__ import annotations
 
+import os
+import sys
 from dataclasses import dataclass
 from typing import Optional
 
 import numpy as np
 
 import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # probability tolerances: fp32 logits 1e-5 absolute, bf16 logits 2e-3 absolute
 PROB_TOL = {"f32": 1e-5, "bf16": 2e-3}
@@ -81,8 +91,48 @@ def gpu_run(w, debug: bool = False, force_ex: bool = False, stream=None, workspa
                      {k: v.cpu().numpy() for k, v in dbg.items()} if dbg else None)
 
 
+_CASE_FIELDS = ("target", "draft", "draft_tokens", "u_accept", "u_sample", "temperature", "lens", "top_k", "top_p")
+
+
+def dump_case(w, g: GpuResult, o, reason: str) -> str:
+    """Writes a failing case to an .npz file (arrays only) and returns its path."""
+    d = os.environ.get("SPECVERIFY_DUMP_DIR", os.path.join(ROOT, "gpurun_out", "parity_failures"))
+    os.makedirs(d, exist_ok=True)
+    path = os.path.join(d, f"{w.name}.npz")
+    arrays = {k: np.asarray(getattr(w, k)) for k in _CASE_FIELDS if getattr(w, k, None) is not None}
+    arrays.update(dtype=np.array(w.dtype), name=np.array(w.name), reason=np.array(reason),
+                  gpu_count=g.count, gpu_out=g.out, oracle_count=o.accepted_count, oracle_out=o.out_tokens,
+                  oracle_flags=o.flags)
+    np.savez_compressed(path, **arrays)
+    return path
+
+
+def replay(path: str) -> int:
+    """Reruns the oracle on a dumped case; prints the requests where the GPU differed."""
+    z = np.load(path, allow_pickle=False)
+    get = (lambda k: z[k] if k in z.files else None)
+    o = oracle.spec_verify(z["target"], z["draft"], z["draft_tokens"], z["u_accept"], z["u_sample"],
+                           z["temperature"], lens=get("lens"), dtype=str(z["dtype"]), top_k=get("top_k"),
+                           top_p=get("top_p"))
+    print(f"{z['name']}: {z['reason']}")
+    bad = np.nonzero((z["gpu_count"] != o.accepted_count) | np.any(z["gpu_out"] != o.out_tokens, axis=1))[0]
+    for b in bad:
+        print(f"  b={b}: gpu count {z['gpu_count'][b]} out {z['gpu_out'][b]} | oracle count {o.accepted_count[b]} "
+              f"out {o.out_tokens[b]} flags {o.flags[b]} margins acc {o.accept_margin[b]:.3g} cdf {o.cdf_margin[b]:.3g}")
+    return len(bad)
+
+
 def check_parity(w, g: GpuResult, o, require_no_flags: bool = True) -> dict:
-    """Bit-exact counts/tokens outside the near-boundary band; greedy fully exact; probability tolerances."""
+    """Bit-exact counts/tokens outside the near-boundary band; greedy fully exact; probability tolerances.
+    A failure dumps the case for replay (see the module docstring)."""
+    try:
+        return _check_parity(w, g, o, require_no_flags)
+    except AssertionError as e:
+        path = dump_case(w, g, o, str(e)[:2000])
+        raise AssertionError(f"{e}\n(case written to {path})") from None
+
+
+def _check_parity(w, g: GpuResult, o, require_no_flags: bool = True) -> dict:
     greedy = w.temperature == 0
     np.testing.assert_array_equal(g.count[greedy], o.accepted_count[greedy], err_msg=f"{w.name} greedy counts")
     np.testing.assert_array_equal(g.out[greedy], o.out_tokens[greedy], err_msg=f"{w.name} greedy tokens")
@@ -137,3 +187,10 @@ def run_and_check(w, debug: bool = True, require_no_flags: bool = True, **kw) ->
     rep = check_parity(w, g, o, require_no_flags=require_no_flags)
     say(f"ok {rep}")
     return rep
+
+
+if __name__ == "__main__":
+    if len(sys.argv) == 3 and sys.argv[1] == "replay":
+        sys.exit(1 if replay(sys.argv[2]) else 0)
+    print("usage: python -m tests._parity replay CASE.npz", file=sys.stderr)
+    sys.exit(2)
