@@ -185,6 +185,54 @@ struct alignas(16) SubSums {
   double p;  // sum of 2^(z_p c - M_p) over the sub-chunk (zero-mass fallback)
 };
 
+// ------------------------------------------------------------------ hand-over between workgroups
+// Where workgroups of one kernel read each other's results (the tree walk's
+// shared passes), the values go through device-scope atomic stores and loads:
+// each XCD has its own L2, not coherent with the others, and these accesses
+// bypass it, so no cache write-back or invalidate is needed (a device-scope
+// fence would write back or invalidate the XCD's whole L2).  A writer waits
+// until its stores are complete before it counts itself done with a
+// device-scope atomic add; a reader that has seen the count issues its loads
+// only afterwards.
+template <bool COH, typename T>
+__device__ __forceinline__ void put(T *p, T v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH, typename T>
+__device__ __forceinline__ T get(const T *p) {
+  if constexpr (COH) return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+
+// Waits until this wave's earlier memory operations (its stores included) are
+// complete.  The signal fences keep the compiler from moving memory accesses
+// across the wait.
+__device__ __forceinline__ void wait_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ unsigned count_up(unsigned *c) {
+  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr unsigned kSpinLimit = 1u << 20;  // polls of a bounded wait (about a second; a correct run needs a few)
+
+// Waits until *c >= target (one lane).  Bounded: if the count never arrives,
+// the error word is set and the caller goes on (its results are then invalid).
+__device__ __forceinline__ void wait_count(const unsigned *c, unsigned target, unsigned *err) {
+  for (unsigned it = 0;; ++it) {
+    if (get<true>(c) >= target) return;
+    if (it >= kSpinLimit) {
+      put<true>(err, 1u);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // ================================================================== K1
 // Rows of request b: r in [0, gamma] are target rows, r in [gamma+1, 2 gamma]
 // are draft rows r - gamma - 1.  A row is needed if it is a target row i <= g_b,
@@ -2136,10 +2184,17 @@ __global__ __launch_bounds__(kFBlock) void k_filter_general(
 // the inverse CDF with u_sample.  T == 0 follows the first child equal to the
 // target arg-max.
 //
-// k_tree_walk: one 512-thread workgroup per request walks its tree.  Row
-// statistics come from K1's partials; the acceptance ratio is fp64 from the
-// two gathered logits; each rejection costs one pass over the position's two
-// rows (2048-token sub-chunk masses kept in LDS for the final draw).
+// k_tree_walk: NW 512-thread workgroups per request walk its tree together.
+// Every workgroup takes the same decisions (row statistics from K1's partials,
+// the acceptance ratio in fp64 from the two gathered logits, all merged and
+// summed in a fixed order); each rejection costs one pass over the position's
+// two rows, shared out as 2048-token sub-chunks over the request's NW x 8
+// waves.  The sub-chunk masses go through device-scope atomic stores into a
+// per-request array (two copies, alternating between passes), the workgroups
+// meet at a per-request counter (cleared by K1), and each then reads back all
+// the masses in sub-chunk order, so Z is the same everywhere.  Workgroup 0
+// writes the outputs and draws the final token.  With NW = 1 (large batches)
+// there is no counter and the masses stay in LDS.
 constexpr int kTBlock = 512;
 constexpr int kTWaves = kTBlock / kWave;
 constexpr int kTMaxSub = SV_TREE_MAX_V / kSub;
@@ -2198,26 +2253,43 @@ __device__ __forceinline__ float tree_lane_mass(const u32x4 *tp, const u32x4 *dq
   return acc;
 }
 
+// How the request's workgroups share a pass and meet after it.
+struct TreeTeam {
+  int w, NW;              // this workgroup, workgroups per request
+  double *sub;            // [2][NSUB] per-request masses (NW > 1)
+  unsigned *meet;         // per-request counter (NW > 1)
+  unsigned *err;          // set if a bounded wait ran out
+  int pass;               // passes done so far in this call
+};
+
 template <int DT, bool USEQ>
 __device__ __forceinline__ void tree_masses_of(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c,
-                               float negMp, float negMq, float r, TreeShared &sh) {
+                               float negMp, float negMq, float r, TreeShared &sh, TreeTeam &tm) {
   constexpr int kN = kLaneElems / Elem<DT>::kVec;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  // Sub-chunks wholly inside an aligned row: wave w takes w, w + kTWaves, ...
+  // this wave's place among the request's NW x 8 waves
+  const int gw = tm.w * kTWaves + wave, stride = tm.NW * kTWaves;
+  double *gsub = tm.NW > 1 ? tm.sub + (tm.pass & 1) * NSUB : nullptr;
+  auto put_mass = [&](int j, double v) {
+    if (lane == 0) {
+      if (gsub) put<true>(gsub + j, v);
+      else sh.sub[j] = v;
+    }
+  };
+  // Sub-chunks wholly inside an aligned row: wave g takes g, g + stride, ...
   // with straight-line loads, the next one requested while the current one is
   // reduced (its index clamped to the last such sub-chunk, so that the loads are
   // unconditional and each wait covers exactly the older sub-chunk).
   const int nfast = aligned ? min(NSUB, V / kSub) : 0;
-  if (wave < nfast) {
+  if (gw < nfast) {
     u32x4 tp[kN], dq[kN], tn[kN], dn[kN];
-    load_lane_fast<DT>(trow, static_cast<long>(wave) * kSub, lane, tp);
-    if constexpr (USEQ) load_lane_fast<DT>(drow, static_cast<long>(wave) * kSub, lane, dq);
-    for (int j = wave; j < nfast; j += kTWaves) {
-      const long jn = min(j + kTWaves, nfast - 1);
+    load_lane_fast<DT>(trow, static_cast<long>(gw) * kSub, lane, tp);
+    if constexpr (USEQ) load_lane_fast<DT>(drow, static_cast<long>(gw) * kSub, lane, dq);
+    for (int j = gw; j < nfast; j += stride) {
+      const long jn = min(j + stride, nfast - 1);
       load_lane_fast<DT>(trow, jn * kSub, lane, tn);
       if constexpr (USEQ) load_lane_fast<DT>(drow, jn * kSub, lane, dn);
-      const double ws = wave_sum(static_cast<double>(tree_lane_mass<DT, USEQ>(tp, dq, c, negMp, negMq, r)));
-      if (lane == 0) sh.sub[j] = ws;
+      put_mass(j, wave_sum(static_cast<double>(tree_lane_mass<DT, USEQ>(tp, dq, c, negMp, negMq, r))));
 #pragma unroll
       for (int u = 0; u < kN; ++u) {
         tp[u] = tn[u];
@@ -2227,12 +2299,24 @@ __device__ __forceinline__ void tree_masses_of(const void *trow, const void *dro
   }
   // the rest (a partial last sub-chunk, or every sub-chunk of a row that is not
   // aligned): guarded loads, one sub-chunk at a time
-  for (int j = nfast + wave; j < NSUB; j += kTWaves) {
+  for (int j = nfast + gw; j < NSUB; j += stride) {
     u32x4 tp[kN], dq[kN];
     load_lane_raw<DT>(trow, aligned, static_cast<long>(j) * kSub, lane, V, tp);
     if constexpr (USEQ) load_lane_raw<DT>(drow, aligned, static_cast<long>(j) * kSub, lane, V, dq);
-    const double ws = wave_sum(static_cast<double>(tree_lane_mass<DT, USEQ>(tp, dq, c, negMp, negMq, r)));
-    if (lane == 0) sh.sub[j] = ws;
+    put_mass(j, wave_sum(static_cast<double>(tree_lane_mass<DT, USEQ>(tp, dq, c, negMp, negMq, r))));
+  }
+  if (gsub) {
+    // every wave's masses are complete before the workgroup counts itself in;
+    // then wait for the request's other workgroups and read all the masses
+    wait_memory();
+    __syncthreads();
+    ++tm.pass;
+    if (threadIdx.x == 0) {
+      count_up(tm.meet);
+      wait_count(tm.meet, static_cast<unsigned>(tm.NW * tm.pass), tm.err);
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < NSUB; j += kTBlock) sh.sub[j] = get<true>(gsub + j);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -2245,9 +2329,9 @@ __device__ __forceinline__ void tree_masses_of(const void *trow, const void *dro
 
 template <int DT>
 __device__ __forceinline__ void tree_masses(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c,
-                            float negMp, float negMq, float r, bool use_q, TreeShared &sh) {
-  if (use_q) tree_masses_of<DT, true>(trow, drow, aligned, V, NSUB, c, negMp, negMq, r, sh);
-  else tree_masses_of<DT, false>(trow, drow, aligned, V, NSUB, c, negMp, negMq, r, sh);
+                            float negMp, float negMq, float r, bool use_q, TreeShared &sh, TreeTeam &tm) {
+  if (use_q) tree_masses_of<DT, true>(trow, drow, aligned, V, NSUB, c, negMp, negMq, r, sh, tm);
+  else tree_masses_of<DT, false>(trow, drow, aligned, V, NSUB, c, negMp, negMq, r, sh, tm);
 }
 
 // Inverse CDF over the masses in sh.sub (of the same w as tree_masses): the
@@ -2337,14 +2421,24 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     const int32_t *__restrict__ tokens, const int32_t *__restrict__ num_nodes, const float *__restrict__ u_accept,
     const float *__restrict__ u_sample, const float *__restrict__ temps, int Nmax, int V, int NS,
     const Partial *__restrict__ part, int32_t *__restrict__ count, int32_t *__restrict__ out_tokens,
-    int32_t *__restrict__ out_nodes) {
-  const int b = blockIdx.x, tid = threadIdx.x;
+    int32_t *__restrict__ out_nodes, int NW, double *__restrict__ tsub, unsigned *__restrict__ tcount,
+    unsigned *__restrict__ terr) {
+  const int b = blockIdx.x / NW, tid = threadIdx.x;
   const int rows = 2 * Nmax + 1;
   const int N = request_len(num_nodes, Nmax, b);
   const float T = temps[b];
   const bool greedy = !(T > 0.0f);
   const float c = greedy ? 0.0f : temp_scale(T);
   const int NSUB = (V + kSub - 1) / kSub;
+  TreeTeam tm;
+  tm.w = blockIdx.x - b * NW;
+  tm.NW = greedy ? 1 : NW;  // a greedy walk makes no pass: workgroup 0 alone
+  tm.sub = tsub + static_cast<long>(b) * 2 * NSUB;
+  tm.meet = tcount + static_cast<long>(b) * rows;  // cleared by K1 (row slot 0 of the request)
+  tm.err = terr;
+  tm.pass = 0;
+  if (greedy && tm.w > 0) return;  // uniform per workgroup
+  const bool lead = tm.w == 0;     // writes the outputs
   __shared__ TreeShared sh;
   __shared__ int s_hit, s_arg, s_Mp, s_Mq;
   __shared__ double s_sp, s_sq;
@@ -2358,8 +2452,10 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     sh.parent[n] = pa;
     sh.token[n] = x;
   }
-  for (int t = tid; t <= Nmax; t += kTBlock) out_tokens[static_cast<long>(b) * (Nmax + 1) + t] = -1;
-  for (int t = tid; t < Nmax; t += kTBlock) out_nodes[static_cast<long>(b) * Nmax + t] = -1;
+  if (lead) {
+    for (int t = tid; t <= Nmax; t += kTBlock) out_tokens[static_cast<long>(b) * (Nmax + 1) + t] = -1;
+    for (int t = tid; t < Nmax; t += kTBlock) out_nodes[static_cast<long>(b) * Nmax + t] = -1;
+  }
   __syncthreads();
   const size_t eb = Elem<DT>::kBytes;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -2369,11 +2465,21 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     const void *drow = pos < Nmax ? static_cast<const char *>(draft) + (static_cast<long>(b) * Nmax + pos) * V * eb
                                   : nullptr;  // position Nmax has no child
     const bool al = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;
-    // the position's children in node order (a block-wide compaction), and the
-    // row statistics (target by thread 0, draft by the first lane of wave 1)
+    // the position's children in node order (a block-wide compaction); then, in
+    // one round trip, the row statistics (target by thread 0, draft by the
+    // first lane of wave 1) and each child's two logits and uniform (threads
+    // 128 + j)
     const bool is_child = tid < N && tid >= pos && sh.parent[tid] == pos - 1;
     const unsigned long long mask = __ballot(is_child);
     if (lane == 0) sh.wcnt[wave] = __popcll(mask);
+    __syncthreads();
+    int nchild = 0, before = 0;
+    for (int w = 0; w < kTWaves; ++w) {
+      if (w < wave) before += sh.wcnt[w];
+      nchild += sh.wcnt[w];
+    }
+    if (is_child) sh.child[before + __popcll(mask & ((1ull << lane) - 1ull))] = tid;
+    __syncthreads();
     if (tid == 0) {
       int M, arg;
       double s;
@@ -2386,20 +2492,14 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
       int arg;
       merged_row(part, static_cast<long>(b) * rows + Nmax + 1 + pos, NS, false, s_Mq, s_sq, arg);
     }
-    __syncthreads();
-    int nchild = 0, before = 0;
-    for (int w = 0; w < kTWaves; ++w) {
-      if (w < wave) before += sh.wcnt[w];
-      nchild += sh.wcnt[w];
-    }
-    if (is_child) sh.child[before + __popcll(mask & ((1ull << lane) - 1ull))] = tid;
-    __syncthreads();
-    if (!greedy && tid < nchild) {  // gather each child's two logits and its uniform
-      const int n = sh.child[tid], x = sh.token[n];
+    static_assert(2 * kWave + SV_TREE_MAX_NODES <= kTBlock, "a thread per child after the first two waves");
+    const int jc = tid - 2 * kWave;
+    if (!greedy && jc >= 0 && jc < nchild) {  // gather each child's two logits and its uniform
+      const int n = sh.child[jc], x = sh.token[n];
       const bool ok = x >= 0 && x < V;  // an id outside the vocabulary is rejected, never dereferenced
-      sh.czp[tid] = ok ? load_one<DT>(trow, x) : 0.0f;
-      sh.czq[tid] = ok ? load_one<DT>(drow, x) : 0.0f;
-      sh.cu[tid] = ok ? u_accept[static_cast<long>(b) * Nmax + n] : 2.0f;  // 2 rejects
+      sh.czp[jc] = ok ? load_one<DT>(trow, x) : 0.0f;
+      sh.czq[jc] = ok ? load_one<DT>(drow, x) : 0.0f;
+      sh.cu[jc] = ok ? u_accept[static_cast<long>(b) * Nmax + n] : 2.0f;  // 2 rejects
     }
     __syncthreads();
     int hit = -1;
@@ -2412,7 +2512,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
       __syncthreads();
       hit = s_hit;
       if (hit < 0) {
-        if (tid == 0) out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = s_arg;
+        if (lead && tid == 0) out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = s_arg;
         break;
       }
     } else {
@@ -2439,7 +2539,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
         // rejected: the next target is max(0, p - (cc + Z) q) / Z'
         cc += Z;
         const float r = static_cast<float>(cc * sp / sq);
-        tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, true, sh);
+        tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, true, sh, tm);
         const double W = sh.W;
         if (W > 0.0) {
           Z = W / sp;
@@ -2454,15 +2554,18 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
         // every child rejected, or none: draw from the current target
         const bool use_q = cc > 0.0;
         const float r = use_q ? static_cast<float>(cc * sp / sq) : 0.0f;
-        if (!masses_current) tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q, sh);
-        const int tok = tree_select<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q,
-                                        u_sample[b], sh);
-        if (tid == 0) out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = tok;
+        if (!masses_current)
+          tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q, sh, tm);
+        if (lead) {  // uniform per workgroup
+          const int tok = tree_select<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q,
+                                          u_sample[b], sh);
+          if (tid == 0) out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = tok;
+        }
         break;
       }
     }
     // accepted node `hit`: emit it and move to its position
-    if (tid == 0) {
+    if (lead && tid == 0) {
       out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = sh.token[hit];
       out_nodes[static_cast<long>(b) * Nmax + depth] = hit;
     }
@@ -2470,7 +2573,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     pos = hit + 1;
     __syncthreads();
   }
-  if (tid == 0) count[b] = depth;
+  if (lead && tid == 0) count[b] = depth;
 }
 
 // ================================================================== draft-side sampler
@@ -2887,6 +2990,51 @@ int dispatch(const void *target, const void *draft, const int32_t *tokens, const
                      B, gamma, V, count, out, ws, P, st, dbg);
 }
 
+constexpr int kMaxDevices = 64;
+
+// ------------------------------------------------------------------ tree walk
+// The tree call's workspace: the linear plan, then one counter per row slot
+// (K1 clears them; the walk uses the one of each request's row slot 0), two
+// copies of each request's sub-chunk masses, and the walk's error word.
+struct TreeLayout {
+  size_t count_off, sub_off, err_off, total;
+};
+
+TreeLayout tree_layout(int B, const Plan &P) {
+  TreeLayout L;
+  size_t off = P.total;
+  L.count_off = off;
+  off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B) * P.rows);
+  L.sub_off = off;
+  off = align_up(off + sizeof(double) * 2 * static_cast<size_t>(B) * P.NSUB);
+  L.err_off = off;
+  off = align_up(off + sizeof(unsigned));
+  L.total = off;
+  return L;
+}
+
+// Workgroups per request for the tree walk: enough for one 2048-token sub-chunk
+// per wave, as long as the whole grid stays within half of the workgroups the
+// device holds at once (the team's workgroups wait for each other after every
+// pass, so they must all be resident); large batches walk with one workgroup
+// per request.
+template <int DT>
+int tree_team_size(int B, int NSUB) {
+  static int cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1;
+  if (!cache[dev]) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_tree_walk<DT>, kTBlock, 0) != hipSuccess)
+      return 1;
+    cache[dev] = max(1, cus * per / 2);
+  }
+  const int want = (NSUB + kTWaves - 1) / kTWaves;
+  const int room = cache[dev] / B;
+  return max(1, min(want, room));
+}
+
 // ------------------------------------------------------------------ built-in scratch
 // Scratch of spec_verify_noalloc: one array per GPU (each GPU that loads the
 // code object holds its own copy).  In host code `scratch` only names the
@@ -2894,7 +3042,6 @@ int dispatch(const void *target, const void *draft, const int32_t *tokens, const
 // device with that device current, and only that address is passed to kernels.
 static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 void *g_scratch_ptr[kMaxDevices];
 
@@ -2977,12 +3124,12 @@ int spec_verify_filtered(const void *target_logits, const void *draft_logits, co
 size_t spec_verify_tree_workspace_bytes(int B, int max_nodes, int V, int dtype) {
   Plan P;
   if (max_nodes < 0 || V > SV_TREE_MAX_V || !make_plan(B, max_nodes, V, dtype, &P, SV_TREE_MAX_NODES)) return 0;
-  return P.total;
+  return tree_layout(B, P).total;
 }
 
 // Row statistics of every tree position by K1 (the linear layout with
-// gamma = max_nodes and draft lengths = node counts), then one workgroup per
-// request walks its tree.
+// gamma = max_nodes and draft lengths = node counts; K1 also clears the walk's
+// per-request counters), then NW workgroups per request walk its tree.
 int spec_verify_tree(const void *target_logits, const void *draft_logits, const int32_t *node_parent,
                      const int32_t *node_tokens, const int32_t *num_nodes, const float *u_accept,
                      const float *u_sample, const float *temperature, int B, int max_nodes, int V, int dtype,
@@ -2994,27 +3141,35 @@ int spec_verify_tree(const void *target_logits, const void *draft_logits, const 
   if (!target_logits || !u_sample || !temperature || !accepted_count || !out_tokens) return SV_EINVAL;
   if (max_nodes > 0 && (!draft_logits || !node_parent || !node_tokens || !u_accept || !out_nodes))
     return SV_EINVAL;
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < P.total)
+  const TreeLayout L = tree_layout(B, P);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < L.total)
     return SV_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char *base = static_cast<char *>(workspace);
   Partial *part = reinterpret_cast<Partial *>(base + P.part_off);
   float *zx = reinterpret_cast<float *>(base + P.zx_off);
+  unsigned *tcount = reinterpret_cast<unsigned *>(base + L.count_off);
+  double *tsub = reinterpret_cast<double *>(base + L.sub_off);
+  unsigned *terr = reinterpret_cast<unsigned *>(base + L.err_off);
   hipError_t e;
   if (dtype == SV_BF16) {
     e = launch_k1<SV_BF16>(target_logits, draft_logits, node_tokens, temperature, 0.0f, num_nodes, max_nodes, V, P,
-                           part, zx, st, nullptr, nullptr);
+                           part, zx, st, nullptr, nullptr, tcount);
     if (e != hipSuccess) return SV_EHIP;
-    hipLaunchKernelGGL((k_tree_walk<SV_BF16>), dim3(B), dim3(kTBlock), 0, st, target_logits, draft_logits,
-                       node_parent, node_tokens, num_nodes, u_accept, u_sample, temperature, max_nodes, V, P.NS,
-                       part, accepted_count, out_tokens, out_nodes);
+    const int NW = tree_team_size<SV_BF16>(B, P.NSUB);
+    hipLaunchKernelGGL((k_tree_walk<SV_BF16>), dim3(static_cast<unsigned>(static_cast<long>(B) * NW)),
+                       dim3(kTBlock), 0, st, target_logits, draft_logits, node_parent, node_tokens, num_nodes,
+                       u_accept, u_sample, temperature, max_nodes, V, P.NS, part, accepted_count, out_tokens,
+                       out_nodes, NW, tsub, tcount, terr);
   } else {
     e = launch_k1<SV_F32>(target_logits, draft_logits, node_tokens, temperature, 0.0f, num_nodes, max_nodes, V, P,
-                          part, zx, st, nullptr, nullptr);
+                          part, zx, st, nullptr, nullptr, tcount);
     if (e != hipSuccess) return SV_EHIP;
-    hipLaunchKernelGGL((k_tree_walk<SV_F32>), dim3(B), dim3(kTBlock), 0, st, target_logits, draft_logits,
-                       node_parent, node_tokens, num_nodes, u_accept, u_sample, temperature, max_nodes, V, P.NS,
-                       part, accepted_count, out_tokens, out_nodes);
+    const int NW = tree_team_size<SV_F32>(B, P.NSUB);
+    hipLaunchKernelGGL((k_tree_walk<SV_F32>), dim3(static_cast<unsigned>(static_cast<long>(B) * NW)),
+                       dim3(kTBlock), 0, st, target_logits, draft_logits, node_parent, node_tokens, num_nodes,
+                       u_accept, u_sample, temperature, max_nodes, V, P.NS, part, accepted_count, out_tokens,
+                       out_nodes, NW, tsub, tcount, terr);
   }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
