@@ -195,7 +195,10 @@ def summarize_profile(root: str):
         copy_name = max(cfetch, key=lambda k: cfetch[k])   # the 1 GiB copy kernel (the fill reads nothing)
         copy_kib = (1 << 30) / 1024
         f_fetch, f_write = copy_kib / cfetch[copy_name], copy_kib / cwrite[copy_name]
-        step = [k for k in fetch if k.split("<")[0] in STEP_KERNELS]
+        # the timed step's own instantiations: the stochastic row-statistics kernel (the per-request-T
+        # one in the same run belongs to the separate row-statistics timing) and the plain K2/K3
+        step = [k for k in fetch if k.split("<")[0] in STEP_KERNELS
+                and ("stochastic" in k if k.startswith("k1_") else "plain" in k)]
         per = {k: round((fetch[k] * f_fetch + write.get(k, 0.0) * f_write) * 1024) for k in step}
         step_bytes = sum(per.values())
         bytes_alg = 64 * 11 * 128256 * 2
