@@ -614,7 +614,7 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
 // crossing lies within the rounding of the masses (about 1e-7 of the kept
 // mass).  The result per row is (tau, kept mass); rows of requests without a
 // filter are not touched.
-constexpr int kFBlock = 512;  // FC workgroup
+constexpr int kFBlock = 256;  // FC and FE workgroup (FC: three workgroups fit a CU, every row of a batch of 64 x 11 is resident)
 constexpr int kFWaves = kFBlock / kWave;
 constexpr int kLBlock = 256;  // FG workgroup
 constexpr int kFBins = 2048;  // general path: y bins; index kFBins collects y <= -64
@@ -1268,7 +1268,11 @@ struct GeneralShared {
       unsigned cnt1[kFBins];
       unsigned long long mass1[kFBins];
     } h;
-    unsigned keys[kFCap];  // gathered logits (order keys)
+    struct {
+      unsigned keys[kFCap];  // gathered logits (order keys)
+      unsigned rcnt[256];    // radix_cut's digit histogram over them (count, mass)
+      unsigned long long rmass[256];
+    } k;
     struct {  // deeper windows: the row's band counts, then capture counts
       unsigned tot[kDeep + 1];
       unsigned wc[kFWaves];
@@ -1514,6 +1518,138 @@ __device__ float scan_sorted(const unsigned *keys, int n, unsigned long long bef
   return tau;
 }
 
+// The cut for one criterion over keys[0, n) in LDS (unsorted, n <= kFCap)
+// that continue a prefix of before_c logits with mass before_m: the first end,
+// from the top, of a group of equal keys whose inclusive count (by_mass false)
+// or fixed-point mass (by_mass true), prefix included, reaches `target` --
+// the definition scan_sorted applies to sorted keys -- found by an exact
+// radix select.  One pass finds the keys' smallest and largest values and
+// their totals; the bits above their highest differing bit are common to
+// all.  Then one pass per 8-bit digit below that, from the top: an LDS
+// histogram of (count, mass) over the digit of the keys that match the
+// digits chosen so far, bins in descending digit order; one wave scans the 256
+// bins and picks the bin where the running total crosses the target.  When
+// every digit is chosen the keys left are one value: tau is that logit and
+// kept the mass of every key >= it, prefix included.  Returns false (kept =
+// the prefix plus the keys' total) when the target exceeds the total.  The
+// keys of bf16 logits have their low 16 bits fixed by the sign (0 for keys
+// >= 2^31, else all ones), so the digits stop at bit 16.
+template <int DT>
+__device__ bool radix_cut(const unsigned *keys, int n, unsigned long long before_c, unsigned long long before_m,
+                          float c, float negM, int fs, bool by_mass, unsigned long long target, float &tau,
+                          unsigned long long &kept, GeneralShared &sh) {
+  constexpr int kLowBits = DT == SV_BF16 ? 16 : 0;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  {  // smallest and largest key, count and mass of all the keys
+    unsigned kmin = 0xffffffffu, kmax = 0u;
+    unsigned long long tm = 0;
+    for (int i = tid; i < n; i += kFBlock) {
+      const unsigned key = keys[i];
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+      tm += fixed_mass(key_value(key), c, negM, fs);
+    }
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off /= 2) {
+      kmin = min(kmin, static_cast<unsigned>(__shfl_xor(static_cast<int>(kmin), off)));
+      kmax = max(kmax, static_cast<unsigned>(__shfl_xor(static_cast<int>(kmax), off)));
+      tm += __shfl_xor(tm, off);
+    }
+    if (lane == 0) {
+      sh.sc.red[wave] = (static_cast<unsigned long long>(kmax) << 32) | kmin;
+      sh.sc.red[kFWaves + wave] = tm;
+    }
+    __syncthreads();
+    kmin = 0xffffffffu;
+    kmax = 0u;
+    tm = 0;
+#pragma unroll
+    for (int w = 0; w < kFWaves; ++w) {
+      kmin = min(kmin, static_cast<unsigned>(sh.sc.red[w]));
+      kmax = max(kmax, static_cast<unsigned>(sh.sc.red[w] >> 32));
+      tm += sh.sc.red[kFWaves + w];
+    }
+    __syncthreads();
+    const unsigned long long total = by_mass ? before_m + tm : before_c + static_cast<unsigned long long>(n);
+    if (n == 0 || total < target) {  // not reached
+      kept = before_m + tm;
+      return false;
+    }
+    if (kmin == kmax) {  // one value
+      tau = key_value(kmax);
+      kept = before_m + tm;
+      return true;
+    }
+    const int hb = 31 - __clz(static_cast<int>(kmin ^ kmax));  // highest differing bit
+    unsigned hi_mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);    // bits common to all keys
+    unsigned hi_val = kmax & hi_mask;
+    int shift = max(hb - 7, kLowBits);
+    for (;;) {
+      for (int j = tid; j < 256; j += kFBlock) {
+        sh.u.k.rcnt[j] = 0;
+        sh.u.k.rmass[j] = 0;
+      }
+      __syncthreads();
+      for (int i = tid; i < n; i += kFBlock) {
+        const unsigned key = keys[i];
+        if ((key & hi_mask) == hi_val) {
+          const int bin = 255 - static_cast<int>((key >> shift) & 255u);
+          atomicAdd(&sh.u.k.rcnt[bin], 1u);
+          atomicAdd(&sh.u.k.rmass[bin], fixed_mass(key_value(key), c, negM, fs));
+        }
+      }
+      __syncthreads();
+      if (tid < kWave) {  // lane L scans bins 4L .. 4L + 3
+        unsigned long long bc[4], bm[4], lc = 0, lm = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bc[q] = sh.u.k.rcnt[4 * lane + q];
+          bm[q] = sh.u.k.rmass[4 * lane + q];
+          lc += bc[q];
+          lm += bm[q];
+        }
+        unsigned long long rc = wave_incl_scan_u64(lc, lane) - lc + before_c;
+        unsigned long long rm = wave_incl_scan_u64(lm, lane) - lm + before_m;
+        int mine = -1;
+        unsigned long long mc = 0, mm = 0, mbin = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const unsigned long long before = by_mass ? rm : rc, here = by_mass ? bm[q] : bc[q];
+          if (mine < 0 && before < target && target <= before + here) {
+            mine = q;
+            mc = rc;
+            mm = rm;
+            mbin = bm[q];
+          }
+          rc += bc[q];
+          rm += bm[q];
+        }
+        if (mine >= 0) {  // exactly one lane: the running total reaches the target in the chosen keys
+          sh.sc.pick = 4 * lane + mine;
+          sh.sc.pick_c = mc;
+          sh.sc.pick_m = mm;
+          sh.sc.res_m = mbin;
+        }
+      }
+      __syncthreads();
+      const unsigned digit = 255u - static_cast<unsigned>(sh.sc.pick);
+      before_c = sh.sc.pick_c;
+      before_m = sh.sc.pick_m;
+      const unsigned long long bin_m = sh.sc.res_m;
+      __syncthreads();
+      hi_val = (hi_val & ~(255u << shift)) | (digit << shift);
+      hi_mask |= 255u << shift;
+      if (shift == kLowBits) {
+        const unsigned low = kLowBits == 0 ? 0u : ((hi_val & 0x80000000u) ? 0u : (1u << kLowBits) - 1u);
+        tau = key_value(hi_val | low);
+        kept = before_m + bin_m;
+        return true;
+      }
+      shift = max(shift - 8, kLowBits);
+    }
+  }
+}
+
 // The threshold for one criterion: the first group of equal logits, from the
 // top, whose inclusive count (by_mass false) or mass (by_mass true) reaches
 // `target`.  Returns its value; `kept` receives the mass of all logits >= it.
@@ -1575,14 +1711,14 @@ __device__ float resolve_cut(const void *row, bool aligned, int V, float c, floa
     const unsigned key = order_key(z);
     if (key >= klo && key <= khi) {
       const unsigned slot = atomicAdd(&sh.sc.nkeys, 1u);
-      if (slot < static_cast<unsigned>(kFCap)) sh.u.keys[slot] = key;
+      if (slot < static_cast<unsigned>(kFCap)) sh.u.k.keys[slot] = key;
     }
   });
   __syncthreads();
   const int n = min(static_cast<int>(sh.sc.nkeys), kFCap);
-  sort_keys_desc(sh.u.keys, n);
+  sort_keys_desc(sh.u.k.keys, n);
   bool found;
-  return scan_sorted(sh.u.keys, n, before_c, before_m, by_mass, target, c, negM, fs, kept, found, sh.sc);
+  return scan_sorted(sh.u.k.keys, n, before_c, before_m, by_mass, target, c, negM, fs, kept, found, sh.sc);
 }
 
 // Row selection shared by the filter kernels: request b's row r (target rows
@@ -1732,9 +1868,10 @@ __global__ __launch_bounds__(kLBlock) void k_filter_capture(
 }
 
 // The cut for one criterion from a row's candidate list, whose histogram is in
-// sh.cnt0 / sh.mass0: the bin that reaches the target, its candidates sorted
-// and scanned from the prefix above it.  ok is false when that bin holds more
-// than kFCap candidates or the scan does not reach the target.
+// sh.cnt0 / sh.mass0: the bin that reaches the target, whose candidates are
+// gathered and resolved by radix_cut from the prefix above it.  ok is false
+// when that bin holds more than kFCap candidates or the target is not reached.
+template <int DT>
 __device__ float list_cut(const unsigned *cand, int n, float c, float negM, int fs, bool by_mass,
                           unsigned long long target, unsigned long long &kept, bool &ok, GeneralShared &sh) {
   const int tid = threadIdx.x;
@@ -1750,21 +1887,39 @@ __device__ float list_cut(const unsigned *cand, int n, float c, float negM, int 
     const unsigned key = cand[i];
     if (ybin(key_value(key), c, negM) == jb) {
       const unsigned q = atomicAdd(&sh.sc.nkeys, 1u);
-      if (q < static_cast<unsigned>(kFCap)) sh.u.keys[q] = key;
+      if (q < static_cast<unsigned>(kFCap)) sh.u.k.keys[q] = key;
     }
   }
   __syncthreads();
   const int m = min(static_cast<int>(sh.sc.nkeys), kFCap);
-  sort_keys_desc(sh.u.keys, m);
-  return scan_sorted(sh.u.keys, m, bc, bm, by_mass, target, c, negM, fs, kept, ok, sh.sc);
+  float tau = -INFINITY;
+  ok = radix_cut<DT>(sh.u.k.keys, m, bc, bm, c, negM, fs, by_mass, target, tau, kept, sh);
+  return tau;
+}
+
+// The top-p target in fixed point: top_p of the top-k mass (k > 0), or of
+// the row's mass (K1's sum s, in the same units), at least 1.
+__device__ __forceinline__ unsigned long long p_target(int k, float p, unsigned long long topk_mass, double s,
+                                                       int fs) {
+  const double base = k > 0 ? static_cast<double>(topk_mass) : ldexp(s, fs);
+  double t = ceil(static_cast<double>(p) * base);
+  if (t < 1.0) t = 1.0;
+  return static_cast<unsigned long long>(t);
 }
 
 // The cut of a row from a list that holds every logit above some floor y = -L
-// (L <= 64): an exact histogram of the list, then the count criterion (top-k)
-// and the mass criterion (top-p of the top-k mass, or of K1's row sum s).
-// Returns false when the list cannot decide the cut; short_list is then true
-// when the k-th logit or the crossing lies below the floor.  list_mass receives
-// the list's fixed-point mass.
+// (L <= 64): the count criterion (top-k), then the mass criterion (top-p of
+// the top-k mass, or of K1's row sum s).  Returns false when the list cannot
+// decide the cut; short_list is then true when the k-th logit or the crossing
+// lies below the floor.  list_mass receives the list's fixed-point mass.
+//   direct     at most kFCap logits: copied into LDS, and each criterion
+//              resolved by radix_cut over all of them;
+//   histogram  more: an exact (count, fixed-point mass) histogram of the list
+//              over 1/32-order bins finds the bin of each crossing, whose
+//              logits are gathered and resolved by radix_cut from the prefix
+//              above it (list_cut).
+// Both take the same sums of the same integers, so they give the same cut.
+template <int DT>
 __device__ bool list_resolve(const unsigned *cand, int n, float c, float negM, int fs, int k, float p, double s,
                              float &tau, unsigned long long &kept, unsigned long long &list_mass, bool &short_list,
                              GeneralShared &sh) {
@@ -1772,6 +1927,33 @@ __device__ bool list_resolve(const unsigned *cand, int n, float c, float negM, i
   tau = -INFINITY;
   kept = 0;
   short_list = false;
+  if (n <= kFCap) {  // uniform: the direct path
+    if (k > n) {  // the k-th logit lies below the floor
+      short_list = true;
+      list_mass = 0;
+      return false;
+    }
+    for (int i = tid; i < n; i += kFBlock) sh.u.k.keys[i] = cand[i];
+    __syncthreads();
+    bool ok = true;
+    if (k > 0)
+      radix_cut<DT>(sh.u.k.keys, n, 0ull, 0ull, c, negM, fs, false, static_cast<unsigned long long>(k), tau, kept, sh);
+    list_mass = 0;  // not needed by the callers on this path
+    if (p < 1.0f) {
+      float tau_p;
+      unsigned long long kept_p;
+      if (!radix_cut<DT>(sh.u.k.keys, n, 0ull, 0ull, c, negM, fs, true, p_target(k, p, kept, s, fs), tau_p, kept_p,
+                         sh)) {
+        ok = false;  // the crossing lies below the floor
+        short_list = true;
+      } else if (tau_p > tau) {
+        tau = tau_p;
+        kept = kept_p;
+      }
+    }
+    __syncthreads();
+    return ok;
+  }
   for (int jb = tid; jb <= kFBins; jb += kFBlock) {
     sh.cnt0[jb] = 0;
     sh.mass0[jb] = 0;
@@ -1798,21 +1980,17 @@ __device__ bool list_resolve(const unsigned *cand, int n, float c, float negM, i
       ok = false;
       short_list = true;
     } else {
-      tau = list_cut(cand, n, c, negM, fs, false, static_cast<unsigned long long>(k), kept, ok, sh);
+      tau = list_cut<DT>(cand, n, c, negM, fs, false, static_cast<unsigned long long>(k), kept, ok, sh);
     }
   }
   if (ok && p < 1.0f) {
-    // top-p of the top-k mass, or of the row's mass (K1's sum, in the same units)
-    const double base = k > 0 ? static_cast<double>(kept) : ldexp(s, fs);
-    double t = ceil(static_cast<double>(p) * base);
-    if (t < 1.0) t = 1.0;
-    const unsigned long long tgt = static_cast<unsigned long long>(t);
+    const unsigned long long tgt = p_target(k, p, kept, s, fs);
     if (total_m < tgt) {  // the crossing lies below the floor
       ok = false;
       short_list = true;
     } else {
       unsigned long long kept_p;
-      const float tau_p = list_cut(cand, n, c, negM, fs, true, tgt, kept_p, ok, sh);
+      const float tau_p = list_cut<DT>(cand, n, c, negM, fs, true, tgt, kept_p, ok, sh);
       if (ok && tau_p > tau) {
         tau = tau_p;
         kept = kept_p;
@@ -1972,9 +2150,9 @@ __device__ unsigned deep_capture(const void *row, bool aligned, int V, float c, 
   }
   __syncthreads();
   if (over || total > static_cast<unsigned>(kFCap)) return static_cast<unsigned>(kGCap) + 1u;
-  for (unsigned i = lane; i < wcount; i += kWave) sh.u.keys[before + i] = part[i];
+  for (unsigned i = lane; i < wcount; i += kWave) sh.u.k.keys[before + i] = part[i];
   __syncthreads();
-  for (unsigned i = tid; i < total; i += kFBlock) cand[i] = sh.u.keys[i];
+  for (unsigned i = tid; i < total; i += kFBlock) cand[i] = sh.u.k.keys[i];
   __syncthreads();
   return total;
 }
@@ -2108,7 +2286,7 @@ __global__ __launch_bounds__(kFBlock) void k_filter_resolve(
     n = L > 0 ? deep_capture<DT>(fr.row, fr.aligned, V, fr.c, fr.negM, L, cand, sh) : kGCap + 1u;
   }
   if (n <= static_cast<unsigned>(kGCap))
-    done = list_resolve(cand, static_cast<int>(n), fr.c, fr.negM, fs, fr.k, fr.p, fr.s, tau, kept, list_mass,
+    done = list_resolve<DT>(cand, static_cast<int>(n), fr.c, fr.negM, fs, fr.k, fr.p, fr.s, tau, kept, list_mass,
                         short_list, sh);
   store_filter_stats(fst, slot, kept, fs, tau, done ? kFResolved : kFGeneral);
 }
