@@ -2385,6 +2385,7 @@ struct TreeShared {
   float czp[SV_TREE_MAX_NODES];    // their target and draft logits, and uniforms
   float czq[SV_TREE_MAX_NODES];
   float cu[SV_TREE_MAX_NODES];
+  double cratio[SV_TREE_MAX_NODES];  // p(x) / q(x) at each child (inf: q(x) = 0 < p(x); nan: both 0)
   int wcnt[kTWaves];
   int nchild;
   double sub[kTMaxSub];       // sub-chunk masses of the current distribution
@@ -2440,9 +2441,31 @@ struct TreeTeam {
   int pass;               // passes done so far in this call
 };
 
+// The sum of sh.sub[0, NSUB) into sh.W by wave 0 (a DPP tree per 64 entries,
+// then the 64-entry totals in order): the same order in every workgroup.
+__device__ __forceinline__ void tree_total(int NSUB, TreeShared &sh) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    double W = 0.0;
+    for (int j0 = 0; j0 < NSUB; j0 += kWave) W += wave_sum(j0 + lane < NSUB ? sh.sub[j0 + lane] : 0.0);
+    if (lane == 0) sh.W = W;
+  }
+}
+
+// A wave's registers of one 2048-token sub-chunk of a position's row pair
+// (the interleaved layout of load_lane_fast), kept across the passes at that
+// position when every wave of the request has at most one such sub-chunk.
+template <int DT>
+struct RowSlice {
+  static constexpr int kN = kLaneElems / Elem<DT>::kVec;
+  u32x4 t[kN], d[kN];
+  bool valid;
+};
+
 template <int DT, bool USEQ>
 __device__ __forceinline__ void tree_masses_of(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c,
-                               float negMp, float negMq, float r, TreeShared &sh, TreeTeam &tm) {
+                               float negMp, float negMq, float r, const RowSlice<DT> &rs, TreeShared &sh,
+                               TreeTeam &tm) {
   constexpr int kN = kLaneElems / Elem<DT>::kVec;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   // this wave's place among the request's NW x 8 waves
@@ -2457,9 +2480,12 @@ __device__ __forceinline__ void tree_masses_of(const void *trow, const void *dro
   // Sub-chunks wholly inside an aligned row: wave g takes g, g + stride, ...
   // with straight-line loads, the next one requested while the current one is
   // reduced (its index clamped to the last such sub-chunk, so that the loads are
-  // unconditional and each wait covers exactly the older sub-chunk).
+  // unconditional and each wait covers exactly the older sub-chunk).  A wave
+  // whose one sub-chunk is already in registers (rs) reduces it directly.
   const int nfast = aligned ? min(NSUB, V / kSub) : 0;
-  if (gw < nfast) {
+  if (rs.valid) {  // uniform per wave: gw < nfast and no other fast sub-chunk
+    put_mass(gw, wave_sum(static_cast<double>(tree_lane_mass<DT, USEQ>(rs.t, rs.d, c, negMp, negMq, r))));
+  } else if (gw < nfast) {
     u32x4 tp[kN], dq[kN], tn[kN], dn[kN];
     load_lane_fast<DT>(trow, static_cast<long>(gw) * kSub, lane, tp);
     if constexpr (USEQ) load_lane_fast<DT>(drow, static_cast<long>(gw) * kSub, lane, dq);
@@ -2497,19 +2523,16 @@ __device__ __forceinline__ void tree_masses_of(const void *trow, const void *dro
     for (int j = threadIdx.x; j < NSUB; j += kTBlock) sh.sub[j] = get<true>(gsub + j);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double W = 0.0;
-    for (int j = 0; j < NSUB; ++j) W += sh.sub[j];  // fixed order
-    sh.W = W;
-  }
+  tree_total(NSUB, sh);
   __syncthreads();
 }
 
 template <int DT>
 __device__ __forceinline__ void tree_masses(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c,
-                            float negMp, float negMq, float r, bool use_q, TreeShared &sh, TreeTeam &tm) {
-  if (use_q) tree_masses_of<DT, true>(trow, drow, aligned, V, NSUB, c, negMp, negMq, r, sh, tm);
-  else tree_masses_of<DT, false>(trow, drow, aligned, V, NSUB, c, negMp, negMq, r, sh, tm);
+                            float negMp, float negMq, float r, bool use_q, const RowSlice<DT> &rs, TreeShared &sh,
+                            TreeTeam &tm) {
+  if (use_q) tree_masses_of<DT, true>(trow, drow, aligned, V, NSUB, c, negMp, negMq, r, rs, sh, tm);
+  else tree_masses_of<DT, false>(trow, drow, aligned, V, NSUB, c, negMp, negMq, r, rs, sh, tm);
 }
 
 // Inverse CDF over the masses in sh.sub (of the same w as tree_masses): the
@@ -2519,30 +2542,36 @@ template <int DT>
 __device__ __forceinline__ int tree_select(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c, float negMp,
                            float negMq, float r, bool use_q, float u, TreeShared &sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  if (tid == 0) {
+  if (tid < kWave) {  // wave 0: the lowest sub-chunk with mass whose inclusive prefix exceeds u W
     const double target = static_cast<double>(u) * sh.W;
-    double run = 0.0;
+    double run = 0.0, base = 0.0, base_last = 0.0;
     int sub = -1, lastm = -1;
-    double base = 0.0, base_last = 0.0;
-    for (int j = 0; j < NSUB; ++j) {
-      const double m = sh.sub[j];
-      if (m > 0.0) {
-        if (sub < 0 && target < run + m) {
-          sub = j;
-          base = run;
-        }
-        lastm = j;
-        base_last = run;
+    for (int j0 = 0; j0 < NSUB && sub < 0; j0 += kWave) {
+      const int j = j0 + lane;
+      const double m = j < NSUB ? sh.sub[j] : 0.0;
+      const double incl = wave_scan(m, lane);
+      const unsigned long long hit = __ballot(j < NSUB && m > 0.0 && target < run + incl);
+      const unsigned long long has = __ballot(j < NSUB && m > 0.0);
+      if (hit) {
+        const int L = __ffsll(static_cast<long long>(hit)) - 1;
+        sub = j0 + L;
+        base = run + lane_value(incl - m, L);
+      } else if (has) {
+        const int L = 63 - __clzll(static_cast<long long>(has));
+        lastm = j0 + L;
+        base_last = run + lane_value(incl - m, L);
       }
-      run += m;
+      run += lane_value(incl, kWave - 1);
     }
-    if (sub < 0) {
+    if (sub < 0) {  // rounding left u W at the very end: the last sub-chunk with mass
       sub = lastm >= 0 ? lastm : 0;
       base = lastm >= 0 ? base_last : 0.0;
     }
-    sh.pick = sub;
-    sh.red[0] = base;
-    sh.red[1] = target;
+    if (lane == 0) {
+      sh.pick = sub;
+      sh.red[0] = base;
+      sh.red[1] = target;
+    }
   }
   __syncthreads();
   const int sub = sh.pick;
@@ -2643,6 +2672,20 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     const void *drow = pos < Nmax ? static_cast<const char *>(draft) + (static_cast<long>(b) * Nmax + pos) * V * eb
                                   : nullptr;  // position Nmax has no child
     const bool al = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;
+    // the wave's sub-chunk of the position's row pair, requested now (the round
+    // trip overlaps the row statistics and the children's logits below) and
+    // kept for every pass at this position, when each wave has at most one
+    RowSlice<DT> rs;
+    {
+      const int gw = tm.w * kTWaves + wave, stride = tm.NW * kTWaves;
+      const int nfast = al ? min(NSUB, V / kSub) : 0;
+      // (bf16 only: an fp32 slice is twice the registers and made the kernel spill)
+      rs.valid = DT == SV_BF16 && !greedy && drow != nullptr && gw < nfast && gw + stride >= nfast;
+      if (rs.valid) {  // uniform per wave
+        load_lane_fast<DT>(trow, static_cast<long>(gw) * kSub, lane, rs.t);
+        load_lane_fast<DT>(drow, static_cast<long>(gw) * kSub, lane, rs.d);
+      }
+    }
     // the position's children in node order (a block-wide compaction); then, in
     // one round trip, the row statistics (target by thread 0, draft by the
     // first lane of wave 1) and each child's two logits and uniform (threads
@@ -2680,6 +2723,14 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
       sh.cu[jc] = ok ? u_accept[static_cast<long>(b) * Nmax + n] : 2.0f;  // 2 rejects
     }
     __syncthreads();
+    // every child's p(x)/q(x) at once, one exponential each:
+    // 2^((zp - zq) c - (Mp - Mq)) * s'_q / s'_p (the logit difference is exact)
+    if (!greedy && jc >= 0 && jc < nchild) {
+      const double d = (static_cast<double>(sh.czp[jc]) - static_cast<double>(sh.czq[jc])) * static_cast<double>(c) -
+                       static_cast<double>(s_Mp - s_Mq);
+      sh.cratio[jc] = exp2(d) * (s_sq / s_sp);
+    }
+    __syncthreads();
     int hit = -1;
     if (greedy) {
       if (tid == 0) {
@@ -2703,11 +2754,9 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
       bool masses_current = false;
       for (int j = 0; j < nchild; ++j) {
         if (tid == 0) {
-          const double cd = static_cast<double>(c);
-          const double px = exp2(static_cast<double>(sh.czp[j]) * cd - Mp) / sp;
-          const double qx = exp2(static_cast<double>(sh.czq[j]) * cd - Mq) / sq;
-          const double num = fmax(0.0, px - cc * qx), den = Z * qx;
-          const double a = den > 0.0 ? fmin(1.0, num / den) : (num > 0.0 ? 1.0 : 0.0);
+          // the current target over q at x: max(0, p - cc q) / (Z q) = max(0, p/q - cc) / Z
+          const double ratio = sh.cratio[j];
+          const double a = fmin(1.0, fmax(0.0, ratio - cc) / Z);
           s_hit = static_cast<double>(sh.cu[j]) < a ? sh.child[j] : -1;
         }
         __syncthreads();
@@ -2717,7 +2766,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
         // rejected: the next target is max(0, p - (cc + Z) q) / Z'
         cc += Z;
         const float r = static_cast<float>(cc * sp / sq);
-        tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, true, sh, tm);
+        tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, true, rs, sh, tm);
         const double W = sh.W;
         if (W > 0.0) {
           Z = W / sp;
@@ -2733,7 +2782,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
         const bool use_q = cc > 0.0;
         const float r = use_q ? static_cast<float>(cc * sp / sq) : 0.0f;
         if (!masses_current)
-          tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q, sh, tm);
+          tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q, rs, sh, tm);
         if (lead) {  // uniform per workgroup
           const int tok = tree_select<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q,
                                           u_sample[b], sh);
