@@ -173,6 +173,20 @@ def summarize_profile(root: str):
                           f"clock, {bl['extra']['device_us_per_step']:.2f} us per step between the HIP events "
                           f"({bl['config']['workload']}); step roofline fraction {bl['roofline']['frac']:.4f} "
                           f"({bl['roofline']['achieved']:.0f} GB/s of algorithmic bytes)."]
+            # the timed step's own kernels (one instantiation of each): their averages summed
+            k1_tag = {"kt": "stochastic", "kt_greedy": "greedy", "kt_config4": "per-request T"}.get(key)
+            if k1_tag is not None:
+                want = [f"k1_row_stats<bf16, {k1_tag}>", "k2_decide_mass<bf16, plain>"]
+                if key != "kt_greedy":
+                    want.append("k3_select<bf16, plain>")
+                if all(k in avg for k in want):
+                    step_sum = sum(avg[k] for k in want)
+                    bytes_step = bl["roofline"]["bytes_per_step"]
+                    lines += ["", f"The step's kernels ({' + '.join(want)}) average {step_sum:.2f} us together: "
+                                  f"{bytes_step / step_sum / 1e3:.0f} GB/s of the step's algorithmic bytes, fraction "
+                                  f"{bytes_step / step_sum / 1e3 / HBM_PEAK_GBS:.4f} of 8 TB/s.  The event time per "
+                                  "step also holds the gaps between the graph's kernel nodes (wider under the "
+                                  "profiler)."]
         lines += ["", "The copy kernels are the benchmark's set-up (input copies), outside the timed region.", ""]
         open(os.path.join(PROFILES, TRACE_FILES[key]), "w").write("\n".join(lines))
         traces[key] = {"kernel_avg_us": avg, "bench": None if bl is None else
