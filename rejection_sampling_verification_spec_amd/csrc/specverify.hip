@@ -190,10 +190,9 @@ struct alignas(16) SubSums {
 // shared passes), the values go through device-scope atomic stores and loads:
 // each XCD has its own L2, not coherent with the others, and these accesses
 // bypass it, so no cache write-back or invalidate is needed (a device-scope
-// fence would write back or invalidate the XCD's whole L2).  A writer waits
-// until its stores are complete before it counts itself done with a
-// device-scope atomic add; a reader that has seen the count issues its loads
-// only afterwards.
+// fence would write back or invalidate the XCD's whole L2).  Each value travels
+// in one 64-bit word together with a tag the reader waits for, so no store
+// completion or counter needs to be awaited.
 template <bool COH, typename T>
 __device__ __forceinline__ void put(T *p, T v) {
   if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -205,33 +204,7 @@ __device__ __forceinline__ T get(const T *p) {
   else return *p;
 }
 
-// Waits until this wave's earlier memory operations (its stores included) are
-// complete.  The signal fences keep the compiler from moving memory accesses
-// across the wait.
-__device__ __forceinline__ void wait_memory() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-__device__ __forceinline__ unsigned count_up(unsigned *c) {
-  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 constexpr unsigned kSpinLimit = 1u << 20;  // polls of a bounded wait (about a second; a correct run needs a few)
-
-// Waits until *c >= target (one lane).  Bounded: if the count never arrives,
-// the error word is set and the caller goes on (its results are then invalid).
-__device__ __forceinline__ void wait_count(const unsigned *c, unsigned target, unsigned *err) {
-  for (unsigned it = 0;; ++it) {
-    if (get<true>(c) >= target) return;
-    if (it >= kSpinLimit) {
-      put<true>(err, 1u);
-      return;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
 
 // ================================================================== K1
 // Rows of request b: r in [0, gamma] are target rows, r in [gamma+1, 2 gamma]
@@ -403,7 +376,8 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
     const void *__restrict__ target, const void *__restrict__ draft,
     const int32_t *__restrict__ tokens, const float *__restrict__ temps, float scalar_T,
     const int32_t *__restrict__ lens, int gamma, int V, int NCH, int chunk_vecs, int grid_rows,
-    Partial *__restrict__ part, float *__restrict__ zx, unsigned *__restrict__ row_counter) {
+    Partial *__restrict__ part, float *__restrict__ zx, unsigned *__restrict__ row_counter,
+    unsigned long long *__restrict__ req_words, int req_words_n) {
   constexpr int kV = Elem<DT>::kVec;
   const int rows = 2 * gamma + 1;
   // the grid covers grid_rows rows per request: all 2 gamma + 1, or the gamma + 1
@@ -414,8 +388,11 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   const int r = gslot - b * grid_rows;
   const int slot = b * rows + r;
   const int wgid = slot * NCH + j;
-  // a per-row counter of the kernels that follow (filtered calls), cleared here
+  // a per-row counter of the kernels that follow (filtered calls), cleared here,
+  // and per-request words of the tree walk, by the request's first chunk of row 0
   if (row_counter && j == 0 && threadIdx.x == 0) row_counter[slot] = 0u;
+  if (req_words && r == 0 && j == 0)
+    for (int t = threadIdx.x; t < req_words_n; t += kBlock) req_words[static_cast<long>(b) * req_words_n + t] = 0ull;
   const bool is_target = r <= gamma;
   const int i = is_target ? r : r - gamma - 1;
   const char *row =
@@ -2367,12 +2344,12 @@ __global__ __launch_bounds__(kFBlock) void k_filter_general(
 // the acceptance ratio in fp64 from the two gathered logits, all merged and
 // summed in a fixed order); each rejection costs one pass over the position's
 // two rows, shared out as 2048-token sub-chunks over the request's NW x 8
-// waves.  The sub-chunk masses go through device-scope atomic stores into a
-// per-request array (two copies, alternating between passes), the workgroups
-// meet at a per-request counter (cleared by K1), and each then reads back all
-// the masses in sub-chunk order, so Z is the same everywhere.  Workgroup 0
-// writes the outputs and draws the final token.  With NW = 1 (large batches)
-// there is no counter and the masses stay in LDS.
+// waves.  Each sub-chunk mass goes out with the pass number in one 64-bit
+// device-scope atomic store into a per-request array (two copies, alternating
+// between passes, cleared by K1); each workgroup polls the words until all
+// carry the pass number and adds the masses in the same order, so Z is the
+// same everywhere.  Workgroup 0 writes the outputs and draws the final token.
+// With NW = 1 (large batches) the masses stay in LDS, in fp64.
 constexpr int kTBlock = 512;
 constexpr int kTWaves = kTBlock / kWave;
 constexpr int kTMaxSub = SV_TREE_MAX_V / kSub;
@@ -2434,12 +2411,21 @@ __device__ __forceinline__ float tree_lane_mass(const u32x4 *tp, const u32x4 *dq
 
 // How the request's workgroups share a pass and meet after it.
 struct TreeTeam {
-  int w, NW;              // this workgroup, workgroups per request
-  double *sub;            // [2][NSUB] per-request masses (NW > 1)
-  unsigned *meet;         // per-request counter (NW > 1)
-  unsigned *err;          // set if a bounded wait ran out
-  int pass;               // passes done so far in this call
+  int w, NW;                // this workgroup, workgroups per request
+  unsigned long long *sub;  // [2][NSUB] per-request mass words (NW > 1), cleared by K1
+  unsigned *err;            // set if a bounded wait ran out
+  int pass;                 // passes done so far in this call
 };
+
+// A sub-chunk mass as the team exchanges it: pass number (from 1) in the high
+// half, the mass rounded to fp32 in the low half, in one 64-bit word written
+// and read with single device-scope atomic accesses, so that a reader that
+// sees the pass number sees the mass.  The rounding moves a prefix of the
+// masses by at most 6e-8 of their total.
+__device__ __forceinline__ unsigned long long mass_word(int pass, double m) {
+  return (static_cast<unsigned long long>(static_cast<unsigned>(pass)) << 32) |
+         __float_as_uint(static_cast<float>(m));
+}
 
 // The sum of sh.sub[0, NSUB) into sh.W by wave 0 (a DPP tree per 64 entries,
 // then the 64-entry totals in order): the same order in every workgroup.
@@ -2470,10 +2456,11 @@ __device__ __forceinline__ void tree_masses_of(const void *trow, const void *dro
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   // this wave's place among the request's NW x 8 waves
   const int gw = tm.w * kTWaves + wave, stride = tm.NW * kTWaves;
-  double *gsub = tm.NW > 1 ? tm.sub + (tm.pass & 1) * NSUB : nullptr;
+  unsigned long long *gsub = tm.NW > 1 ? tm.sub + (tm.pass & 1) * NSUB : nullptr;
+  const int stamp = tm.pass + 1;
   auto put_mass = [&](int j, double v) {
     if (lane == 0) {
-      if (gsub) put<true>(gsub + j, v);
+      if (gsub) put<true>(gsub + j, mass_word(stamp, v));
       else sh.sub[j] = v;
     }
   };
@@ -2510,17 +2497,29 @@ __device__ __forceinline__ void tree_masses_of(const void *trow, const void *dro
     put_mass(j, wave_sum(static_cast<double>(tree_lane_mass<DT, USEQ>(tp, dq, c, negMp, negMq, r))));
   }
   if (gsub) {
-    // every wave's masses are complete before the workgroup counts itself in;
-    // then wait for the request's other workgroups and read all the masses
-    wait_memory();
-    __syncthreads();
-    ++tm.pass;
-    if (threadIdx.x == 0) {
-      count_up(tm.meet);
-      wait_count(tm.meet, static_cast<unsigned>(tm.NW * tm.pass), tm.err);
+    // wave 0 polls the request's words until each carries this pass's number
+    // (bounded: if one never arrives the error word is set), the other waves
+    // wait at the barrier.  The two copies alternate between passes: a
+    // workgroup writes copy p + 1 only after reading all of copy p - 1's
+    // successor p, so a copy is never overwritten while a reader waits on it.
+    if (threadIdx.x < kWave) {
+      for (int j0 = 0; j0 < NSUB; j0 += kWave) {
+        const int j = j0 + lane;
+        unsigned long long word = 0;
+        for (unsigned it = 0;; ++it) {
+          if (j < NSUB) word = get<true>(gsub + j);
+          const bool ready = j >= NSUB || static_cast<int>(word >> 32) == stamp;
+          if (__all(ready)) break;
+          if (it >= kSpinLimit) {
+            if (lane == 0) put<true>(tm.err, 1u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (j < NSUB) sh.sub[j] = static_cast<double>(__uint_as_float(static_cast<unsigned>(word)));
+      }
     }
-    __syncthreads();
-    for (int j = threadIdx.x; j < NSUB; j += kTBlock) sh.sub[j] = get<true>(gsub + j);
+    ++tm.pass;
   }
   __syncthreads();
   tree_total(NSUB, sh);
@@ -2628,8 +2627,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     const int32_t *__restrict__ tokens, const int32_t *__restrict__ num_nodes, const float *__restrict__ u_accept,
     const float *__restrict__ u_sample, const float *__restrict__ temps, int Nmax, int V, int NS,
     const Partial *__restrict__ part, int32_t *__restrict__ count, int32_t *__restrict__ out_tokens,
-    int32_t *__restrict__ out_nodes, int NW, double *__restrict__ tsub, unsigned *__restrict__ tcount,
-    unsigned *__restrict__ terr) {
+    int32_t *__restrict__ out_nodes, int NW, unsigned long long *__restrict__ tsub, unsigned *__restrict__ terr) {
   const int b = blockIdx.x / NW, tid = threadIdx.x;
   const int rows = 2 * Nmax + 1;
   const int N = request_len(num_nodes, Nmax, b);
@@ -2640,8 +2638,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
   TreeTeam tm;
   tm.w = blockIdx.x - b * NW;
   tm.NW = greedy ? 1 : NW;  // a greedy walk makes no pass: workgroup 0 alone
-  tm.sub = tsub + static_cast<long>(b) * 2 * NSUB;
-  tm.meet = tcount + static_cast<long>(b) * rows;  // cleared by K1 (row slot 0 of the request)
+  tm.sub = tsub + static_cast<long>(b) * 2 * NSUB;  // cleared by K1
   tm.err = terr;
   tm.pass = 0;
   if (greedy && tm.w > 0) return;  // uniform per workgroup
@@ -3095,16 +3092,18 @@ template <int DT, int KIND>
 hipError_t launch_k1_kind(const void *target, const void *draft, const int32_t *tokens, const float *temps,
                           float scalar_T, const int32_t *lens, int gamma, int V, const Plan &P,
                           Partial *part, float *zx, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
-                          unsigned *row_counter) {
+                          unsigned *row_counter, unsigned long long *req_words, int req_words_n) {
   const bool g = KIND == kGreedyOnly;
   const dim3 grid(static_cast<unsigned>(g ? P.k1_groups_g : P.k1_groups)), block(kBlock);
   const int grows = g ? gamma + 1 : P.rows;
   if (ev0 && ev1) {
     hipExtLaunchKernelGGL((k1_row_stats<DT, kK1U, KIND>), grid, block, 0, st, ev0, ev1, 0, target, draft,
-                          tokens, temps, scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, grows, part, zx, row_counter);
+                          tokens, temps, scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, grows, part, zx, row_counter,
+                          req_words, req_words_n);
   } else {
     hipLaunchKernelGGL((k1_row_stats<DT, kK1U, KIND>), grid, block, 0, st, target, draft, tokens, temps,
-                       scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, grows, part, zx, row_counter);
+                       scalar_T, lens, gamma, V, P.NS, P.chunk_vecs, grows, part, zx, row_counter, req_words,
+                       req_words_n);
   }
   return hipGetLastError();
 }
@@ -3113,15 +3112,16 @@ template <int DT>
 hipError_t launch_k1(const void *target, const void *draft, const int32_t *tokens, const float *temps,
                      float scalar_T, const int32_t *lens, int gamma, int V, const Plan &P, Partial *part,
                      float *zx, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1,
-                     unsigned *row_counter = nullptr) {
+                     unsigned *row_counter = nullptr, unsigned long long *req_words = nullptr,
+                     int req_words_n = 0) {
   if (temps)
     return launch_k1_kind<DT, kMixed>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx,
-                                      st, ev0, ev1, row_counter);
+                                      st, ev0, ev1, row_counter, req_words, req_words_n);
   if (scalar_T > 0.0f)
     return launch_k1_kind<DT, kStochasticOnly>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P,
-                                               part, zx, st, ev0, ev1, row_counter);
+                                               part, zx, st, ev0, ev1, row_counter, req_words, req_words_n);
   return launch_k1_kind<DT, kGreedyOnly>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx,
-                                         st, ev0, ev1, row_counter);
+                                         st, ev0, ev1, row_counter, req_words, req_words_n);
 }
 
 // fractional bits of the filter's fixed-point masses: V * 2^(fs + 1) <= 2^62
@@ -3220,20 +3220,17 @@ int dispatch(const void *target, const void *draft, const int32_t *tokens, const
 constexpr int kMaxDevices = 64;
 
 // ------------------------------------------------------------------ tree walk
-// The tree call's workspace: the linear plan, then one counter per row slot
-// (K1 clears them; the walk uses the one of each request's row slot 0), two
-// copies of each request's sub-chunk masses, and the walk's error word.
+// The tree call's workspace: the linear plan, then two copies of each
+// request's sub-chunk mass words (K1 clears them), and the walk's error word.
 struct TreeLayout {
-  size_t count_off, sub_off, err_off, total;
+  size_t sub_off, err_off, total;
 };
 
 TreeLayout tree_layout(int B, const Plan &P) {
   TreeLayout L;
   size_t off = P.total;
-  L.count_off = off;
-  off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B) * P.rows);
   L.sub_off = off;
-  off = align_up(off + sizeof(double) * 2 * static_cast<size_t>(B) * P.NSUB);
+  off = align_up(off + sizeof(unsigned long long) * 2 * static_cast<size_t>(B) * P.NSUB);
   L.err_off = off;
   off = align_up(off + sizeof(unsigned));
   L.total = off;
@@ -3356,7 +3353,7 @@ size_t spec_verify_tree_workspace_bytes(int B, int max_nodes, int V, int dtype) 
 
 // Row statistics of every tree position by K1 (the linear layout with
 // gamma = max_nodes and draft lengths = node counts; K1 also clears the walk's
-// per-request counters), then NW workgroups per request walk its tree.
+// per-request mass words), then NW workgroups per request walk its tree.
 int spec_verify_tree(const void *target_logits, const void *draft_logits, const int32_t *node_parent,
                      const int32_t *node_tokens, const int32_t *num_nodes, const float *u_accept,
                      const float *u_sample, const float *temperature, int B, int max_nodes, int V, int dtype,
@@ -3375,28 +3372,27 @@ int spec_verify_tree(const void *target_logits, const void *draft_logits, const 
   char *base = static_cast<char *>(workspace);
   Partial *part = reinterpret_cast<Partial *>(base + P.part_off);
   float *zx = reinterpret_cast<float *>(base + P.zx_off);
-  unsigned *tcount = reinterpret_cast<unsigned *>(base + L.count_off);
-  double *tsub = reinterpret_cast<double *>(base + L.sub_off);
+  unsigned long long *tsub = reinterpret_cast<unsigned long long *>(base + L.sub_off);
   unsigned *terr = reinterpret_cast<unsigned *>(base + L.err_off);
   hipError_t e;
   if (dtype == SV_BF16) {
     e = launch_k1<SV_BF16>(target_logits, draft_logits, node_tokens, temperature, 0.0f, num_nodes, max_nodes, V, P,
-                           part, zx, st, nullptr, nullptr, tcount);
+                           part, zx, st, nullptr, nullptr, nullptr, tsub, 2 * P.NSUB);
     if (e != hipSuccess) return SV_EHIP;
     const int NW = tree_team_size<SV_BF16>(B, P.NSUB);
     hipLaunchKernelGGL((k_tree_walk<SV_BF16>), dim3(static_cast<unsigned>(static_cast<long>(B) * NW)),
                        dim3(kTBlock), 0, st, target_logits, draft_logits, node_parent, node_tokens, num_nodes,
                        u_accept, u_sample, temperature, max_nodes, V, P.NS, part, accepted_count, out_tokens,
-                       out_nodes, NW, tsub, tcount, terr);
+                       out_nodes, NW, tsub, terr);
   } else {
     e = launch_k1<SV_F32>(target_logits, draft_logits, node_tokens, temperature, 0.0f, num_nodes, max_nodes, V, P,
-                          part, zx, st, nullptr, nullptr, tcount);
+                          part, zx, st, nullptr, nullptr, nullptr, tsub, 2 * P.NSUB);
     if (e != hipSuccess) return SV_EHIP;
     const int NW = tree_team_size<SV_F32>(B, P.NSUB);
     hipLaunchKernelGGL((k_tree_walk<SV_F32>), dim3(static_cast<unsigned>(static_cast<long>(B) * NW)),
                        dim3(kTBlock), 0, st, target_logits, draft_logits, node_parent, node_tokens, num_nodes,
                        u_accept, u_sample, temperature, max_nodes, V, P.NS, part, accepted_count, out_tokens,
-                       out_nodes, NW, tsub, tcount, terr);
+                       out_nodes, NW, tsub, terr);
   }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
