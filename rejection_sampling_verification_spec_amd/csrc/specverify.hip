@@ -454,12 +454,19 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
   int M = kEmptyM;  // stochastic: (M, s, max)
   double s = 0.0;
   float mx = -INFINITY;
-  float bv = -INFINITY;  // greedy: the maximum and its lowest index; a thread's
-  int bi = 0x7fffffff;   // elements come in increasing index order, so a strict > keeps the first
+  // greedy: the maximum and its lowest index.  Per vector only its maximum is
+  // compared; the vector holding the running maximum is kept whole (bvec, at
+  // vector bt + tid) and the index inside it is found once, after the stream.
+  // A thread's vectors come in increasing index order, so a strict > keeps the
+  // first of equal maxima.
+  float bv = -INFINITY;
+  int bt = -1;
+  u32x4 bvec = u32x4{0u, 0u, 0u, 0u};
   stream_chunk_k1<DT, U, kPre>(rv, v0, v1, tid, pre, [&](const u32x4 *tile, int t0) {
+    // only a tile that reaches past v1 is masked (the chunk's last one)
+    const bool full = t0 + U * kBlock <= v1;  // uniform per workgroup
     if (!greedy) {
-      // only a tile that reaches past v1 is masked (the chunk's last one)
-      if (t0 + U * kBlock <= v1) {  // uniform per workgroup
+      if (full) {
         fold_tile<DT, U>(tile, c, M, s, mx);
       } else {
         u32x4 m[U];
@@ -467,23 +474,41 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
         fold_tile<DT, U>(m, c, M, s, mx);
       }
     } else {
+      u32x4 m[U];
+      if (full) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {  // lanes past v1 are skipped
-        const int vi = t0 + u * kBlock + tid;
-        if (vi < v1) {
-          float x[kV];
-          widen_vec<DT>(tile[u], x);
+        for (int u = 0; u < U; ++u) m[u] = tile[u];
+      } else {
+        mask_tile<DT, U>(tile, t0, v1, tid, m);  // -inf never passes the strict >
+      }
 #pragma unroll
-          for (int e = 0; e < kV; ++e) {
-            if (x[e] > bv || bi == 0x7fffffff) {
-              bv = x[e];
-              bi = vi * kV + e;
-            }
-          }
-        }
+      for (int u = 0; u < U; ++u) {
+        float x[kV];
+        widen_vec<DT>(m[u], x);
+        float vm = x[0];
+#pragma unroll
+        for (int e = 1; e < kV; ++e) vm = fmaxf(vm, x[e]);
+        const bool take = vm > bv;
+        bv = take ? vm : bv;
+        bt = take ? t0 + u * kBlock : bt;
+        bvec = take ? m[u] : bvec;
       }
     }
   });
+  int bi = 0x7fffffff;
+  if (greedy) {
+    if (bt >= 0) {
+      float x[kV];
+      widen_vec<DT>(bvec, x);
+      int e0 = kV - 1;
+#pragma unroll
+      for (int e = kV - 1; e >= 0; --e)
+        if (x[e] == bv) e0 = e;
+      bi = (bt + tid) * kV + e0;
+    } else if (v0 + tid < v1) {
+      bi = (v0 + tid) * kV;  // every element of this thread's vectors is -inf
+    }
+  }
 
   if (!greedy) {
     for (long e = se0 + tid; e < se1; e += kBlock) {

@@ -104,13 +104,25 @@ def test_large_vocabulary(dtype, mode):
     run_and_check(w, debug=True, require_no_flags=False)
 
 
-def test_greedy_ties_lowest_index():
-    rng = np.random.default_rng(0)
-    B, gamma, V = 16, 4, 5000
+@pytest.mark.parametrize("B,gamma,V", [(16, 4, 5000), (6, 3, 128256), (5, 2, 100003)])
+def test_greedy_ties_lowest_index(B, gamma, V):
+    """Greedy rows with many exact ties (the lowest index wins), across several
+    chunks and whole tiles at the larger sizes (V = 100003 rows are not 16-byte
+    aligned); one target row is -inf throughout (its arg-max is token 0) and one
+    is -inf except for a tie of two finite logits late in the row."""
+    rng = np.random.default_rng(V)
     zp = rng.integers(-2, 3, size=(B, gamma + 1, V)).astype(np.float32)  # many exact ties
+    zp[1, 1] = -np.inf
+    zp[2, 0] = -np.inf
+    zp[2, 0, V - 5] = zp[2, 0, V - 2] = -7.0
     zq = zp[:, :gamma] + rng.integers(-1, 2, size=(B, gamma, V)).astype(np.float32)
+    zq[1, 1] = 0.0
+    zq[2, 0] = 0.0
     tok = np.argmax(zq, axis=2)
+    tok[1, 1] = 0
+    tok[2, 0] = V - 5
     for dtype in ("f32", "bf16"):
+        say(f"greedy ties {dtype} B={B} gamma={gamma} V={V}")
         w = W.from_logits(zp, zq, tok, np.zeros((B, gamma)), np.zeros(B), 0.0, dtype=dtype)
         rep = run_and_check(w, debug=True)
         assert rep["flagged"] == 0
