@@ -673,7 +673,8 @@ __device__ __forceinline__ void decide_request(
     int V, int NS, const Partial *__restrict__ part, const float *__restrict__ zx,
     const int32_t *__restrict__ topk, const float *__restrict__ topp, const FilterStats *__restrict__ fst,
     int32_t *__restrict__ accepted_count, int32_t *__restrict__ out_tokens,
-    SelParams *__restrict__ sel, const sv_debug &dbg_in, int b, bool writer, DecideShared &sh) {
+    SelParams *__restrict__ sel, const sv_debug &dbg_in, int b, bool writer, DecideShared &sh,
+    bool drawn_elsewhere = false) {
   const int tid = threadIdx.x;
   const int rows = 2 * gamma + 1;
   const int g = request_len(lens, gamma, b);
@@ -798,12 +799,15 @@ __device__ __forceinline__ void decide_request(
   __syncthreads();
   const int k = sh_k;
 
-  // accepted prefix, the greedy replacement / bonus, -1 padding
+  // accepted prefix, the greedy replacement / bonus, -1 padding; a stochastic
+  // request's token at k is left to the draw when another workgroup of the
+  // same kernel makes it (drawn_elsewhere), which this store must not overwrite
   if (writer) {
     for (int t = tid; t <= gamma; t += kBlock) {
       int32_t v = -1;
       if (t < k) v = tokens[static_cast<long>(b) * gamma + t];
       else if (t == k && greedy) v = sh_arg[k];
+      else if (t == k && drawn_elsewhere) continue;
       out_tokens[static_cast<long>(b) * (gamma + 1) + t] = v;
     }
   }
@@ -996,11 +1000,17 @@ __device__ __forceinline__ void load_lane_fast(const void *row, long base, int l
   for (int u = 0; u < kLaneElems / kV; ++u) raw[u] = r[u * kWave + lane];
 }
 
+// A sub-chunk mass as a hand-over word: the fp64 bits plus one, so that a
+// mass (never negative) is never the cleared value 0.
+__device__ __forceinline__ unsigned long long sub_mass_word(double m) {
+  return static_cast<unsigned long long>(__double_as_longlong(m)) + 1ull;
+}
+
 // The masses of the wave's SPW consecutive sub-chunks [first, ...) of the row
 // pair to sample (USEQ: residual at a rejection, else the bonus row), loading
 // sub-chunk t+1 while sub-chunk t is reduced.  FAST: every one of them lies
 // wholly inside an aligned row.
-template <int DT, bool FILT, bool FAST, bool USEQ>
+template <int DT, bool FILT, bool FAST, bool USEQ, bool COH>
 __device__ __forceinline__ void mass_pass(const RowPair &rp, const SelParams &sp, int first, int SPW, int NSUB,
                                           int V, int lane, SubSums *__restrict__ out) {
   constexpr int kN = kLaneElems / Elem<DT>::kVec;
@@ -1044,10 +1054,16 @@ __device__ __forceinline__ void mass_pass(const RowPair &rp, const SelParams &sp
     const double sw = wave_sum(static_cast<double>(lw));
     const double spp = wave_sum(static_cast<double>(lp));
     if (lane == 0) {
-      SubSums ss;
-      ss.w = sw;
-      ss.p = spp;
-      out[sub] = ss;
+      if constexpr (COH) {  // hand-over words read by the request's workgroup 0
+        unsigned long long *w = reinterpret_cast<unsigned long long *>(out + sub);
+        put<true>(w, sub_mass_word(sw));
+        put<true>(w + 1, sub_mass_word(spp));
+      } else {
+        SubSums ss;
+        ss.w = sw;
+        ss.p = spp;
+        out[sub] = ss;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kN; ++u) {
@@ -1057,72 +1073,27 @@ __device__ __forceinline__ void mass_pass(const RowPair &rp, const SelParams &sp
   }
 }
 
-// K2 (decide) fused with K3a (mass): NW workgroups per request.  Each one
-// recomputes the request's decision (cheap and deterministic) and workgroup 0
-// stores it; then every wave writes the masses of SPW consecutive 2048-token
-// sub-chunks of the row pair to sample, loading sub-chunk t+1 while it reduces
-// sub-chunk t.
-template <int DT, bool FILT>
-__global__ __launch_bounds__(kBlock) void k2_decide_mass(
-    const void *__restrict__ target, const void *__restrict__ draft,
-    const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
-    const float *__restrict__ temps, float scalar_T, const int32_t *__restrict__ lens, int gamma,
-    int V, int NS, int NSUB, int NW, int SPW, const Partial *__restrict__ part,
-    const float *__restrict__ zx, const int32_t *__restrict__ topk, const float *__restrict__ topp,
-    const FilterStats *__restrict__ fst, int32_t *__restrict__ accepted_count,
-    int32_t *__restrict__ out_tokens, SelParams *__restrict__ sel, SubSums *__restrict__ sums,
-    sv_debug dbg) {
-  const int b = blockIdx.x / NW;
-  const int wg = blockIdx.x - b * NW;
-  // greedy requests need the decision only (workgroup 0)
-  if (wg > 0 && !(request_T(temps, scalar_T, b) > 0.0f)) return;
-  __shared__ DecideShared sh;
-  decide_request<DT, FILT>(target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V, NS, part, zx,
-                     topk, topp, fst, accepted_count, out_tokens, sel, dbg, b, wg == 0, sh);
-  const SelParams sp = sh.sp;
-  const int first = (wg * kWaves + static_cast<int>(threadIdx.x) / kWave) * SPW;
-  if (sp.mode == 0 || first >= NSUB) return;  // uniform per wave; no barrier below
-  const int lane = threadIdx.x & (kWave - 1);
-  const RowPair rp = selected_rows<DT>(target, draft, gamma, V, b, sp);
-  SubSums *out = sums + static_cast<long>(b) * NSUB;
-  // the wave's sub-chunks lie wholly inside an aligned row: straight-line
-  // loads, so that the arithmetic on each vector can start as it arrives
-  const bool fast = rp.aligned && static_cast<long>(min(first + SPW, NSUB)) * kSub <= static_cast<long>(V);
-  if (sp.mode == 1) {
-    if (fast) mass_pass<DT, FILT, true, true>(rp, sp, first, SPW, NSUB, V, lane, out);
-    else mass_pass<DT, FILT, false, true>(rp, sp, first, SPW, NSUB, V, lane, out);
-  } else {
-    if (fast) mass_pass<DT, FILT, true, false>(rp, sp, first, SPW, NSUB, V, lane, out);
-    else mass_pass<DT, FILT, false, false>(rp, sp, first, SPW, NSUB, V, lane, out);
-  }
-}
-
-// K3b: one workgroup per request.  Every wave redundantly finds the total mass
-// Z (zero residual mass falls back to p_k) and the lowest sub-chunk with mass
-// whose inclusive prefix exceeds u*Z; then wave w scans tokens
-// [512 w, 512 w + 512) of that sub-chunk, 8 contiguous tokens per lane, and the
-// lowest token with mass whose running prefix exceeds u*Z is emitted.
-template <int DT, bool FILT>
-__global__ __launch_bounds__(kBlock) void k3_select(
-    const void *__restrict__ target, const void *__restrict__ draft,
-    const float *__restrict__ u_sample, int gamma, int V, int NSUB,
-    const SelParams *__restrict__ sel, const SubSums *__restrict__ sums,
-    int32_t *__restrict__ out_tokens, double *__restrict__ dbg_mass) {
-  const int b = blockIdx.x;
+// The draw of request b at position sp.k from its sub-chunk masses, read
+// through mass(s, p) (p: the bonus row's mass of p, else the residual mass w);
+// with subs_per_wg > 0 only workgroup wg's sub-chunks are drawn from here;
+// w0, p0 are the masses of sub-chunks [0, 64) of this lane, fetched early by
+// the caller.  Every wave redundantly finds the total mass Z (zero residual
+// mass falls back to p_k) and the lowest sub-chunk with mass whose inclusive
+// prefix exceeds u*Z; then wave w scans tokens [512 w, 512 w + 512) of that
+// sub-chunk, 8 contiguous tokens per lane, and the lowest token with mass whose
+// running prefix exceeds u*Z is emitted.  One 256-thread workgroup, every
+// thread present.
+template <int DT, bool FILT, typename Mass>
+__device__ __forceinline__ void select_token(const void *__restrict__ target, const void *__restrict__ draft,
+                                             float u, int gamma, int V, int NSUB, int b, const SelParams &sp,
+                                             double w0, double p0, Mass &&mass, int32_t *__restrict__ out_tokens,
+                                             double *__restrict__ dbg_mass, int wg = 0, int subs_per_wg = 0) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const SubSums *bs = sums + static_cast<long>(b) * NSUB;
-  // the first 64 sub-chunk masses are fetched together with the parameters
-  const double w0 = (lane < NSUB) ? bs[lane].w : 0.0;
-  const double p0 = (lane < NSUB) ? bs[lane].p : 0.0;
-  const SelParams sp = sel[b];
-  if (sp.mode == 0) return;  // uniform per workgroup
-  const float u = u_sample[b];
-
   double Zw = wave_sum(w0), Zp = wave_sum(p0);
   for (int base = kWave; base < NSUB; base += kWave) {
     const int s = base + lane;
-    Zw += wave_sum(s < NSUB ? bs[s].w : 0.0);
-    Zp += wave_sum(s < NSUB ? bs[s].p : 0.0);
+    Zw += wave_sum(s < NSUB ? mass(s, false) : 0.0);
+    Zp += wave_sum(s < NSUB ? mass(s, true) : 0.0);
   }
   const bool use_p = !(Zw > 0.0);  // zero residual mass: fall back to p_k
   const double Z = use_p ? Zp : Zw;
@@ -1132,7 +1103,7 @@ __global__ __launch_bounds__(kBlock) void k3_select(
   double base_mass = 0.0, run = 0.0;
   for (int base = 0; base < NSUB; base += kWave) {
     const int s = base + lane;
-    const double v = (base == 0) ? (use_p ? p0 : w0) : (s < NSUB ? (use_p ? bs[s].p : bs[s].w) : 0.0);
+    const double v = (base == 0) ? (use_p ? p0 : w0) : (s < NSUB ? mass(s, use_p) : 0.0);
     const double incl = wave_scan(v, lane);
     const unsigned long long hit = __ballot(s < NSUB && v > 0.0 && run + incl > target_mass);
     if (hit) {
@@ -1147,7 +1118,7 @@ __global__ __launch_bounds__(kBlock) void k3_select(
     run = 0.0;
     for (int base = 0; base < NSUB; base += kWave) {
       const int s = base + lane;
-      const double v = s < NSUB ? (use_p ? bs[s].p : bs[s].w) : 0.0;
+      const double v = s < NSUB ? mass(s, use_p) : 0.0;
       const double incl = wave_scan(v, lane);
       const unsigned long long has = __ballot(s < NSUB && v > 0.0);
       if (has) {
@@ -1162,6 +1133,10 @@ __global__ __launch_bounds__(kBlock) void k3_select(
       base_mass = 0.0;
     }
   }
+
+  // with subs_per_wg, only the workgroup that computed the sub-chunk's mass
+  // goes on (its data is in this XCD's L2); the same result in every wave
+  if (subs_per_wg > 0 && sub / subs_per_wg != wg) return;
 
   // tokens [first, first + 8) of this lane, in order through waves and lanes
   const RowPair rp = selected_rows<DT>(target, draft, gamma, V, b, sp);
@@ -1221,6 +1196,118 @@ __global__ __launch_bounds__(kBlock) void k3_select(
     out_tokens[static_cast<long>(b) * (gamma + 1) + sp.k] = tok;
     if (dbg_mass) dbg_mass[b] = Z * sp.ip;
   }
+}
+
+
+// Requests whose sub-chunk masses fit workgroup 0's LDS when K2 also draws.
+constexpr int kSelMaxSub = 512;  // V <= 2^20
+
+// K2 (decide) fused with K3a (mass): NW workgroups per request.  Each one
+// recomputes the request's decision (cheap and deterministic) and workgroup 0
+// stores it; then every wave writes the masses of SPW consecutive 2048-token
+// sub-chunks of the row pair to sample, loading sub-chunk t+1 while it reduces
+// sub-chunk t.
+//
+// SEL: the draw as well (K3b is not launched).  The masses go out as
+// hand-over words (cleared by K1 in the same call) and are polled by the first
+// wave of a workgroup until all have arrived (bounded: past the limit the
+// token is -1).  With `owner` (a grid that is resident at once) every
+// workgroup of the request polls, finds the sub-chunk holding u*Z, and the one
+// that computed its mass draws the token in it as K3b does, from its own XCD's
+// L2; otherwise workgroup 0 alone polls and draws, so that waiting workgroups
+// do not hold back the dispatch of later ones.  The earliest request not yet
+// done never waits for a workgroup dispatched after a later request's, so the
+// waits end.
+template <int DT, bool FILT, bool SEL>
+__global__ __launch_bounds__(kBlock) void k2_decide_mass(
+    const void *__restrict__ target, const void *__restrict__ draft,
+    const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
+    const float *__restrict__ temps, float scalar_T, const int32_t *__restrict__ lens, int gamma,
+    int V, int NS, int NSUB, int NW, int SPW, const Partial *__restrict__ part,
+    const float *__restrict__ zx, const int32_t *__restrict__ topk, const float *__restrict__ topp,
+    const FilterStats *__restrict__ fst, int32_t *__restrict__ accepted_count,
+    int32_t *__restrict__ out_tokens, SelParams *__restrict__ sel, SubSums *__restrict__ sums,
+    const float *__restrict__ u_sample, bool owner, sv_debug dbg) {
+  const int b = blockIdx.x / NW;
+  const int wg = blockIdx.x - b * NW;
+  // greedy requests need the decision only (workgroup 0)
+  if (wg > 0 && !(request_T(temps, scalar_T, b) > 0.0f)) return;
+  __shared__ DecideShared sh;
+  decide_request<DT, FILT>(target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V, NS, part, zx,
+                           topk, topp, fst, accepted_count, out_tokens, sel, dbg, b, wg == 0, sh, SEL);
+  const SelParams sp = sh.sp;
+  const int first = (wg * kWaves + static_cast<int>(threadIdx.x) / kWave) * SPW;
+  const int lane = threadIdx.x & (kWave - 1);
+  SubSums *out = sums + static_cast<long>(b) * NSUB;
+  if (sp.mode != 0 && first < NSUB) {  // uniform per wave; no barrier inside
+    const RowPair rp = selected_rows<DT>(target, draft, gamma, V, b, sp);
+    // the wave's sub-chunks lie wholly inside an aligned row: straight-line
+    // loads, so that the arithmetic on each vector can start as it arrives
+    const bool fast = rp.aligned && static_cast<long>(min(first + SPW, NSUB)) * kSub <= static_cast<long>(V);
+    if (sp.mode == 1) {
+      if (fast) mass_pass<DT, FILT, true, true, SEL>(rp, sp, first, SPW, NSUB, V, lane, out);
+      else mass_pass<DT, FILT, false, true, SEL>(rp, sp, first, SPW, NSUB, V, lane, out);
+    } else {
+      if (fast) mass_pass<DT, FILT, true, false, SEL>(rp, sp, first, SPW, NSUB, V, lane, out);
+      else mass_pass<DT, FILT, false, false, SEL>(rp, sp, first, SPW, NSUB, V, lane, out);
+    }
+  }
+  if constexpr (SEL) {
+    if (sp.mode == 0 || (!owner && wg != 0)) return;  // uniform per workgroup
+    __shared__ double sh_w[kSelMaxSub], sh_p[kSelMaxSub];
+    __shared__ int s_late;
+    const unsigned long long *words = reinterpret_cast<const unsigned long long *>(out);
+    if (threadIdx.x < kWave) {
+      bool late = false;
+      for (int j0 = 0; j0 < 2 * NSUB; j0 += kWave) {
+        const int j = j0 + lane;
+        unsigned long long word = 0;
+        for (unsigned it = 0;; ++it) {
+          if (j < 2 * NSUB) word = get<true>(words + j);
+          if (__all(j >= 2 * NSUB || word != 0ull)) break;
+          if (it >= kSpinLimit) {
+            late = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (j < 2 * NSUB) {
+          const double m = __longlong_as_double(static_cast<long long>(word - 1ull));
+          if (j & 1) sh_p[j >> 1] = m;
+          else sh_w[j >> 1] = m;
+        }
+      }
+      if (lane == 0) s_late = late;
+    }
+    __syncthreads();
+    if (s_late) {  // a mass never arrived: no token (uniform per workgroup)
+      if (threadIdx.x == 0 && wg == 0) out_tokens[static_cast<long>(b) * (gamma + 1) + sp.k] = -1;
+      return;
+    }
+    const double w0 = lane < NSUB ? sh_w[lane] : 0.0, p0 = lane < NSUB ? sh_p[lane] : 0.0;
+    select_token<DT, FILT>(target, draft, u_sample[b], gamma, V, NSUB, b, sp, w0, p0,
+                           [&](int s, bool p) { return p ? sh_p[s] : sh_w[s]; }, out_tokens, dbg.residual_mass,
+                           wg, owner ? kWaves * SPW : 0);
+  }
+}
+
+// K3b: one workgroup per request, the draw from the masses K2 wrote.
+template <int DT, bool FILT>
+__global__ __launch_bounds__(kBlock) void k3_select(
+    const void *__restrict__ target, const void *__restrict__ draft,
+    const float *__restrict__ u_sample, int gamma, int V, int NSUB,
+    const SelParams *__restrict__ sel, const SubSums *__restrict__ sums,
+    int32_t *__restrict__ out_tokens, double *__restrict__ dbg_mass) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const SubSums *bs = sums + static_cast<long>(b) * NSUB;
+  // the first 64 sub-chunk masses are fetched together with the parameters
+  const double w0 = (lane < NSUB) ? bs[lane].w : 0.0;
+  const double p0 = (lane < NSUB) ? bs[lane].p : 0.0;
+  const SelParams sp = sel[b];
+  if (sp.mode == 0) return;  // uniform per workgroup
+  select_token<DT, FILT>(target, draft, u_sample[b], gamma, V, NSUB, b, sp, w0, p0,
+                         [&](int s, bool p) { return p ? bs[s].p : bs[s].w; }, out_tokens, dbg_mass);
 }
 
 // ================================================================== top-k / top-p kernel
@@ -3171,9 +3258,19 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
   memset(&dbg, 0, sizeof dbg);
   if (dbgp) dbg = *dbgp;
   unsigned *ncand = fst ? reinterpret_cast<unsigned *>(base + P.ncand_off) : nullptr;
+  // K2 also draws when workgroup 0 can hold the request's sub-chunk masses;
+  // K1 then clears the hand-over words (the sub-chunk mass array)
+  const bool sel2 = !all_greedy && P.NSUB <= kSelMaxSub;
+  // every workgroup waits for its request's masses only when the whole grid is
+  // resident at once (K2's registers allow 4 workgroups per CU for bf16 rows,
+  // 2 for fp32; 256 CUs).  On the ragged B = 128 batch (2432 workgroups) the
+  // waiting workgroups held back the later ones: 79.9 us per call against
+  // 76.5 with workgroup 0 drawing; workload 3 (1024) 46.1 against 46.4.
+  const bool owner = static_cast<long>(B) * P.NW <= (DT == SV_BF16 ? 1024L : 512L);
+  unsigned long long *words = sel2 ? reinterpret_cast<unsigned long long *>(sums) : nullptr;
   hipError_t e = launch_k1<DT>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx, st,
                                static_cast<hipEvent_t>(dbg.k1_events[0]),
-                               static_cast<hipEvent_t>(dbg.k1_events[1]), ncand);
+                               static_cast<hipEvent_t>(dbg.k1_events[1]), ncand, words, sel2 ? 2 * P.NSUB : 0);
   if (e != hipSuccess) return SV_EHIP;
   if (fst) {
     FilterWork fw;
@@ -3197,16 +3294,21 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
   }
   // greedy-only batches need the decision alone: one workgroup per request
   const int nw = all_greedy ? 1 : P.NW;
-  if (fst)
-    hipLaunchKernelGGL((k2_decide_mass<DT, true>), dim3(static_cast<unsigned>(static_cast<long>(B) * nw)),
-                       dim3(kBlock), 0, st, target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V,
-                       P.NS, P.NSUB, nw, P.SPW, part, zx, topk, topp, fst, count, out, sel, sums, dbg);
-  else
-    hipLaunchKernelGGL((k2_decide_mass<DT, false>), dim3(static_cast<unsigned>(static_cast<long>(B) * nw)),
-                       dim3(kBlock), 0, st, target, draft, tokens, u_accept, temps, scalar_T, lens, gamma, V,
-                       P.NS, P.NSUB, nw, P.SPW, part, zx, topk, topp, fst, count, out, sel, sums, dbg);
+  const dim3 g2(static_cast<unsigned>(static_cast<long>(B) * nw));
+#define SV_K2(FILT, SEL)                                                                                  \
+  hipLaunchKernelGGL((k2_decide_mass<DT, FILT, SEL>), g2, dim3(kBlock), 0, st, target, draft, tokens, u_accept, \
+                     temps, scalar_T, lens, gamma, V, P.NS, P.NSUB, nw, P.SPW, part, zx, topk, topp, fst, count,  \
+                     out, sel, sums, u_sample, owner, dbg)
+  if (fst) {
+    if (sel2) SV_K2(true, true);
+    else SV_K2(true, false);
+  } else {
+    if (sel2) SV_K2(false, true);
+    else SV_K2(false, false);
+  }
+#undef SV_K2
   if (hipGetLastError() != hipSuccess) return SV_EHIP;
-  if (!all_greedy) {
+  if (!all_greedy && !sel2) {
     if (fst)
       hipLaunchKernelGGL((k3_select<DT, true>), dim3(B), dim3(kBlock), 0, st, target, draft, u_sample, gamma,
                          V, P.NSUB, sel, sums, out, dbg.residual_mass);

@@ -88,6 +88,37 @@ def test_random_shapes(B, gamma, V, dtype, mode):
     run_and_check(w, debug=False, require_no_flags=False)
 
 
+# The draw runs inside the decision kernel when a request has at most 512
+# sub-chunks: drawn by the workgroup that computed the chosen sub-chunk's mass
+# while the decision kernel's grid (B times the workgroups per request) fits
+# the chip at once (1024 workgroups for bf16 rows, 512 for fp32), by
+# workgroup 0 of the request beyond that; V = 2^20 (512 sub-chunks) is the
+# largest fused case.  The three-kernel path (more sub-chunks) is covered by
+# test_large_vocabulary.
+DRAW_PATHS = [
+    # (B, gamma, V, dtype): workgroups of the decision kernel
+    (64, 2, 128256, "bf16"),   # 1024: every workgroup of a request waits
+    (65, 2, 128256, "bf16"),   # 1040: workgroup 0 draws
+    (128, 2, 32000, "f32"),    # 512
+    (129, 2, 32000, "f32"),    # 516
+    (2, 2, 1 << 20, "bf16"),   # 512 sub-chunks in workgroup 0's list
+]
+
+
+@pytest.mark.parametrize("B,gamma,V,dtype", DRAW_PATHS)
+def test_draw_paths(B, gamma, V, dtype):
+    seed = zlib.crc32(repr((B, gamma, V, dtype, "draw")).encode()) % 100000
+    rng = np.random.default_rng(seed)
+    temps = rng.choice(np.array([0.0, 0.7, 1.0], np.float32), size=B)
+    lens = rng.integers(0, gamma + 1, size=B).astype(np.int32)
+    w = W.make_random(seed, B, gamma, V, dtype, temps=temps, lens=lens, target_scale=4.0, sigma=0.8,
+                      zipf=True)
+    say(f"draw path B={B} gamma={gamma} V={V} {dtype}")
+    run_and_check(w, debug=True, require_no_flags=False)
+    w = W.make_random(seed + 1, B, gamma, V, dtype, temps=1.0, target_scale=3.0, sigma=0.7, zipf=True)
+    run_and_check(w, debug=False, require_no_flags=False)
+
+
 @pytest.mark.parametrize("dtype,mode", [("bf16", "uniform"), ("f32", "mixed")])
 def test_large_vocabulary(dtype, mode):
     """V = 2^20 + 3: 513 sub-chunks per row (the selection scans the sub-chunk masses
