@@ -1012,7 +1012,8 @@ __device__ __forceinline__ unsigned long long sub_mass_word(double m) {
 // wholly inside an aligned row.
 template <int DT, bool FILT, bool FAST, bool USEQ, bool COH>
 __device__ __forceinline__ void mass_pass(const RowPair &rp, const SelParams &sp, int first, int SPW, int NSUB,
-                                          int V, int lane, SubSums *__restrict__ out) {
+                                          int V, int lane, SubSums *__restrict__ out, double *lds_w = nullptr,
+                                          double *lds_p = nullptr) {
   constexpr int kN = kLaneElems / Elem<DT>::kVec;
   auto load = [&](const void *row, int sub, u32x4 *dst) {
     if constexpr (FAST) load_lane_fast<DT>(row, static_cast<long>(sub) * kSub, lane, dst);
@@ -1054,7 +1055,10 @@ __device__ __forceinline__ void mass_pass(const RowPair &rp, const SelParams &sp
     const double sw = wave_sum(static_cast<double>(lw));
     const double spp = wave_sum(static_cast<double>(lp));
     if (lane == 0) {
-      if constexpr (COH) {  // hand-over words read by the request's workgroup 0
+      if (lds_w) {  // the only workgroup of its request: the masses stay in LDS
+        lds_w[sub] = sw;
+        lds_p[sub] = spp;
+      } else if constexpr (COH) {  // hand-over words read by other workgroups
         unsigned long long *w = reinterpret_cast<unsigned long long *>(out + sub);
         put<true>(w, sub_mass_word(sw));
         put<true>(w + 1, sub_mass_word(spp));
@@ -1218,8 +1222,10 @@ constexpr int kSelMaxSub = 512;  // V <= 2^20
 // do not hold back the dispatch of later ones.  The earliest request not yet
 // done never waits for a workgroup dispatched after a later request's, so the
 // waits end.
+// bf16 rows: at most 128 registers (4 waves per SIMD, 4 workgroups per CU),
+// the residency the drawing mode is chosen for
 template <int DT, bool FILT, bool SEL>
-__global__ __launch_bounds__(kBlock) void k2_decide_mass(
+__global__ __launch_bounds__(kBlock, DT == SV_BF16 ? 4 : 1) void k2_decide_mass(
     const void *__restrict__ target, const void *__restrict__ draft,
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
     const float *__restrict__ temps, float scalar_T, const int32_t *__restrict__ lens, int gamma,
@@ -1239,25 +1245,29 @@ __global__ __launch_bounds__(kBlock) void k2_decide_mass(
   const int first = (wg * kWaves + static_cast<int>(threadIdx.x) / kWave) * SPW;
   const int lane = threadIdx.x & (kWave - 1);
   SubSums *out = sums + static_cast<long>(b) * NSUB;
+  __shared__ double sh_w[SEL ? kSelMaxSub : 1], sh_p[SEL ? kSelMaxSub : 1];
+  // a request with one workgroup keeps its masses in LDS (no hand-over)
+  double *lw = SEL && NW == 1 ? sh_w : nullptr, *lp = SEL && NW == 1 ? sh_p : nullptr;
   if (sp.mode != 0 && first < NSUB) {  // uniform per wave; no barrier inside
     const RowPair rp = selected_rows<DT>(target, draft, gamma, V, b, sp);
     // the wave's sub-chunks lie wholly inside an aligned row: straight-line
     // loads, so that the arithmetic on each vector can start as it arrives
     const bool fast = rp.aligned && static_cast<long>(min(first + SPW, NSUB)) * kSub <= static_cast<long>(V);
     if (sp.mode == 1) {
-      if (fast) mass_pass<DT, FILT, true, true, SEL>(rp, sp, first, SPW, NSUB, V, lane, out);
-      else mass_pass<DT, FILT, false, true, SEL>(rp, sp, first, SPW, NSUB, V, lane, out);
+      if (fast) mass_pass<DT, FILT, true, true, SEL>(rp, sp, first, SPW, NSUB, V, lane, out, lw, lp);
+      else mass_pass<DT, FILT, false, true, SEL>(rp, sp, first, SPW, NSUB, V, lane, out, lw, lp);
     } else {
-      if (fast) mass_pass<DT, FILT, true, false, SEL>(rp, sp, first, SPW, NSUB, V, lane, out);
-      else mass_pass<DT, FILT, false, false, SEL>(rp, sp, first, SPW, NSUB, V, lane, out);
+      if (fast) mass_pass<DT, FILT, true, false, SEL>(rp, sp, first, SPW, NSUB, V, lane, out, lw, lp);
+      else mass_pass<DT, FILT, false, false, SEL>(rp, sp, first, SPW, NSUB, V, lane, out, lw, lp);
     }
   }
   if constexpr (SEL) {
     if (sp.mode == 0 || (!owner && wg != 0)) return;  // uniform per workgroup
-    __shared__ double sh_w[kSelMaxSub], sh_p[kSelMaxSub];
     __shared__ int s_late;
     const unsigned long long *words = reinterpret_cast<const unsigned long long *>(out);
-    if (threadIdx.x < kWave) {
+    if (NW == 1) {
+      if (threadIdx.x == 0) s_late = 0;
+    } else if (threadIdx.x < kWave) {
       bool late = false;
       for (int j0 = 0; j0 < 2 * NSUB; j0 += kWave) {
         const int j = j0 + lane;
