@@ -41,7 +41,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 PROFILE_PMC = os.path.join(PROFILES, "step_B64_g5_V128256_bf16.pmc.json")
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verification_spec_amd", "csrc", "specverify.hip")
 PROBE_LIB = os.path.join(ROOT, "rejection_sampling_verification_spec_amd", "libsvprobe.so")
-STEP_KERNELS = ("k1_row_stats", "k2_decide_mass", "k3_select")
+# the step's kernels on these workloads (every row has at most 512 sub-chunks, so the decision kernel
+# also draws and k3_select is not launched)
+STEP_KERNELS = ("k1_row_stats", "k2_decide_mass")
 
 
 def log(msg):
@@ -123,8 +125,10 @@ def _kernel_short(name: str) -> str:
     tags = [{"0": "f32", "1": "bf16"}.get(args[0], args[0])]
     if kname == "k1_row_stats" and len(args) == 3:
         tags.append({"0": "per-request T", "1": "stochastic", "2": "greedy"}.get(args[2], args[2]))
-    elif len(args) == 2 and args[1] in ("true", "false"):
+    elif len(args) in (2, 3) and args[1] in ("true", "false"):
         tags.append("filtered" if args[1] == "true" else "plain")
+        if len(args) == 3 and args[2] == "true":
+            tags.append("draws")
     return f"{kname}<{', '.join(tags)}>"
 
 
@@ -176,9 +180,8 @@ def summarize_profile(root: str):
             # the timed step's own kernels (one instantiation of each): their averages summed
             k1_tag = {"kt": "stochastic", "kt_greedy": "greedy", "kt_config4": "per-request T"}.get(key)
             if k1_tag is not None:
-                want = [f"k1_row_stats<bf16, {k1_tag}>", "k2_decide_mass<bf16, plain>"]
-                if key != "kt_greedy":
-                    want.append("k3_select<bf16, plain>")
+                want = [f"k1_row_stats<bf16, {k1_tag}>",
+                        "k2_decide_mass<bf16, plain>" if key == "kt_greedy" else "k2_decide_mass<bf16, plain, draws>"]
                 if all(k in avg for k in want):
                     step_sum = sum(avg[k] for k in want)
                     bytes_step = bl["roofline"]["bytes_per_step"]
@@ -210,7 +213,7 @@ def summarize_profile(root: str):
         copy_kib = (1 << 30) / 1024
         f_fetch, f_write = copy_kib / cfetch[copy_name], copy_kib / cwrite[copy_name]
         # the timed step's own instantiations: the stochastic row-statistics kernel (the per-request-T
-        # one in the same run belongs to the separate row-statistics timing) and the plain K2/K3
+        # one in the same run belongs to the separate row-statistics timing) and the plain K2
         step = [k for k in fetch if k.split("<")[0] in STEP_KERNELS
                 and ("stochastic" in k if k.startswith("k1_") else "plain" in k)]
         per = {k: round((fetch[k] * f_fetch + write.get(k, 0.0) * f_write) * 1024) for k in step}
@@ -237,9 +240,10 @@ def summarize_profile(root: str):
         lines += ["", f"Calibration: the plain 1 GiB device copy ({copy_name}) reads {cfetch[copy_name]:.1f} KiB "
                   f"and writes {cwrite[copy_name]:.1f} KiB by these counters, so FETCH_SIZE is scaled by "
                   f"{f_fetch:.4f} and WRITE_SIZE by {f_write:.4f} to give bytes.", "",
-                  f"The step (k1_row_stats + k2_decide_mass + k3_select): {step_bytes / 1e6:.2f} MB per step against "
+                  f"The step (k1_row_stats + k2_decide_mass): {step_bytes / 1e6:.2f} MB per step against "
                   f"{bytes_alg / 1e6:.2f} MB algorithmic (ratio {step_bytes / bytes_alg:.4f}); the excess is "
-                  f"the residual pass re-reading the sampled row pair of each request.", ""]
+                  f"the residual pass re-reading the sampled row pair of each request (and one sub-chunk of "
+                  f"it for the draw).", ""]
         open(os.path.join(PROFILES, "hbm_traffic_B64_g5_V128256_bf16.md"), "w").write("\n".join(lines))
     json.dump(rec, open(PROFILE_PMC, "w"), indent=2)
     print(json.dumps(rec, indent=2))
@@ -555,10 +559,11 @@ def main():
     traffic = None
     if pmc_current and args.config == 3 and not greedy and pmc.get("mode") == "stochastic":
         traffic = pmc.get("hbm_bytes_per_step")
-    kernels = STEP_KERNELS[:2] if greedy else STEP_KERNELS
+    kernels = STEP_KERNELS
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "scope": "whole step: " + " + ".join(kernels), "step_us": round(dev_s_per_step * 1e6, 3),
+                "scope": "whole step: " + " + ".join(kernels) + ("" if greedy else " (which also draws)"),
+                "step_us": round(dev_s_per_step * 1e6, 3),
                 "bytes_per_step": bytes_alg}
 
     # the row-statistics kernel on its own: event pairs the library records around its dispatch.  They

@@ -13,9 +13,10 @@
 //   [P4] "LLM推測デコーディング最適化実踐", section 検証アルゴリズムの実装
 //        (gamma+1 target rows, bonus draw from the last one)
 //
-// Three launches on the caller's stream for the verify step, no host
-// synchronisation, no device-wide fences (each kernel boundary is the only
-// cross-workgroup sync):
+// Two launches on the caller's stream for the verify step (three when a row has
+// more than 512 sub-chunks), no host synchronisation, no device-wide fences:
+// K1's results reach K2 through the kernel boundary, and K2's workgroups hand
+// their sub-chunk masses to each other through device-scope atomic words.
 //
 //   K1  k1_row_stats    one workgroup per (request, logit row, vocabulary chunk).
 //                       Streams the chunk once (16-byte non-temporal loads, next
@@ -30,17 +31,20 @@
 //                       gathered logits and finds the first rejection with a
 //                       wave ballot (workgroup 0 stores the outputs); then its
 //                       waves write the mass of w = max(0, p - q) (or p for the
-//                       bonus) of the selected row pair per 2048-token sub-chunk.
-//   K3  k3_select       one workgroup per request: the sub-chunk whose prefix
-//                       crosses u*Z, then the token inside it.
+//                       bonus) of the selected row pair per 2048-token sub-chunk;
+//                       then the sub-chunk whose prefix crosses u*Z, and the
+//                       token inside it, are found by the workgroup that
+//                       computed that sub-chunk (or by workgroup 0).
+//   K3  k3_select       the same draw as a kernel of its own, one workgroup per
+//                       request, for rows of more than 512 sub-chunks.
 //
 // Extensions, on the same row statistics:
 //   top-k / top-p       k_filter_capture, k_filter_deep_count, k_filter_resolve
 //                       and k_filter_general between K1 and K2 find each
 //                       filtered row's cut; K2 and K3 are instantiated with
 //                       the cut compares.
-//   tree of drafts      K1 over every tree position, then k_tree_walk (one
-//                       workgroup per request).
+//   tree of drafts      K1 over every tree position, then k_tree_walk (a team
+//                       of workgroups per request).
 //   draft-side sampling k_sample_stats (several workgroups per row), then
 //                       k_sample_pick (one wave per row).
 //
