@@ -3155,7 +3155,7 @@ struct Plan {
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 constexpr int kK1U = 8;                 // 16-byte vectors per thread per K1 tile
-constexpr long kK1TargetGroups = 2816;  // about 11 workgroups per CU on 256 CUs
+constexpr long kK1TargetGroups = 4224;  // about 16 workgroups per CU on 256 CUs (a sweep)
 
 bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV_GAMMA_MAX) {
   if (B < 1 || gamma < 0 || gamma > gamma_limit || V < 1) return false;
