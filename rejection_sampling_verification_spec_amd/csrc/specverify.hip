@@ -37,6 +37,11 @@
 //                       computed that sub-chunk (or by workgroup 0).
 //   K3  k3_select       the same draw as a kernel of its own, one workgroup per
 //                       request, for rows of more than 512 sub-chunks.
+//   KS  k_small_verify  one 1024-thread workgroup per request, the whole step in
+//                       one launch, when a request's rows hold at most 12288
+//                       logits: the rows are staged in LDS with one batch of
+//                       loads, and the statistics, decision and draw follow on
+//                       chip.
 //
 // Extensions, on the same row statistics:
 //   top-k / top-p       k_filter_capture, k_filter_deep_count, k_filter_resolve
@@ -54,6 +59,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -936,6 +942,32 @@ __device__ __forceinline__ double lane_value(double v, int lane) {
 
 // sum over the wave, the same value in every lane
 __device__ __forceinline__ double wave_sum(double v) { return lane_value(wave_scan(v, 0), kWave - 1); }
+
+// maximum over the wave, the same value in every lane (lanes without a DPP
+// source keep -inf, the identity)
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x111, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x112, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x114, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x118, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x142, 0xa, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+// integer maximum / minimum over the wave, the same value in every lane
+template <bool MAX>
+__device__ __forceinline__ int wave_ext_i32(int v) {
+  constexpr int id = MAX ? INT_MIN : INT_MAX;
+  auto f = [](int x, int y) { return MAX ? (x > y ? x : y) : (x < y ? x : y); };
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xf, 0xf, false));
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xf, 0xf, false));
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xf, 0xf, false));
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xf, 0xf, false));
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xa, 0xf, false));
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, kWave - 1);
+}
 
 struct RowPair {
   const void *trow, *drow;
@@ -2926,6 +2958,283 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
   if (lead && tid == 0) count[b] = depth;
 }
 
+// ================================================================== small problems
+// A request whose rows hold at most kSmElems logits in all ((2 gamma + 1) V)
+// is verified by one workgroup, in one kernel: its rows are read once into LDS
+// (one batch of loads), and the statistics, the decision and the draw follow
+// on chip, with no hand-over between workgroups and no second launch.  For
+// such rows the two-kernel path is a chain of launches and round trips over a
+// few kilobytes.
+//   stage     every needed logit of the request -> LDS (fp32), rows in order;
+//   stats     wave w takes rows w, w + kSmWaves, ...: (M, s) as K1 computes
+//             them (integer M of the lane's maximum, exact power-of-two
+//             merges), or the maximum and its lowest index for a greedy row;
+//   decide    wave 0, as decide_request: fp64 ratio from the staged logits at
+//             the draft tokens, ballot for the first rejection;
+//   draw      thread t takes the contiguous tokens [t C, (t+1) C) of the row
+//             sampled (C = ceil(V / kSmBlock)); a block scan of the threads'
+//             fp64 sums gives every thread its prefix, and the thread whose
+//             range holds u*Z walks its tokens.
+constexpr int kSmBlock = 1024;
+constexpr int kSmWaves = kSmBlock / kWave;
+constexpr int kSmElems = 12288;                  // logits staged in LDS (48 KB)
+constexpr int kSmBatch = kSmElems / kSmBlock;    // loads in flight per thread
+constexpr int kSmRun = 16;                       // staged logits a lane folds at a time
+
+struct SmallArgs {
+  const void *target, *draft;
+  const int32_t *tokens;
+  const float *u_accept, *u_sample, *temps;
+  float scalar_T;
+  const int32_t *lens;
+  int gamma, V;
+  int32_t *count, *out;
+  sv_debug dbg;
+};
+
+template <int DT, int KIND>
+__global__ __launch_bounds__(kSmBlock) void k_small_verify(SmallArgs a) {
+  extern __shared__ float zs[];  // [2 gamma + 1][V] staged logits, target rows first
+  __shared__ int sh_M[2 * SV_GAMMA_MAX + 1], sh_arg[2 * SV_GAMMA_MAX + 1];
+  __shared__ double sh_s[2 * SV_GAMMA_MAX + 1];
+  __shared__ float sh_mx[2 * SV_GAMMA_MAX + 1];
+  __shared__ double sh_wtot[kSmWaves];
+  __shared__ int sh_k;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int gamma = a.gamma, V = a.V, rows = 2 * gamma + 1;
+  // one round trip for everything a uniform batch needs: the request's target
+  // rows (contiguous), its draft rows, its draft tokens and uniforms.  With
+  // per-request temperatures the draft rows and uniforms wait for T (a greedy
+  // request reads neither); padding rows past a ragged request's length are
+  // staged but never used.
+  const int nt = (gamma + 1) * V, nd = gamma * V;
+  const char *tb = static_cast<const char *>(a.target) + static_cast<long>(b) * nt * Elem<DT>::kBytes;
+  const char *db = static_cast<const char *>(a.draft) + static_cast<long>(b) * nd * Elem<DT>::kBytes;
+  float bt[kSmBatch], bd[kSmBatch];
+#pragma unroll
+  for (int q = 0; q < kSmBatch; ++q) {
+    const int e = q * kSmBlock + tid;
+    bt[q] = e < nt ? load_one<DT>(tb, e) : -INFINITY;
+  }
+  const int x = (wave == 0 && lane < gamma) ? a.tokens[static_cast<long>(b) * gamma + lane] : -1;
+  const int g = request_len(a.lens, gamma, b);
+  const float T = request_T(a.temps, a.scalar_T, b);
+  const bool greedy = KIND == kGreedyOnly ? true : (KIND == kStochasticOnly ? false : !(T > 0.0f));
+  const float c = greedy ? 0.0f : temp_scale(T);
+  float ua = 0.0f, us = 0.0f;
+  if (!greedy) {
+#pragma unroll
+    for (int q = 0; q < kSmBatch; ++q) {
+      const int e = q * kSmBlock + tid;
+      bd[q] = e < nd ? load_one<DT>(db, e) : -INFINITY;
+    }
+    if (wave == 0 && lane < g) ua = a.u_accept[static_cast<long>(b) * gamma + lane];
+    us = a.u_sample[b];
+  }
+#pragma unroll
+  for (int q = 0; q < kSmBatch; ++q) {
+    const int e = q * kSmBlock + tid;
+    if (e < nt) zs[e] = bt[q];
+  }
+  if (!greedy) {
+#pragma unroll
+    for (int q = 0; q < kSmBatch; ++q) {
+      const int e = q * kSmBlock + tid;
+      if (e < nd) zs[nt + e] = bd[q];
+    }
+  }
+  auto row_needed = [&](int r) { return r <= gamma ? r <= g : (!greedy && r - gamma - 1 < g); };
+  __syncthreads();
+
+  // row statistics, one wave per row; a lane takes kSmRun tokens at a time
+  // (read together, folded as K1 folds a tile)
+  for (int r = wave; r < rows; r += kSmWaves) {
+    if (!row_needed(r)) continue;  // uniform per wave
+    const float *z = zs + static_cast<long>(r) * V;
+    int M = kEmptyM;
+    double s = 0.0;
+    float mx = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int v0 = lane; v0 < V; v0 += kSmRun * kWave) {
+      float zz[kSmRun];
+#pragma unroll
+      for (int q = 0; q < kSmRun; ++q) {  // clamped reads, then a select: no branch per token
+        const int v = v0 + q * kWave;
+        const float zv = z[min(v, V - 1)];
+        zz[q] = v < V ? zv : -INFINITY;
+      }
+      if (!greedy) {
+        fold_values<kSmRun>(zz, c, M, s, mx);
+      } else {
+        // a lane's tokens come in increasing order: a strict > keeps the first
+#pragma unroll
+        for (int q = 0; q < kSmRun; ++q) {
+          const bool take = v0 + q * kWave < V && (bi == 0x7fffffff || zz[q] > mx);
+          mx = take ? zz[q] : mx;
+          bi = take ? v0 + q * kWave : bi;
+        }
+      }
+    }
+    // merged over the wave with DPP: the largest M, every lane's sum rescaled
+    // to it exactly (a power of two), then one fp64 sum; greedy: the maximum,
+    // then the lowest index holding it
+    const float wmx = wave_max_f32(mx);
+    if (!greedy) {
+      const int Mw = wave_ext_i32<true>(M);
+      const double sw = wave_sum(M == kEmptyM ? 0.0 : ldexp(s, M - Mw));
+      if (lane == 0) {
+        sh_M[r] = Mw;
+        sh_s[r] = sw;
+        sh_mx[r] = wmx;
+      }
+    } else {
+      const int wbi = wave_ext_i32<false>(mx == wmx ? bi : INT_MAX);
+      if (lane == 0) {
+        sh_arg[r] = wbi;
+        sh_mx[r] = wmx;
+      }
+    }
+  }
+  __syncthreads();
+
+  // decision (wave 0): acceptance of each draft and the first rejection
+  if (wave == 0) {
+    const sv_debug &d = a.dbg;
+    const int p = lane;
+    bool reject = false;
+    if (p < g) {
+      if (x < 0 || x >= V) {
+        reject = true;  // a draft id outside the vocabulary is rejected, never dereferenced
+      } else if (greedy) {
+        reject = x != sh_arg[p];
+      } else {
+        const float zpx = zs[static_cast<long>(p) * V + x];
+        const float zqx = zs[static_cast<long>(gamma + 1 + p) * V + x];
+        const double cd = static_cast<double>(c);
+        const int Mp = sh_M[p], Mq = sh_M[gamma + 1 + p];
+        const double sp_ = sh_s[p], sq_ = sh_s[gamma + 1 + p];
+        // p/q at x = 2^((zp - zq) c - (Mp - Mq)) * s_q / s_p, in fp64
+        const double dd = (static_cast<double>(zpx) - static_cast<double>(zqx)) * cd - static_cast<double>(Mp - Mq);
+        const double ratio = exp2(dd) * (sq_ / sp_);
+        const double acc = ratio < 1.0 ? ratio : 1.0;
+        reject = !(static_cast<double>(ua) < acc);
+        const long o = static_cast<long>(b) * gamma + p;
+        if (d.p_draft) d.p_draft[o] = exp2(static_cast<double>(zpx) * cd - Mp) / sp_;
+        if (d.q_draft) d.q_draft[o] = exp2(static_cast<double>(zqx) * cd - Mq) / sq_;
+        if (d.accept_prob) d.accept_prob[o] = acc;
+      }
+    }
+    const unsigned long long rej = __ballot(reject);
+    const int k = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : g;
+    // row diagnostics of every row read
+    for (int r = lane; r < rows; r += kWave) {
+      if (!row_needed(r)) continue;
+      if (!greedy) {
+        if (d.row_max) d.row_max[static_cast<long>(b) * rows + r] = sh_mx[r];
+        if (d.row_sum)  // sum_v exp((z_v - max)/T) = s * 2^(M - max c)
+          d.row_sum[static_cast<long>(b) * rows + r] =
+              sh_s[r] * exp2(static_cast<double>(sh_M[r]) - static_cast<double>(sh_mx[r]) * static_cast<double>(c));
+      } else if (d.row_argmax && r <= gamma) {
+        d.row_argmax[static_cast<long>(b) * (gamma + 1) + r] = sh_arg[r];
+      }
+    }
+    // outputs; a stochastic request's token at k is drawn below
+    if (lane <= gamma) {  // gamma < 64: lane t holds draft t
+      const int t = lane;
+      int32_t v = -1;
+      if (t < k) v = x;
+      else if (t == k && greedy) v = sh_arg[k];
+      if (t != k || greedy) a.out[static_cast<long>(b) * (gamma + 1) + t] = v;
+    }
+    if (lane == 0) {
+      a.count[b] = k;
+      sh_k = k;
+    }
+  }
+  __syncthreads();
+  if (greedy) return;  // uniform per workgroup
+
+  // draw at position k: the residual max(0, p_k - q_k) in units of the target
+  // row's scale (e_p - r e_q), or p_k for the bonus / a residual of mass zero
+  const int k = sh_k;
+  const bool useq = k < g;
+  const float negMp = -static_cast<float>(sh_M[k]);
+  const float negMq = useq ? -static_cast<float>(sh_M[gamma + 1 + k]) : 0.0f;
+  const float rr = useq ? static_cast<float>(sh_s[k] / sh_s[gamma + 1 + k]) : 0.0f;
+  const float *zp = zs + static_cast<long>(k) * V;
+  const float *zq = zs + static_cast<long>(gamma + 1 + k) * V;
+  const int C = (V + kSmBlock - 1) / kSmBlock;
+  const int v0 = min(tid * C, V), v1 = min(v0 + C, V);
+  auto value = [&](int v, bool use_p) -> float {
+    const float ep = __builtin_amdgcn_exp2f(fmaf(zp[v], c, negMp));
+    if (use_p || !useq) return ep;
+    const float eq = __builtin_amdgcn_exp2f(fmaf(zq[v], c, negMq));
+    return fmaxf(0.0f, fmaf(-eq, rr, ep));
+  };
+  // the threads' sums, their block prefix and the total (two passes: the
+  // residual, then p when its mass is zero)
+  double excl = 0.0, mine = 0.0, Z = 0.0;
+  bool use_p = false;
+  for (int pass = 0; pass < 2; ++pass) {
+    use_p = pass == 1;
+    mine = 0.0;
+    for (int v = v0; v < v1; ++v) mine += static_cast<double>(value(v, use_p));
+    const double incl = wave_scan(mine, lane);
+    if (lane == kWave - 1) sh_wtot[wave] = incl;
+    __syncthreads();
+    double before = 0.0;
+    Z = 0.0;
+    for (int w = 0; w < kSmWaves; ++w) {
+      const double t = sh_wtot[w];
+      if (w < wave) before += t;
+      Z += t;
+    }
+    excl = before + (incl - mine);
+    if (Z > 0.0 || !useq) break;  // uniform: every thread read the same totals
+    __syncthreads();              // sh_wtot is rewritten by the second pass
+  }
+  const double target = static_cast<double>(us) * Z;
+  // the first thread whose range crosses u*Z (tokens with mass only), found
+  // by every wave from the same wave totals: the crossing wave, then its
+  // lane by a ballot; if rounding leaves u*Z past the end, the last thread
+  // with mass
+  int cw = -1, lw = -1;
+  {
+    double run = 0.0;
+    for (int w = 0; w < kSmWaves; ++w) {
+      const double t = sh_wtot[w];
+      if (t > 0.0) {
+        if (cw < 0 && run + t > target) cw = w;
+        lw = w;
+      }
+      run += t;
+    }
+  }
+  const bool past_end = cw < 0;
+  if (past_end) cw = lw < 0 ? 0 : lw;
+  if (wave != cw) return;  // uniform per wave
+  const unsigned long long hit = __ballot(mine > 0.0 && excl + mine > target);
+  const unsigned long long has = __ballot(mine > 0.0);
+  const int L = (!past_end && hit) ? __ffsll(static_cast<long long>(hit)) - 1
+                                   : (has ? 63 - __clzll(static_cast<long long>(has)) : 0);
+  if (lane == L) {
+    double acc = excl;
+    int tok = -1, lastm = -1;
+    for (int v = v0; v < v1; ++v) {
+      const float w = value(v, use_p);
+      if (w > 0.0f) {
+        lastm = v;
+        acc += static_cast<double>(w);
+        if (tok < 0 && target < acc) tok = v;
+      }
+    }
+    if (tok < 0) tok = lastm >= 0 ? lastm : v0;
+    a.out[static_cast<long>(b) * (gamma + 1) + k] = tok;
+    if (a.dbg.residual_mass) a.dbg.residual_mass[b] = Z / sh_s[k];
+  }
+}
+
 // ================================================================== draft-side sampler
 // One token per row of softmax(z/T), in two kernels.
 //   S1 k_sample_stats: kSBlock-thread workgroups, several per row; each wave
@@ -2945,15 +3254,6 @@ struct alignas(16) SubRecord {
   int mi;    // M_j (stochastic) or the maximum's lowest index (greedy)
 };
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x111, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x112, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x114, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x118, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x142, 0xa, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x143, 0xc, 0xf, false)));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
-}
 
 // S1: workgroup g of row r (SG workgroups per row); wave w takes sub-chunks
 // g * kSWaves + w, then every SG * kSWaves further.
@@ -3334,6 +3634,45 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
   return SV_OK;
 }
 
+// ------------------------------------------------------------------ small problems
+// One workgroup per request when a request's rows hold at most kSmElems logits.
+bool small_problem(int gamma, int V) { return static_cast<long>(2 * gamma + 1) * V <= kSmElems; }
+
+template <int DT>
+int run_small(const void *target, const void *draft, const int32_t *tokens, const float *u_accept,
+              const float *u_sample, const float *temps, float scalar_T, const int32_t *lens, int B, int gamma,
+              int V, int32_t *count, int32_t *out, hipStream_t st, const sv_debug *dbgp) {
+  SmallArgs sa;
+  memset(&sa, 0, sizeof sa);
+  if (dbgp) sa.dbg = *dbgp;
+  sa.target = target;
+  sa.draft = draft;
+  sa.tokens = tokens;
+  sa.u_accept = u_accept;
+  sa.u_sample = u_sample;
+  sa.temps = temps;
+  sa.scalar_T = scalar_T;
+  sa.lens = lens;
+  sa.gamma = gamma;
+  sa.V = V;
+  sa.count = count;
+  sa.out = out;
+  const size_t lds = sizeof(float) * static_cast<size_t>(2 * gamma + 1) * V;
+  const hipEvent_t ev0 = static_cast<hipEvent_t>(sa.dbg.k1_events[0]), ev1 = static_cast<hipEvent_t>(sa.dbg.k1_events[1]);
+#define SV_SMALL(KIND)                                                                                        \
+  do {                                                                                                        \
+    if (ev0 && ev1)                                                                                           \
+      hipExtLaunchKernelGGL((k_small_verify<DT, KIND>), dim3(B), dim3(kSmBlock), lds, st, ev0, ev1, 0, sa);   \
+    else                                                                                                      \
+      hipLaunchKernelGGL((k_small_verify<DT, KIND>), dim3(B), dim3(kSmBlock), lds, st, sa);                   \
+  } while (0)
+  if (temps) SV_SMALL(kMixed);
+  else if (scalar_T > 0.0f) SV_SMALL(kStochasticOnly);
+  else SV_SMALL(kGreedyOnly);
+#undef SV_SMALL
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
 int dispatch(const void *target, const void *draft, const int32_t *tokens, const float *u_accept,
              const float *u_sample, const float *temps, float scalar_T, bool all_greedy,
              const int32_t *lens, const int32_t *topk, const float *topp, int B, int gamma, int V,
@@ -3351,6 +3690,13 @@ int dispatch(const void *target, const void *draft, const int32_t *tokens, const
   if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0 || ws_bytes < need) return SV_EWORKSPACE;
   if (dbg && ((dbg->k1_events[0] == nullptr) != (dbg->k1_events[1] == nullptr))) return SV_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!(topk || topp) && small_problem(gamma, V)) {
+    if (dtype == SV_BF16)
+      return run_small<SV_BF16>(target, draft, tokens, u_accept, u_sample, temps, scalar_T, lens, B, gamma, V,
+                                count, out, st, dbg);
+    return run_small<SV_F32>(target, draft, tokens, u_accept, u_sample, temps, scalar_T, lens, B, gamma, V, count,
+                             out, st, dbg);
+  }
   if (dtype == SV_BF16)
     return run<SV_BF16>(target, draft, tokens, u_accept, u_sample, temps, scalar_T, all_greedy, lens, topk,
                         topp, B, gamma, V, count, out, ws, P, st, dbg);

@@ -159,6 +159,65 @@ def test_greedy_ties_lowest_index(B, gamma, V):
         assert rep["flagged"] == 0
 
 
+# ------------------------------------------------------------------ one workgroup per request
+# A request whose (2 gamma + 1) V logits fit 12288 (48 KB of LDS) is verified by
+# one workgroup, in one kernel; one logit more takes the two-kernel path.
+SMALL = [
+    # (B, gamma, V, dtype)
+    (1, 4, 1000, "f32"),     # workload 0's shape
+    (3, 5, 1117, "bf16"),    # 11 * 1117 = 12287
+    (2, 0, 12288, "f32"),    # one row of 12288 logits: the limit
+    (2, 0, 12289, "f32"),    # one logit more: the two-kernel path
+    (4, 1, 4096, "bf16"),    # 3 * 4096 = 12288
+    (200, 2, 512, "bf16"),   # many requests
+    (5, 32, 100, "f32"),     # the longest drafts
+    (7, 6, 511, "bf16"),     # rows that are not 16-byte aligned
+]
+
+
+@pytest.mark.parametrize("B,gamma,V,dtype", SMALL)
+@pytest.mark.parametrize("mode", ["uniform", "mixed", "greedy"])
+def test_small_problems(B, gamma, V, dtype, mode):
+    seed = zlib.crc32(repr((B, gamma, V, dtype, mode, "small")).encode()) % 100000
+    rng = np.random.default_rng(seed)
+    if mode == "uniform":
+        w = W.make_random(seed, B, gamma, V, dtype, temps=0.9, target_scale=3.0, sigma=0.7, zipf=V > 100)
+    elif mode == "greedy":
+        w = W.make_random(seed, B, gamma, V, dtype, temps=0.0, target_scale=3.0, sigma=0.7, zipf=V > 100)
+    else:
+        temps = rng.choice(np.array([0.0, 0.6, 1.0, 1.7], np.float32), size=B)
+        lens = rng.integers(0, gamma + 1, size=B).astype(np.int32)
+        w = W.make_random(seed, B, gamma, V, dtype, temps=temps, lens=lens, target_scale=4.0, sigma=1.0,
+                          zipf=V > 100)
+    say(f"small problem B={B} gamma={gamma} V={V} {dtype} {mode}")
+    run_and_check(w, debug=True, require_no_flags=False)
+    run_and_check(w, debug=False, require_no_flags=False)
+
+
+def test_small_problem_misaligned_rows():
+    """The one-workgroup path reads element by element: rows only 2-byte aligned."""
+    w = W.make_random(9, 6, 4, 1000, "bf16", temps=np.array([1.0, 0.0, 0.7, 1.3, 0.0, 2.0], np.float32),
+                      zipf=True)
+    import oracle
+    import rejection_sampling_verification_spec_amd as sv
+    o = oracle.run_workload(w)
+    dev = torch.device("cuda:0")
+    t = w.to_torch(dev)
+
+    def shifted(x):
+        buf = torch.empty(x.numel() + 1, dtype=x.dtype, device=dev)
+        v = buf[1:].view(x.shape)
+        v.copy_(x)
+        return v
+    count, out = sv.spec_verify_ex(shifted(t["target"]), shifted(t["draft"]), t["draft_tokens"], t["u_accept"],
+                                   t["u_sample"], t["temperature"])
+    torch.cuda.synchronize()
+    ok = o.flags == 0
+    assert ok.sum() >= w.B // 2
+    np.testing.assert_array_equal(count.cpu().numpy()[ok], o.accepted_count[ok])
+    np.testing.assert_array_equal(out.cpu().numpy()[ok], o.out_tokens[ok])
+
+
 # ------------------------------------------------------------------ the pins' inputs through the library
 def _lnp(p):
     p = np.asarray(p, dtype=np.float64)
