@@ -115,8 +115,21 @@ typedef struct {
     int32_t *row_argmax;   /* [B][gamma+1] lowest-index arg-max of greedy target rows */
     double *residual_mass; /* [B] Z, the mass of the distribution sampled at k       */
     void *k1_events[2];    /* hipEvent_t pair recorded around the row-statistics
-                              kernel on `stream` (both or neither)                  */
+                              kernel on `stream` (both or neither; the one-workgroup
+                              kernel of a small request, which is the whole step)  */
 } sv_debug;
+
+/* spec_verify with diagnostics (dbg may be NULL): the same kernels as
+ * spec_verify (one host temperature for the batch), so that k1_events time the
+ * row-statistics kernel the uniform entry point runs (the one-workgroup kernel
+ * for requests of at most 12288 logits, where the step is that one kernel).
+ * Arguments, layouts and errors as spec_verify and spec_verify_ex. */
+int spec_verify_dbg(const void *target_logits, const void *draft_logits,
+                    const int32_t *draft_tokens, const float *u_accept,
+                    const float *u_sample, float temperature, int B, int gamma,
+                    int V, int dtype, int32_t *accepted_count,
+                    int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                    void *stream, const sv_debug *dbg);
 
 /* Ragged / mixed batch.
  * temperature: DEVICE array [B]; 0 = greedy request, else > 0 and finite.

@@ -32,6 +32,7 @@ SV_NOALLOC_SCRATCH_BYTES = 4 << 20
 EXPORTED_SYMBOLS = (
     "spec_verify_workspace_bytes",
     "spec_verify",
+    "spec_verify_dbg",
     "spec_verify_ex",
     "spec_verify_filtered",
     "spec_verify_filtered_workspace_bytes",
@@ -120,6 +121,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32,
                                 vp, vp, vp, sz, vp]
     lib.spec_verify.restype = i32
+    lib.spec_verify_dbg.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32,
+                                    vp, vp, vp, sz, vp, ctypes.POINTER(SvDebug)]
+    lib.spec_verify_dbg.restype = i32
     lib.spec_verify_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                    vp, vp, vp, sz, vp, ctypes.POINTER(SvDebug)]
     lib.spec_verify_ex.restype = i32
@@ -265,8 +269,12 @@ def _on(stream):
 
 
 def spec_verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature: float,
-                accepted_count=None, out_tokens=None, workspace=None, stream=None):
-    """Uniform batch (one temperature, gamma drafts per request).  Returns (accepted_count, out_tokens)."""
+                accepted_count=None, out_tokens=None, workspace=None, stream=None, debug: Optional[dict] = None,
+                k1_events=None):
+    """Uniform batch (one temperature, gamma drafts per request).  Returns (accepted_count, out_tokens).
+
+    ``debug`` / ``k1_events``: as for ``spec_verify_ex`` (the call then goes through spec_verify_dbg,
+    which runs the same kernels as spec_verify)."""
     lib = load_library()
     B, gamma, V = _shapes(target_logits)
     dt = _dtype_code(target_logits)
@@ -276,10 +284,13 @@ def spec_verify(target_logits, draft_logits, draft_tokens, u_accept, u_sample, t
         _check_all(target_logits, draft_logits, draft_tokens, u_accept, u_sample, accepted_count, out_tokens,
                    greedy_only=float(temperature) == 0.0)
         workspace, need = _workspace(B, gamma, V, dt, target_logits.device, workspace)
-    rc = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
-                         _ptr(u_sample), float(temperature), B, gamma, V, dt,
-                         _ptr(accepted_count), _ptr(out_tokens), _ptr(workspace),
-                         workspace.numel(), _stream(stream))
+    args = (_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_sample),
+            float(temperature), B, gamma, V, dt, _ptr(accepted_count), _ptr(out_tokens), _ptr(workspace),
+            workspace.numel(), _stream(stream))
+    if debug or k1_events:
+        rc = lib.spec_verify_dbg(*args, _debug_struct(B, gamma, debug, k1_events))
+    else:
+        rc = lib.spec_verify(*args)
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify")
     return accepted_count, out_tokens
@@ -332,6 +343,25 @@ def spec_verify_filtered(target_logits, draft_logits, draft_tokens, u_accept, u_
                                  workspace, stream, debug, k1_events)
 
 
+def _debug_struct(B, gamma, debug, k1_events):
+    """An sv_debug pointing at the caller's preallocated diagnostic tensors and event pair."""
+    import torch
+    d = SvDebug()
+    rows = 2 * gamma + 1
+    dshapes = {"p_draft": ((B, gamma), torch.float64), "q_draft": ((B, gamma), torch.float64),
+               "accept_prob": ((B, gamma), torch.float64), "row_max": ((B, rows), torch.float32),
+               "row_sum": ((B, rows), torch.float64), "row_argmax": ((B, gamma + 1), torch.int32),
+               "residual_mass": ((B,), torch.float64)}
+    for name, (shape, dtype) in dshapes.items():
+        t = (debug or {}).get(name)
+        _expect(t, shape, dtype, f"debug[{name}]", optional=True)
+        setattr(d, name, _ptr(t))
+    if k1_events:
+        d.k1_events[0] = k1_events[0].cuda_event
+        d.k1_events[1] = k1_events[1].cuda_event
+    return ctypes.pointer(d)
+
+
 def _verify_device_params(entry, target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature,
                           draft_lens, top_k, top_p, accepted_count, out_tokens, workspace, stream, debug,
                           k1_events):
@@ -354,22 +384,7 @@ def _verify_device_params(entry, target_logits, draft_logits, draft_tokens, u_ac
                                      filtered=entry == "spec_verify_filtered")
     if workspace.numel() < need:
         raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
-    dbg = None
-    if debug or k1_events:
-        d = SvDebug()
-        rows = 2 * gamma + 1
-        dshapes = {"p_draft": ((B, gamma), torch.float64), "q_draft": ((B, gamma), torch.float64),
-                   "accept_prob": ((B, gamma), torch.float64), "row_max": ((B, rows), torch.float32),
-                   "row_sum": ((B, rows), torch.float64), "row_argmax": ((B, gamma + 1), torch.int32),
-                   "residual_mass": ((B,), torch.float64)}
-        for name, (shape, dtype) in dshapes.items():
-            t = (debug or {}).get(name)
-            _expect(t, shape, dtype, f"debug[{name}]", optional=True)
-            setattr(d, name, _ptr(t))
-        if k1_events:
-            d.k1_events[0] = k1_events[0].cuda_event
-            d.k1_events[1] = k1_events[1].cuda_event
-        dbg = ctypes.pointer(d)
+    dbg = _debug_struct(B, gamma, debug, k1_events) if (debug or k1_events) else None
     head = (_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_sample),
             _ptr(temperature), _ptr(draft_lens))
     tail = (B, gamma, V, dt, _ptr(accepted_count), _ptr(out_tokens), _ptr(workspace), workspace.numel(),

@@ -3790,6 +3790,16 @@ int spec_verify(const void *target_logits, const void *draft_logits, const int32
                   out_tokens, workspace, workspace_bytes, stream, nullptr);
 }
 
+int spec_verify_dbg(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
+                    const float *u_accept, const float *u_sample, float temperature, int B, int gamma,
+                    int V, int dtype, int32_t *accepted_count, int32_t *out_tokens, void *workspace,
+                    size_t workspace_bytes, void *stream, const sv_debug *dbg) {
+  if (!(temperature >= 0.0f) || isinf(temperature)) return SV_EINVAL;
+  return dispatch(target_logits, draft_logits, draft_tokens, u_accept, u_sample, nullptr, temperature,
+                  temperature == 0.0f, nullptr, nullptr, nullptr, B, gamma, V, dtype, accepted_count,
+                  out_tokens, workspace, workspace_bytes, stream, dbg);
+}
+
 int spec_verify_noalloc(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
                         const float *u_accept, const float *u_sample, float temperature, int B, int gamma,
                         int V, int dtype, int32_t *accepted_count, int32_t *out_tokens, void *stream) {

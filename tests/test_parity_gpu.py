@@ -455,3 +455,40 @@ def test_non_current_stream_without_workspace():
     ref, tr = oracle.sample(w.target[:, 0], w.u_sample, 0.7, dtype=w.dtype, top_p=0.9)
     okr = tr.flags == 0
     np.testing.assert_array_equal(tok.cpu().numpy()[okr], ref[okr])
+
+
+@pytest.mark.parametrize("cfg,greedy", [(2, False), (3, True), (0, False)])
+def test_uniform_entry_with_diagnostics(cfg, greedy):
+    """spec_verify_dbg (spec_verify's kernels, with diagnostics and the row-statistics events) gives
+    the outputs and diagnostics of spec_verify_ex on the same uniform batch."""
+    import rejection_sampling_verification_spec_amd as sv
+    w = W.make_config(cfg, greedy=greedy)
+    dev = torch.device("cuda:0")
+    t = w.to_torch(dev)
+    B, gamma = w.B, w.gamma
+    rows = 2 * gamma + 1
+
+    def dbg():
+        f64 = dict(dtype=torch.float64, device=dev)
+        return dict(p_draft=torch.full((B, gamma), float("nan"), **f64),
+                    q_draft=torch.full((B, gamma), float("nan"), **f64),
+                    accept_prob=torch.full((B, gamma), float("nan"), **f64),
+                    row_max=torch.full((B, rows), float("nan"), dtype=torch.float32, device=dev),
+                    row_sum=torch.full((B, rows), float("nan"), **f64),
+                    row_argmax=torch.full((B, gamma + 1), -1, dtype=torch.int32, device=dev),
+                    residual_mass=torch.full((B,), float("nan"), **f64))
+    d1, d2 = dbg(), dbg()
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in ev:
+        e.record()   # torch's own bookkeeping: elapsed_time needs events it has recorded once
+    T = float(w.scalar_temperature)
+    say(f"{w.name} via spec_verify_dbg")
+    c1, o1 = sv.spec_verify(t["target"], None if greedy else t["draft"], t["draft_tokens"],
+                            None if greedy else t["u_accept"], t["u_sample"], T, debug=d1, k1_events=ev)
+    c2, o2 = sv.spec_verify_ex(t["target"], t["draft"], t["draft_tokens"], t["u_accept"], t["u_sample"],
+                               t["temperature"], debug=d2)
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) > 0.0
+    assert torch.equal(c1, c2) and torch.equal(o1, o2)
+    for k in d1:
+        np.testing.assert_array_equal(d1[k].cpu().numpy(), d2[k].cpu().numpy(), err_msg=k)
