@@ -1113,6 +1113,94 @@ __device__ __forceinline__ void mass_pass(const RowPair &rp, const SelParams &sp
   }
 }
 
+// The draw inside one 2048-token sub-chunk from the vectors a wave holds in
+// the interleaved layout of load_lane_fast (vector u of a lane is vector
+// u*64 + lane of the sub-chunk, so the sub-chunk's order is vector slot, then
+// lane, then element): per-vector sums, a wave scan per slot, the slot whose
+// prefix crosses the target, the lane by a ballot, the element by the lane.
+// Rounding past the sub-chunk's end: its last token with mass.  sub_tok: the
+// sub-chunk's first token; base_mass: the mass before it.  Called by the whole
+// wave; one lane writes the token.
+template <int DT, bool FILT>
+__device__ __forceinline__ void draw_held(const u32x4 *tv, const u32x4 *dv, const SelParams &sp, bool use_p,
+                                          long sub_tok, double base_mass, double target_mass, int lane,
+                                          int32_t *dst) {
+  constexpr int kV = Elem<DT>::kVec;
+  constexpr int kN = kLaneElems / kV;
+  auto vals_of = [&](u32x4 t, u32x4 d, float *v) {
+    float zp[kV], zq[kV];
+    widen_vec<DT>(t, zp);
+    if (sp.mode == 1) widen_vec<DT>(d, zq);
+#pragma unroll
+    for (int e = 0; e < kV; ++e) {
+      float w, p;
+      residual_value<FILT>(sp, zp[e], sp.mode == 1 ? zq[e] : 0.0f, w, p);
+      v[e] = use_p ? p : w;
+    }
+  };
+  float vs[kN];
+  double incl[kN];
+  int us = -1, ulast = -1;
+  double run = base_mass, at = base_mass, at_last = base_mass;
+#pragma unroll
+  for (int u = 0; u < kN; ++u) {
+    float v[kV];
+    vals_of(tv[u], sp.mode == 1 ? dv[u] : tv[u], v);
+    float t;
+    if constexpr (kV == 8) t = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    else t = (v[0] + v[1]) + (v[2] + v[3]);
+    vs[u] = t;
+    incl[u] = wave_scan(static_cast<double>(t), lane);
+    const double tot = lane_value(incl[u], kWave - 1);
+    if (tot > 0.0) {
+      if (us < 0 && run + tot > target_mass) {
+        us = u;
+        at = run;
+      }
+      ulast = u;
+      at_last = run;
+    }
+    run += tot;
+  }
+  if (us < 0) {
+    us = ulast >= 0 ? ulast : 0;
+    at = ulast >= 0 ? at_last : base_mass;
+  }
+  // the slot's values, selected without indexing the register arrays by a
+  // runtime value (that would move them to scratch memory)
+  float vu = 0.0f;
+  double iu = 0.0;
+  u32x4 tu = tv[0], du = tv[0];
+#pragma unroll
+  for (int u = 0; u < kN; ++u)
+    if (u == us) {
+      vu = vs[u];
+      iu = incl[u];
+      tu = tv[u];
+      if (sp.mode == 1) du = dv[u];
+    }
+  const double excl = at + (iu - static_cast<double>(vu));
+  const unsigned long long hit = __ballot(vu > 0.0f && excl + static_cast<double>(vu) > target_mass);
+  const unsigned long long has = __ballot(vu > 0.0f);
+  const int L = hit ? __ffsll(static_cast<long long>(hit)) - 1 : (has ? 63 - __clzll(static_cast<long long>(has)) : 0);
+  if (lane == L) {
+    float v[kV];
+    vals_of(tu, du, v);
+    double acc = excl;
+    int tok = -1, lastm = -1;
+#pragma unroll
+    for (int e = 0; e < kV; ++e) {
+      if (v[e] > 0.0f) {
+        lastm = e;
+        acc += static_cast<double>(v[e]);
+        if (tok < 0 && target_mass < acc) tok = e;
+      }
+    }
+    if (tok < 0) tok = lastm >= 0 ? lastm : 0;
+    *dst = static_cast<int32_t>(sub_tok + static_cast<long>(us * kWave + L) * kV + tok);
+  }
+}
+
 // The draw of request b at position sp.k from its sub-chunk masses, read
 // through mass(s, p) (p: the bonus row's mass of p, else the residual mass w);
 // with subs_per_wg > 0 only workgroup wg's sub-chunks are drawn from here;
@@ -2695,10 +2783,10 @@ __device__ __forceinline__ void tree_masses(const void *trow, const void *drow, 
 // Inverse CDF over the masses in sh.sub (of the same w as tree_masses): the
 // lowest token with mass whose running prefix exceeds u * W; if rounding
 // leaves none, the last token with mass.
-template <int DT>
-__device__ __forceinline__ int tree_select(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c, float negMp,
-                           float negMq, float r, bool use_q, float u, TreeShared &sh) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+// The sub-chunk of the draw (sh.pick), the mass before it (sh.red[0]) and the
+// target u W (sh.red[1]), by wave 0 from sh.sub / sh.W; every thread calls.
+__device__ __forceinline__ void tree_crossing(int NSUB, float u, TreeShared &sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
   if (tid < kWave) {  // wave 0: the lowest sub-chunk with mass whose inclusive prefix exceeds u W
     const double target = static_cast<double>(u) * sh.W;
     double run = 0.0, base = 0.0, base_last = 0.0;
@@ -2731,6 +2819,14 @@ __device__ __forceinline__ int tree_select(const void *trow, const void *drow, b
     }
   }
   __syncthreads();
+}
+
+// The token of the draw, read again from memory by one workgroup (the
+// crossing from tree_crossing): four contiguous tokens per thread.
+template <int DT>
+__device__ __forceinline__ int tree_select(const void *trow, const void *drow, int V, float c, float negMp,
+                                           float negMq, float r, bool use_q, TreeShared &sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int sub = sh.pick;
   const double base = sh.red[0], target = sh.red[1];
   __syncthreads();
@@ -2813,10 +2909,6 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     }
     sh.parent[n] = pa;
     sh.token[n] = x;
-  }
-  if (lead) {
-    for (int t = tid; t <= Nmax; t += kTBlock) out_tokens[static_cast<long>(b) * (Nmax + 1) + t] = -1;
-    for (int t = tid; t < Nmax; t += kTBlock) out_nodes[static_cast<long>(b) * Nmax + t] = -1;
   }
   __syncthreads();
   const size_t eb = Elem<DT>::kBytes;
@@ -2938,10 +3030,31 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
         const float r = use_q ? static_cast<float>(cc * sp / sq) : 0.0f;
         if (!masses_current)
           tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q, rs, sh, tm);
-        if (lead) {  // uniform per workgroup
-          const int tok = tree_select<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q,
-                                          u_sample[b], sh);
-          if (tid == 0) out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = tok;
+        // every workgroup finds the crossing from the same masses; the wave that
+        // holds that sub-chunk in registers draws from them, else the lead
+        // workgroup reads it again
+        tree_crossing(NSUB, u_sample[b], sh);
+        const int sub = sh.pick;
+        const int stride = tm.NW * kTWaves, nfast = al ? min(NSUB, V / kSub) : 0;
+        const bool held = DT == SV_BF16 && drow != nullptr && sub < nfast && sub + stride >= nfast;
+        int32_t *dst = out_tokens + static_cast<long>(b) * (Nmax + 1) + depth;
+        if (held) {
+          if (tm.w * kTWaves + wave == sub) {  // uniform per wave: this wave's rs holds the sub-chunk
+            SelParams sp;
+            sp.mode = use_q ? 1 : 2;
+            sp.k = depth;
+            sp.c = c;
+            sp.negMp = negMp;
+            sp.negMq = -static_cast<float>(Mq);
+            sp.r = r;
+            sp.ip = 0.0;
+            sp.tau_p = sp.tau_q = -INFINITY;
+            draw_held<DT, false>(rs.t, rs.d, sp, false, static_cast<long>(sub) * kSub, sh.red[0], sh.red[1], lane,
+                                 dst);
+          }
+        } else if (lead) {  // uniform per workgroup
+          const int tok = tree_select<DT>(trow, drow, V, c, negMp, -static_cast<float>(Mq), r, use_q, sh);
+          if (tid == 0) *dst = tok;
         }
         break;
       }
@@ -2955,7 +3068,14 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     pos = hit + 1;
     __syncthreads();
   }
-  if (lead && tid == 0) count[b] = depth;
+  // the padding after the last token and node, written last: the token at
+  // `depth` may come from another workgroup of the team, and a store of this
+  // workgroup to the same word could reach memory after it
+  if (lead) {
+    for (int t = depth + 1 + tid; t <= Nmax; t += kTBlock) out_tokens[static_cast<long>(b) * (Nmax + 1) + t] = -1;
+    for (int t = depth + tid; t < Nmax; t += kTBlock) out_nodes[static_cast<long>(b) * Nmax + t] = -1;
+    if (tid == 0) count[b] = depth;
+  }
 }
 
 // ================================================================== small problems
