@@ -42,15 +42,17 @@ def tail_ok(buf, rows, fill):
     return bool(torch.all(buf[rows:] == fill).item())
 
 
+# V = 1000: requests of at most 12288 logits, verified by one workgroup each
+@pytest.mark.parametrize("V", [5003, 1000], ids=["two_kernels", "one_workgroup"])
 @pytest.mark.parametrize("entry", ["spec_verify", "spec_verify_ex", "spec_verify_filtered", "spec_verify_noalloc"])
-def test_no_write_past_the_outputs(entry):
+def test_no_write_past_the_outputs(entry, V):
     import oracle
     import rejection_sampling_verification_spec_amd as sv
     dev = torch.device("cuda:0")
     if entry in ("spec_verify", "spec_verify_noalloc"):
-        w = W.make_random(501, 6, 4, 5003, "bf16", temps=0.9, zipf=True)
+        w = W.make_random(501, 6, 4, V, "bf16", temps=0.9, zipf=True)
     else:
-        w = W.make_random(502, 7, 5, 4099, "bf16", temps=np.array([0, 1, 0.6, 1.3, 0, 1, 0.8], np.float32),
+        w = W.make_random(502, 7, 5, V - 904, "bf16", temps=np.array([0, 1, 0.6, 1.3, 0, 1, 0.8], np.float32),
                           lens=np.array([5, 0, 3, 5, 2, 4, 1], np.int32), zipf=True)
         w.scalar_temperature = None
     if entry == "spec_verify_filtered":

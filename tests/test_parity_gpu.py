@@ -354,16 +354,18 @@ def test_side_stream():
     check_parity(w, g, oracle.run_workload(w))
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("cfg", [2, 0], ids=["two_kernels", "one_workgroup"])
+def test_graph_replay_matches_eager(cfg):
     """The step captured in a HIP graph (as the benchmark replays it) equals the eager call on every replay."""
     import oracle
     import rejection_sampling_verification_spec_amd as sv
-    w = W.make_config(2)
+    w = W.make_config(cfg)
     dev = torch.device("cuda:0")
     t = w.to_torch(dev)
     count = torch.empty(w.B, dtype=torch.int32, device=dev)
     out = torch.empty((w.B, w.gamma + 1), dtype=torch.int32, device=dev)
-    ws = sv.new_workspace(sv.spec_verify_workspace_bytes(w.B, w.gamma, w.V, sv.SV_BF16), dev)
+    dt = sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32
+    ws = sv.new_workspace(sv.spec_verify_workspace_bytes(w.B, w.gamma, w.V, dt), dev)
     s = torch.cuda.Stream()
 
     def call():
