@@ -3079,8 +3079,10 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
 }
 
 // ================================================================== small problems
-// A request whose rows hold at most kSmElems logits in all ((2 gamma + 1) V)
-// is verified by one workgroup, in one kernel: its rows are read once into LDS
+// The same step as K1 + K2 (temperature softmax, acceptance test and first
+// rejection, residual or bonus draw; the pages' sections cited at the top of
+// this file) for a request whose rows hold at most kSmElems logits in all
+// ((2 gamma + 1) V): one workgroup, one kernel.  Its rows are read once into LDS
 // (one batch of loads), and the statistics, the decision and the draw follow
 // on chip, with no hand-over between workgroups and no second launch.  For
 // such rows the two-kernel path is a chain of launches and round trips over a
