@@ -3578,8 +3578,16 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 constexpr int kK1U = 8;                 // 16-byte vectors per thread per K1 tile
 constexpr long kK1TargetGroups = 4224;  // about 16 workgroups per CU on 256 CUs (a sweep)
+// Uniform greedy batches (max and index only, 90 registers): fewer, longer
+// workgroups.  Workload 3 greedy (384 target rows of 8 tiles): 768 workgroups
+// (2 chunks per row) 20.7-21.2 us per call, 1152 21.8, 1536 21.2-21.5, 3072
+// about 21.8.
+constexpr long kK1GreedyTargetGroups = 768;
 
-bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV_GAMMA_MAX) {
+// greedy_only: a uniform greedy batch, whose K1 grid covers the gamma + 1 target
+// rows of each request only; its chunks are sized for kK1GreedyTargetGroups.
+bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV_GAMMA_MAX,
+               bool greedy_only = false) {
   if (B < 1 || gamma < 0 || gamma > gamma_limit || V < 1) return false;
   if (dtype != SV_F32 && dtype != SV_BF16) return false;
   const int vec = dtype == SV_BF16 ? 8 : 4;
@@ -3591,7 +3599,9 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV
   const long vecs = (V + vec - 1) / vec;
   const long tile = static_cast<long>(kK1U) * kBlock;
   const long tiles_per_row = (vecs + tile - 1) / tile;
-  long NS = (kK1TargetGroups + slots / 2) / slots;
+  const long plan_slots = greedy_only ? static_cast<long>(B) * (gamma + 1) : slots;
+  const long target = greedy_only ? kK1GreedyTargetGroups : kK1TargetGroups;
+  long NS = (target + plan_slots / 2) / plan_slots;
   if (NS < 1) NS = 1;
   if (NS > tiles_per_row) NS = tiles_per_row;
   const long tiles_per_chunk = (tiles_per_row + NS - 1) / NS;
@@ -3599,9 +3609,7 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV
   NS = (tiles_per_row + tiles_per_chunk - 1) / tiles_per_chunk;  // every chunk non-empty
   P->NS = static_cast<int>(NS);
   P->k1_groups = slots * NS;
-  // greedy-only batches: the grid covers the target rows only, with the same
-  // chunks (one chunk per tile, 3072 workgroups instead of 1536 on workload 3
-  // greedy, measured 0.5 us slower)
+  // greedy-only batches: the grid covers the target rows only
   P->k1_groups_g = static_cast<long>(B) * (gamma + 1) * NS;
   P->NSUB = (V + kSub - 1) / kSub;
   // sub-chunks per wave in the mass pass: one (two, the second prefetched,
@@ -3801,7 +3809,7 @@ int dispatch(const void *target, const void *draft, const int32_t *tokens, const
              int dtype, int32_t *count, int32_t *out, void *ws, size_t ws_bytes, void *stream,
              const sv_debug *dbg) {
   Plan P;
-  if (!make_plan(B, gamma, V, dtype, &P)) return SV_EINVAL;
+  if (!make_plan(B, gamma, V, dtype, &P, SV_GAMMA_MAX, all_greedy && !temps)) return SV_EINVAL;
   if ((topk || topp) &&
       (!temps || V > SV_FILTER_MAX_V || static_cast<long>(B) * P.rows * kFBlock >= (1L << 32)))
     return SV_EINVAL;
