@@ -3132,7 +3132,8 @@ __global__ __launch_bounds__(kSmBlock) void k_small_verify(SmallArgs a) {
   // staged but never used.
   const int nt = (gamma + 1) * V, nd = gamma * V;
   const char *tb = static_cast<const char *>(a.target) + static_cast<long>(b) * nt * Elem<DT>::kBytes;
-  const char *db = static_cast<const char *>(a.draft) + static_cast<long>(b) * nd * Elem<DT>::kBytes;
+  const char *db =  // NULL for a batch that reads no draft row
+      a.draft ? static_cast<const char *>(a.draft) + static_cast<long>(b) * nd * Elem<DT>::kBytes : nullptr;
   float bt[kSmBatch], bd[kSmBatch];
 #pragma unroll
   for (int q = 0; q < kSmBatch; ++q) {
