@@ -3579,16 +3579,25 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 constexpr int kK1U = 8;                 // 16-byte vectors per thread per K1 tile
 constexpr long kK1TargetGroups = 4224;  // about 16 workgroups per CU on 256 CUs (a sweep)
+// Unfiltered verify calls: about 1408 workgroups, at least two chunks per row.
+// Workload 3 (704 rows of 8 tiles): 2 chunks per row (1408 workgroups) 45.6-46.2
+// us per call against 46.6-47.8 with 4 (2816); the ragged B = 128 batch (1920
+// row slots of 10 tiles) keeps 2 chunks per row (1 measured 76.8-77.0 us
+// against 75.0).
+constexpr long kK1VerifyTargetGroups = 1408;
 // Uniform greedy batches (max and index only, 90 registers): fewer, longer
 // workgroups.  Workload 3 greedy (384 target rows of 8 tiles): 768 workgroups
 // (2 chunks per row) 20.7-21.2 us per call, 1152 21.8, 1536 21.2-21.5, 3072
 // about 21.8.
 constexpr long kK1GreedyTargetGroups = 768;
 
-// greedy_only: a uniform greedy batch, whose K1 grid covers the gamma + 1 target
-// rows of each request only; its chunks are sized for kK1GreedyTargetGroups.
+// kind: the K1 grid the chunks are sized for (kPlanVerify and kPlanGreedy: an
+// unfiltered verify call, stochastic or mixed / a uniform greedy batch, whose K1
+// grid covers the gamma + 1 target rows of each request only).
+enum { kPlanDefault = 0, kPlanVerify = 1, kPlanGreedy = 2 };
 bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV_GAMMA_MAX,
-               bool greedy_only = false) {
+               int kind = kPlanDefault) {
+  const bool greedy_only = kind == kPlanGreedy;
   if (B < 1 || gamma < 0 || gamma > gamma_limit || V < 1) return false;
   if (dtype != SV_F32 && dtype != SV_BF16) return false;
   const int vec = dtype == SV_BF16 ? 8 : 4;
@@ -3601,9 +3610,10 @@ bool make_plan(int B, int gamma, int V, int dtype, Plan *P, int gamma_limit = SV
   const long tile = static_cast<long>(kK1U) * kBlock;
   const long tiles_per_row = (vecs + tile - 1) / tile;
   const long plan_slots = greedy_only ? static_cast<long>(B) * (gamma + 1) : slots;
-  const long target = greedy_only ? kK1GreedyTargetGroups : kK1TargetGroups;
+  const long target = greedy_only ? kK1GreedyTargetGroups
+                                  : (kind == kPlanVerify ? kK1VerifyTargetGroups : kK1TargetGroups);
   long NS = (target + plan_slots / 2) / plan_slots;
-  if (NS < 1) NS = 1;
+  if (NS < (kind == kPlanVerify ? 2 : 1)) NS = kind == kPlanVerify ? 2 : 1;
   if (NS > tiles_per_row) NS = tiles_per_row;
   const long tiles_per_chunk = (tiles_per_row + NS - 1) / NS;
   P->chunk_vecs = static_cast<int>(tiles_per_chunk * tile);
@@ -3810,7 +3820,8 @@ int dispatch(const void *target, const void *draft, const int32_t *tokens, const
              int dtype, int32_t *count, int32_t *out, void *ws, size_t ws_bytes, void *stream,
              const sv_debug *dbg) {
   Plan P;
-  if (!make_plan(B, gamma, V, dtype, &P, SV_GAMMA_MAX, all_greedy && !temps)) return SV_EINVAL;
+  const int plan_kind = (topk || topp) ? kPlanDefault : ((all_greedy && !temps) ? kPlanGreedy : kPlanVerify);
+  if (!make_plan(B, gamma, V, dtype, &P, SV_GAMMA_MAX, plan_kind)) return SV_EINVAL;
   if ((topk || topp) &&
       (!temps || V > SV_FILTER_MAX_V || static_cast<long>(B) * P.rows * kFBlock >= (1L << 32)))
     return SV_EINVAL;
@@ -3900,15 +3911,25 @@ void *scratch_address() {
   return g_scratch_ptr[dev];
 }
 
+// Workspace of an unfiltered verify call: the largest over the K1 grids that
+// dispatch may choose for it (0 for an invalid shape).
+size_t verify_total(int B, int gamma, int V, int dtype) {
+  size_t total = 0;
+  for (int kind : {kPlanDefault, kPlanVerify, kPlanGreedy}) {
+    Plan P;
+    if (!make_plan(B, gamma, V, dtype, &P, SV_GAMMA_MAX, kind)) return 0;
+    if (P.total > total) total = P.total;
+  }
+  return total;
+}
+
 }  // namespace
 
 // ================================================================== C ABI
 extern "C" {
 
 size_t spec_verify_workspace_bytes(int B, int gamma, int V, int dtype) {
-  Plan P;
-  if (!make_plan(B, gamma, V, dtype, &P)) return 0;
-  return P.total;
+  return verify_total(B, gamma, V, dtype);
 }
 
 int spec_verify(const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
@@ -3935,9 +3956,9 @@ int spec_verify_noalloc(const void *target_logits, const void *draft_logits, con
                         const float *u_accept, const float *u_sample, float temperature, int B, int gamma,
                         int V, int dtype, int32_t *accepted_count, int32_t *out_tokens, void *stream) {
   if (!(temperature >= 0.0f) || isinf(temperature)) return SV_EINVAL;
-  Plan P;
-  if (!make_plan(B, gamma, V, dtype, &P)) return SV_EINVAL;
-  if (P.total > static_cast<size_t>(SV_NOALLOC_SCRATCH_BYTES)) return SV_ESCRATCH;
+  const size_t total = verify_total(B, gamma, V, dtype);
+  if (total == 0) return SV_EINVAL;
+  if (total > static_cast<size_t>(SV_NOALLOC_SCRATCH_BYTES)) return SV_ESCRATCH;
   void *ws = scratch_address();
   if (!ws) return SV_EHIP;
   return dispatch(target_logits, draft_logits, draft_tokens, u_accept, u_sample, nullptr, temperature,
