@@ -101,6 +101,17 @@ __device__ __forceinline__ float load_one(const void *row, long e) {
   }
 }
 
+// Element e of a row as raw bits (bf16: zero-extended), and their value.
+template <int DT>
+__device__ __forceinline__ unsigned load_bits(const void *row, long e) {
+  if constexpr (DT == SV_F32) return static_cast<const unsigned *>(row)[e];
+  else return static_cast<unsigned>(static_cast<const uint16_t *>(row)[e]);
+}
+template <int DT>
+__device__ __forceinline__ float bits_value(unsigned v) {
+  return __uint_as_float(DT == SV_F32 ? v : v << 16);
+}
+
 // One aligned 16-byte vector starting at element e0.
 template <int DT>
 __device__ __forceinline__ void load_vec(const void *row, long e0, float *x) {
@@ -2585,7 +2596,7 @@ __global__ __launch_bounds__(kFBlock) void k_filter_general(
 // the inverse CDF with u_sample.  T == 0 follows the first child equal to the
 // target arg-max.
 //
-// k_tree_walk: NW 512-thread workgroups per request walk its tree together.
+// k_tree_walk: NW 256-thread workgroups per request walk its tree together.
 // Every workgroup takes the same decisions (row statistics from K1's partials,
 // the acceptance ratio in fp64 from the two gathered logits, all merged and
 // summed in a fixed order); each rejection costs one pass over the position's
@@ -2596,9 +2607,23 @@ __global__ __launch_bounds__(kFBlock) void k_filter_general(
 // carry the pass number and adds the masses in the same order, so Z is the
 // same everywhere.  Workgroup 0 writes the outputs and draws the final token.
 // With NW = 1 (large batches) the masses stay in LDS, in fp64.
-constexpr int kTBlock = 512;
+// The walk's workgroup barrier orders LDS only.  Its threads share nothing
+// else through memory (the team's words are device-scope atomics), and a full
+// barrier would wait for every global load the wave has in flight, such as the
+// row slices requested for the passes to come.
+__device__ __forceinline__ void tree_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima, 7 and 15)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+constexpr int kTBlock = 256;
 constexpr int kTWaves = kTBlock / kWave;
 constexpr int kTMaxSub = SV_TREE_MAX_V / kSub;
+constexpr int kTMaxNS = 2 * kWave;  // chunks per row: at most 128 (V <= 2^20 fp32 is 128 K1 tiles)
 static_assert(SV_TREE_MAX_NODES <= kTBlock, "one thread per node in the child compaction");
 
 struct TreeShared {
@@ -2611,22 +2636,23 @@ struct TreeShared {
   double cratio[SV_TREE_MAX_NODES];  // p(x) / q(x) at each child (inf: q(x) = 0 < p(x); nan: both 0)
   int wcnt[kTWaves];
   int nchild;
+  Partial part[2][kTMaxNS];   // chunk partials of the position's target and draft rows
   double sub[kTMaxSub];       // sub-chunk masses of the current distribution
   double red[2 + kTWaves];
   double W;                   // their sum
   int pick, last;             // selection results
+  int path[SV_TREE_MAX_NODES];  // the accepted nodes, in walk order
 };
 
 // (M, s) of a stochastic row, or (max, lowest arg-max) of a greedy one, from
-// K1's chunk partials merged in chunk order.
-__device__ __forceinline__ void merged_row(const Partial *part, long slot, int NS, bool greedy, int &M, double &s,
-                                           int &arg) {
+// K1's chunk partials (staged in LDS) merged in chunk order.
+__device__ __forceinline__ void merged_row(const Partial *part, int NS, bool greedy, int &M, double &s, int &arg) {
   M = kEmptyM;
   s = 0.0;
   float mx = -INFINITY, v = -INFINITY;
   int ix = 0x7fffffff;
   for (int j = 0; j < NS; ++j) {
-    const Partial q = part[slot * NS + j];
+    const Partial q = part[j];
     if (greedy) merge_arg(v, ix, q.mx, q.mi);
     else merge_sm(M, s, mx, q.mi, q.s, q.mx);
   }
@@ -2767,9 +2793,9 @@ __device__ __forceinline__ void tree_masses_of(const void *trow, const void *dro
     }
     ++tm.pass;
   }
-  __syncthreads();
+  tree_barrier();
   tree_total(NSUB, sh);
-  __syncthreads();
+  tree_barrier();
 }
 
 template <int DT>
@@ -2818,7 +2844,7 @@ __device__ __forceinline__ void tree_crossing(int NSUB, float u, TreeShared &sh)
       sh.red[1] = target;
     }
   }
-  __syncthreads();
+  tree_barrier();
 }
 
 // The token of the draw, read again from memory by one workgroup (the
@@ -2829,7 +2855,7 @@ __device__ __forceinline__ int tree_select(const void *trow, const void *drow, i
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int sub = sh.pick;
   const double base = sh.red[0], target = sh.red[1];
-  __syncthreads();
+  tree_barrier();
   // four contiguous tokens per thread, in token order through waves and lanes
   constexpr int kPer = kSub / kTBlock;
   const long first = static_cast<long>(sub) * kSub + static_cast<long>(tid) * kPer;
@@ -2848,14 +2874,14 @@ __device__ __forceinline__ int tree_select(const void *trow, const void *drow, i
   }
   const double incl = wave_scan(lsum, lane);
   if (lane == kWave - 1) sh.red[2 + wave] = incl;  // red[2 .. 2 + kTWaves) is free after the broadcast
-  __syncthreads();
+  tree_barrier();
   double before = base;
   for (int q = 0; q < wave; ++q) before += sh.red[2 + q];
   if (tid == 0) {
     sh.pick = 0x7fffffff;
     sh.last = -1;
   }
-  __syncthreads();
+  tree_barrier();
   double acc = before + (incl - lsum);
   int cand = -1, lastp = -1;
 #pragma unroll
@@ -2868,10 +2894,10 @@ __device__ __forceinline__ int tree_select(const void *trow, const void *drow, i
   }
   if (cand >= 0) atomicMin(&sh.pick, cand);
   if (lastp >= 0) atomicMax(&sh.last, lastp);
-  __syncthreads();
+  tree_barrier();
   int tok = sh.pick;
   if (tok == 0x7fffffff) tok = sh.last >= 0 ? sh.last : static_cast<int>(static_cast<long>(sub) * kSub);
-  __syncthreads();
+  tree_barrier();
   return tok;
 }
 
@@ -2881,11 +2907,13 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     const int32_t *__restrict__ tokens, const int32_t *__restrict__ num_nodes, const float *__restrict__ u_accept,
     const float *__restrict__ u_sample, const float *__restrict__ temps, int Nmax, int V, int NS,
     const Partial *__restrict__ part, int32_t *__restrict__ count, int32_t *__restrict__ out_tokens,
-    int32_t *__restrict__ out_nodes, int NW, unsigned long long *__restrict__ tsub, unsigned *__restrict__ terr) {
+    int32_t *__restrict__ out_nodes, int NW, unsigned long long *__restrict__ tsub, unsigned *__restrict__ terr,
+    const void *__restrict__ spare) {
   const int b = blockIdx.x / NW, tid = threadIdx.x;
   const int rows = 2 * Nmax + 1;
   const int N = request_len(num_nodes, Nmax, b);
   const float T = temps[b];
+  const float us = u_sample[b];
   const bool greedy = !(T > 0.0f);
   const float c = greedy ? 0.0f : temp_scale(T);
   const int NSUB = (V + kSub - 1) / kSub;
@@ -2910,7 +2938,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     sh.parent[n] = pa;
     sh.token[n] = x;
   }
-  __syncthreads();
+  tree_barrier();
   const size_t eb = Elem<DT>::kBytes;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   int pos = 0, depth = 0;
@@ -2919,65 +2947,103 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     const void *drow = pos < Nmax ? static_cast<const char *>(draft) + (static_cast<long>(b) * Nmax + pos) * V * eb
                                   : nullptr;  // position Nmax has no child
     const bool al = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;
-    // the wave's sub-chunk of the position's row pair, requested now (the round
-    // trip overlaps the row statistics and the children's logits below) and
-    // kept for every pass at this position, when each wave has at most one
-    RowSlice<DT> rs;
-    {
-      const int gw = tm.w * kTWaves + wave, stride = tm.NW * kTWaves;
-      const int nfast = al ? min(NSUB, V / kSub) : 0;
-      // (bf16 only: an fp32 slice is twice the registers and made the kernel spill)
-      rs.valid = DT == SV_BF16 && !greedy && drow != nullptr && gw < nfast && gw + stride >= nfast;
-      if (rs.valid) {  // uniform per wave
-        load_lane_fast<DT>(trow, static_cast<long>(gw) * kSub, lane, rs.t);
-        load_lane_fast<DT>(drow, static_cast<long>(gw) * kSub, lane, rs.d);
-      }
-    }
-    // the position's children in node order (a block-wide compaction); then, in
-    // one round trip, the row statistics (target by thread 0, draft by the
-    // first lane of wave 1) and each child's two logits and uniform (threads
-    // 128 + j)
+    // the position's children in node order (a block-wide compaction)
     const bool is_child = tid < N && tid >= pos && sh.parent[tid] == pos - 1;
     const unsigned long long mask = __ballot(is_child);
     if (lane == 0) sh.wcnt[wave] = __popcll(mask);
-    __syncthreads();
+    tree_barrier();
     int nchild = 0, before = 0;
     for (int w = 0; w < kTWaves; ++w) {
       if (w < wave) before += sh.wcnt[w];
       nchild += sh.wcnt[w];
     }
     if (is_child) sh.child[before + __popcll(mask & ((1ull << lane) - 1ull))] = tid;
-    __syncthreads();
+    tree_barrier();
+    // then everything the position needs, requested together (one round trip):
+    // the chunk partials of its two rows (wave 0: the target row, wave 1: the
+    // draft row; lane j: chunks j and j + 64), each child's two logits and its
+    // uniform (the other waves, a thread per child and, past their count, a
+    // second), and every wave's sub-chunk of the row pair, kept in registers
+    // for the passes at this position when each wave has at most one
+    const bool want_part = wave == 0 || (wave == 1 && !greedy && pos < N);
+    u32x4 pv0 = {0u, 0u, 0u, 0u}, pv1 = {0u, 0u, 0u, 0u};  // the records as raw 16-byte vectors
+    if (want_part) {
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(part) +
+                         (static_cast<long>(b) * rows + (wave == 0 ? pos : Nmax + 1 + pos)) * NS;
+      if (lane < NS) pv0 = src[lane];
+      if (lane + kWave < NS) pv1 = src[lane + kWave];
+    }
+    constexpr int kGather = kTBlock - 2 * kWave;  // threads that gather children
+    static_assert(2 * kGather >= SV_TREE_MAX_NODES, "at most two children per gathering thread");
+    const int jc = tid - 2 * kWave;
+    unsigned zc[2][3];  // raw bits: nothing waits for them before the stores below
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = jc + h * kGather;
+      zc[h][0] = zc[h][1] = 0u;
+      zc[h][2] = __float_as_uint(2.0f);  // 2 rejects
+      if (!greedy && jc >= 0 && j < nchild) {
+        const int n = sh.child[j], x = sh.token[n];
+        if (x >= 0 && x < V) {  // an id outside the vocabulary is rejected, never dereferenced
+          zc[h][0] = load_bits<DT>(trow, x);
+          zc[h][1] = load_bits<DT>(drow, x);
+          zc[h][2] = __float_as_uint(u_accept[static_cast<long>(b) * Nmax + n]);
+        }
+      }
+    }
+    RowSlice<DT> rs;
+    {
+      const int gw = tm.w * kTWaves + wave, stride = tm.NW * kTWaves;
+      const int nfast = al ? min(NSUB, V / kSub) : 0;
+      // (bf16 only: an fp32 slice is twice the registers)
+      rs.valid = DT == SV_BF16 && !greedy && drow != nullptr && gw < nfast && gw + stride >= nfast;
+      if constexpr (DT == SV_BF16) {
+        // unconditional loads (from the workspace's spare block when the wave
+        // holds no slice), so that waiting for the loads above never waits
+        // for these
+        const void *ts = rs.valid ? trow : spare, *ds = rs.valid ? drow : spare;
+        const long off = rs.valid ? static_cast<long>(gw) * kSub : 0;
+        load_lane_fast<DT>(ts, off, lane, rs.t);
+        load_lane_fast<DT>(ds, off, lane, rs.d);
+      }
+    }
+    if (want_part) {
+      u32x4 *dst = reinterpret_cast<u32x4 *>(sh.part[wave]);
+      if (lane < NS) dst[lane] = pv0;
+      if (lane + kWave < NS) dst[lane + kWave] = pv1;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = jc + h * kGather;
+      if (!greedy && jc >= 0 && j < nchild) {
+        sh.czp[j] = bits_value<DT>(zc[h][0]);
+        sh.czq[j] = bits_value<DT>(zc[h][1]);
+        sh.cu[j] = __uint_as_float(zc[h][2]);
+      }
+    }
+    tree_barrier();
+    // the two rows' statistics (target by thread 0, draft by the first lane of wave 1)
     if (tid == 0) {
       int M, arg;
       double s;
-      merged_row(part, static_cast<long>(b) * rows + pos, NS, greedy, M, s, arg);
+      merged_row(sh.part[0], NS, greedy, M, s, arg);
       s_Mp = M;
       s_sp = s;
       s_arg = arg;
     }
     if (tid == kWave && !greedy && pos < N) {
       int arg;
-      merged_row(part, static_cast<long>(b) * rows + Nmax + 1 + pos, NS, false, s_Mq, s_sq, arg);
+      merged_row(sh.part[1], NS, false, s_Mq, s_sq, arg);
     }
-    static_assert(2 * kWave + SV_TREE_MAX_NODES <= kTBlock, "a thread per child after the first two waves");
-    const int jc = tid - 2 * kWave;
-    if (!greedy && jc >= 0 && jc < nchild) {  // gather each child's two logits and its uniform
-      const int n = sh.child[jc], x = sh.token[n];
-      const bool ok = x >= 0 && x < V;  // an id outside the vocabulary is rejected, never dereferenced
-      sh.czp[jc] = ok ? load_one<DT>(trow, x) : 0.0f;
-      sh.czq[jc] = ok ? load_one<DT>(drow, x) : 0.0f;
-      sh.cu[jc] = ok ? u_accept[static_cast<long>(b) * Nmax + n] : 2.0f;  // 2 rejects
-    }
-    __syncthreads();
+    tree_barrier();
     // every child's p(x)/q(x) at once, one exponential each:
     // 2^((zp - zq) c - (Mp - Mq)) * s'_q / s'_p (the logit difference is exact)
-    if (!greedy && jc >= 0 && jc < nchild) {
-      const double d = (static_cast<double>(sh.czp[jc]) - static_cast<double>(sh.czq[jc])) * static_cast<double>(c) -
+    for (int j = tid; !greedy && j < nchild; j += kTBlock) {
+      const double d = (static_cast<double>(sh.czp[j]) - static_cast<double>(sh.czq[j])) * static_cast<double>(c) -
                        static_cast<double>(s_Mp - s_Mq);
-      sh.cratio[jc] = exp2(d) * (s_sq / s_sp);
+      sh.cratio[j] = exp2(d) * (s_sq / s_sp);
     }
-    __syncthreads();
+    tree_barrier();
     int hit = -1;
     if (greedy) {
       if (tid == 0) {
@@ -2985,7 +3051,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
           if (sh.token[sh.child[j]] == s_arg) hit = sh.child[j];
         s_hit = hit;
       }
-      __syncthreads();
+      tree_barrier();
       hit = s_hit;
       if (hit < 0) {
         if (lead && tid == 0) out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = s_arg;
@@ -3006,9 +3072,9 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
           const double a = fmin(1.0, fmax(0.0, ratio - cc) / Z);
           s_hit = static_cast<double>(sh.cu[j]) < a ? sh.child[j] : -1;
         }
-        __syncthreads();
+        tree_barrier();
         hit = s_hit;
-        __syncthreads();
+        tree_barrier();
         if (hit >= 0) break;
         // rejected: the next target is max(0, p - (cc + Z) q) / Z'
         cc += Z;
@@ -3033,7 +3099,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
         // every workgroup finds the crossing from the same masses; the wave that
         // holds that sub-chunk in registers draws from them, else the lead
         // workgroup reads it again
-        tree_crossing(NSUB, u_sample[b], sh);
+        tree_crossing(NSUB, us, sh);
         const int sub = sh.pick;
         const int stride = tm.NW * kTWaves, nfast = al ? min(NSUB, V / kSub) : 0;
         const bool held = DT == SV_BF16 && drow != nullptr && sub < nfast && sub + stride >= nfast;
@@ -3059,19 +3125,25 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
         break;
       }
     }
-    // accepted node `hit`: emit it and move to its position
-    if (lead && tid == 0) {
-      out_tokens[static_cast<long>(b) * (Nmax + 1) + depth] = sh.token[hit];
-      out_nodes[static_cast<long>(b) * Nmax + depth] = hit;
-    }
+    // accepted node `hit`: the path is kept in LDS (written out after the walk)
+    if (lead && tid == 0) sh.path[depth] = hit;
     ++depth;
     pos = hit + 1;
-    __syncthreads();
+    // Every load of this position has long arrived (a row slice no pass used,
+    // at the latest); waiting for them here lets the next position's waits
+    // count only its own loads.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    tree_barrier();
   }
-  // the padding after the last token and node, written last: the token at
-  // `depth` may come from another workgroup of the team, and a store of this
-  // workgroup to the same word could reach memory after it
+  // the accepted path, then the padding after the last token and node, written
+  // last: the token at `depth` may come from another workgroup of the team, and
+  // a store of this workgroup to the same word could reach memory after it
   if (lead) {
+    for (int t = tid; t < depth; t += kTBlock) {
+      const int n = sh.path[t];
+      out_tokens[static_cast<long>(b) * (Nmax + 1) + t] = sh.token[n];
+      out_nodes[static_cast<long>(b) * Nmax + t] = n;
+    }
     for (int t = depth + 1 + tid; t <= Nmax; t += kTBlock) out_tokens[static_cast<long>(b) * (Nmax + 1) + t] = -1;
     for (int t = depth + tid; t < Nmax; t += kTBlock) out_nodes[static_cast<long>(b) * Nmax + t] = -1;
     if (tid == 0) count[b] = depth;
@@ -3852,7 +3924,7 @@ constexpr int kMaxDevices = 64;
 // The tree call's workspace: the linear plan, then two copies of each
 // request's sub-chunk mass words (K1 clears them), and the walk's error word.
 struct TreeLayout {
-  size_t sub_off, err_off, total;
+  size_t sub_off, err_off, spare_off, total;
 };
 
 TreeLayout tree_layout(int B, const Plan &P) {
@@ -3862,6 +3934,8 @@ TreeLayout tree_layout(int B, const Plan &P) {
   off = align_up(off + sizeof(unsigned long long) * 2 * static_cast<size_t>(B) * P.NSUB);
   L.err_off = off;
   off = align_up(off + sizeof(unsigned));
+  L.spare_off = off;  // a block the walk's unused row-slice loads read (contents never used)
+  off = align_up(off + sizeof(float) * kSub);
   L.total = off;
   return L;
 }
@@ -4011,6 +4085,7 @@ int spec_verify_tree(const void *target_logits, const void *draft_logits, const 
   Plan P;
   if (max_nodes < 0 || V > SV_TREE_MAX_V || !make_plan(B, max_nodes, V, dtype, &P, SV_TREE_MAX_NODES))
     return SV_EINVAL;
+  if (P.NS > kTMaxNS) return SV_EINVAL;  // the walk stages a row's chunk partials in LDS
   if (!target_logits || !u_sample || !temperature || !accepted_count || !out_tokens) return SV_EINVAL;
   if (max_nodes > 0 && (!draft_logits || !node_parent || !node_tokens || !u_accept || !out_nodes))
     return SV_EINVAL;
@@ -4032,7 +4107,7 @@ int spec_verify_tree(const void *target_logits, const void *draft_logits, const 
     hipLaunchKernelGGL((k_tree_walk<SV_BF16>), dim3(static_cast<unsigned>(static_cast<long>(B) * NW)),
                        dim3(kTBlock), 0, st, target_logits, draft_logits, node_parent, node_tokens, num_nodes,
                        u_accept, u_sample, temperature, max_nodes, V, P.NS, part, accepted_count, out_tokens,
-                       out_nodes, NW, tsub, terr);
+                       out_nodes, NW, tsub, terr, base + L.spare_off);
   } else {
     e = launch_k1<SV_F32>(target_logits, draft_logits, node_tokens, temperature, 0.0f, num_nodes, max_nodes, V, P,
                           part, zx, st, nullptr, nullptr, nullptr, tsub, 2 * P.NSUB);
@@ -4041,7 +4116,7 @@ int spec_verify_tree(const void *target_logits, const void *draft_logits, const 
     hipLaunchKernelGGL((k_tree_walk<SV_F32>), dim3(static_cast<unsigned>(static_cast<long>(B) * NW)),
                        dim3(kTBlock), 0, st, target_logits, draft_logits, node_parent, node_tokens, num_nodes,
                        u_accept, u_sample, temperature, max_nodes, V, P.NS, part, accepted_count, out_tokens,
-                       out_nodes, NW, tsub, terr);
+                       out_nodes, NW, tsub, terr, base + L.spare_off);
   }
   return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
