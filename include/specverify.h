@@ -229,7 +229,13 @@ int spec_verify_filtered(const void *target_logits, const void *draft_logits,
  * A parent outside [-1, n) makes the node nobody's child; a token outside
  * [0, V) is rejected when tested and never dereferenced.  0 <= max_nodes <=
  * SV_TREE_MAX_NODES, V <= SV_TREE_MAX_V.  The workspace is sized by
- * spec_verify_tree_workspace_bytes. */
+ * spec_verify_tree_workspace_bytes.
+ * Row statistics: with max_nodes >= 16 the walk computes them for the
+ * positions it visits only (two launches: a clear of the exchange words, the
+ * walk); smaller trees take them from one streaming pass over every row, then
+ * walk.  The environment variable SPECVERIFY_TREE_STATS, read on each call,
+ * forces one way ("walk" or "rows"; for testing): the results agree to
+ * rounding either way. */
 size_t spec_verify_tree_workspace_bytes(int B, int max_nodes, int V, int dtype);
 
 int spec_verify_tree(const void *target_logits, const void *draft_logits,

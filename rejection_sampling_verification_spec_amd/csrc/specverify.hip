@@ -62,6 +62,7 @@
 #include <limits.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -2621,6 +2622,10 @@ __device__ __forceinline__ void tree_barrier() {
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 constexpr int kTBlock = 256;
+// Trees of at least this many nodes take their row statistics from the walk
+// itself (only the positions it visits: a path of a wide tree is a small share
+// of its rows); smaller trees take them from K1 over every row.
+constexpr int kTreeOnDemandNodes = 16;
 constexpr int kTWaves = kTBlock / kWave;
 constexpr int kTMaxSub = SV_TREE_MAX_V / kSub;
 constexpr int kTMaxNS = 2 * kWave;  // chunks per row: at most 128 (V <= 2^20 fp32 is 128 K1 tiles)
@@ -2642,6 +2647,8 @@ struct TreeShared {
   double W;                   // their sum
   int pick, last;             // selection results
   int path[SV_TREE_MAX_NODES];  // the accepted nodes, in walk order
+  int wsA[2][kTMaxSub];         // per-wave row statistics (target, draft): M or arg-max,
+  float wsB[2][kTMaxSub];       // and s or the maximum (statistics on demand)
 };
 
 // (M, s) of a stochastic row, or (max, lowest arg-max) of a greedy one, from
@@ -2683,10 +2690,12 @@ __device__ __forceinline__ float tree_lane_mass(const u32x4 *tp, const u32x4 *dq
 
 // How the request's workgroups share a pass and meet after it.
 struct TreeTeam {
-  int w, NW;                // this workgroup, workgroups per request
-  unsigned long long *sub;  // [2][NSUB] per-request mass words (NW > 1), cleared by K1
-  unsigned *err;            // set if a bounded wait ran out
-  int pass;                 // passes done so far in this call
+  int w, NW;                 // this workgroup, workgroups per request
+  unsigned long long *sub;   // [2][NSUB] per-request mass words (NW > 1), cleared before the walk
+  unsigned long long *stat;  // [2][Wmax][4] per-request row-statistics words (statistics on demand)
+  int Wmax;                  // waves a team can have (the words' stride)
+  unsigned *err;             // set if a bounded wait ran out
+  int pass;                  // exchanges done so far in this call
 };
 
 // A sub-chunk mass as the team exchanges it: pass number (from 1) in the high
@@ -2901,14 +2910,188 @@ __device__ __forceinline__ int tree_select(const void *trow, const void *drow, i
   return tok;
 }
 
+// A lane's tokens of one sub-chunk (interleaved layout, base = its first
+// token): the largest value and its lowest index folded into (v, i); the first
+// token is taken even when it is -inf, so an all -inf row yields index 0.
 template <int DT>
+__device__ __forceinline__ void lane_argmax(const u32x4 *raw, long base, int lane, float &v, int &i) {
+  constexpr int kV = Elem<DT>::kVec;
+#pragma unroll
+  for (int u = 0; u < kLaneElems / kV; ++u) {
+    float x[kV];
+    widen_vec<DT>(raw[u], x);
+#pragma unroll
+    for (int e = 0; e < kV; ++e) {
+      const int idx = static_cast<int>(base + static_cast<long>(u * kWave + lane) * kV + e);
+      if (x[e] > v || i == INT_MAX) {
+        v = x[e];
+        i = idx;
+      }
+    }
+  }
+}
+
+// A team-exchanged statistic: the exchange number in the high half, 32 bits of
+// payload (an int, or a float's bits) in the low half.
+__device__ __forceinline__ unsigned long long stat_word(int stamp, unsigned bits) {
+  return (static_cast<unsigned long long>(static_cast<unsigned>(stamp)) << 32) | bits;
+}
+
+// The statistics of a position's rows, computed by the team (no K1): each wave
+// folds its sub-chunks of the target row (and of the draft row when need_q) as
+// K1 folds a tile, its lanes merge with DPP (the largest M, each sum rescaled to
+// it by an exact power of two, one fp64 sum; greedy: the maximum, then the
+// lowest index holding it), and the waves' results go to every workgroup of
+// the team (tagged words, or LDS when the team is one workgroup), which merges
+// them in wave order: (M, s) into sh.wsA/wsB, then the caller's merge.  The
+// sub-chunks are shared out as in tree_masses_of; the wave's one fast
+// sub-chunk is taken from its registers (rs) when it has them.
+template <int DT>
+__device__ __forceinline__ int tree_stats(const void *trow, const void *drow, bool al, int V, int NSUB, float c,
+                                          bool greedy, bool need_q, const RowSlice<DT> &rs, TreeShared &sh,
+                                          TreeTeam &tm) {
+  constexpr int kN = kLaneElems / Elem<DT>::kVec;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int gw = tm.w * kTWaves + wave, stride = tm.NW * kTWaves;
+  const int nfast = al ? min(NSUB, V / kSub) : 0;
+  const int nwv = min(stride, NSUB);  // waves that hold a sub-chunk
+  int Mt = kEmptyM, Mq = kEmptyM;
+  double st = 0.0, sq = 0.0;
+  float mt = -INFINITY, mq = -INFINITY;
+  float gv = -INFINITY;
+  int gi = INT_MAX;
+  auto fold = [&](const u32x4 *tv, const u32x4 *dv, long base) {
+    if (greedy) {
+      lane_argmax<DT>(tv, base, lane, gv, gi);
+    } else {
+      fold_tile<DT, kN>(tv, c, Mt, st, mt);
+      if (need_q) fold_tile<DT, kN>(dv, c, Mq, sq, mq);
+    }
+  };
+  if (rs.valid) {  // uniform per wave
+    fold(rs.t, rs.d, static_cast<long>(gw) * kSub);
+  } else {
+    for (int j = gw; j < nfast; j += stride) {
+      u32x4 tv[kN], dv[kN];
+      load_lane_fast<DT>(trow, static_cast<long>(j) * kSub, lane, tv);
+      if (need_q) load_lane_fast<DT>(drow, static_cast<long>(j) * kSub, lane, dv);
+      fold(tv, dv, static_cast<long>(j) * kSub);
+    }
+  }
+  for (int j = nfast + gw; j < NSUB; j += stride) {
+    u32x4 tv[kN], dv[kN];
+    load_lane_raw<DT>(trow, al, static_cast<long>(j) * kSub, lane, V, tv);
+    if (need_q) load_lane_raw<DT>(drow, al, static_cast<long>(j) * kSub, lane, V, dv);
+    fold(tv, dv, static_cast<long>(j) * kSub);
+  }
+  // the wave's results: (A, B) = (M, s) or (arg-max, max) per row
+  int A0, A1 = kEmptyM;
+  float B0, B1 = 0.0f;
+  if (greedy) {
+    const float vm = wave_max_f32(gv);
+    A0 = wave_ext_i32<false>(gv == vm ? gi : INT_MAX);
+    B0 = vm;
+  } else {
+    A0 = wave_ext_i32<true>(Mt);
+    B0 = static_cast<float>(wave_sum(ldexp(st, Mt - A0)));
+    if (need_q) {
+      A1 = wave_ext_i32<true>(Mq);
+      B1 = static_cast<float>(wave_sum(ldexp(sq, Mq - A1)));
+    }
+  }
+  const int nk = need_q ? 4 : 2;  // words per wave
+  if (tm.NW > 1) {
+    unsigned long long *wd = tm.stat + static_cast<long>(tm.pass & 1) * tm.Wmax * 4;
+    const int stamp = tm.pass + 1;
+    if (lane == 0 && gw < nwv) {
+      put<true>(wd + gw * 4 + 0, stat_word(stamp, static_cast<unsigned>(A0)));
+      put<true>(wd + gw * 4 + 1, stat_word(stamp, __float_as_uint(B0)));
+      if (need_q) {
+        put<true>(wd + gw * 4 + 2, stat_word(stamp, static_cast<unsigned>(A1)));
+        put<true>(wd + gw * 4 + 3, stat_word(stamp, __float_as_uint(B1)));
+      }
+    }
+    // wave 0 polls the team's words until each carries this exchange's number
+    // (bounded: if one never arrives the error word is set); the two copies
+    // alternate between exchanges as the mass words do
+    if (wave == 0) {  // lane l polls the words of waves l, l + 64, ..., all of a wave's words at once
+      for (int w0 = 0; w0 < nwv; w0 += kWave) {
+        const int w = w0 + lane;
+        const bool mine = w < nwv;
+        unsigned long long word[4] = {0ull, 0ull, 0ull, 0ull};
+        for (unsigned it = 0;; ++it) {
+          bool ready = true;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if (mine && k < nk) word[k] = get<true>(wd + w * 4 + k);
+            ready = ready && (!mine || k >= nk || static_cast<int>(word[k] >> 32) == stamp);
+          }
+          if (__all(ready)) break;
+          if (it >= kSpinLimit) {
+            if (lane == 0) put<true>(tm.err, 1u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (mine) {
+          sh.wsA[0][w] = static_cast<int>(static_cast<unsigned>(word[0]));
+          sh.wsB[0][w] = __uint_as_float(static_cast<unsigned>(word[1]));
+          sh.wsA[1][w] = static_cast<int>(static_cast<unsigned>(word[2]));
+          sh.wsB[1][w] = __uint_as_float(static_cast<unsigned>(word[3]));
+        }
+      }
+    }
+    ++tm.pass;
+  } else if (lane == 0 && gw < nwv) {
+    sh.wsA[0][gw] = A0;
+    sh.wsB[0][gw] = B0;
+    sh.wsA[1][gw] = A1;
+    sh.wsB[1][gw] = B1;
+  }
+  tree_barrier();
+  return nwv;
+}
+
+// The merged statistics of row t (0: target, 1: draft) from the per-wave
+// results in sh.wsA/wsB, by one wave (every lane calls; lane l takes waves l,
+// l + 64, ...): the same DPP merge as within a wave, 64 waves at a time.
+__device__ __forceinline__ void merged_waves(const TreeShared &sh, int t, int nwv, bool greedy, int lane, int &M,
+                                             double &s, int &arg) {
+  M = kEmptyM;
+  s = 0.0;
+  float mx = -INFINITY, v = -INFINITY;
+  int ix = INT_MAX;
+  for (int w0 = 0; w0 < nwv; w0 += kWave) {
+    const int w = w0 + lane;
+    const bool in = w < nwv;
+    if (greedy) {
+      const float b = in ? sh.wsB[t][w] : -INFINITY;
+      const float vm = wave_max_f32(b);
+      merge_arg(v, ix, vm, wave_ext_i32<false>(in && b == vm ? sh.wsA[t][w] : INT_MAX));
+    } else {
+      const int a = in ? sh.wsA[t][w] : kEmptyM;
+      const int Mw = wave_ext_i32<true>(a);
+      const double sw = wave_sum(in ? ldexp(static_cast<double>(sh.wsB[t][w]), a - Mw) : 0.0);
+      merge_sm(M, s, mx, Mw, sw, 0.0f);
+    }
+  }
+  arg = ix;
+}
+
+// Zeroes the walk's exchange words before a walk with statistics on demand.
+__global__ __launch_bounds__(kBlock) void k_tree_clear(unsigned long long *__restrict__ words, long n) {
+  for (long i = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += static_cast<long>(gridDim.x) * kBlock)
+    words[i] = 0ull;
+}
+
+template <int DT, bool OD>
 __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     const void *__restrict__ target, const void *__restrict__ draft, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ tokens, const int32_t *__restrict__ num_nodes, const float *__restrict__ u_accept,
     const float *__restrict__ u_sample, const float *__restrict__ temps, int Nmax, int V, int NS,
     const Partial *__restrict__ part, int32_t *__restrict__ count, int32_t *__restrict__ out_tokens,
     int32_t *__restrict__ out_nodes, int NW, unsigned long long *__restrict__ tsub, unsigned *__restrict__ terr,
-    const void *__restrict__ spare) {
+    const void *__restrict__ spare, unsigned long long *__restrict__ tstat, int Wmax) {
   const int b = blockIdx.x / NW, tid = threadIdx.x;
   const int rows = 2 * Nmax + 1;
   const int N = request_len(num_nodes, Nmax, b);
@@ -2919,11 +3102,14 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
   const int NSUB = (V + kSub - 1) / kSub;
   TreeTeam tm;
   tm.w = blockIdx.x - b * NW;
-  tm.NW = greedy ? 1 : NW;  // a greedy walk makes no pass: workgroup 0 alone
-  tm.sub = tsub + static_cast<long>(b) * 2 * NSUB;  // cleared by K1
+  // a greedy walk with K1's statistics makes no pass: workgroup 0 alone
+  tm.NW = (greedy && !OD) ? 1 : NW;
+  tm.sub = tsub + static_cast<long>(b) * 2 * NSUB;  // cleared before the walk
+  tm.stat = OD ? tstat + static_cast<long>(b) * 2 * Wmax * 4 : nullptr;
+  tm.Wmax = Wmax;
   tm.err = terr;
   tm.pass = 0;
-  if (greedy && tm.w > 0) return;  // uniform per workgroup
+  if (tm.w >= tm.NW) return;  // uniform per workgroup
   const bool lead = tm.w == 0;     // writes the outputs
   __shared__ TreeShared sh;
   __shared__ int s_hit, s_arg, s_Mp, s_Mq;
@@ -2965,7 +3151,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     // uniform (the other waves, a thread per child and, past their count, a
     // second), and every wave's sub-chunk of the row pair, kept in registers
     // for the passes at this position when each wave has at most one
-    const bool want_part = wave == 0 || (wave == 1 && !greedy && pos < N);
+    const bool want_part = !OD && (wave == 0 || (wave == 1 && !greedy && pos < N));
     u32x4 pv0 = {0u, 0u, 0u, 0u}, pv1 = {0u, 0u, 0u, 0u};  // the records as raw 16-byte vectors
     if (want_part) {
       const u32x4 *src = reinterpret_cast<const u32x4 *>(part) +
@@ -2996,12 +3182,12 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
       const int gw = tm.w * kTWaves + wave, stride = tm.NW * kTWaves;
       const int nfast = al ? min(NSUB, V / kSub) : 0;
       // (bf16 only: an fp32 slice is twice the registers)
-      rs.valid = DT == SV_BF16 && !greedy && drow != nullptr && gw < nfast && gw + stride >= nfast;
+      rs.valid = DT == SV_BF16 && (OD || (!greedy && drow != nullptr)) && gw < nfast && gw + stride >= nfast;
       if constexpr (DT == SV_BF16) {
         // unconditional loads (from the workspace's spare block when the wave
         // holds no slice), so that waiting for the loads above never waits
         // for these
-        const void *ts = rs.valid ? trow : spare, *ds = rs.valid ? drow : spare;
+        const void *ts = rs.valid ? trow : spare, *ds = rs.valid && drow && !greedy ? drow : spare;
         const long off = rs.valid ? static_cast<long>(gw) * kSub : 0;
         load_lane_fast<DT>(ts, off, lane, rs.t);
         load_lane_fast<DT>(ds, off, lane, rs.d);
@@ -3022,18 +3208,43 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
       }
     }
     tree_barrier();
-    // the two rows' statistics (target by thread 0, draft by the first lane of wave 1)
-    if (tid == 0) {
-      int M, arg;
-      double s;
-      merged_row(sh.part[0], NS, greedy, M, s, arg);
-      s_Mp = M;
-      s_sp = s;
-      s_arg = arg;
-    }
-    if (tid == kWave && !greedy && pos < N) {
-      int arg;
-      merged_row(sh.part[1], NS, false, s_Mq, s_sq, arg);
+    // the two rows' statistics (target by thread 0, draft by the first lane of
+    // wave 1), from K1's chunk partials or computed here by the team
+    if constexpr (OD) {
+      const bool need_q = !greedy && nchild > 0;
+      const int nwv = tree_stats<DT>(trow, drow, al, V, NSUB, c, greedy, need_q, rs, sh, tm);
+      if (wave == 0) {
+        int M, arg;
+        double s;
+        merged_waves(sh, 0, nwv, greedy, lane, M, s, arg);
+        if (lane == 0) {
+          s_Mp = M;
+          s_sp = s;
+          s_arg = arg;
+        }
+      }
+      if (wave == 1 && need_q) {
+        int M, arg;
+        double s;
+        merged_waves(sh, 1, nwv, false, lane, M, s, arg);
+        if (lane == 0) {
+          s_Mq = M;
+          s_sq = s;
+        }
+      }
+    } else {
+      if (tid == 0) {
+        int M, arg;
+        double s;
+        merged_row(sh.part[0], NS, greedy, M, s, arg);
+        s_Mp = M;
+        s_sp = s;
+        s_arg = arg;
+      }
+      if (tid == kWave && !greedy && pos < N) {
+        int arg;
+        merged_row(sh.part[1], NS, false, s_Mq, s_sq, arg);
+      }
     }
     tree_barrier();
     // every child's p(x)/q(x) at once, one exponential each:
@@ -3924,14 +4135,18 @@ constexpr int kMaxDevices = 64;
 // The tree call's workspace: the linear plan, then two copies of each
 // request's sub-chunk mass words (K1 clears them), and the walk's error word.
 struct TreeLayout {
-  size_t sub_off, err_off, spare_off, total;
+  size_t sub_off, stat_off, err_off, spare_off, total;
+  int Wmax;  // waves a team can have
 };
 
 TreeLayout tree_layout(int B, const Plan &P) {
   TreeLayout L;
+  L.Wmax = (P.NSUB + kTWaves - 1) / kTWaves * kTWaves;
   size_t off = P.total;
-  L.sub_off = off;
+  L.sub_off = off;  // mass words, then statistics words, then the error word: one region to clear
   off = align_up(off + sizeof(unsigned long long) * 2 * static_cast<size_t>(B) * P.NSUB);
+  L.stat_off = off;
+  off = align_up(off + sizeof(unsigned long long) * 2 * static_cast<size_t>(B) * L.Wmax * 4);
   L.err_off = off;
   off = align_up(off + sizeof(unsigned));
   L.spare_off = off;  // a block the walk's unused row-slice loads read (contents never used)
@@ -3945,7 +4160,7 @@ TreeLayout tree_layout(int B, const Plan &P) {
 // device holds at once (the team's workgroups wait for each other after every
 // pass, so they must all be resident); large batches walk with one workgroup
 // per request.
-template <int DT>
+template <int DT, bool OD>
 int tree_team_size(int B, int NSUB) {
   static int cache[kMaxDevices];
   int dev = 0;
@@ -3953,7 +4168,7 @@ int tree_team_size(int B, int NSUB) {
   if (!cache[dev]) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_tree_walk<DT>, kTBlock, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_tree_walk<DT, OD>, kTBlock, 0) != hipSuccess)
       return 1;
     cache[dev] = max(1, cus * per / 2);
   }
@@ -3983,6 +4198,30 @@ void *scratch_address() {
     g_scratch_ptr[dev] = ptr;
   }
   return g_scratch_ptr[dev];
+}
+
+// The tree walk, after K1 over every position's rows (statistics from K1) or
+// alone (OD: statistics on demand, the exchange words already cleared).
+template <int DT, bool OD>
+int launch_tree(const void *target, const void *draft, const int32_t *parent, const int32_t *tokens,
+                const int32_t *num_nodes, const float *u_accept, const float *u_sample, const float *temps, int B,
+                int max_nodes, int V, const Plan &P, const TreeLayout &L, char *base, int32_t *count, int32_t *out,
+                int32_t *out_nodes, hipStream_t st) {
+  Partial *part = reinterpret_cast<Partial *>(base + P.part_off);
+  float *zx = reinterpret_cast<float *>(base + P.zx_off);
+  unsigned long long *tsub = reinterpret_cast<unsigned long long *>(base + L.sub_off);
+  unsigned long long *tstat = reinterpret_cast<unsigned long long *>(base + L.stat_off);
+  unsigned *terr = reinterpret_cast<unsigned *>(base + L.err_off);
+  if constexpr (!OD) {
+    if (launch_k1<DT>(target, draft, tokens, temps, 0.0f, num_nodes, max_nodes, V, P, part, zx, st, nullptr, nullptr,
+                      nullptr, tsub, 2 * P.NSUB) != hipSuccess)
+      return SV_EHIP;
+  }
+  const int NW = tree_team_size<DT, OD>(B, P.NSUB);
+  hipLaunchKernelGGL((k_tree_walk<DT, OD>), dim3(static_cast<unsigned>(static_cast<long>(B) * NW)), dim3(kTBlock),
+                     0, st, target, draft, parent, tokens, num_nodes, u_accept, u_sample, temps, max_nodes, V, P.NS,
+                     part, count, out, out_nodes, NW, tsub, terr, base + L.spare_off, tstat, L.Wmax);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 // Workspace of an unfiltered verify call: the largest over the K1 grids that
@@ -4094,31 +4333,32 @@ int spec_verify_tree(const void *target_logits, const void *draft_logits, const 
     return SV_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char *base = static_cast<char *>(workspace);
-  Partial *part = reinterpret_cast<Partial *>(base + P.part_off);
-  float *zx = reinterpret_cast<float *>(base + P.zx_off);
-  unsigned long long *tsub = reinterpret_cast<unsigned long long *>(base + L.sub_off);
-  unsigned *terr = reinterpret_cast<unsigned *>(base + L.err_off);
-  hipError_t e;
-  if (dtype == SV_BF16) {
-    e = launch_k1<SV_BF16>(target_logits, draft_logits, node_tokens, temperature, 0.0f, num_nodes, max_nodes, V, P,
-                           part, zx, st, nullptr, nullptr, nullptr, tsub, 2 * P.NSUB);
-    if (e != hipSuccess) return SV_EHIP;
-    const int NW = tree_team_size<SV_BF16>(B, P.NSUB);
-    hipLaunchKernelGGL((k_tree_walk<SV_BF16>), dim3(static_cast<unsigned>(static_cast<long>(B) * NW)),
-                       dim3(kTBlock), 0, st, target_logits, draft_logits, node_parent, node_tokens, num_nodes,
-                       u_accept, u_sample, temperature, max_nodes, V, P.NS, part, accepted_count, out_tokens,
-                       out_nodes, NW, tsub, terr, base + L.spare_off);
-  } else {
-    e = launch_k1<SV_F32>(target_logits, draft_logits, node_tokens, temperature, 0.0f, num_nodes, max_nodes, V, P,
-                          part, zx, st, nullptr, nullptr, nullptr, tsub, 2 * P.NSUB);
-    if (e != hipSuccess) return SV_EHIP;
-    const int NW = tree_team_size<SV_F32>(B, P.NSUB);
-    hipLaunchKernelGGL((k_tree_walk<SV_F32>), dim3(static_cast<unsigned>(static_cast<long>(B) * NW)),
-                       dim3(kTBlock), 0, st, target_logits, draft_logits, node_parent, node_tokens, num_nodes,
-                       u_accept, u_sample, temperature, max_nodes, V, P.NS, part, accepted_count, out_tokens,
-                       out_nodes, NW, tsub, terr, base + L.spare_off);
+  bool od = max_nodes >= kTreeOnDemandNodes;
+  if (const char *m = getenv("SPECVERIFY_TREE_STATS")) {  // a forced choice (testing)
+    if (!strcmp(m, "walk")) od = true;
+    else if (!strcmp(m, "rows")) od = false;
   }
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+  if (od) {  // the exchange words (and the error word) start at zero; K1 clears the mass words when it runs
+    const long n = static_cast<long>((L.err_off - L.sub_off) / sizeof(unsigned long long)) + 1;
+    const long groups = min((n + kBlock - 1) / kBlock, 1024L);
+    hipLaunchKernelGGL(k_tree_clear, dim3(static_cast<unsigned>(groups)), dim3(kBlock), 0, st,
+                       reinterpret_cast<unsigned long long *>(base + L.sub_off), n);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  }
+  const int rc = dtype == SV_BF16
+                     ? (od ? launch_tree<SV_BF16, true>(target_logits, draft_logits, node_parent, node_tokens,
+                                                          num_nodes, u_accept, u_sample, temperature, B, max_nodes,
+                                                          V, P, L, base, accepted_count, out_tokens, out_nodes, st)
+                           : launch_tree<SV_BF16, false>(target_logits, draft_logits, node_parent, node_tokens,
+                                                           num_nodes, u_accept, u_sample, temperature, B, max_nodes,
+                                                           V, P, L, base, accepted_count, out_tokens, out_nodes, st))
+                     : (od ? launch_tree<SV_F32, true>(target_logits, draft_logits, node_parent, node_tokens,
+                                                         num_nodes, u_accept, u_sample, temperature, B, max_nodes, V,
+                                                         P, L, base, accepted_count, out_tokens, out_nodes, st)
+                           : launch_tree<SV_F32, false>(target_logits, draft_logits, node_parent, node_tokens,
+                                                          num_nodes, u_accept, u_sample, temperature, B, max_nodes,
+                                                          V, P, L, base, accepted_count, out_tokens, out_nodes, st));
+  return rc;
 }
 
 size_t spec_sample_workspace_bytes(int R, int V, int dtype) {

@@ -29,6 +29,16 @@ def _gpu():
     sv.load_library()
 
 
+@pytest.fixture(params=["rows", "walk"], autouse=True)
+def stats_path(request, monkeypatch):
+    """Every tree test runs with each way of getting the row statistics: one
+    streaming pass over every row, and the walk's own statistics of the
+    positions it visits (by default chosen by the node count)."""
+    monkeypatch.setenv("SPECVERIFY_TREE_STATS", request.param)
+    say(f"tree statistics: {request.param}")
+    return request.param
+
+
 def gpu_tree(w, **kw):
     import rejection_sampling_verification_spec_amd as sv
     t = w.to_torch(torch.device("cuda:0"))
