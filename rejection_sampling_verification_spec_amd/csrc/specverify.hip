@@ -2635,6 +2635,7 @@ struct TreeShared {
   int parent[SV_TREE_MAX_NODES];
   int token[SV_TREE_MAX_NODES];
   int child[SV_TREE_MAX_NODES];    // children of the current position, in node order
+  int childp[SV_TREE_MAX_NODES];   // children of the prefetched position
   float czp[SV_TREE_MAX_NODES];    // their target and draft logits, and uniforms
   float czq[SV_TREE_MAX_NODES];
   float cu[SV_TREE_MAX_NODES];
@@ -2729,6 +2730,14 @@ struct RowSlice {
   bool valid;
 };
 
+// Wave gw of a team of `stride` waves takes sub-chunks gw, gw + stride, ...:
+// first those wholly inside an aligned row (index < nfast), then the others (a
+// partial last sub-chunk, or every sub-chunk of a row that is not aligned);
+// this is its first index of the others.
+__device__ __forceinline__ int first_guarded(int gw, int stride, int nfast) {
+  return gw >= nfast ? gw : gw + (nfast - gw + stride - 1) / stride * stride;
+}
+
 template <int DT, bool USEQ>
 __device__ __forceinline__ void tree_masses_of(const void *trow, const void *drow, bool aligned, int V, int NSUB, float c,
                                float negMp, float negMq, float r, const RowSlice<DT> &rs, TreeShared &sh,
@@ -2745,13 +2754,13 @@ __device__ __forceinline__ void tree_masses_of(const void *trow, const void *dro
       else sh.sub[j] = v;
     }
   };
-  // Sub-chunks wholly inside an aligned row: wave g takes g, g + stride, ...
-  // with straight-line loads, the next one requested while the current one is
-  // reduced (its index clamped to the last such sub-chunk, so that the loads are
-  // unconditional and each wait covers exactly the older sub-chunk).  A wave
-  // whose one sub-chunk is already in registers (rs) reduces it directly.
+  // Sub-chunks wholly inside an aligned row: straight-line loads, the next one
+  // requested while the current one is reduced (its index clamped to the last
+  // such sub-chunk, so that the loads are unconditional and each wait covers
+  // exactly the older sub-chunk).  A wave whose one sub-chunk is already in
+  // registers (rs) reduces it directly.
   const int nfast = aligned ? min(NSUB, V / kSub) : 0;
-  if (rs.valid) {  // uniform per wave: gw < nfast and no other fast sub-chunk
+  if (rs.valid) {  // uniform per wave: gw is the wave's only sub-chunk
     put_mass(gw, wave_sum(static_cast<double>(tree_lane_mass<DT, USEQ>(rs.t, rs.d, c, negMp, negMq, r))));
   } else if (gw < nfast) {
     u32x4 tp[kN], dq[kN], tn[kN], dn[kN];
@@ -2769,9 +2778,8 @@ __device__ __forceinline__ void tree_masses_of(const void *trow, const void *dro
       }
     }
   }
-  // the rest (a partial last sub-chunk, or every sub-chunk of a row that is not
-  // aligned): guarded loads, one sub-chunk at a time
-  for (int j = nfast + gw; j < NSUB; j += stride) {
+  // the rest: guarded loads, one sub-chunk at a time
+  for (int j = rs.valid ? NSUB : first_guarded(gw, stride, nfast); j < NSUB; j += stride) {
     u32x4 tp[kN], dq[kN];
     load_lane_raw<DT>(trow, aligned, static_cast<long>(j) * kSub, lane, V, tp);
     if constexpr (USEQ) load_lane_raw<DT>(drow, aligned, static_cast<long>(j) * kSub, lane, V, dq);
@@ -2968,7 +2976,7 @@ __device__ __forceinline__ int tree_stats(const void *trow, const void *drow, bo
       if (need_q) fold_tile<DT, kN>(dv, c, Mq, sq, mq);
     }
   };
-  if (rs.valid) {  // uniform per wave
+  if (rs.valid) {  // uniform per wave: gw is the wave's only sub-chunk
     fold(rs.t, rs.d, static_cast<long>(gw) * kSub);
   } else {
     for (int j = gw; j < nfast; j += stride) {
@@ -2978,7 +2986,7 @@ __device__ __forceinline__ int tree_stats(const void *trow, const void *drow, bo
       fold(tv, dv, static_cast<long>(j) * kSub);
     }
   }
-  for (int j = nfast + gw; j < NSUB; j += stride) {
+  for (int j = rs.valid ? NSUB : first_guarded(gw, stride, nfast); j < NSUB; j += stride) {
     u32x4 tv[kN], dv[kN];
     load_lane_raw<DT>(trow, al, static_cast<long>(j) * kSub, lane, V, tv);
     if (need_q) load_lane_raw<DT>(drow, al, static_cast<long>(j) * kSub, lane, V, dv);
@@ -3127,76 +3135,116 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
   tree_barrier();
   const size_t eb = Elem<DT>::kBytes;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
-  int pos = 0, depth = 0;
-  for (;;) {
-    const void *trow = static_cast<const char *>(target) + (static_cast<long>(b) * (Nmax + 1) + pos) * V * eb;
-    const void *drow = pos < Nmax ? static_cast<const char *>(draft) + (static_cast<long>(b) * Nmax + pos) * V * eb
-                                  : nullptr;  // position Nmax has no child
-    const bool al = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;
-    // the position's children in node order (a block-wide compaction)
-    const bool is_child = tid < N && tid >= pos && sh.parent[tid] == pos - 1;
+  auto target_row = [&](int p) -> const void * {
+    return static_cast<const char *>(target) + (static_cast<long>(b) * (Nmax + 1) + p) * V * eb;
+  };
+  auto draft_row = [&](int p) -> const void * {  // position Nmax has no child, so no draft row
+    return p < Nmax ? static_cast<const char *>(draft) + (static_cast<long>(b) * Nmax + p) * V * eb : nullptr;
+  };
+  // position p's children in node order, into list (a block-wide compaction)
+  auto children = [&](int p, int *list) -> int {
+    const bool is_child = tid < N && tid >= p && sh.parent[tid] == p - 1;
     const unsigned long long mask = __ballot(is_child);
     if (lane == 0) sh.wcnt[wave] = __popcll(mask);
     tree_barrier();
-    int nchild = 0, before = 0;
+    int n = 0, before = 0;
     for (int w = 0; w < kTWaves; ++w) {
       if (w < wave) before += sh.wcnt[w];
-      nchild += sh.wcnt[w];
+      n += sh.wcnt[w];
     }
-    if (is_child) sh.child[before + __popcll(mask & ((1ull << lane) - 1ull))] = tid;
+    if (is_child) list[before + __popcll(mask & ((1ull << lane) - 1ull))] = tid;
     tree_barrier();
-    // then everything the position needs, requested together (one round trip):
-    // the chunk partials of its two rows (wave 0: the target row, wave 1: the
-    // draft row; lane j: chunks j and j + 64), each child's two logits and its
-    // uniform (the other waves, a thread per child and, past their count, a
-    // second), and every wave's sub-chunk of the row pair, kept in registers
-    // for the passes at this position when each wave has at most one
-    const bool want_part = !OD && (wave == 0 || (wave == 1 && !greedy && pos < N));
-    u32x4 pv0 = {0u, 0u, 0u, 0u}, pv1 = {0u, 0u, 0u, 0u};  // the records as raw 16-byte vectors
-    if (want_part) {
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(part) +
-                         (static_cast<long>(b) * rows + (wave == 0 ? pos : Nmax + 1 + pos)) * NS;
-      if (lane < NS) pv0 = src[lane];
-      if (lane + kWave < NS) pv1 = src[lane + kWave];
-    }
-    constexpr int kGather = kTBlock - 2 * kWave;  // threads that gather children
-    static_assert(2 * kGather >= SV_TREE_MAX_NODES, "at most two children per gathering thread");
-    const int jc = tid - 2 * kWave;
-    unsigned zc[2][3];  // raw bits: nothing waits for them before the stores below
+    return n;
+  };
+  // each child's two logits and its uniform, as raw bits (the threads past the
+  // first two waves, a thread per child and, past their count, a second)
+  constexpr int kGather = kTBlock - 2 * kWave;  // threads that gather children
+  static_assert(2 * kGather >= SV_TREE_MAX_NODES, "at most two children per gathering thread");
+  const int jc = tid - 2 * kWave;
+  auto gather = [&](const int *list, int n, const void *tr, const void *dr, unsigned (&z)[2][3]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int j = jc + h * kGather;
-      zc[h][0] = zc[h][1] = 0u;
-      zc[h][2] = __float_as_uint(2.0f);  // 2 rejects
-      if (!greedy && jc >= 0 && j < nchild) {
-        const int n = sh.child[j], x = sh.token[n];
+      z[h][0] = z[h][1] = 0u;
+      z[h][2] = __float_as_uint(2.0f);  // 2 rejects
+      if (!greedy && jc >= 0 && j < n) {
+        const int nd = list[j], x = sh.token[nd];
         if (x >= 0 && x < V) {  // an id outside the vocabulary is rejected, never dereferenced
-          zc[h][0] = load_bits<DT>(trow, x);
-          zc[h][1] = load_bits<DT>(drow, x);
-          zc[h][2] = __float_as_uint(u_accept[static_cast<long>(b) * Nmax + n]);
+          z[h][0] = load_bits<DT>(tr, x);
+          z[h][1] = load_bits<DT>(dr, x);
+          z[h][2] = __float_as_uint(u_accept[static_cast<long>(b) * Nmax + nd]);
         }
       }
     }
-    RowSlice<DT> rs;
-    {
-      const int gw = tm.w * kTWaves + wave, stride = tm.NW * kTWaves;
-      const int nfast = al ? min(NSUB, V / kSub) : 0;
-      // (bf16 only: an fp32 slice is twice the registers)
-      rs.valid = DT == SV_BF16 && (OD || (!greedy && drow != nullptr)) && gw < nfast && gw + stride >= nfast;
-      if constexpr (DT == SV_BF16) {
+  };
+  // the wave's sub-chunk of a position's row pair, kept in registers for the
+  // passes at that position when each wave has at most one (bf16 only: an fp32
+  // slice is twice the registers)
+  auto load_slice = [&](const void *tr, const void *dr, bool al, RowSlice<DT> &r) {
+    const int gw = tm.w * kTWaves + wave, stride = tm.NW * kTWaves;
+    r.valid = DT == SV_BF16 && (OD || (!greedy && dr != nullptr)) && gw < NSUB && gw + stride >= NSUB;
+    if constexpr (DT == SV_BF16) {
+      const bool need_d = dr && !greedy;
+      if (r.valid && !(al && static_cast<long>(gw + 1) * kSub <= V)) {  // a guarded sub-chunk (uniform per wave)
+        load_lane_raw<DT>(tr, al, static_cast<long>(gw) * kSub, lane, V, r.t);
+        if (need_d) load_lane_raw<DT>(dr, al, static_cast<long>(gw) * kSub, lane, V, r.d);
+        else load_lane_fast<DT>(spare, 0, lane, r.d);
+      } else {
         // unconditional loads (from the workspace's spare block when the wave
-        // holds no slice), so that waiting for the loads above never waits
-        // for these
-        const void *ts = rs.valid ? trow : spare, *ds = rs.valid && drow && !greedy ? drow : spare;
-        const long off = rs.valid ? static_cast<long>(gw) * kSub : 0;
-        load_lane_fast<DT>(ts, off, lane, rs.t);
-        load_lane_fast<DT>(ds, off, lane, rs.d);
+        // holds no slice), so that waiting for the loads before them never
+        // waits for these
+        const void *ts = r.valid ? tr : spare, *ds = r.valid && need_d ? dr : spare;
+        const long off = r.valid ? static_cast<long>(gw) * kSub : 0;
+        load_lane_fast<DT>(ts, off, lane, r.t);
+        load_lane_fast<DT>(ds, off, lane, r.d);
       }
     }
-    if (want_part) {
-      u32x4 *dst = reinterpret_cast<u32x4 *>(sh.part[wave]);
-      if (lane < NS) dst[lane] = pv0;
-      if (lane + kWave < NS) dst[lane + kWave] = pv1;
+  };
+  // With statistics on demand, the position of the current one's first child
+  // (the most likely next) is prefetched while this one is decided: its
+  // children, their logits and the row slices.
+  int ppos = -1, nchild_pf = 0;
+  unsigned zc_pf[2][3];
+  RowSlice<DT> rs_pf;
+  int pos = 0, depth = 0;
+  for (;;) {
+    const void *trow = target_row(pos);
+    const void *drow = draft_row(pos);
+    const bool al = ((reinterpret_cast<uintptr_t>(trow) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;
+    // everything the position needs, requested together (one round trip): with
+    // K1, the chunk partials of its two rows (wave 0: the target row, wave 1:
+    // the draft row; lane j: chunks j and j + 64); each child's two logits and
+    // its uniform; every wave's sub-chunk of the row pair.  A prefetched
+    // position has them already.
+    const bool pre = OD && pos == ppos;  // uniform across the team
+    const bool want_part = !OD && (wave == 0 || (wave == 1 && !greedy && pos < N));
+    int nchild;
+    unsigned zc[2][3];
+    RowSlice<DT> rs;
+    if (pre) {
+      nchild = nchild_pf;
+      for (int j = tid; j < nchild; j += kTBlock) sh.child[j] = sh.childp[j];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) zc[h][k] = zc_pf[h][k];
+      rs = rs_pf;
+    } else {
+      nchild = children(pos, sh.child);
+      u32x4 pv0 = {0u, 0u, 0u, 0u}, pv1 = {0u, 0u, 0u, 0u};  // the records as raw 16-byte vectors
+      if (want_part) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(part) +
+                           (static_cast<long>(b) * rows + (wave == 0 ? pos : Nmax + 1 + pos)) * NS;
+        if (lane < NS) pv0 = src[lane];
+        if (lane + kWave < NS) pv1 = src[lane + kWave];
+      }
+      gather(sh.child, nchild, trow, drow, zc);
+      load_slice(trow, drow, al, rs);
+      if (want_part) {
+        u32x4 *dst = reinterpret_cast<u32x4 *>(sh.part[wave]);
+        if (lane < NS) dst[lane] = pv0;
+        if (lane + kWave < NS) dst[lane + kWave] = pv1;
+      }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -3247,6 +3295,25 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
       }
     }
     tree_barrier();
+    if constexpr (OD) {
+      // the prefetch of the likely next position: the first child's (for a
+      // greedy walk, the child equal to the arg-max: the next one for sure)
+      int nxt = -1;
+      if (greedy) {
+        for (int j = 0; j < nchild && nxt < 0; ++j)
+          if (sh.token[sh.child[j]] == s_arg) nxt = sh.child[j];
+      } else {
+        nxt = nchild > 0 ? sh.child[0] : -1;
+      }
+      ppos = nxt >= 0 ? nxt + 1 : -1;
+      if (ppos >= 0) {  // uniform across the team
+        const void *tp = target_row(ppos), *dp = draft_row(ppos);
+        const bool alp = ((reinterpret_cast<uintptr_t>(tp) | reinterpret_cast<uintptr_t>(dp)) & 15u) == 0;
+        nchild_pf = children(ppos, sh.childp);
+        gather(sh.childp, nchild_pf, tp, dp, zc_pf);
+        load_slice(tp, dp, alp, rs_pf);
+      }
+    }
     // every child's p(x)/q(x) at once, one exponential each:
     // 2^((zp - zq) c - (Mp - Mq)) * s'_q / s'_p (the logit difference is exact)
     for (int j = tid; !greedy && j < nchild; j += kTBlock) {
@@ -3305,15 +3372,27 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
         // every child rejected, or none: draw from the current target
         const bool use_q = cc > 0.0;
         const float r = use_q ? static_cast<float>(cc * sp / sq) : 0.0f;
-        if (!masses_current)
-          tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q, rs, sh, tm);
+        if (!masses_current) {
+          if (OD && !use_q && tm.NW * kTWaves >= NSUB) {
+            // p's sub-chunk masses are the waves' statistics already exchanged
+            // (one sub-chunk per wave), rescaled to the row's M: no pass
+            for (int j = tid; j < NSUB; j += kTBlock)
+              sh.sub[j] = ldexp(static_cast<double>(sh.wsB[0][j]), sh.wsA[0][j] - Mp);
+            tree_barrier();
+            tree_total(NSUB, sh);
+            tree_barrier();
+          } else {
+            tree_masses<DT>(trow, drow, al, V, NSUB, c, negMp, -static_cast<float>(Mq), r, use_q, rs, sh, tm);
+          }
+        }
         // every workgroup finds the crossing from the same masses; the wave that
         // holds that sub-chunk in registers draws from them, else the lead
         // workgroup reads it again
         tree_crossing(NSUB, us, sh);
         const int sub = sh.pick;
-        const int stride = tm.NW * kTWaves, nfast = al ? min(NSUB, V / kSub) : 0;
-        const bool held = DT == SV_BF16 && drow != nullptr && sub < nfast && sub + stride >= nfast;
+        const int stride = tm.NW * kTWaves;
+        // (the wave `sub` holds it when that is its only sub-chunk: rs.valid there)
+        const bool held = DT == SV_BF16 && (OD || drow != nullptr) && sub + stride >= NSUB;
         int32_t *dst = out_tokens + static_cast<long>(b) * (Nmax + 1) + depth;
         if (held) {
           if (tm.w * kTWaves + wave == sub) {  // uniform per wave: this wave's rs holds the sub-chunk
