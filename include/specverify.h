@@ -230,7 +230,7 @@ int spec_verify_filtered(const void *target_logits, const void *draft_logits,
  * [0, V) is rejected when tested and never dereferenced.  0 <= max_nodes <=
  * SV_TREE_MAX_NODES, V <= SV_TREE_MAX_V.  The workspace is sized by
  * spec_verify_tree_workspace_bytes.
- * Row statistics: with max_nodes >= 16 the walk computes them for the
+ * Row statistics: with max_nodes >= 8 the walk computes them for the
  * positions it visits only (two launches: a clear of the exchange words, the
  * walk); smaller trees take them from one streaming pass over every row, then
  * walk.  The environment variable SPECVERIFY_TREE_STATS, read on each call,

@@ -2624,8 +2624,12 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kTBlock = 256;
 // Trees of at least this many nodes take their row statistics from the walk
 // itself (only the positions it visits: a path of a wide tree is a small share
-// of its rows); smaller trees take them from K1 over every row.
-constexpr int kTreeOnDemandNodes = 16;
+// of its rows); smaller trees take them from K1 over every row.  Per call on
+// trees of V = 128256 bf16 (B = 8 unless stated; K1 then walk / walk alone):
+// width 4 depth 3 (84 nodes) 82.3 / 40.0 us, B = 32 252 / 75.6, width 2 depth
+// 4 (30) 58.2 / 40.9, width 2 depth 3 (14) 44.2 / 40.6, width 3 depth 2 (12)
+// 38.4 / 33.0, a chain of 6 52.3 / 54.6.
+constexpr int kTreeOnDemandNodes = 8;
 constexpr int kTWaves = kTBlock / kWave;
 constexpr int kTMaxSub = SV_TREE_MAX_V / kSub;
 constexpr int kTMaxNS = 2 * kWave;  // chunks per row: at most 128 (V <= 2^20 fp32 is 128 K1 tiles)
