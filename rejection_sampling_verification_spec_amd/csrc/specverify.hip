@@ -3397,8 +3397,9 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
         tree_crossing(NSUB, us, sh);
         const int sub = sh.pick;
         const int stride = tm.NW * kTWaves;
-        // (the wave `sub` holds it when that is its only sub-chunk: rs.valid there)
-        const bool held = DT == SV_BF16 && (OD || drow != nullptr) && sub + stride >= NSUB;
+        // (wave `sub` of the team, if there is one, holds it when that is its
+        // only sub-chunk: rs.valid there)
+        const bool held = DT == SV_BF16 && (OD || drow != nullptr) && sub < stride && sub + stride >= NSUB;
         int32_t *dst = out_tokens + static_cast<long>(b) * (Nmax + 1) + depth;
         if (held) {
           if (tm.w * kTWaves + wave == sub) {  // uniform per wave: this wave's rs holds the sub-chunk

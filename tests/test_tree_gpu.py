@@ -158,6 +158,22 @@ def test_tree_largest_vocabulary():
     check(w, max_flagged=1)
 
 
+def test_tree_waves_with_several_sub_chunks():
+    """B = 64 trees over V = 40000 bf16: the team is smaller than a wave per
+    sub-chunk (each wave takes several, the last one partial)."""
+    w = W.build_tree("B64_w2_d2_V40000_bf16", 3200, 64, 2, 2, 40000, "bf16", target_scale=3.0, zipf=True,
+                     sigma=0.6, temps=np.where(np.arange(64) % 4 == 0, 0.0, 0.8).astype(np.float32))
+    check(w, max_flagged=2)
+
+
+def test_tree_team_of_one_workgroup():
+    """B = 130 trees: one workgroup per request, so the sub-chunk statistics and
+    masses stay in LDS (no exchange words)."""
+    w = W.build_tree("B130_w2_d2_V9000_bf16", 3300, 130, 2, 2, 9000, "bf16", target_scale=3.0, zipf=True,
+                     sigma=0.6, temps=np.where(np.arange(130) % 5 == 0, 0.0, 1.0).astype(np.float32))
+    check(w, max_flagged=2)
+
+
 def test_tree_deterministic():
     w = W.build_tree("det", 74, 6, 3, 3, 9000, "bf16", target_scale=3.0, zipf=True, sigma=0.6, temps=1.0)
     a = gpu_tree(w)
