@@ -2600,16 +2600,19 @@ __global__ __launch_bounds__(kFBlock) void k_filter_general(
 // target arg-max.
 //
 // k_tree_walk: NW 256-thread workgroups per request walk its tree together.
-// Every workgroup takes the same decisions (row statistics from K1's partials,
-// the acceptance ratio in fp64 from the two gathered logits, all merged and
-// summed in a fixed order); each rejection costs one pass over the position's
-// two rows, shared out as 2048-token sub-chunks over the request's NW x 8
-// waves.  Each sub-chunk mass goes out with the pass number in one 64-bit
-// device-scope atomic store into a per-request array (two copies, alternating
-// between passes, cleared by K1); each workgroup polls the words until all
-// carry the pass number and adds the masses in the same order, so Z is the
-// same everywhere.  Workgroup 0 writes the outputs and draws the final token.
-// With NW = 1 (large batches) the masses stay in LDS, in fp64.
+// Every workgroup takes the same decisions (the row statistics, from K1's
+// partials or computed by the team for the positions it visits, the acceptance
+// ratio in fp64 from the two gathered logits, all merged and summed in a fixed
+// order); each rejection costs one pass over the position's two rows, shared
+// out as 2048-token sub-chunks over the request's NW x 4 waves.  Each
+// sub-chunk mass (and each wave's statistics) goes out with the exchange
+// number in 64-bit device-scope atomic stores into per-request arrays (two
+// copies each, alternating between exchanges, zeroed before the walk by K1 or
+// by a clear); each workgroup polls the words until all carry the exchange
+// number and merges them in the same order, so the results are the same
+// everywhere.  Workgroup 0 writes the outputs; the final token is drawn by the
+// wave that holds its sub-chunk, else by workgroup 0.  With NW = 1 (large
+// batches) the exchanged values stay in LDS.
 // The walk's workgroup barrier orders LDS only.  Its threads share nothing
 // else through memory (the team's words are device-scope atomics), and a full
 // barrier would wait for every global load the wave has in flight, such as the
@@ -2750,7 +2753,7 @@ __device__ __forceinline__ void tree_masses_of(const void *trow, const void *dro
                                TreeTeam &tm) {
   constexpr int kN = kLaneElems / Elem<DT>::kVec;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  // this wave's place among the request's NW x 8 waves
+  // this wave's place among the request's NW x 4 waves
   const int gw = tm.w * kTWaves + wave, stride = tm.NW * kTWaves;
   unsigned long long *gsub = tm.NW > 1 ? tm.sub + (tm.pass & 1) * NSUB : nullptr;
   const int stamp = tm.pass + 1;
@@ -4219,7 +4222,9 @@ constexpr int kMaxDevices = 64;
 
 // ------------------------------------------------------------------ tree walk
 // The tree call's workspace: the linear plan, then two copies of each
-// request's sub-chunk mass words (K1 clears them), and the walk's error word.
+// request's sub-chunk mass words and of its per-wave statistics words, the
+// walk's error word (these three zeroed before each walk, by K1 or by a
+// clear), and a spare block the walk's unused row-slice loads read.
 struct TreeLayout {
   size_t sub_off, stat_off, err_off, spare_off, total;
   int Wmax;  // waves a team can have
