@@ -668,14 +668,19 @@ def main():
         with torch.cuda.stream(stream):
             tstep(0)
         torch.cuda.synchronize()
-        rc, ro = tc.cpu().clone(), to.cpu().clone()
+        rc, ro, rn = tc.cpu().clone(), to.cpu().clone(), tn.cpu().clone()
         per = graph_time(torch, stream, tstep, tcopies, args.steps // 4)
         assert torch.equal(tc.cpu(), rc) and torch.equal(to.cpu(), ro), "tree replay differs"
         emitted = float(rc.sum()) + tw.B
         extras["spec_verify_tree"] = {
             "workload": tw.name, "us_per_call": round(per * 1e6, 3), "nodes_per_s": round(tw.B * tw.N / per, 1),
             "emitted_tokens_per_s": round(emitted / per, 1), "mean_accepted_path": round(float(rc.float().mean()), 3),
-            "GBps_alg": round(tw.bytes_alg() / per / 1e9, 1)}
+            # the walk reads the rows of the positions it visits (a wide tree's path is a small
+            # share of its rows), so bandwidth is quoted on those bytes; every row of the trees
+            # would be 'bytes_all_rows'
+            "bytes_walked_rows": tw.bytes_walked(rn.numpy(), rc.numpy()),
+            "GBps_walked_rows": round(tw.bytes_walked(rn.numpy(), rc.numpy()) / per / 1e9, 1),
+            "bytes_all_rows": tw.bytes_alg()}
         log(f"[bench] spec_verify_tree {extras['spec_verify_tree']}")
         del ttg, tdr, tt
 

@@ -336,11 +336,26 @@ class TreeWorkload:
         return np.full(self.B, self.N, np.int32) if self.num_nodes is None else self.num_nodes
 
     def bytes_alg(self) -> int:
-        """Logit bytes the row statistics read: every target row of a used position and, for
-        stochastic requests, every draft row of a position that can have children."""
+        """Logit bytes of every row a tree could need: every target row of a used position and,
+        for stochastic requests, every draft row of a position that can have children."""
         n = self.node_counts().astype(np.int64)
         stoch = (self.temperature > 0).astype(np.int64)
         return int(((n + 1) + stoch * n).sum()) * self.V * (2 if self.dtype == BF16 else 4)
+
+    def bytes_walked(self, out_nodes: np.ndarray, accepted_count: np.ndarray) -> int:
+        """Logit bytes of the rows a walk needs, given its accepted paths: the target row of
+        every position it visits and, for stochastic requests, the draft row of each visited
+        position that has children."""
+        n = self.node_counts()
+        rows = 0
+        for b in range(self.B):
+            par = self.parent[b, :n[b]]
+            visited = [0] + [int(x) + 1 for x in out_nodes[b, :int(accepted_count[b])]]
+            for p in visited:
+                rows += 1
+                if self.temperature[b] > 0 and np.any(par == p - 1):
+                    rows += 1
+        return rows * self.V * (2 if self.dtype == BF16 else 4)
 
     def to_torch(self, device):
         import torch
