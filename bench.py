@@ -125,6 +125,8 @@ def _kernel_short(name: str) -> str:
     tags = [{"0": "f32", "1": "bf16"}.get(args[0], args[0])]
     if kname == "k1_row_stats" and len(args) == 3:
         tags.append({"0": "per-request T", "1": "stochastic", "2": "greedy"}.get(args[2], args[2]))
+    elif kname == "k_tree_walk" and len(args) == 2:
+        tags.append("own statistics" if args[1] == "true" else "statistics from K1")
     elif len(args) in (2, 3) and args[1] in ("true", "false"):
         tags.append("filtered" if args[1] == "true" else "plain")
         if len(args) == 3 and args[2] == "true":
