@@ -345,6 +345,27 @@ def test_misaligned_rows_and_workspace_garbage():
     np.testing.assert_array_equal(out.cpu().numpy()[ok], o.out_tokens[ok])
 
 
+def test_large_batch_with_the_queried_workspace():
+    """B = 1300 requests, 9100 row slots: the unfiltered verify grid takes two chunks
+    per row where the default plan takes one, so the size spec_verify_workspace_bytes
+    reports must cover the larger plan.  Exactly that many bytes are passed, and a
+    sample of the requests (they are independent) is checked against the oracle."""
+    import dataclasses
+
+    import oracle
+    import rejection_sampling_verification_spec_amd as sv
+    w = W.make_random(4242, 1300, 3, 16400, "bf16", temps=1.0)
+    nbytes = sv.spec_verify_workspace_bytes(w.B, w.gamma, w.V, sv.SV_BF16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    g = gpu_run(w, workspace=ws)
+    idx = np.array([0, 1, 2, 3, 647, 648, 649, 1296, 1297, 1298, 1299])
+    sub = dataclasses.replace(w, name=w.name + "_sample", B=idx.size, target=w.target[idx], draft=w.draft[idx],
+                              draft_tokens=w.draft_tokens[idx], u_accept=w.u_accept[idx],
+                              u_sample=w.u_sample[idx], temperature=w.temperature[idx])
+    gs = type(g)(count=g.count[idx], out=g.out[idx])
+    check_parity(sub, gs, oracle.run_workload(sub), require_no_flags=False)
+
+
 def test_side_stream():
     w = W.make_config(2)
     s = torch.cuda.Stream()
