@@ -67,9 +67,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0: enough for 1.2 GB)")
-    ap.add_argument("--config", type=int, default=3, help="workload timed as the step (default 3)")
+    ap.add_argument("--config", type=int, default=3, help="workload timed as the step, by its index in workloads.make_config (default 3: B = 64, gamma = 5, V = 128256 bf16)")
     ap.add_argument("--mode", choices=["stochastic", "greedy"], default="stochastic",
-                    help="workload 3 at T = 1 or at T = 0")
+                    help="the B = 64, gamma = 5, V = 128256 bf16 batch at T = 1 or at T = 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the step only (no sampler, filter, tree, other workloads, cold latency, probe)")
@@ -474,7 +474,7 @@ def main():
     dev = torch.device("cuda:0")
     greedy = args.mode == "greedy"
     if greedy and args.config != 3:
-        print("--mode greedy applies to workload 3", file=sys.stderr)
+        print("--mode greedy applies to the B = 64, gamma = 5, V = 128256 bf16 batch (--config 3)", file=sys.stderr)
         sys.exit(2)
     cache = {}
     t0 = time.perf_counter()

@@ -3952,13 +3952,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 constexpr int kK1U = 8;                 // 16-byte vectors per thread per K1 tile
 constexpr long kK1TargetGroups = 4224;  // about 16 workgroups per CU on 256 CUs (a sweep)
 // Unfiltered verify calls: about 1408 workgroups, at least two chunks per row.
-// Workload 3 (704 rows of 8 tiles): 2 chunks per row (1408 workgroups) 45.6-46.2
+// B = 64, gamma = 5, V = 128256 bf16 (704 rows of 8 tiles): 2 chunks per row (1408 workgroups) 45.6-46.2
 // us per call against 46.6-47.8 with 4 (2816); the ragged B = 128 batch (1920
 // row slots of 10 tiles) keeps 2 chunks per row (1 measured 76.8-77.0 us
 // against 75.0).
 constexpr long kK1VerifyTargetGroups = 1408;
 // Uniform greedy batches (max and index only, 90 registers): fewer, longer
-// workgroups.  Workload 3 greedy (384 target rows of 8 tiles): 768 workgroups
+// workgroups.  B = 64, gamma = 5, V = 128256 bf16, greedy (384 target rows of 8 tiles): 768 workgroups
 // (2 chunks per row) 20.7-21.2 us per call, 1152 21.8, 1536 21.2-21.5, 3072
 // about 21.8.
 constexpr long kK1GreedyTargetGroups = 768;
@@ -4092,7 +4092,7 @@ int run(const void *target, const void *draft, const int32_t *tokens, const floa
   // resident at once (K2's registers allow 4 workgroups per CU for bf16 rows,
   // 2 for fp32; 256 CUs).  On the ragged B = 128 batch (2432 workgroups) the
   // waiting workgroups held back the later ones: 79.9 us per call against
-  // 76.5 with workgroup 0 drawing; workload 3 (1024) 46.1 against 46.4.
+  // 76.5 with workgroup 0 drawing; B = 64, V = 128256 (1024) 46.1 against 46.4.
   const bool owner = static_cast<long>(B) * P.NW <= (DT == SV_BF16 ? 1024L : 512L);
   unsigned long long *words = sel2 ? reinterpret_cast<unsigned long long *>(sums) : nullptr;
   hipError_t e = launch_k1<DT>(target, draft, tokens, temps, scalar_T, lens, gamma, V, P, part, zx, st,

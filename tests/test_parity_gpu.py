@@ -164,7 +164,7 @@ def test_greedy_ties_lowest_index(B, gamma, V):
 # one workgroup, in one kernel; one logit more takes the two-kernel path.
 SMALL = [
     # (B, gamma, V, dtype)
-    (1, 4, 1000, "f32"),     # workload 0's shape
+    (1, 4, 1000, "f32"),     # the B = 1, gamma = 4, V = 1000 fp32 shape
     (3, 5, 1117, "bf16"),    # 11 * 1117 = 12287
     (2, 0, 12288, "f32"),    # one row of 12288 logits: the limit
     (2, 0, 12289, "f32"),    # one logit more: the two-kernel path
