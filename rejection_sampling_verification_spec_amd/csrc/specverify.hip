@@ -2637,7 +2637,8 @@ constexpr int kTBlock = 256;
 constexpr int kTreeOnDemandNodes = 8;
 constexpr int kTWaves = kTBlock / kWave;
 constexpr int kTMaxSub = SV_TREE_MAX_V / kSub;
-constexpr int kTMaxNS = 2 * kWave;  // chunks per row: at most 128 (V <= 2^20 fp32 is 128 K1 tiles)
+constexpr int kTMaxNS = 2 * kWave;
+constexpr int kTMaxNodesPerLane = SV_TREE_MAX_NODES / kWave;  // children of a position per lane of one wave  // chunks per row: at most 128 (V <= 2^20 fp32 is 128 K1 tiles)
 static_assert(SV_TREE_MAX_NODES <= kTBlock, "one thread per node in the child compaction");
 
 struct TreeShared {
@@ -2657,6 +2658,7 @@ struct TreeShared {
   double W;                   // their sum
   int pick, last;             // selection results
   int path[SV_TREE_MAX_NODES];  // the accepted nodes, in walk order
+  int nchildp;                  // children of the prefetched position
   int wsA[2][kTMaxSub];         // per-wave row statistics (target, draft): M or arg-max,
   float wsB[2][kTMaxSub];       // and s or the maximum (statistics on demand)
 };
@@ -3212,8 +3214,10 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
   // With statistics on demand, the position of the current one's first child
   // (the most likely next) is prefetched while this one is decided: its
   // children, their logits and the row slices.
-  int ppos = -1, nchild_pf = 0;
-  unsigned zc_pf[2][3];
+  // (the children's list, logits and uniforms by the last wave alone, which
+  // holds child j's in lane j % 64, slot j / 64; no workgroup barrier)
+  int ppos = -1;
+  unsigned zc_pf[kTMaxNodesPerLane][3];
   RowSlice<DT> rs_pf;
   int pos = 0, depth = 0;
   for (;;) {
@@ -3231,12 +3235,19 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
     unsigned zc[2][3];
     RowSlice<DT> rs;
     if (pre) {
-      nchild = nchild_pf;
+      nchild = sh.nchildp;
       for (int j = tid; j < nchild; j += kTBlock) sh.child[j] = sh.childp[j];
+      if (wave == kTWaves - 1 && !greedy) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int k = 0; k < 3; ++k) zc[h][k] = zc_pf[h][k];
+        for (int h = 0; h < kTMaxNodesPerLane; ++h) {
+          const int j = lane + h * kWave;
+          if (j < nchild) {
+            sh.czp[j] = bits_value<DT>(zc_pf[h][0]);
+            sh.czq[j] = bits_value<DT>(zc_pf[h][1]);
+            sh.cu[j] = __uint_as_float(zc_pf[h][2]);
+          }
+        }
+      }
       rs = rs_pf;
     } else {
       nchild = children(pos, sh.child);
@@ -3258,7 +3269,7 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int j = jc + h * kGather;
-      if (!greedy && jc >= 0 && j < nchild) {
+      if (!pre && !greedy && jc >= 0 && j < nchild) {
         sh.czp[j] = bits_value<DT>(zc[h][0]);
         sh.czq[j] = bits_value<DT>(zc[h][1]);
         sh.cu[j] = __uint_as_float(zc[h][2]);
@@ -3318,9 +3329,36 @@ __global__ __launch_bounds__(kTBlock) void k_tree_walk(
       if (ppos >= 0) {  // uniform across the team
         const void *tp = target_row(ppos), *dp = draft_row(ppos);
         const bool alp = ((reinterpret_cast<uintptr_t>(tp) | reinterpret_cast<uintptr_t>(dp)) & 15u) == 0;
-        nchild_pf = children(ppos, sh.childp);
-        gather(sh.childp, nchild_pf, tp, dp, zc_pf);
         load_slice(tp, dp, alp, rs_pf);
+        if (wave == kTWaves - 1) {
+          // children of ppos are nodes >= ppos: a wave-level compaction, 64 at a time
+          int n = 0;
+          for (int base = ppos; base < N; base += kWave) {
+            const int t = base + lane;
+            const bool is_child = t < N && sh.parent[t] == ppos - 1;
+            const unsigned long long m = __ballot(is_child);
+            if (is_child) sh.childp[n + __popcll(m & ((1ull << lane) - 1ull))] = t;
+            n += __popcll(m);
+          }
+          if (lane == 0) sh.nchildp = n;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+          for (int h = 0; h < kTMaxNodesPerLane; ++h) {
+            const int j = lane + h * kWave;
+            zc_pf[h][0] = zc_pf[h][1] = 0u;
+            zc_pf[h][2] = __float_as_uint(2.0f);  // 2 rejects
+            if (!greedy && j < n) {
+              const int nd = sh.childp[j], x = sh.token[nd];
+              if (x >= 0 && x < V) {  // an id outside the vocabulary is rejected, never dereferenced
+                zc_pf[h][0] = load_bits<DT>(tp, x);
+                zc_pf[h][1] = load_bits<DT>(dp, x);
+                zc_pf[h][2] = __float_as_uint(u_accept[static_cast<long>(b) * Nmax + nd]);
+              }
+            }
+          }
+        }
       }
     }
     // every child's p(x)/q(x) at once, one exponential each:
