@@ -228,6 +228,65 @@ __device__ __forceinline__ T get(const T *p) {
 
 constexpr unsigned kSpinLimit = 1u << 20;  // polls of a bounded wait (about a second; a correct run needs a few)
 
+// ------------------------------------------------------------------ wave reductions
+// fp64 wave scan / sum with DPP row shifts and row broadcasts (no LDS round
+// trip).  Lanes without a source read 0, the identity of the sum.  Called with
+// the whole wave active.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const long long bits = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), CTRL, ROW_MASK, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), CTRL, ROW_MASK, 0xf, true);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
+// inclusive prefix over the 64 lanes of a wave
+__device__ __forceinline__ double wave_scan(double v, int /*lane*/) {
+  v += dpp_f64<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_f64<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_f64<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_f64<0x118, 0xf>(v);  // row_shr:8   (each row of 16 now holds its own prefix)
+  v += dpp_f64<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f64<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+__device__ __forceinline__ double lane_value(double v, int lane) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(bits), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(bits >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
+// sum over the wave, the same value in every lane
+__device__ __forceinline__ double wave_sum(double v) { return lane_value(wave_scan(v, 0), kWave - 1); }
+
+// maximum over the wave, the same value in every lane (lanes without a DPP
+// source keep -inf, the identity)
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x111, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x112, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x114, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x118, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x142, 0xa, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+// integer maximum / minimum over the wave, the same value in every lane
+template <bool MAX>
+__device__ __forceinline__ int wave_ext_i32(int v) {
+  constexpr int id = MAX ? INT_MIN : INT_MAX;
+  auto f = [](int x, int y) { return MAX ? (x > y ? x : y) : (x < y ? x : y); };
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xf, 0xf, false));
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xf, 0xf, false));
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xf, 0xf, false));
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xf, 0xf, false));
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xa, 0xf, false));
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
 // ================================================================== K1
 // Rows of request b: r in [0, gamma] are target rows, r in [gamma+1, 2 gamma]
 // are draft rows r - gamma - 1.  A row is needed if it is a target row i <= g_b,
@@ -539,17 +598,15 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
       const float z = load_one<DT>(row, e);
       fold_values<1>(&z, c, M, s, mx);
     }
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off /= 2) {
-      const int Mo = __shfl_xor(M, off);
-      const double so = __shfl_xor(s, off);
-      const float mo = __shfl_xor(mx, off);
-      merge_sm(M, s, mx, Mo, so, mo);
-    }
+    // the wave's lanes merged with DPP: the largest M, every lane's sum
+    // rescaled to it by an exact power of two, one fp64 sum
+    const int Mw = wave_ext_i32<true>(M);
+    const double sw = wave_sum(ldexp(s, M - Mw));
+    const float mw = wave_max_f32(mx);
     if (lane == 0) {
-      sh_s[wave] = s;
-      sh_mx[wave] = mx;
-      sh_mi[wave] = M;
+      sh_s[wave] = sw;
+      sh_mx[wave] = mw;
+      sh_mi[wave] = Mw;
     }
     __syncthreads();
     if (tid == 0) {
@@ -571,15 +628,12 @@ __global__ __launch_bounds__(kBlock) void k1_row_stats(
         bi = static_cast<int>(e);
       }
     }
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off /= 2) {
-      const float vo = __shfl_xor(bv, off);
-      const int io = __shfl_xor(bi, off);
-      merge_arg(bv, bi, vo, io);
-    }
+    // the wave's maximum, then the lowest index holding it (DPP)
+    const float vw = wave_max_f32(bv);
+    const int iw = wave_ext_i32<false>(bv == vw ? bi : INT_MAX);
     if (lane == 0) {
-      sh_mx[wave] = bv;
-      sh_mi[wave] = bi;
+      sh_mx[wave] = vw;
+      sh_mi[wave] = iw;
     }
     __syncthreads();
     if (tid == 0) {
@@ -923,64 +977,6 @@ __device__ __forceinline__ void load_lane32(const void *row, bool aligned, long 
       for (int e = 0; e < kV; ++e) idx[u * kV + e] = static_cast<int>(e0 + e);
     }
   }
-}
-
-// fp64 wave scan / sum with DPP row shifts and row broadcasts (no LDS round
-// trip).  Lanes without a source read 0, the identity of the sum.  Called with
-// the whole wave active.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const long long bits = __double_as_longlong(x);
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), CTRL, ROW_MASK, 0xf, true);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), CTRL, ROW_MASK, 0xf, true);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
-}
-
-// inclusive prefix over the 64 lanes of a wave
-__device__ __forceinline__ double wave_scan(double v, int /*lane*/) {
-  v += dpp_f64<0x111, 0xf>(v);  // row_shr:1
-  v += dpp_f64<0x112, 0xf>(v);  // row_shr:2
-  v += dpp_f64<0x114, 0xf>(v);  // row_shr:4
-  v += dpp_f64<0x118, 0xf>(v);  // row_shr:8   (each row of 16 now holds its own prefix)
-  v += dpp_f64<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
-  v += dpp_f64<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
-  return v;
-}
-
-__device__ __forceinline__ double lane_value(double v, int lane) {
-  const long long bits = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane(static_cast<int>(bits), lane);
-  const int hi = __builtin_amdgcn_readlane(static_cast<int>(bits >> 32), lane);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
-}
-
-// sum over the wave, the same value in every lane
-__device__ __forceinline__ double wave_sum(double v) { return lane_value(wave_scan(v, 0), kWave - 1); }
-
-// maximum over the wave, the same value in every lane (lanes without a DPP
-// source keep -inf, the identity)
-__device__ __forceinline__ float wave_max_f32(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x111, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x112, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x114, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x118, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x142, 0xa, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), 0x143, 0xc, 0xf, false)));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
-}
-
-// integer maximum / minimum over the wave, the same value in every lane
-template <bool MAX>
-__device__ __forceinline__ int wave_ext_i32(int v) {
-  constexpr int id = MAX ? INT_MIN : INT_MAX;
-  auto f = [](int x, int y) { return MAX ? (x > y ? x : y) : (x < y ? x : y); };
-  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xf, 0xf, false));
-  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xf, 0xf, false));
-  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xf, 0xf, false));
-  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xf, 0xf, false));
-  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xa, 0xf, false));
-  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xc, 0xf, false));
-  return __builtin_amdgcn_readlane(v, kWave - 1);
 }
 
 struct RowPair {
