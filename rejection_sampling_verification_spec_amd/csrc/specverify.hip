@@ -3850,15 +3850,10 @@ __global__ __launch_bounds__(kSBlock) void k_sample_stats(const void *__restrict
           }
         }
       }
-#pragma unroll
-      for (int off = kWave / 2; off >= 1; off /= 2) {
-        const float vo = __shfl_xor(bv, off);
-        const int io = __shfl_xor(bi, off);
-        merge_arg(bv, bi, vo, io);
-      }
+      const float vw = wave_max_f32(bv);  // then the lowest index holding it (DPP)
       rc.s = 0.0;
-      rc.mx = bv;
-      rc.mi = bi;
+      rc.mx = vw;
+      rc.mi = wave_ext_i32<false>(bv == vw ? bi : INT_MAX);
     }
     if (lane == 0) rec[static_cast<long>(r) * NSUB + sub] = rc;
   }
@@ -3883,20 +3878,15 @@ __global__ __launch_bounds__(kWave) void k_sample_pick(const void *__restrict__ 
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     for (int j = lane; j < NSUB; j += kWave) merge_arg(bv, bi, rr[j].mx, rr[j].mi);
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off /= 2) {
-      const float vo = __shfl_xor(bv, off);
-      const int io = __shfl_xor(bi, off);
-      merge_arg(bv, bi, vo, io);
-    }
-    if (lane == 0) tokens[r] = bi;
+    const float vw = wave_max_f32(bv);  // then the lowest index holding it (DPP)
+    const int iw = wave_ext_i32<false>(bv == vw ? bi : INT_MAX);
+    if (lane == 0) tokens[r] = iw;
     return;
   }
   // the row's reference exponent and the sub-chunk masses m_j = s_j 2^(M_j - M)
   int M = kEmptyM;
   for (int j = lane; j < NSUB; j += kWave) M = max(M, rr[j].mi);
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off /= 2) M = max(M, __shfl_xor(M, off));
+  M = wave_ext_i32<true>(M);
   auto mass = [&](int j) { return j < NSUB ? ldexp(rr[j].s, rr[j].mi - M) : 0.0; };
   double Z = 0.0;
   for (int base = 0; base < NSUB; base += kWave) Z += wave_sum(mass(base + lane));
